@@ -1,0 +1,527 @@
+// C ABI of the forward pass (declared in include/fs.h): model state, argument
+// validation and the order of kernel launches for prefill and decode.
+//
+// Forward pass ("Coming back to Failed Star", Second sitting, data-flow
+// figure; "Milestones", M2): ids -> embedding -> per block [RMSNorm, QKV,
+// q/k RMSNorm + RoPE, GQA attention, output projection + residual, RMSNorm,
+// SwiGLU MLP + residual] -> final RMSNorm of the last row -> tied head.
+// KV-cached decode ("Milestones", M4) appends one position per step.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/fs.h"
+#include "kernels.h"
+
+using namespace fsk;
+
+namespace {
+
+thread_local std::string g_err;
+
+fs_status fail(fs_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                     \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return fail(FS_ERR_HIP, std::string(#expr) + " failed: " + hipGetErrorString(e_)); \
+  } while (0)
+
+// Up to this many rows per call the projections run as GEMV (weights streamed
+// once, fp32 activations); above it as MFMA GEMM on bf16 activations.
+constexpr int SKINNY_MAX_ROWS = GEMV_LOGITS_MAX_M;
+constexpr int STAGE_RING = 64;
+
+struct LayerW {
+  void *wqkv, *wo, *wgu, *wdown;
+  float *attn_norm, *q_norm, *k_norm, *mlp_norm;
+};
+
+template <class T>
+hipError_t dalloc(T** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) return hipSuccess;
+  return hipMalloc(reinterpret_cast<void**>(p), bytes);
+}
+
+}  // namespace
+
+struct fs_model {
+  fs_config cfg{};
+  int device = 0;
+  int dt = 0;
+  size_t esz = 0;
+  int qkv_w = 0, qw = 0, kvw = 0;
+  // weights
+  void* wblob = nullptr;
+  float* nblob = nullptr;
+  void* embed = nullptr;
+  float* final_norm = nullptr;
+  std::vector<LayerW> layers;
+  // KV cache [layer][slot][kv_head][pos][d]
+  void* kcache = nullptr;
+  void* vcache = nullptr;
+  long long head_stride = 0, slot_stride = 0, layer_stride = 0;
+  float *rope_cos = nullptr, *rope_sin = nullptr;
+  std::vector<int32_t> slot_len;
+  // activation scratch, grown on demand
+  long long scratch_rows = 0;
+  float* x = nullptr;
+  void* xn = nullptr;
+  void* qkv = nullptr;
+  void* qr = nullptr;
+  void* attn = nullptr;
+  void* hbuf = nullptr;
+  // decode scratch
+  int32_t* d_pos = nullptr;
+  int32_t* d_slot = nullptr;
+  float* part = nullptr;
+  int max_chunks = 0;
+  uint32_t* counters = nullptr;   // [max_seqs * nkv] attention + 1 lm_head
+  float* lm_pv = nullptr;
+  int32_t* lm_pi = nullptr;
+  float* logits_tmp = nullptr;    // [max_seqs, V] when the caller passes none
+  // pinned staging of per-call host arrays
+  int32_t* stage = nullptr;       // [STAGE_RING][2 * max_seqs]
+  hipEvent_t stage_ev[STAGE_RING] = {};
+  bool stage_used[STAGE_RING] = {};
+  int stage_next = 0;
+
+  ~fs_model() {
+    hipDeviceSynchronize();
+    hipFree(wblob); hipFree(nblob); hipFree(kcache); hipFree(vcache);
+    hipFree(rope_cos); hipFree(rope_sin);
+    hipFree(x); hipFree(xn); hipFree(qkv); hipFree(qr); hipFree(attn); hipFree(hbuf);
+    hipFree(d_pos); hipFree(d_slot); hipFree(part); hipFree(counters);
+    hipFree(lm_pv); hipFree(lm_pi); hipFree(logits_tmp);
+    for (int i = 0; i < STAGE_RING; ++i)
+      if (stage_ev[i]) hipEventDestroy(stage_ev[i]);
+    if (stage) hipHostFree(stage);
+  }
+};
+
+namespace {
+
+fs_status ensure_rows(fs_model* m, long long rows, hipStream_t s) {
+  if (rows <= m->scratch_rows) return FS_OK;
+  HIP_TRY(hipStreamSynchronize(s));
+  hipFree(m->x); hipFree(m->xn); hipFree(m->qkv); hipFree(m->qr); hipFree(m->attn); hipFree(m->hbuf);
+  m->x = nullptr; m->xn = m->qkv = m->qr = m->attn = m->hbuf = nullptr;
+  m->scratch_rows = 0;
+  const fs_config& c = m->cfg;
+  const size_t R = (size_t)rows;
+  // fp32-sized buffers so either activation dtype fits
+  if (dalloc(&m->x, R * c.hidden * 4) != hipSuccess || dalloc(&m->xn, R * c.hidden * 4) != hipSuccess ||
+      dalloc(&m->qkv, R * m->qkv_w * 4) != hipSuccess || dalloc(&m->qr, R * m->qw * 4) != hipSuccess ||
+      dalloc(&m->attn, R * m->qw * 4) != hipSuccess || dalloc(&m->hbuf, R * c.ffn * 4) != hipSuccess)
+    return fail(FS_ERR_OOM, "activation scratch allocation failed");
+  m->scratch_rows = rows;
+  return FS_OK;
+}
+
+// Copies two host int arrays [n] to d_pos / d_slot through the pinned ring.
+fs_status stage_ints(fs_model* m, const int32_t* a, const int32_t* b, int n, hipStream_t s) {
+  const int i = m->stage_next;
+  m->stage_next = (i + 1) % STAGE_RING;
+  if (m->stage_used[i]) HIP_TRY(hipEventSynchronize(m->stage_ev[i]));
+  int32_t* buf = m->stage + (size_t)i * 2 * m->cfg.max_seqs;
+  if (a) std::memcpy(buf, a, sizeof(int32_t) * n);
+  std::memcpy(buf + m->cfg.max_seqs, b, sizeof(int32_t) * n);
+  if (a) HIP_TRY(hipMemcpyAsync(m->d_pos, buf, sizeof(int32_t) * n, hipMemcpyHostToDevice, s));
+  HIP_TRY(hipMemcpyAsync(m->d_slot, buf + m->cfg.max_seqs, sizeof(int32_t) * n, hipMemcpyHostToDevice, s));
+  HIP_TRY(hipEventRecord(m->stage_ev[i], s));
+  m->stage_used[i] = true;
+  return FS_OK;
+}
+
+fs_status check_slots(const fs_model* m, const int32_t* slots, int B) {
+  std::vector<char> seen(m->cfg.max_seqs, 0);
+  for (int i = 0; i < B; ++i) {
+    const int s = slots[i];
+    if (s < 0 || s >= m->cfg.max_seqs)
+      return fail(FS_ERR_INVALID_ARG, "slot " + std::to_string(s) + " out of range");
+    if (seen[s]) return fail(FS_ERR_INVALID_ARG, "slot " + std::to_string(s) + " repeated in one call");
+    seen[s] = 1;
+  }
+  return FS_OK;
+}
+
+int cpl_ok(int K) { return K % 8 == 0 && K <= 4096; }
+
+// Final RMSNorm of `rows` rows of x at stride ldx, tied head E . h, and
+// optionally the greedy IDs.  logits may be null only when `next` is set.
+fs_status head(fs_model* m, const float* xrows, int rows, int ldx, float* logits, int32_t* next,
+               hipStream_t s) {
+  const fs_config& c = m->cfg;
+  if (rows <= GEMV_LOGITS_MAX_M) {
+    GemvParams p{};
+    p.w = m->embed; p.N = c.vocab; p.K = c.hidden;
+    p.a = xrows; p.lda = ldx; p.M = rows;
+    p.gamma = m->final_norm; p.eps = c.rms_eps;
+    p.logits = logits; p.ldo = c.vocab; p.next = next;
+    p.part_val = m->lm_pv; p.part_idx = m->lm_pi;
+    p.counter = m->counters + (size_t)c.max_seqs * c.n_kv_heads;
+    HIP_TRY(gemv(m->dt, EPI_LOGITS, p, s));
+    return FS_OK;
+  }
+  float* lg = logits;
+  if (lg == nullptr) {
+    if (m->logits_tmp == nullptr &&
+        dalloc(&m->logits_tmp, (size_t)c.max_seqs * c.vocab * sizeof(float)) != hipSuccess)
+      return fail(FS_ERR_OOM, "logits scratch allocation failed");
+    lg = m->logits_tmp;
+  }
+  if (m->dt == DT_BF16) {
+    HIP_TRY(rmsnorm(xrows, rows, c.hidden, ldx, m->final_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s));
+    HIP_TRY(gemm_bf16(GEPI_STORE_F32, m->xn, c.hidden, m->embed, c.hidden, lg, c.vocab, rows, c.vocab,
+                      c.hidden, s));
+  } else {
+    GemvParams p{};
+    p.w = m->embed; p.N = c.vocab; p.K = c.hidden;
+    p.a = xrows; p.lda = ldx; p.M = rows;
+    p.gamma = m->final_norm; p.eps = c.rms_eps;
+    p.out = lg; p.ldo = c.vocab;
+    HIP_TRY(gemv(m->dt, EPI_STORE, p, s));
+  }
+  if (next) HIP_TRY(argmax_rows(lg, rows, c.vocab, c.vocab, next, s));
+  return FS_OK;
+}
+
+// One transformer block over `rows` activation rows in the skinny (GEMV) form.
+// attention: a callable that consumes m->qkv (fp32) and fills m->attn (fp32).
+template <class Attn>
+fs_status block_skinny(fs_model* m, const LayerW& L, int rows, Attn&& attention, hipStream_t s) {
+  const fs_config& c = m->cfg;
+  GemvParams p{};
+  p.eps = c.rms_eps;
+  // Q/K/V projection with the input RMSNorm fused in
+  p.w = L.wqkv; p.N = m->qkv_w; p.K = c.hidden;
+  p.a = m->x; p.lda = c.hidden; p.M = rows; p.gamma = L.attn_norm;
+  p.out = (float*)m->qkv; p.ldo = m->qkv_w;
+  HIP_TRY(gemv(m->dt, EPI_STORE, p, s));
+  fs_status st = attention();
+  if (st != FS_OK) return st;
+  // output projection + residual
+  p.w = L.wo; p.N = c.hidden; p.K = m->qw;
+  p.a = (const float*)m->attn; p.lda = m->qw; p.gamma = nullptr;
+  p.out = m->x; p.ldo = c.hidden;
+  HIP_TRY(gemv(m->dt, EPI_RESID, p, s));
+  // RMSNorm + gate/up + SwiGLU
+  p.w = L.wgu; p.N = c.ffn; p.K = c.hidden;
+  p.a = m->x; p.lda = c.hidden; p.gamma = L.mlp_norm;
+  p.out = (float*)m->hbuf; p.ldo = c.ffn;
+  HIP_TRY(gemv(m->dt, EPI_SWIGLU, p, s));
+  // down projection + residual
+  p.w = L.wdown; p.N = c.hidden; p.K = c.ffn;
+  p.a = (const float*)m->hbuf; p.lda = c.ffn; p.gamma = nullptr;
+  p.out = m->x; p.ldo = c.hidden;
+  HIP_TRY(gemv(m->dt, EPI_RESID, p, s));
+  return FS_OK;
+}
+
+// One transformer block over `rows` rows in the GEMM (MFMA, bf16) form.
+// qkv_f32: the QKV projection is stored fp32 (decode attention) or bf16 (prefill).
+template <class Attn>
+fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&& attention,
+                     hipStream_t s) {
+  const fs_config& c = m->cfg;
+  // The attention input keeps ~16 significant bits (bf16 value + bf16 remainder):
+  // rounding it to bf16 alone moves the logits by about as much as the whole
+  // error budget, while the MLP input tolerates plain bf16.
+  void* xn_lo = (char*)m->xn + (size_t)rows * c.hidden * 2;
+  HIP_TRY(rmsnorm(m->x, rows, c.hidden, c.hidden, L.attn_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s, xn_lo));
+  HIP_TRY(gemm_bf16(qkv_f32 ? GEPI_STORE_F32 : GEPI_STORE_BF16, m->xn, c.hidden, L.wqkv, c.hidden,
+                    m->qkv, m->qkv_w, rows, m->qkv_w, c.hidden, s, xn_lo));
+  fs_status st = attention();
+  if (st != FS_OK) return st;
+  HIP_TRY(gemm_bf16(GEPI_RESID_F32, m->attn, m->qw, L.wo, m->qw, m->x, c.hidden, rows, c.hidden, m->qw, s));
+  HIP_TRY(rmsnorm(m->x, rows, c.hidden, c.hidden, L.mlp_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s));
+  HIP_TRY(gemm_bf16(GEPI_SWIGLU_BF16, m->xn, c.hidden, L.wgu, c.hidden, m->hbuf, c.ffn, rows, 2 * c.ffn,
+                    c.hidden, s));
+  HIP_TRY(gemm_bf16(GEPI_RESID_F32, m->hbuf, c.ffn, L.wdown, c.ffn, m->x, c.hidden, rows, c.hidden, c.ffn, s));
+  return FS_OK;
+}
+
+}  // namespace
+
+// ===================================================================== C ABI
+extern "C" {
+
+const char* fs_last_error(void) { return g_err.c_str(); }
+
+fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* stream, fs_model** out) {
+  g_err.clear();
+  if (out == nullptr) return fail(FS_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (cfg == nullptr || w == nullptr) return fail(FS_ERR_INVALID_ARG, "cfg or weights is NULL");
+  const fs_config c = *cfg;
+  if (c.dtype != FS_F32 && c.dtype != FS_BF16) return fail(FS_ERR_UNSUPPORTED, "unknown dtype");
+  if (c.n_layers < 0 || c.hidden <= 0 || c.n_heads <= 0 || c.n_kv_heads <= 0 || c.head_dim <= 0 ||
+      c.ffn <= 0 || c.vocab <= 0 || c.max_seqs <= 0 || c.max_ctx <= 0)
+    return fail(FS_ERR_INVALID_ARG, "non-positive size in config");
+  if (c.n_heads % c.n_kv_heads != 0) return fail(FS_ERR_INVALID_ARG, "n_heads % n_kv_heads != 0");
+  const int rep = c.n_heads / c.n_kv_heads;
+  if (rep != 1 && rep != 2 && rep != 4 && rep != 8)
+    return fail(FS_ERR_UNSUPPORTED, "n_heads / n_kv_heads must be 1, 2, 4 or 8");
+  if (c.head_dim != 64 && c.head_dim != 128) return fail(FS_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c.hidden % 64 != 0 || c.ffn % 64 != 0)
+    return fail(FS_ERR_UNSUPPORTED, "hidden and ffn must be multiples of 64");
+  if (!cpl_ok(c.hidden) || !cpl_ok(c.ffn) || !cpl_ok(c.n_heads * c.head_dim))
+    return fail(FS_ERR_UNSUPPORTED, "hidden, ffn and n_heads*head_dim must be <= 4096");
+  if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return fail(FS_ERR_INVALID_ARG, "bad rms_eps or rope_theta");
+  if (w->embed == nullptr || w->final_norm == nullptr || (c.n_layers > 0 && w->layers == nullptr))
+    return fail(FS_ERR_INVALID_ARG, "NULL weight pointer");
+  for (int l = 0; l < c.n_layers; ++l) {
+    const fs_layer_weights& L = w->layers[l];
+    const void* ps[] = {L.attn_norm, L.wq, L.wk, L.wv, L.q_norm, L.k_norm, L.wo, L.mlp_norm, L.w_gate, L.w_up, L.w_down};
+    for (const void* p : ps)
+      if (p == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL weight pointer in layer " + std::to_string(l));
+  }
+  hipStream_t s = (hipStream_t)stream;
+  int device = 0;
+  HIP_TRY(hipGetDevice(&device));
+  fs_model* m = new fs_model();
+  m->cfg = c;
+  m->device = device;
+  m->dt = c.dtype;
+  m->esz = dt_size(c.dtype);
+  m->qw = c.n_heads * c.head_dim;
+  m->kvw = c.n_kv_heads * c.head_dim;
+  m->qkv_w = m->qw + 2 * m->kvw;
+  const size_t H = c.hidden, I = c.ffn, V = c.vocab, es = m->esz;
+  const size_t per_layer = ((size_t)m->qkv_w * H + H * m->qw + 2 * I * H + H * I) * es;
+  const size_t wbytes = V * H * es + per_layer * c.n_layers;
+  const size_t nfloats = H + (size_t)c.n_layers * (2 * H + 2 * c.head_dim);
+  auto bail = [&](fs_status st, const std::string& msg) {
+    delete m;
+    return fail(st, msg);
+  };
+  if (dalloc(&m->wblob, wbytes) != hipSuccess) return bail(FS_ERR_OOM, "weight allocation failed");
+  if (dalloc(&m->nblob, nfloats * 4) != hipSuccess) return bail(FS_ERR_OOM, "norm allocation failed");
+  char* wp = (char*)m->wblob;
+  float* np = m->nblob;
+  hipError_t e = hipSuccess;
+  auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+  m->embed = wp; wp += V * H * es;
+  chk(hipMemcpyAsync(m->embed, w->embed, V * H * es, hipMemcpyDeviceToDevice, s));
+  m->final_norm = np; np += H;
+  chk(convert_f32(w->final_norm, m->dt, m->final_norm, H, s));
+  m->layers.resize(c.n_layers);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const fs_layer_weights& src = w->layers[l];
+    LayerW& L = m->layers[l];
+    L.wqkv = wp; wp += (size_t)m->qkv_w * H * es;
+    chk(hipMemcpyAsync(L.wqkv, src.wq, (size_t)m->qw * H * es, hipMemcpyDeviceToDevice, s));
+    chk(hipMemcpyAsync((char*)L.wqkv + (size_t)m->qw * H * es, src.wk, (size_t)m->kvw * H * es,
+                       hipMemcpyDeviceToDevice, s));
+    chk(hipMemcpyAsync((char*)L.wqkv + (size_t)(m->qw + m->kvw) * H * es, src.wv, (size_t)m->kvw * H * es,
+                       hipMemcpyDeviceToDevice, s));
+    L.wo = wp; wp += H * m->qw * es;
+    chk(hipMemcpyAsync(L.wo, src.wo, H * m->qw * es, hipMemcpyDeviceToDevice, s));
+    L.wgu = wp; wp += 2 * I * H * es;
+    chk(pack_gate_up(src.w_gate, src.w_up, m->dt, (int)I, (int)H, L.wgu, s));
+    L.wdown = wp; wp += H * I * es;
+    chk(hipMemcpyAsync(L.wdown, src.w_down, H * I * es, hipMemcpyDeviceToDevice, s));
+    L.attn_norm = np; np += H;
+    L.mlp_norm = np; np += H;
+    L.q_norm = np; np += c.head_dim;
+    L.k_norm = np; np += c.head_dim;
+    chk(convert_f32(src.attn_norm, m->dt, L.attn_norm, H, s));
+    chk(convert_f32(src.mlp_norm, m->dt, L.mlp_norm, H, s));
+    chk(convert_f32(src.q_norm, m->dt, L.q_norm, c.head_dim, s));
+    chk(convert_f32(src.k_norm, m->dt, L.k_norm, c.head_dim, s));
+  }
+  if (e != hipSuccess) return bail(FS_ERR_HIP, std::string("weight repack failed: ") + hipGetErrorString(e));
+
+  // KV cache
+  m->head_stride = (long long)c.max_ctx * c.head_dim;
+  m->slot_stride = m->head_stride * c.n_kv_heads;
+  m->layer_stride = m->slot_stride * c.max_seqs;
+  const size_t kvbytes = (size_t)m->layer_stride * std::max(c.n_layers, 1) * es;
+  if (dalloc(&m->kcache, kvbytes) != hipSuccess || dalloc(&m->vcache, kvbytes) != hipSuccess)
+    return bail(FS_ERR_OOM, "KV cache allocation failed");
+
+  // RoPE tables: angle p * theta^(-2i/d) in double, cos/sin stored as fp32
+  const int half = c.head_dim / 2;
+  std::vector<float> hc((size_t)c.max_ctx * half), hs((size_t)c.max_ctx * half);
+  for (int p = 0; p < c.max_ctx; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)p * std::pow((double)c.rope_theta, -2.0 * i / (double)c.head_dim);
+      hc[(size_t)p * half + i] = (float)std::cos(ang);
+      hs[(size_t)p * half + i] = (float)std::sin(ang);
+    }
+  if (dalloc(&m->rope_cos, hc.size() * 4) != hipSuccess || dalloc(&m->rope_sin, hs.size() * 4) != hipSuccess)
+    return bail(FS_ERR_OOM, "RoPE table allocation failed");
+  chk(hipMemcpyAsync(m->rope_cos, hc.data(), hc.size() * 4, hipMemcpyHostToDevice, s));
+  chk(hipMemcpyAsync(m->rope_sin, hs.data(), hs.size() * 4, hipMemcpyHostToDevice, s));
+
+  // decode scratch
+  m->max_chunks = (c.max_ctx + 31) / 32;
+  const int lm_blocks = gemv_logits_blocks(c.vocab, c.hidden);
+  if (dalloc(&m->d_pos, (size_t)c.max_seqs * 4) != hipSuccess ||
+      dalloc(&m->d_slot, (size_t)c.max_seqs * 4) != hipSuccess ||
+      dalloc(&m->part, (size_t)c.max_seqs * c.n_heads * m->max_chunks * (c.head_dim + 2) * 4) != hipSuccess ||
+      dalloc(&m->counters, ((size_t)c.max_seqs * c.n_kv_heads + 1) * 4) != hipSuccess ||
+      dalloc(&m->lm_pv, (size_t)GEMV_LOGITS_MAX_M * lm_blocks * 4) != hipSuccess ||
+      dalloc(&m->lm_pi, (size_t)GEMV_LOGITS_MAX_M * lm_blocks * 4) != hipSuccess)
+    return bail(FS_ERR_OOM, "decode scratch allocation failed");
+  chk(hipMemsetAsync(m->counters, 0, ((size_t)c.max_seqs * c.n_kv_heads + 1) * 4, s));
+  if (hipHostMalloc((void**)&m->stage, sizeof(int32_t) * 2 * c.max_seqs * STAGE_RING, hipHostMallocDefault) !=
+      hipSuccess)
+    return bail(FS_ERR_OOM, "pinned staging allocation failed");
+  for (int i = 0; i < STAGE_RING; ++i) chk(hipEventCreateWithFlags(&m->stage_ev[i], hipEventDisableTiming));
+  chk(hipStreamSynchronize(s));
+  if (e != hipSuccess) return bail(FS_ERR_HIP, std::string("model setup failed: ") + hipGetErrorString(e));
+  m->slot_len.assign(c.max_seqs, 0);
+  *out = m;
+  return FS_OK;
+}
+
+void fs_model_destroy(fs_model* m) { delete m; }
+
+int32_t fs_slot_length(const fs_model* m, int32_t slot) {
+  if (m == nullptr || slot < 0 || slot >= m->cfg.max_seqs) return -1;
+  return m->slot_len[slot];
+}
+
+fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, const int32_t* slots,
+                     float* logits, void* stream) {
+  g_err.clear();
+  if (m == nullptr || tokens == nullptr || slots == nullptr || logits == nullptr)
+    return fail(FS_ERR_INVALID_ARG, "NULL argument");
+  const fs_config& c = m->cfg;
+  if (B <= 0 || B > c.max_seqs) return fail(FS_ERR_INVALID_ARG, "B out of range");
+  if (S <= 0) return fail(FS_ERR_INVALID_ARG, "empty prompt (S <= 0)");
+  if (S > c.max_ctx) return fail(FS_ERR_CAPACITY, "prompt longer than max_ctx");
+  fs_status st = check_slots(m, slots, B);
+  if (st != FS_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const long long T = (long long)B * S;
+  if (T > (1LL << 31) / std::max(m->qkv_w, c.ffn)) return fail(FS_ERR_UNSUPPORTED, "B*S too large");
+  if ((st = ensure_rows(m, T, s)) != FS_OK) return st;
+  if ((st = stage_ints(m, nullptr, slots, B, s)) != FS_OK) return st;
+  HIP_TRY(embed(m->embed, m->dt, tokens, (int)T, c.hidden, c.vocab, m->x, s));
+  const bool skinny = (m->dt == DT_F32) || T <= SKINNY_MAX_ROWS;
+  const int act_dt = skinny ? DT_F32 : DT_BF16;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& L = m->layers[l];
+    char* kc = (char*)m->kcache + (size_t)l * m->layer_stride * m->esz;
+    char* vc = (char*)m->vcache + (size_t)l * m->layer_stride * m->esz;
+    auto attention = [&]() -> fs_status {
+      RopeKvParams r{};
+      r.qkv = m->qkv; r.in_dt = act_dt; r.qout = m->qr; r.q_dt = act_dt;
+      r.kcache = kc; r.vcache = vc; r.kv_dt = m->dt;
+      r.gq = L.q_norm; r.gk = L.k_norm; r.eps = c.rms_eps;
+      r.cos_t = m->rope_cos; r.sin_t = m->rope_sin; r.slots = m->d_slot;
+      r.T = (int)T; r.S_per = S; r.nq = c.n_heads; r.nkv = c.n_kv_heads; r.d = c.head_dim;
+      r.slot_stride = m->slot_stride; r.head_stride = m->head_stride;
+      HIP_TRY(rope_kv(r, s));
+      AttnPrefillParams a{};
+      a.q = m->qr; a.q_dt = act_dt; a.kcache = kc; a.vcache = vc; a.kv_dt = m->dt;
+      a.out = m->attn; a.o_dt = act_dt; a.slots = m->d_slot;
+      a.B = B; a.S = S; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim;
+      a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
+      a.scale = 1.0f / std::sqrt((float)c.head_dim);
+      HIP_TRY(skinny ? attn_prefill_vec(a, s) : attn_prefill(a, s));
+      return FS_OK;
+    };
+    st = skinny ? block_skinny(m, L, (int)T, attention, s) : block_gemm(m, L, (int)T, false, attention, s);
+    if (st != FS_OK) return st;
+  }
+  // last row of each sequence: rows b*S + S-1
+  st = head(m, m->x + (size_t)(S - 1) * c.hidden, B, S * c.hidden, logits, nullptr, s);
+  if (st != FS_OK) return st;
+  for (int b = 0; b < B; ++b) m->slot_len[slots[b]] = S;
+  return FS_OK;
+}
+
+fs_status fs_decode_step(fs_model* m, const int32_t* tokens, const int32_t* positions, const int32_t* slots,
+                         int32_t B, float* logits, int32_t* next, void* stream) {
+  g_err.clear();
+  if (m == nullptr || tokens == nullptr || positions == nullptr || slots == nullptr)
+    return fail(FS_ERR_INVALID_ARG, "NULL argument");
+  if (logits == nullptr && next == nullptr) return fail(FS_ERR_INVALID_ARG, "logits and next are both NULL");
+  const fs_config& c = m->cfg;
+  if (B <= 0 || B > c.max_seqs) return fail(FS_ERR_INVALID_ARG, "B out of range");
+  fs_status st = check_slots(m, slots, B);
+  if (st != FS_OK) return st;
+  int maxn = 0;
+  for (int i = 0; i < B; ++i) {
+    if (positions[i] != m->slot_len[slots[i]])
+      return fail(FS_ERR_INVALID_ARG, "position " + std::to_string(positions[i]) + " != length " +
+                                          std::to_string(m->slot_len[slots[i]]) + " of slot " +
+                                          std::to_string(slots[i]));
+    if (positions[i] >= c.max_ctx) return fail(FS_ERR_CAPACITY, "context exhausted (position >= max_ctx)");
+    maxn = std::max(maxn, positions[i] + 1);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = ensure_rows(m, B, s)) != FS_OK) return st;
+  if ((st = stage_ints(m, positions, slots, B, s)) != FS_OK) return st;
+  // split-K chunking of the context: enough workgroups to cover the chip
+  int chunk = 32;
+  while (chunk < 256 && (long long)((maxn + chunk - 1) / chunk) * c.n_kv_heads * B > 1024) chunk *= 2;
+  const int nchunks = (maxn + chunk - 1) / chunk;
+  if (nchunks > m->max_chunks) return fail(FS_ERR_HIP, "internal: chunk count exceeds scratch");
+  HIP_TRY(embed(m->embed, m->dt, tokens, B, c.hidden, c.vocab, m->x, s));
+  const bool skinny = (m->dt == DT_F32) || B <= SKINNY_MAX_ROWS;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& L = m->layers[l];
+    char* kc = (char*)m->kcache + (size_t)l * m->layer_stride * m->esz;
+    char* vc = (char*)m->vcache + (size_t)l * m->layer_stride * m->esz;
+    auto attention = [&]() -> fs_status {
+      AttnDecodeParams a{};
+      a.qkv = (const float*)m->qkv; a.kcache = kc; a.vcache = vc; a.kv_dt = m->dt;
+      a.gq = L.q_norm; a.gk = L.k_norm; a.eps = c.rms_eps;
+      a.cos_t = m->rope_cos; a.sin_t = m->rope_sin; a.positions = m->d_pos; a.slots = m->d_slot;
+      a.out = m->attn; a.o_dt = skinny ? DT_F32 : DT_BF16;
+      a.part = m->part; a.counters = m->counters;
+      a.B = B; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim; a.chunk = chunk; a.nchunks = nchunks;
+      a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
+      a.scale = 1.0f / std::sqrt((float)c.head_dim);
+      HIP_TRY(attn_decode(a, s));
+      return FS_OK;
+    };
+    st = skinny ? block_skinny(m, L, B, attention, s) : block_gemm(m, L, B, true, attention, s);
+    if (st != FS_OK) return st;
+  }
+  st = head(m, m->x, B, c.hidden, logits, next, s);
+  if (st != FS_OK) return st;
+  for (int i = 0; i < B; ++i) m->slot_len[slots[i]] = positions[i] + 1;
+  return FS_OK;
+}
+
+fs_status fs_argmax(const float* logits, int32_t B, int32_t V, int32_t* out, void* stream) {
+  g_err.clear();
+  if (logits == nullptr || out == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+  if (B <= 0 || V <= 0) return fail(FS_ERR_INVALID_ARG, "B and V must be positive");
+  HIP_TRY(argmax_rows(logits, B, V, V, out, (hipStream_t)stream));
+  return FS_OK;
+}
+
+fs_status fs_kv_read(const fs_model* m, int32_t layer, int32_t slot, int32_t kv_head, int32_t pos0, int32_t n,
+                     void* k_out, void* v_out, void* stream) {
+  g_err.clear();
+  if (m == nullptr || k_out == nullptr || v_out == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+  const fs_config& c = m->cfg;
+  if (layer < 0 || layer >= c.n_layers || slot < 0 || slot >= c.max_seqs || kv_head < 0 ||
+      kv_head >= c.n_kv_heads || pos0 < 0 || n <= 0 || pos0 + n > c.max_ctx)
+    return fail(FS_ERR_INVALID_ARG, "kv_read range out of bounds");
+  const size_t off = ((size_t)layer * m->layer_stride + (size_t)slot * m->slot_stride +
+                      (size_t)kv_head * m->head_stride + (size_t)pos0 * c.head_dim) * m->esz;
+  const size_t bytes = (size_t)n * c.head_dim * m->esz;
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(hipMemcpyAsync(k_out, (const char*)m->kcache + off, bytes, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipMemcpyAsync(v_out, (const char*)m->vcache + off, bytes, hipMemcpyDeviceToDevice, s));
+  return FS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,345 @@
+// Grouped-query causal attention over the KV cache (wave64 vector path).
+//
+// Query head h reads KV head h / (nq/nkv); the query at position p attends to
+// keys 0..p inclusive with scores scaled by 1/sqrt(d) and a max-subtracted
+// softmax ("Failed Star (fs)", How it's built: GQA; "Coming back to Failed
+// Star", Second sitting: 16 query heads and 8 KV heads of width 128).
+//
+// Work layout: a wave is four groups of 16 lanes; each group walks its own
+// key positions, lane i of a group holding elements [i*d/16, (i+1)*d/16) of
+// q, k, v.  Each group keeps an online-softmax state (running max m, sum l,
+// unnormalised output o) in base 2 (q is pre-scaled by log2(e)/sqrt(d)).
+// Group states merge exactly: m = max, l and o rescaled by 2^(m_g - m).
+//
+// Decode kernel: one workgroup per (sequence, KV head, context chunk).  It
+// also normalises and rotates the new token's q and k and appends k, v to
+// the cache (fused), and the last workgroup of each (sequence, KV head)
+// combines the chunk partials (split-K flash decoding).
+#include "common.h"
+#include "kernels.h"
+
+namespace fsk {
+
+static constexpr float LOG2E = 1.4426950408889634f;
+
+template <typename KV, int N> __device__ __forceinline__ void loadn(const KV* p, float* o);
+template <> __device__ __forceinline__ void loadn<bf16, 8>(const bf16* p, float* o) { load8(p, o); }
+template <> __device__ __forceinline__ void loadn<bf16, 4>(const bf16* p, float* o) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  o[0] = __uint_as_float(u.x << 16); o[1] = __uint_as_float(u.x & 0xffff0000u);
+  o[2] = __uint_as_float(u.y << 16); o[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+template <> __device__ __forceinline__ void loadn<float, 8>(const float* p, float* o) { load8(p, o); }
+template <> __device__ __forceinline__ void loadn<float, 4>(const float* p, float* o) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+}
+
+template <int REP, int DP>
+struct SoftState {
+  float m[REP], l[REP], o[REP][DP];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int r = 0; r < REP; ++r) {
+      m[r] = -INFINITY;
+      l[r] = 0.f;
+#pragma unroll
+      for (int e = 0; e < DP; ++e) o[r][e] = 0.f;
+    }
+  }
+  // fold one key position: s[r] = base-2 score, v = this lane's value slice
+  __device__ __forceinline__ void add(const float* s, const float* v) {
+#pragma unroll
+    for (int r = 0; r < REP; ++r) {
+      const float mn = fmaxf(m[r], s[r]);
+      const float corr = exp2f(m[r] - mn);
+      const float pp = exp2f(s[r] - mn);
+      l[r] = l[r] * corr + pp;
+#pragma unroll
+      for (int e = 0; e < DP; ++e) o[r][e] = o[r][e] * corr + pp * v[e];
+      m[r] = mn;
+    }
+  }
+  // merge with the state held `off` lanes away (xor)
+  __device__ __forceinline__ void merge_xor(int off) {
+#pragma unroll
+    for (int r = 0; r < REP; ++r) {
+      const float mo = __shfl_xor(m[r], off);
+      const float lo = __shfl_xor(l[r], off);
+      const float mn = fmaxf(m[r], mo);
+      const float a = (m[r] == -INFINITY) ? 0.f : exp2f(m[r] - mn);
+      const float b = (mo == -INFINITY) ? 0.f : exp2f(mo - mn);
+      l[r] = l[r] * a + lo * b;
+#pragma unroll
+      for (int e = 0; e < DP; ++e) {
+        const float oo = __shfl_xor(o[r][e], off);
+        o[r][e] = o[r][e] * a + oo * b;
+      }
+      m[r] = mn;
+    }
+  }
+};
+
+// Walks positions u = first + 4*i (< end) for this lane's group; uniform trip
+// count across the wave so the 16-lane shuffles stay converged.
+template <typename KV, int D, int REP>
+__device__ __forceinline__ void attend(SoftState<REP, D / 16>& st, const float (&q)[REP][D / 16],
+                                       const KV* __restrict__ kb, const KV* __restrict__ vb,
+                                       int wave_first, int end, int stride, int grp, int li,
+                                       int u_new, const float* knew, const float* vnew) {
+  constexpr int DP = D / 16;
+  for (int base = wave_first; base < end; base += stride) {
+    const int u = base + grp;
+    const bool valid = u < end;
+    const int uu = valid ? u : wave_first;
+    float k[DP], v[DP];
+    if (uu == u_new) {
+#pragma unroll
+      for (int e = 0; e < DP; ++e) { k[e] = knew[li * DP + e]; v[e] = vnew[li * DP + e]; }
+    } else {
+      loadn<KV, DP>(kb + (size_t)uu * D + li * DP, k);
+      loadn<KV, DP>(vb + (size_t)uu * D + li * DP, v);
+    }
+    float s[REP];
+#pragma unroll
+    for (int r = 0; r < REP; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < DP; ++e) acc = fmaf(q[r][e], k[e], acc);
+      s[r] = group_sum<16>(acc);
+    }
+    if (valid) st.add(s, v);
+  }
+}
+
+// ------------------------------------------------------------------ decode
+template <typename KV, int D, int REP, typename TO>
+__global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams p) {
+  constexpr int DP = D / 16;
+  constexpr int HALF = D / 2;
+  __shared__ float qs[REP][D];
+  __shared__ float knew[D], vnew[D];
+  __shared__ float sm[4][REP], sl[4][REP];
+  __shared__ float so[4][REP][D];
+  __shared__ bool last;
+
+  const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int grp = lane >> 4, li = lane & 15;
+  const int pos = p.positions[b];
+  const int slot = p.slots[b];
+  const int n = pos + 1;
+  const int c0 = c * p.chunk;
+  if (c0 >= n) return;                                  // chunk past this sequence
+  const int c1 = min(c0 + p.chunk, n);
+  const int nvalid = (n + p.chunk - 1) / p.chunk;
+  const int W = (p.nq + 2 * p.nkv) * D;
+  const float* row = p.qkv + (size_t)b * W;
+  const size_t kvoff = (size_t)slot * p.slot_stride + (size_t)j * p.head_stride;
+  KV* kb = reinterpret_cast<KV*>(p.kcache) + kvoff;
+  KV* vb = reinterpret_cast<KV*>(p.vcache) + kvoff;
+  const float qscale = p.scale * LOG2E;
+
+  // ---- q heads of this group: RMSNorm over d, RoPE at pos, pre-scale
+  for (int r = wid; r < REP; r += 4) {
+    const int h = j * REP + r;
+    const bool on = lane < HALF;
+    float x0 = on ? row[h * D + lane] : 0.f;
+    float x1 = on ? row[h * D + lane + HALF] : 0.f;
+    const float inv = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)D + p.eps);
+    if (on) {
+      x0 *= inv * p.gq[lane];
+      x1 *= inv * p.gq[lane + HALF];
+      const float cs = p.cos_t[(size_t)pos * HALF + lane], sn = p.sin_t[(size_t)pos * HALF + lane];
+      qs[r][lane] = (x0 * cs - x1 * sn) * qscale;
+      qs[r][lane + HALF] = (x1 * cs + x0 * sn) * qscale;
+    }
+  }
+  // ---- the new token's k, v if it falls in this chunk: normalise, rotate, append
+  const bool has_new = (pos >= c0 && pos < c1);
+  if (has_new && wid == 3) {
+    const bool on = lane < HALF;
+    const float* kr = row + p.nq * D + j * D;
+    const float* vr = row + (p.nq + p.nkv) * D + j * D;
+    float x0 = on ? kr[lane] : 0.f;
+    float x1 = on ? kr[lane + HALF] : 0.f;
+    const float inv = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)D + p.eps);
+    if (on) {
+      x0 *= inv * p.gk[lane];
+      x1 *= inv * p.gk[lane + HALF];
+      const float cs = p.cos_t[(size_t)pos * HALF + lane], sn = p.sin_t[(size_t)pos * HALF + lane];
+      const KV k0 = from_f32<KV>(x0 * cs - x1 * sn), k1 = from_f32<KV>(x1 * cs + x0 * sn);
+      const KV v0 = from_f32<KV>(vr[lane]), v1 = from_f32<KV>(vr[lane + HALF]);
+      kb[(size_t)pos * D + lane] = k0;
+      kb[(size_t)pos * D + lane + HALF] = k1;
+      vb[(size_t)pos * D + lane] = v0;
+      vb[(size_t)pos * D + lane + HALF] = v1;
+      knew[lane] = to_f32(k0); knew[lane + HALF] = to_f32(k1);
+      vnew[lane] = to_f32(v0); vnew[lane + HALF] = to_f32(v1);
+    }
+  }
+  __syncthreads();
+
+  float q[REP][DP];
+#pragma unroll
+  for (int r = 0; r < REP; ++r)
+#pragma unroll
+    for (int e = 0; e < DP; ++e) q[r][e] = qs[r][li * DP + e];
+
+  SoftState<REP, DP> st;
+  st.init();
+  attend<KV, D, REP>(st, q, kb, vb, c0 + wid * 4, c1, 16, grp, li, has_new ? pos : -1, knew, vnew);
+  st.merge_xor(16);
+  st.merge_xor(32);
+  if (lane < 16) {
+#pragma unroll
+    for (int r = 0; r < REP; ++r) {
+      if (lane == 0) { sm[wid][r] = st.m[r]; sl[wid][r] = st.l[r]; }
+#pragma unroll
+      for (int e = 0; e < DP; ++e) so[wid][r][li * DP + e] = st.o[r][e];
+    }
+  }
+  __syncthreads();
+
+  TO* out = reinterpret_cast<TO*>(p.out) + (size_t)b * p.nq * D;
+  for (int idx = tid; idx < REP * D; idx += 256) {
+    const int r = idx / D, e = idx % D;
+    float M = sm[0][r];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm[w][r]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = (sm[w][r] == -INFINITY) ? 0.f : exp2f(sm[w][r] - M);
+      L += sl[w][r] * a;
+      O += so[w][r][e] * a;
+    }
+    const int h = j * REP + r;
+    if (nvalid == 1) {
+      out[h * D + e] = from_f32<TO>(O / L);
+    } else {
+      float* pr = p.part + (((size_t)b * p.nq + h) * p.nchunks + c) * (D + 2);
+      pr[e] = O;
+      if (e == 0) { pr[D] = M; pr[D + 1] = L; }
+    }
+  }
+  if (nvalid == 1) return;
+
+  // ---- split-K combine by the last chunk workgroup of this (sequence, KV head)
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t done = atomicAdd(p.counters + (size_t)b * p.nkv + j, 1u);
+    last = (done == (uint32_t)(nvalid - 1));
+  }
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  for (int idx = tid; idx < REP * D; idx += 256) {
+    const int r = idx / D, e = idx % D;
+    const int h = j * REP + r;
+    const float* pr = p.part + ((size_t)b * p.nq + h) * p.nchunks * (D + 2);
+    float M = -INFINITY;
+    for (int cc = 0; cc < nvalid; ++cc) M = fmaxf(M, pr[cc * (D + 2) + D]);
+    float L = 0.f, O = 0.f;
+    for (int cc = 0; cc < nvalid; ++cc) {
+      const float a = exp2f(pr[cc * (D + 2) + D] - M);
+      L += pr[cc * (D + 2) + D + 1] * a;
+      O += pr[cc * (D + 2) + e] * a;
+    }
+    out[h * D + e] = from_f32<TO>(O / L);
+  }
+  if (tid == 0) p.counters[(size_t)b * p.nkv + j] = 0u;
+}
+
+template <typename KV, int D, typename TO>
+static hipError_t decode_rep(const AttnDecodeParams& p, hipStream_t s) {
+  const dim3 grid(p.nchunks, p.nkv, p.B);
+  switch (p.nq / p.nkv) {
+    case 1: attn_decode_kernel<KV, D, 1, TO><<<grid, 256, 0, s>>>(p); break;
+    case 2: attn_decode_kernel<KV, D, 2, TO><<<grid, 256, 0, s>>>(p); break;
+    case 4: attn_decode_kernel<KV, D, 4, TO><<<grid, 256, 0, s>>>(p); break;
+    case 8: attn_decode_kernel<KV, D, 8, TO><<<grid, 256, 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t attn_decode(const AttnDecodeParams& p, hipStream_t s) {
+  if (p.B <= 0) return hipSuccess;
+  if (p.kv_dt == DT_BF16) {
+    if (p.o_dt == DT_BF16) {
+      if (p.d == 128) return decode_rep<bf16, 128, bf16>(p, s);
+      if (p.d == 64) return decode_rep<bf16, 64, bf16>(p, s);
+    } else {
+      if (p.d == 128) return decode_rep<bf16, 128, float>(p, s);
+      if (p.d == 64) return decode_rep<bf16, 64, float>(p, s);
+    }
+  } else {
+    if (p.o_dt == DT_F32) {
+      if (p.d == 128) return decode_rep<float, 128, float>(p, s);
+      if (p.d == 64) return decode_rep<float, 64, float>(p, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------------ prefill (vector path)
+// One wave per (query, head); four queries of one head per workgroup.
+template <typename TQ, typename KV, int D, typename TO>
+__global__ __launch_bounds__(256) void attn_prefill_vec_kernel(const AttnPrefillParams p) {
+  constexpr int DP = D / 16;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int grp = lane >> 4, li = lane & 15;
+  const int t = blockIdx.x * 4 + wid;
+  const int h = blockIdx.y, b = blockIdx.z;
+  if (t >= p.S) return;
+  const int rep = p.nq / p.nkv;
+  const int j = h / rep;
+  const int slot = p.slots[b];
+  const size_t kvoff = (size_t)slot * p.slot_stride + (size_t)j * p.head_stride;
+  const KV* kb = reinterpret_cast<const KV*>(p.kcache) + kvoff;
+  const KV* vb = reinterpret_cast<const KV*>(p.vcache) + kvoff;
+  const size_t qrow = ((size_t)b * p.S + t) * p.nq * D + h * D;
+  const TQ* qp = reinterpret_cast<const TQ*>(p.q) + qrow;
+  float q[1][DP];
+  const float qscale = p.scale * LOG2E;
+#pragma unroll
+  for (int e = 0; e < DP; ++e) q[0][e] = to_f32(qp[li * DP + e]) * qscale;
+  SoftState<1, DP> st;
+  st.init();
+  attend<KV, D, 1>(st, q, kb, vb, 0, t + 1, 4, grp, li, -1, nullptr, nullptr);
+  st.merge_xor(16);
+  st.merge_xor(32);
+  if (lane < 16) {
+    TO* o = reinterpret_cast<TO*>(p.out) + qrow;
+    const float inv = 1.f / st.l[0];
+#pragma unroll
+    for (int e = 0; e < DP; ++e) o[li * DP + e] = from_f32<TO>(st.o[0][e] * inv);
+  }
+}
+
+template <typename TQ, typename KV, typename TO>
+static hipError_t prefill_vec(const AttnPrefillParams& p, hipStream_t s) {
+  const dim3 grid((p.S + 3) / 4, p.nq, p.B);
+  if (p.d == 128)
+    attn_prefill_vec_kernel<TQ, KV, 128, TO><<<grid, 256, 0, s>>>(p);
+  else if (p.d == 64)
+    attn_prefill_vec_kernel<TQ, KV, 64, TO><<<grid, 256, 0, s>>>(p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t attn_prefill_vec(const AttnPrefillParams& p, hipStream_t s) {
+  if (p.B <= 0 || p.S <= 0) return hipSuccess;
+  if (p.kv_dt == DT_BF16) {
+    if (p.q_dt == DT_BF16 && p.o_dt == DT_BF16) return prefill_vec<bf16, bf16, bf16>(p, s);
+    if (p.q_dt == DT_F32 && p.o_dt == DT_F32) return prefill_vec<float, bf16, float>(p, s);
+  } else if (p.q_dt == DT_F32 && p.o_dt == DT_F32) {
+    return prefill_vec<float, float, float>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fsk

@@ -1,0 +1,147 @@
+// bf16 MFMA GEMM for the prefill projections and MLP (the dense contractions).
+//
+// C[M, N] = A[M, K] . B[N, K]^T: A holds activation rows, B a weight stored
+// [out, in] ("Coming back to Failed Star", First sitting, item 3), so both
+// operands are K-contiguous.  fp32 accumulation in v_mfma_f32_32x32x16_bf16.
+//
+// Tiling: 128x128 output tile per workgroup of 4 waves (2x2, 64x64 per wave =
+// 2x2 MFMA blocks), K step 64, double-buffered LDS with rows padded by 16 B
+// so that the 128-bit fragment reads are bank-conflict free.  One barrier per
+// K step: the next tile's global loads are issued before the MFMAs of the
+// current one and written to the other LDS buffer after them.
+//
+// Fragment layout: lane l supplies row (l % 32) of its 32-row block and the
+// 8 consecutive k at 8*(l/32) of the 16-wide step, identically for A and B,
+// so the product sums over the same k whatever order the unit uses.  The
+// 32x32 result holds element (8*(r/4) + 4*(l/32) + r%4, l%32) in register r.
+#include "common.h"
+#include "kernels.h"
+
+namespace fsk {
+
+static constexpr int BM = 128, BN = 128, BK = 64;
+static constexpr int LDK = BK + 8;   // padded row length (elements)
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16* __restrict__ A, int lda,
+                                                        const bf16* __restrict__ B, int ldb,
+                                                        void* __restrict__ out, int ldc,
+                                                        int M, int N, int K,
+                                                        const bf16* __restrict__ A_lo) {
+  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * LDK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+
+  // global -> register staging: 4 x 16 B of A and of B per thread
+  u32x4 ra[4], rb[4];
+  // K steps [0, nk0) read A; with A_lo, steps [nk0, 2*nk0) read A_lo against the same B
+  const int nk0 = K / BK;
+  auto gload = [&](int kt) {
+    const bf16* a = (kt < nk0) ? A : A_lo;
+    const int k0 = (kt < nk0 ? kt : kt - nk0) * BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = tid + 256 * i;
+      const int r = id >> 3, c8 = (id & 7) * 8;
+      const int gm = m0 + r, gn = n0 + r;
+      ra[i] = (gm < M) ? *reinterpret_cast<const u32x4*>(a + (size_t)gm * lda + k0 + c8) : u32x4{0, 0, 0, 0};
+      rb[i] = (gn < N) ? *reinterpret_cast<const u32x4*>(B + (size_t)gn * ldb + k0 + c8) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = tid + 256 * i;
+      const int r = id >> 3, c8 = (id & 7) * 8;
+      *reinterpret_cast<u32x4*>(&As[buf][r * LDK + c8]) = ra[i];
+      *reinterpret_cast<u32x4*>(&Bs[buf][r * LDK + c8]) = rb[i];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (A_lo != nullptr) ? 2 * nk0 : nk0;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  const int lrow = lane & 31, lk = (lane >> 5) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(&As[cur][(wm * 64 + i * 32 + lrow) * LDK + kk + lk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][(wn * 64 + j * 32 + lrow) * LDK + kk + lk]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  const int col_in = lane & 31, rq = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + rq + (r & 3);
+      if (row >= M) continue;
+      if (EPI == GEPI_SWIGLU_BF16) {
+        // the wave's 64 columns are [32 gate | matching 32 up] of the packed matrix
+        if (n0 + wn * 64 >= N) continue;
+        const int f = (n0 + wn * 64) / 2 + col_in;
+        const float g = acc[i][0][r], u = acc[i][1][r];
+        reinterpret_cast<bf16*>(out)[(size_t)row * ldc + f] = (bf16)(silu(g) * u);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + wn * 64 + j * 32 + col_in;
+          if (col >= N) continue;
+          const size_t o = (size_t)row * ldc + col;
+          const float v = acc[i][j][r];
+          if (EPI == GEPI_STORE_BF16) reinterpret_cast<bf16*>(out)[o] = (bf16)v;
+          else if (EPI == GEPI_STORE_F32) reinterpret_cast<float*>(out)[o] = v;
+          else reinterpret_cast<float*>(out)[o] += v;
+        }
+      }
+    }
+  }
+}
+
+hipError_t gemm_bf16(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc,
+                     int M, int N, int K, hipStream_t s, const void* A_lo) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (K % BK != 0) return hipErrorInvalidValue;
+  if (epi == GEPI_SWIGLU_BF16 && N % 64 != 0) return hipErrorInvalidValue;
+  const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
+  const bf16* a = (const bf16*)A;
+  const bf16* b = (const bf16*)B;
+  switch (epi) {
+    case GEPI_STORE_BF16: gemm_bf16_kernel<GEPI_STORE_BF16><<<grid, 256, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, (const bf16*)A_lo); break;
+    case GEPI_RESID_F32: gemm_bf16_kernel<GEPI_RESID_F32><<<grid, 256, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, (const bf16*)A_lo); break;
+    case GEPI_SWIGLU_BF16: gemm_bf16_kernel<GEPI_SWIGLU_BF16><<<grid, 256, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, (const bf16*)A_lo); break;
+    case GEPI_STORE_F32: gemm_bf16_kernel<GEPI_STORE_F32><<<grid, 256, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, (const bf16*)A_lo); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fsk

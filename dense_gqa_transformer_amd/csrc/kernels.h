@@ -1,0 +1,117 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fsk {
+
+enum Dt { DT_F32 = 0, DT_BF16 = 1 };
+
+inline size_t dt_size(int dt) { return dt == DT_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- small ops
+// x[t, :] = E[tok[t], :] widened to fp32 (ids clamped to [0, V)).
+hipError_t embed(const void* E, int dt, const int32_t* tok, int T, int H, int V,
+                 float* x, hipStream_t s);
+// out[t, :] = x[t*ldx, :] / sqrt(mean(x^2) + eps) * g; out of out_dt at row stride ldo.
+// lo (bf16 only, optional): the rounding remainder, y - out, also as bf16.
+hipError_t rmsnorm(const float* x, int T, int H, int ldx, const float* g, float eps,
+                   void* out, int out_dt, int ldo, hipStream_t s, void* lo = nullptr);
+// dst[i] = float(src[i])
+hipError_t convert_f32(const void* src, int dt, float* dst, size_t n, hipStream_t s);
+// Packs gate/up [I, H] into blocks of 32 gate rows followed by the matching 32 up rows.
+hipError_t pack_gate_up(const void* gate, const void* up, int dt, int I, int H, void* dst,
+                        hipStream_t s);
+
+// ---------------------------------------------------------------- GEMV (skinny M)
+enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+static constexpr int GEMV_LOGITS_MAX_M = 4;
+
+struct GemvParams {
+  const void* w;       // [N, K] of dt (SWIGLU: packed gate/up, 2*N rows, N = ffn)
+  int N, K;            // output features, reduction length
+  const float* a;      // activations, M rows at stride lda (fp32)
+  int lda, M;
+  const float* gamma;  // optional RMSNorm weight [K] applied to each activation row
+  float eps;
+  float* out;          // STORE/SWIGLU: out[m*ldo + n] = y; RESID: out[m*ldo + n] += y
+  int ldo;
+  // LOGITS epilogue (M <= GEMV_LOGITS_MAX_M)
+  float* logits;       // optional, [M, N] at row stride ldo
+  int32_t* next;       // optional [M]: greedy IDs
+  float* part_val;     // [M * gemv_logits_blocks] per-block best values
+  int32_t* part_idx;   // [M * gemv_logits_blocks] per-block best indices
+  uint32_t* counter;   // one zeroed counter; the last block resets it
+  int groups;          // set by the launcher
+};
+hipError_t gemv(int dt, int epi, GemvParams p, hipStream_t s);
+int gemv_logits_blocks(int N, int K);
+
+// ---------------------------------------------------------------- MFMA GEMM (bf16)
+enum GemmEpi { GEPI_STORE_BF16 = 0, GEPI_RESID_F32 = 1, GEPI_SWIGLU_BF16 = 2, GEPI_STORE_F32 = 3 };
+// C[M, N] = A[M, K] . B[N, K]^T; A, B bf16 row-major with K contiguous (lda, ldb);
+// fp32 accumulation.  STORE_*: out[m*ldc + n] = C; RESID_F32: out[m*ldc + n] += C;
+// SWIGLU_BF16: B is packed gate/up (blocks of 32+32 rows, N = 2*ffn) and
+// out[m*ldc + f] = silu(gate_f) * up_f.  Requires K % 64 == 0 (and N % 64 == 0 for SWIGLU).
+// A_lo (optional): a second bf16 operand of A's shape; C = (A + A_lo) . B^T, the
+// remainder pass reusing each B tile (keeps activations near fp32 precision).
+hipError_t gemm_bf16(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc,
+                     int M, int N, int K, hipStream_t s, const void* A_lo = nullptr);
+
+// ---------------------------------------------------------------- q/k norm + RoPE + KV write
+// For T tokens: token t belongs to sequence t / S_per (slot slots[t / S_per]) at
+// position pos0 + t % S_per (prefill: pos0 = 0).  Reads qkv rows [T, (nq+2nkv)*d]
+// of in_dt; writes q' [T, nq*d] of q_dt (RMSNorm over d with g_q, RoPE), and
+// K' (RMSNorm with g_k, RoPE), V into the cache of kv_dt.
+struct RopeKvParams {
+  const void* qkv; int in_dt;
+  void* qout; int q_dt;
+  void* kcache; void* vcache; int kv_dt;
+  const float* gq; const float* gk; float eps;
+  const float* cos_t; const float* sin_t;   // [max_ctx, d/2]
+  const int32_t* slots;                     // device [B]
+  int T, S_per, nq, nkv, d;
+  long long slot_stride;                    // elements per (layer, slot)
+  long long head_stride;                    // elements per KV head (= max_ctx * d)
+};
+hipError_t rope_kv(const RopeKvParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+// Prefill: causal attention of T = B*S queries against their slot's cache
+// positions 0..p.  q [T, nq*d] of q_dt; out [T, nq*d] of o_dt.
+struct AttnPrefillParams {
+  const void* q; int q_dt;
+  const void* kcache; const void* vcache; int kv_dt;
+  void* out; int o_dt;
+  const int32_t* slots;        // device [B]
+  int B, S, nq, nkv, d;
+  long long slot_stride, head_stride;
+  float scale;
+};
+hipError_t attn_prefill(const AttnPrefillParams& p, hipStream_t s);      // MFMA path when bf16
+hipError_t attn_prefill_vec(const AttnPrefillParams& p, hipStream_t s);  // vector path, any dtype
+
+// Decode: one new token per sequence, split over context chunks, with the
+// q/k RMSNorm + RoPE + KV append of the new token fused in, and the partial
+// results combined by the last workgroup of each (sequence, KV head).
+struct AttnDecodeParams {
+  const float* qkv;            // [B, (nq+2nkv)*d] fp32 (raw projections)
+  void* kcache; void* vcache; int kv_dt;
+  const float* gq; const float* gk; float eps;
+  const float* cos_t; const float* sin_t;
+  const int32_t* positions;    // device [B]
+  const int32_t* slots;        // device [B]
+  void* out; int o_dt;         // [B, nq*d]
+  float* part;                 // [B, nq, nchunks, d + 2]
+  uint32_t* counters;          // [B, nkv], zeroed; self-resetting
+  int B, nq, nkv, d, chunk, nchunks;
+  long long slot_stride, head_stride;
+  float scale;
+};
+hipError_t attn_decode(const AttnDecodeParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------- argmax
+// out[b] = greedy ID of row b of logits [B, V] (row stride ldl).
+hipError_t argmax_rows(const float* logits, int B, int V, int ldl, int32_t* out, hipStream_t s);
+
+}  // namespace fsk

@@ -1,0 +1,156 @@
+// Small bandwidth-bound kernels: embedding gather, RMSNorm, dtype widening,
+// gate/up packing and row argmax.
+#include "common.h"
+#include "kernels.h"
+
+namespace fsk {
+
+__device__ __forceinline__ float block_sum256(float v, float* sh) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) sh[wid] = v;
+  __syncthreads();
+  v = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return v;
+}
+
+// ------------------------------------------------------------------ embedding
+// Token embedding gather ("Coming back to Failed Star", Second sitting:
+// ids[S] -> embedding[S,H]); the residual stream is kept in fp32.
+template <typename W>
+__global__ __launch_bounds__(256) void embed_kernel(const W* __restrict__ E, const int32_t* __restrict__ tok,
+                                                    int H, int V, float* __restrict__ x) {
+  const int t = blockIdx.x;
+  int id = tok[t];
+  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+  const W* row = E + (size_t)id * H;
+  float* dst = x + (size_t)t * H;
+  for (int k = threadIdx.x * 8; k < H; k += 256 * 8) {
+    float v[8];
+    load8(row + k, v);
+    *reinterpret_cast<float4*>(dst + k) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(dst + k + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+hipError_t embed(const void* E, int dt, const int32_t* tok, int T, int H, int V, float* x, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (dt == DT_BF16)
+    embed_kernel<bf16><<<T, 256, 0, s>>>((const bf16*)E, tok, H, V, x);
+  else
+    embed_kernel<float><<<T, 256, 0, s>>>((const float*)E, tok, H, V, x);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ RMSNorm
+// x / sqrt(mean(x^2) + eps) * g over one row ("Failed Star (fs)", How it's built).
+// With `lo` set (bf16 output only) the value is also split: out = bf16(y),
+// lo = bf16(y - out), so that out + lo carries y to about 16 significant bits.
+template <typename O>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int H, int ldx,
+                                                      const float* __restrict__ g, float eps,
+                                                      O* __restrict__ out, O* __restrict__ lo, int ldo) {
+  __shared__ float sh[4];
+  const float* row = x + (size_t)blockIdx.x * ldx;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < H; k += 256) {
+    float v = row[k];
+    ss += v * v;
+  }
+  ss = block_sum256(ss, sh);
+  const float inv = rsqrtf(ss / (float)H + eps);
+  O* o = out + (size_t)blockIdx.x * ldo;
+  for (int k = threadIdx.x; k < H; k += 256) {
+    const float y = row[k] * inv * g[k];
+    const O hi = from_f32<O>(y);
+    o[k] = hi;
+    if (lo != nullptr) lo[(size_t)blockIdx.x * ldo + k] = from_f32<O>(y - to_f32(hi));
+  }
+}
+
+hipError_t rmsnorm(const float* x, int T, int H, int ldx, const float* g, float eps, void* out,
+                   int out_dt, int ldo, hipStream_t s, void* lo) {
+  if (T <= 0) return hipSuccess;
+  if (out_dt == DT_BF16)
+    rmsnorm_kernel<bf16><<<T, 256, 0, s>>>(x, H, ldx, g, eps, (bf16*)out, (bf16*)lo, ldo);
+  else if (lo == nullptr)
+    rmsnorm_kernel<float><<<T, 256, 0, s>>>(x, H, ldx, g, eps, (float*)out, nullptr, ldo);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ widening
+template <typename W>
+__global__ void convert_kernel(const W* __restrict__ src, float* __restrict__ dst, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = to_f32(src[i]);
+}
+
+hipError_t convert_f32(const void* src, int dt, float* dst, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)((n + 255) / 256);
+  if (dt == DT_BF16)
+    convert_kernel<bf16><<<blocks, 256, 0, s>>>((const bf16*)src, dst, n);
+  else
+    convert_kernel<float><<<blocks, 256, 0, s>>>((const float*)src, dst, n);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ gate/up packing
+template <typename W>
+__global__ void pack_gate_up_kernel(const W* __restrict__ gate, const W* __restrict__ up, int H,
+                                    W* __restrict__ dst) {
+  const int r = blockIdx.x;                // packed row in [0, 2I)
+  const int blk = r >> 6, within = r & 63;
+  const W* src = (within < 32 ? gate : up) + (size_t)(blk * 32 + (within & 31)) * H;
+  W* d = dst + (size_t)r * H;
+  for (int k = threadIdx.x; k < H; k += blockDim.x) d[k] = src[k];
+}
+
+hipError_t pack_gate_up(const void* gate, const void* up, int dt, int I, int H, void* dst, hipStream_t s) {
+  if (dt == DT_BF16)
+    pack_gate_up_kernel<bf16><<<2 * I, 256, 0, s>>>((const bf16*)gate, (const bf16*)up, H, (bf16*)dst);
+  else
+    pack_gate_up_kernel<float><<<2 * I, 256, 0, s>>>((const float*)gate, (const float*)up, H, (float*)dst);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ argmax
+// Greedy selection ("Coming back to Failed Star", section Next): the largest
+// finite logit, lowest ID on an exact tie, -1 when no logit is finite.
+__global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ logits, int V, int ldl,
+                                                      int32_t* __restrict__ out) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const float* row = logits + (size_t)blockIdx.x * ldl;
+  float bv = 0.f;
+  int bi = -1;
+  for (int i = threadIdx.x; i < V; i += 1024) {
+    const float v = row[i];
+    if (__builtin_isfinite(v) && better(v, i, bv, bi)) { bv = v; bi = i; }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) { sv[wid] = bv; si[wid] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 16; ++w)
+      if (better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
+    out[blockIdx.x] = bi;
+  }
+}
+
+hipError_t argmax_rows(const float* logits, int B, int V, int ldl, int32_t* out, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  argmax_kernel<<<B, 1024, 0, s>>>(logits, V, ldl, out);
+  return hipGetLastError();
+}
+
+}  // namespace fsk

@@ -1,0 +1,130 @@
+"""Python face of the C ABI: a model handle plus the greedy argmax call.
+
+PyTorch supplies device memory and the HIP stream; the forward pass itself
+runs inside libfs.so.  Nothing here computes any part of the pass.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import native
+from .native import FsConfig, FsLayerWeights, FsWeights, check, int_array
+
+LAYER_KEYS = native.LAYER_FIELDS
+
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream]) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[ctypes.c_void_p]:
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _to_device(a, torch_dtype, device) -> torch.Tensor:
+    if isinstance(a, np.ndarray):
+        a = torch.from_numpy(np.ascontiguousarray(a))
+    return a.to(device=device, dtype=torch_dtype).contiguous()
+
+
+class Model:
+    """A model on one GPU: packed weights, KV cache of max_seqs x max_ctx.
+
+    ``shape`` carries n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn,
+    vocab, rms_eps, rope_theta and dtype ("f32" or "bf16"); ``weights`` is
+    ``{"embed", "final_norm", "layers": [{attn_norm, wq, ...}]}`` of numpy
+    arrays or tensors, ``[out, in]`` row-major.  The values are copied into
+    library-owned memory; for bf16 models they must be bf16-representable.
+    """
+
+    def __init__(self, shape, weights: dict, max_seqs: int, max_ctx: int,
+                 device: str = "cuda", stream: Optional[torch.cuda.Stream] = None):
+        lib = native.load()
+        self.shape = shape
+        self.device = torch.device(device)
+        self.dtype = native.FS_BF16 if shape.dtype == "bf16" else native.FS_F32
+        self.torch_dtype = torch.bfloat16 if self.dtype == native.FS_BF16 else torch.float32
+        self.vocab = shape.vocab
+        self.cfg = FsConfig(shape.n_layers, shape.hidden, shape.n_heads, shape.n_kv_heads,
+                            shape.head_dim, shape.ffn, shape.vocab, float(shape.rms_eps),
+                            float(shape.rope_theta), self.dtype, int(max_seqs), int(max_ctx))
+        with torch.cuda.device(self.device):
+            keep = []
+
+            def up(a):
+                t = _to_device(a, self.torch_dtype, self.device)
+                keep.append(t)
+                return ctypes.c_void_p(t.data_ptr())
+
+            layers = (FsLayerWeights * max(1, shape.n_layers))()
+            for i, lw in enumerate(weights["layers"]):
+                for k in LAYER_KEYS:
+                    setattr(layers[i], k, up(lw[k]))
+            w = FsWeights(up(weights["embed"]), up(weights["final_norm"]), layers)
+            handle = ctypes.c_void_p()
+            st = lib.fs_model_create(ctypes.byref(self.cfg), ctypes.byref(w), _stream_ptr(stream),
+                                     ctypes.byref(handle))
+            check(st)
+            self._h = handle
+            del keep
+        self._lib = lib
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            self._lib.fs_model_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------------ calls
+    def prefill(self, tokens: torch.Tensor, slots: Sequence[int],
+                logits: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """tokens: int32 [B, S] on the device; returns last-token logits [B, V] fp32."""
+        assert tokens.dtype == torch.int32 and tokens.is_contiguous() and tokens.dim() == 2
+        B, S = tokens.shape
+        if logits is None:
+            logits = torch.empty((B, self.vocab), dtype=torch.float32, device=self.device)
+        check(self._lib.fs_prefill(self._h, _ptr(tokens), B, S, int_array(slots), _ptr(logits),
+                                   _stream_ptr(stream)))
+        return logits
+
+    def decode_step(self, tokens: torch.Tensor, positions: Sequence[int], slots: Sequence[int],
+                    logits: Optional[torch.Tensor] = None, next_ids: Optional[torch.Tensor] = None,
+                    stream: Optional[torch.cuda.Stream] = None) -> None:
+        """tokens int32 [B] on the device; fills logits [B, V] and/or next_ids [B]."""
+        B = len(slots)
+        check(self._lib.fs_decode_step(self._h, _ptr(tokens), int_array(positions), int_array(slots), B,
+                                       _ptr(logits), _ptr(next_ids), _stream_ptr(stream)))
+
+    def slot_length(self, slot: int) -> int:
+        return int(self._lib.fs_slot_length(self._h, slot))
+
+    def kv_read(self, layer: int, slot: int, kv_head: int, pos0: int, n: int,
+                stream: Optional[torch.cuda.Stream] = None):
+        k = torch.empty((n, self.shape.head_dim), dtype=self.torch_dtype, device=self.device)
+        v = torch.empty_like(k)
+        check(self._lib.fs_kv_read(self._h, layer, slot, kv_head, pos0, n, _ptr(k), _ptr(v),
+                                   _stream_ptr(stream)))
+        return k, v
+
+
+def argmax(logits: torch.Tensor, out: Optional[torch.Tensor] = None,
+           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Greedy IDs of each row of fp32 logits [B, V] (lowest ID on ties, -1 if none finite)."""
+    lib = native.load()
+    assert logits.dtype == torch.float32 and logits.is_contiguous() and logits.dim() == 2
+    B, V = logits.shape
+    if out is None:
+        out = torch.empty((B,), dtype=torch.int32, device=logits.device)
+    check(lib.fs_argmax(_ptr(logits), B, V, _ptr(out), _stream_ptr(stream)))
+    return out

@@ -1,0 +1,148 @@
+/*
+ * fs.h - C ABI of the dense GQA decoder forward pass for gfx950 (MI355X).
+ *
+ * The library computes the forward pass of a small dense decoder-only
+ * transformer of the Qwen3-0.6B kind: token embedding, N blocks of
+ * (RMSNorm, Q/K/V projection, per-head q/k RMSNorm, rotate-half RoPE,
+ * grouped-query causal attention over a KV cache, output projection and
+ * residual, RMSNorm, SwiGLU MLP and residual), a final RMSNorm and the tied
+ * embedding as lm_head, of the last row only.  Sources on the pages:
+ *   - pipeline ids -> embedding -> blocks -> final norm -> last row -> logits:
+ *     "Coming back to Failed Star", section "Second sitting" (data-flow figure);
+ *     "Milestones", section M2;
+ *   - GQA, RoPE, SwiGLU, RMSNorm: "Failed Star (fs)", section "How it's built";
+ *   - Linear weights stored [out, in]: "Coming back to Failed Star",
+ *     section "First sitting", item 3;
+ *   - tied head: "Failed Star (fs)", section "Status";
+ *   - KV cache, one-token decode work, cached == uncached: "Milestones", M4;
+ *   - greedy selection (finite logits, lowest ID wins a tie) and the
+ *     position budget: "Coming back to Failed Star", section "Next".
+ *
+ * Conventions for every entry point:
+ *   - Return FS_OK (0) or a negative fs_status.  On an error nothing has been
+ *     enqueued and fs_last_error() describes it.  No exception crosses the ABI.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it; results are valid once the
+ *     stream has reached that point.  Device faults surface at the caller's
+ *     next synchronisation.
+ *   - "device" pointers are HIP device allocations on the current device;
+ *     "host" pointers are ordinary CPU memory read before the call returns.
+ *   - A model handle is not thread-safe: serialise calls on it, all on one
+ *     stream (or order the streams yourself).
+ */
+#ifndef FS_H
+#define FS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FS_OK = 0,
+  FS_ERR_INVALID_ARG = -1,   /* NULL pointer, bad size, bad slot, position mismatch */
+  FS_ERR_OOM = -2,           /* device allocation failed */
+  FS_ERR_HIP = -3,           /* a HIP runtime call or kernel launch failed */
+  FS_ERR_CAPACITY = -4,      /* sequence would run past max_ctx (context exhausted) */
+  FS_ERR_UNSUPPORTED = -5    /* dtype or shape this build does not implement */
+} fs_status;
+
+typedef enum { FS_F32 = 0, FS_BF16 = 1 } fs_dtype;
+
+/* Model shape and KV capacity.
+ *   n_heads % n_kv_heads == 0; query head h reads KV head h / (n_heads/n_kv_heads).
+ *   head_dim in {64, 128}; hidden, n_heads*head_dim and ffn multiples of 64.
+ *   rms_eps: the eps of every RMSNorm, inside the square root.
+ *   rope_theta: base of the rotary frequencies theta^(-2i/head_dim).
+ *   dtype: element type of every weight, the KV cache, and GEMM operands.
+ *          Accumulation and the residual stream are always fp32.
+ *   max_seqs: number of KV slots; max_ctx: positions per slot.
+ */
+typedef struct {
+  int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
+  float rms_eps, rope_theta;
+  int32_t dtype;             /* fs_dtype */
+  int32_t max_seqs, max_ctx;
+} fs_config;
+
+/* One layer's weights, device pointers of cfg.dtype, row-major [out, in]:
+ *   attn_norm [hidden], wq [n_heads*head_dim, hidden], wk/wv [n_kv_heads*head_dim, hidden],
+ *   q_norm/k_norm [head_dim] (shared by all heads), wo [hidden, n_heads*head_dim],
+ *   mlp_norm [hidden], w_gate/w_up [ffn, hidden], w_down [hidden, ffn]. */
+typedef struct {
+  const void *attn_norm, *wq, *wk, *wv, *q_norm, *k_norm, *wo,
+             *mlp_norm, *w_gate, *w_up, *w_down;
+} fs_layer_weights;
+
+/* embed [vocab, hidden] (also the lm_head), final_norm [hidden], both device;
+ * layers: host array of n_layers entries. */
+typedef struct {
+  const void *embed, *final_norm;
+  const fs_layer_weights *layers;
+} fs_weights;
+
+typedef struct fs_model fs_model;
+
+/* Creates a model on the current device.  Synchronous: copies and repacks
+ * the weights into library-owned device memory (fused QKV, paired gate/up),
+ * so the caller may free its tensors on return.  Allocates the KV cache
+ * (max_seqs * max_ctx positions per layer) and the RoPE tables.  All slots
+ * start empty.  *out receives the handle (NULL on error). */
+fs_status fs_model_create(const fs_config *cfg, const fs_weights *w,
+                          void *stream, fs_model **out);
+
+/* Frees everything the model owns (waits for its pending work).  NULL is a no-op. */
+void fs_model_destroy(fs_model *m);
+
+/* Uncached scorer that also fills the KV cache.
+ *   tokens: device int32 [B, S], row b is the prompt for slots[b], token IDs in [0, vocab).
+ *   slots:  host int32 [B], distinct, in [0, max_seqs); each slot is reset.
+ *   logits: device fp32 [B, vocab]; receives the logits of the LAST position
+ *           of each row ("Coming back to Failed Star", First sitting, item 4).
+ * Positions are 0..S-1 (no implicit BOS).  After the call slot length = S.
+ * Errors: INVALID_ARG for NULL pointers, B <= 0 or > max_seqs, S <= 0 (empty
+ * input), bad or duplicate slots; CAPACITY for S > max_ctx.  Token IDs out
+ * of range are clamped on the device (not detected). */
+fs_status fs_prefill(fs_model *m, const int32_t *tokens, int32_t B, int32_t S,
+                     const int32_t *slots, float *logits, void *stream);
+
+/* One KV-cached decode step for B sequences.
+ *   tokens:    device int32 [B] (e.g. the previous step's `next`; may alias `next`).
+ *   positions: host int32 [B], positions[i] must equal the current length of slots[i].
+ *   slots:     host int32 [B], distinct, in [0, max_seqs).
+ *   logits:    device fp32 [B, vocab] or NULL.
+ *   next:      device int32 [B] or NULL: greedy ID per row (argmax over finite
+ *              logits, lowest ID on an exact tie, -1 if none is finite).
+ * Appends K/V at positions[i] and attends over 0..positions[i]; afterwards
+ * the slot length is positions[i]+1.
+ * Errors: INVALID_ARG (NULL tokens, B out of range, bad/duplicate slot,
+ * position != slot length, both outputs NULL); CAPACITY if positions[i] >= max_ctx. */
+fs_status fs_decode_step(fs_model *m, const int32_t *tokens, const int32_t *positions,
+                         const int32_t *slots, int32_t B, float *logits, int32_t *next,
+                         void *stream);
+
+/* Greedy selection over rows of logits.
+ *   logits: device fp32 [B, V]; out: device int32 [B].
+ * out[b] = index of the largest finite logit of row b, the lowest index among
+ * exact ties ("Coming back to Failed Star", section "Next", Selection);
+ * -1 if the row holds no finite value.  Errors: INVALID_ARG for NULL or B, V <= 0. */
+fs_status fs_argmax(const float *logits, int32_t B, int32_t V, int32_t *out, void *stream);
+
+/* Current length (positions filled) of a slot, or -1 for a bad handle/slot. */
+int32_t fs_slot_length(const fs_model *m, int32_t slot);
+
+/* Copies cached K (normed and rotated) and V of one layer, slot and KV head,
+ * positions [pos0, pos0+n), into device buffers k_out, v_out of cfg.dtype,
+ * [n, head_dim] each.  For inspection and tests.  Errors: INVALID_ARG. */
+fs_status fs_kv_read(const fs_model *m, int32_t layer, int32_t slot, int32_t kv_head,
+                     int32_t pos0, int32_t n, void *k_out, void *v_out, void *stream);
+
+/* Message of the last error on this thread ("" if none); valid until the
+ * next fs_* call on this thread. */
+const char *fs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FS_H */

@@ -76,9 +76,11 @@ QWEN3_0P6B = ModelShape(n_layers=28, hidden=1024, n_heads=16, n_kv_heads=8,
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16, nearest-even; returns the uint16 bit patterns."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    rounding = np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
-    out = ((u + rounding) >> np.uint64(16)).astype(np.uint16)
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    lsb += np.uint32(0x7FFF)
+    lsb += u                       # wraps only for NaN patterns, fixed below
+    out = (lsb >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
         out[nan] = np.uint16(0x7FC0)
@@ -109,7 +111,8 @@ def make_weights(shape: ModelShape, seed: int = 0, std: float = 0.02,
     def draw(shp, norm):
         a = rng.standard_normal(size=shp, dtype=np.float32)
         if norm:
-            a = (np.float32(1.0) + a * np.float32(norm_std)).astype(np.float32)
+            a *= np.float32(norm_std)
+            a += np.float32(1.0)
         else:
             a *= np.float32(std)
         if shape.dtype == BF16:
