@@ -1,10 +1,19 @@
 """Benchmark of the forward pass on one MI355X.
 
-Workload (a "step" is one pass of the whole hot path): the 0.6B-shape bf16
-model decoding at batch 1 with a bf16 KV cache -- a 512-token uniform-random
-prompt is prefilled (untimed), then each step is one fs_decode_step whose
-greedy output is fed back on the device, at positions 512, 513, ...  The
-prefill side is reported in the same line: one fs_prefill of 4 x 4096 tokens.
+Workload of `value` (a "step" is one pass of the whole hot path): the
+0.6B-shape bf16 model decoding at batch 1 with a bf16 KV cache.  A 512-token
+uniform-random prompt is prefilled (untimed); each step is one
+fs_decode_step whose greedy output is fed back on the device, at positions
+512, 513, ...  The prefill side is reported in the same line: fs_prefill of
+4 x 4096 tokens.
+
+Also reported:
+  roofline     -- the dominant decode kernel: algorithmic bytes per launch over
+                  its average launch time (HIP events on the library's stream,
+                  from a pass with per-launch timing switched on), against
+                  8 TB/s HBM;
+  prefill      -- prefill tok/s and the MFMA roofline of its dominant kernel;
+  cpu_baseline -- the CPU oracle on a bounded sample of the same decode workload.
 
 Prints one JSON line.  Inputs are seeded synthetic weights and tokens
 (random-init, no checkpoint).
@@ -20,30 +29,79 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK = 8.0e12           # bytes/s, MI355X
+HBM_PEAK = 8.0e12           # bytes/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15     # dense bf16 flop/s, MI355X
 
 
-def decode_bytes(shape, ctx):
-    """Algorithmic HBM bytes of one bs1 decode step at context length ctx (incl. new token)."""
-    es = 2 if shape.dtype == "bf16" else 4
+# --------------------------------------------------------------------------- algorithmic work
+def decode_bytes_per_step(shape, ctx):
+    """HBM bytes one bs1 decode step must move at context length ctx (incl. the new token)."""
+    es = 2
     H, L, I, V = shape.hidden, shape.n_layers, shape.ffn, shape.vocab
     qw, kvw = shape.q_width, shape.kv_width
-    per_layer_w = ((qw + 2 * kvw) * H + H * qw + 2 * I * H + H * I) * es + (2 * H + 2 * shape.head_dim) * es
-    weights = L * per_layer_w + V * H * es + H * es
-    kv_read = L * 2 * kvw * es * (ctx - 1)
-    kv_write = L * 2 * kvw * es
-    return weights + kv_read + kv_write + H * es
+    per_layer = ((qw + 2 * kvw) * H + H * qw + 2 * I * H + H * I) * es + (2 * H + 2 * shape.head_dim) * es
+    return L * per_layer + V * H * es + H * es + L * 2 * kvw * es * ctx + H * es
+
+
+def decode_label_bytes(shape, label, ctx):
+    """Algorithmic bytes of ONE launch of a decode kernel (bs1), by step label."""
+    es = 2
+    H, I, V, d = shape.hidden, shape.ffn, shape.vocab, shape.head_dim
+    qw, kvw = shape.q_width, shape.kv_width
+    if label == "qkv":      # weights + fp32 x in + fp32 q/k/v out
+        return (qw + 2 * kvw) * H * es + 4 * H + 4 * (qw + 2 * kvw)
+    if label == "o_proj":   # weights + attention partials in + residual read/write
+        return H * qw * es + 4 * qw + 8 * H
+    if label == "gate_up":  # weights + x in + h out
+        return 2 * I * H * es + 4 * H + 4 * I
+    if label == "down":     # weights + h in + residual read/write
+        return H * I * es + 4 * I + 8 * H
+    if label == "head":     # tied embedding + x in
+        return V * H * es + 4 * H
+    if label == "attn":     # K and V of ctx positions of all KV heads + new k/v written
+        return 2 * kvw * es * ctx + 2 * kvw * es + 4 * (qw + 2 * kvw)
+    if label == "combine":  # one (o[d], m, l) partial per 32-position chunk and head, output row
+        return 4 * shape.n_heads * (d + 2) * -(-ctx // 32) + 4 * qw
+    return None
+
+
+def prefill_label_flops(shape, label, B, S):
+    """Algorithmic flops of ONE launch of a prefill kernel, by step label."""
+    H, I = shape.hidden, shape.ffn
+    qw, kvw, d = shape.q_width, shape.kv_width, shape.head_dim
+    T = B * S
+    return {"qkv": 2 * T * (qw + 2 * kvw) * H, "o_proj": 2 * T * H * qw,
+            "gate_up": 2 * T * 2 * I * H, "down": 2 * T * H * I,
+            "attn": B * shape.n_heads * 2 * d * S * (S + 1)}.get(label)
 
 
 def prefill_flops(shape, B, S):
-    H, L, I = shape.hidden, shape.n_layers, shape.ffn
-    qw, kvw, d = shape.q_width, shape.kv_width, shape.head_dim
-    T = B * S
-    gemm = 2 * T * L * ((qw + 2 * kvw) * H + H * qw + 2 * I * H + H * I)
-    attn = B * L * shape.n_heads * 2 * d * S * (S + 1)
-    head = 2 * B * shape.vocab * H
-    return gemm, attn, head
+    L = shape.n_layers
+    total = sum(prefill_label_flops(shape, k, B, S) for k in ("qkv", "o_proj", "gate_up", "down", "attn"))
+    return L * total + 2 * B * shape.vocab * shape.hidden
+
+
+# --------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, w, steps):
+    """The CPU oracle on a bounded sample: prefill (untimed), then `steps` decode steps."""
+    import numpy as np
+    from oracle import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = 1
+    orc = O.Oracle(wl.shape, w)
+    prompt = wl.prompts[0]
+    logits = orc.prefill(0, prompt)
+    t0 = time.perf_counter()
+    for k in range(steps):
+        tok = O.greedy_argmax_fast(logits)
+        logits = orc.decode_step(0, tok, len(prompt) + k)
+    dt = time.perf_counter() - t0
+    return {"value": round(steps / dt, 3), "unit": "tok/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{steps} greedy bs1 decode steps from position {len(prompt)} of the same "
+                      f"512-token prompt (float64 NumPy oracle; prefill untimed)"}
 
 
 def main():
@@ -53,9 +111,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=48)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only: --gpus must be 1 "
+                                   "(sharding across GPUs is not part of this library)"}))
         sys.exit(2)
 
     import numpy as np
@@ -67,38 +127,58 @@ def main():
     wl = synth.workload("decode_0p6b_bs1")
     shape = wl.shape
     prompt = wl.prompts[0]
-    steps = min(args.steps, wl.decode_steps)
+    steps = max(1, min(args.steps, wl.decode_steps))
     w = synth.make_weights(shape, 0)
     model = Model(shape, w, max_seqs=5, max_ctx=4096)
     dev = torch.device("cuda")
     tok = torch.from_numpy(prompt[None, :].astype(np.int32)).to(dev)
     nxt = torch.empty((1,), dtype=torch.int32, device=dev)
+    P = len(prompt)
 
-    # warmup on slot 1
+    # warmup on slot 1 (also captures the decode graphs used below)
     lg = model.prefill(tok, [1])
     argmax(lg, out=nxt)
-    for k in range(args.warmup):
-        model.decode_step(nxt, [len(prompt) + k], [1], next_ids=nxt)
+    for k in range(min(args.warmup, wl.decode_steps)):
+        model.decode_step(nxt, [P + k], [1], next_ids=nxt)
     torch.cuda.synchronize()
 
-    # timed: decode steps on slot 0 after an untimed prefill
+    # timed: `steps` decode steps on slot 0 after an untimed prefill
     lg = model.prefill(tok, [0])
     argmax(lg, out=nxt)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
-        model.decode_step(nxt, [len(prompt) + k], [0], next_ids=nxt)
+        model.decode_step(nxt, [P + k], [0], next_ids=nxt)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_step = dt * 1e3 / steps
-    tok_s = steps / dt
-    ctx_avg = len(prompt) + (steps + 1) / 2.0
-    bytes_avg = decode_bytes(shape, ctx_avg)
-    hbm_frac = bytes_avg / (dt / steps) / HBM_PEAK
+    ctx_avg = P + (steps + 1) / 2.0
+    hbm_frac = decode_bytes_per_step(shape, ctx_avg) / (dt / steps) / HBM_PEAK
 
+    # per-kernel times of the same steps (events around every launch, no graph)
+    lg = model.prefill(tok, [2])
+    argmax(lg, out=nxt)
+    torch.cuda.synchronize()
+    model.timing(True)
+    nt = min(steps, 64)
+    for k in range(nt):
+        model.decode_step(nxt, [P + k], [2], next_ids=nxt)
+    torch.cuda.synchronize()
+    labels = ("embed", "qkv", "attn", "combine", "o_proj", "gate_up", "down", "head", "argmax")
+    per = {}
+    for lab in labels:
+        ms, n = model.timing_read(lab)
+        if n:
+            per[lab] = (ms, n)
+    model.timing(False)
+    dom = max(per, key=lambda k: per[k][0])
+    avg_s = per[dom][0] / per[dom][1] / 1e3
+    ctx_t = P + (nt + 1) / 2.0
+    bytes_launch = decode_label_bytes(shape, dom, ctx_t)
+    achieved = bytes_launch / avg_s
     out = {
-        "metric": "decode tok/s @bs1 (0.6B shape, bf16 weights + KV)",
-        "value": round(tok_s, 2),
+        "metric": "decode tok/s @bs1 (0.6B shape, bf16 weights + bf16 KV cache)",
+        "value": round(steps / dt, 2),
         "unit": "tok/s",
         "n_gpus": 1,
         "steps": steps,
@@ -109,9 +189,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded random-init weights, uniform-random tokens)",
-        "config": {"workload": "decode_0p6b_bs1: 512-token prompt, greedy bs1 decode from position 512",
-                   "global_batch": 1, "seq_len": len(prompt) + steps, "parallelism": "none"},
+        "config": {"workload": "decode_0p6b_bs1: 28-layer 0.6B-shape bf16 model, 512-token prompt, "
+                               "greedy batch-1 decode steps from position 512",
+                   "global_batch": 1, "seq_len": P + steps, "parallelism": "none"},
         "decode_hbm_frac_step": round(hbm_frac, 4),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved / 1e9, 1),
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
+                     "traffic": None, "avg_launch_us": round(avg_s * 1e6, 3),
+                     "bytes_per_launch": int(bytes_launch)},
+        "decode_kernel_us_per_step": {k: round(v[0] * 1e3 / nt, 2) for k, v in per.items()},
     }
 
     if not args.no_prefill:
@@ -120,16 +206,42 @@ def main():
         logits = torch.empty((4, shape.vocab), dtype=torch.float32, device=dev)
         model.prefill(ptok, [0, 1, 2, 3], logits=logits)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
         reps = 2
+        t0 = time.perf_counter()
         for _ in range(reps):
             model.prefill(ptok, [0, 1, 2, 3], logits=logits)
         torch.cuda.synchronize()
         pdt = (time.perf_counter() - t0) / reps
-        g, a, h = prefill_flops(shape, 4, 4096)
-        out["prefill"] = {"workload": "prefill_0p6b_4x4096", "tok_s": round(4 * 4096 / pdt, 1),
-                          "ms": round(pdt * 1e3, 3),
-                          "mfma_frac_pass": round((g + a + h) / pdt / MFMA_BF16_PEAK, 4)}
+        model.timing(True)
+        model.prefill(ptok, [0, 1, 2, 3], logits=logits)
+        torch.cuda.synchronize()
+        pper = {}
+        for lab in ("embed", "norm", "qkv", "rope_kv", "attn", "o_proj", "gate_up", "down", "head"):
+            ms, n = model.timing_read(lab)
+            if n:
+                pper[lab] = (ms, n)
+        model.timing(False)
+        mf = {k: v for k, v in pper.items() if prefill_label_flops(shape, k, 4, 4096)}
+        pdom = max(mf, key=lambda k: mf[k][0])
+        pavg = mf[pdom][0] / mf[pdom][1] / 1e3
+        pach = prefill_label_flops(shape, pdom, 4, 4096) / pavg
+        gemm_time = sum(pper[k][0] for k in ("qkv", "o_proj", "gate_up", "down") if k in pper) / 1e3
+        gemm_flops = shape.n_layers * sum(prefill_label_flops(shape, k, 4, 4096)
+                                          for k in ("qkv", "o_proj", "gate_up", "down"))
+        out["prefill"] = {
+            "workload": "prefill_0p6b_4x4096: 4 x 4096 uniform-random tokens, KV for all positions, "
+                        "last-token logits",
+            "tok_s": round(4 * 4096 / pdt, 1), "ms": round(pdt * 1e3, 3),
+            "mfma_frac_pass": round(prefill_flops(shape, 4, 4096) / pdt / MFMA_BF16_PEAK, 4),
+            "mfma_frac_gemms": round(gemm_flops / gemm_time / MFMA_BF16_PEAK, 4),
+            "roofline": {"bound": "mfma", "kernel": pdom, "achieved": round(pach / 1e12, 1),
+                         "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s", "frac": round(pach / MFMA_BF16_PEAK, 4),
+                         "traffic": None, "avg_launch_us": round(pavg * 1e6, 1)},
+            "kernel_ms_per_pass": {k: round(v[0], 3) for k, v in pper.items()},
+        }
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, w, args.cpu_steps)
     print(json.dumps(out), flush=True)
 
 

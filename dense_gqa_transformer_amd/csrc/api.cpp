@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -39,11 +40,35 @@ fs_status fail(fs_status st, const std::string& msg) {
 // Up to this many rows per call the projections run as GEMV (weights streamed
 // once, fp32 activations); above it as MFMA GEMM on bf16 activations.
 constexpr int SKINNY_MAX_ROWS = GEMV_LOGITS_MAX_M;
+// In timing mode each call starts with a short device-side wait so the host
+// can queue the whole call behind it: the event pairs then bracket kernels
+// that run back to back instead of waiting on the host.
+constexpr int TIMING_GATE_US = 3000;
 constexpr int STAGE_RING = 64;
 
 struct LayerW {
   void *wqkv, *wo, *wgu, *wdown;
   float *attn_norm, *q_norm, *k_norm, *mlp_norm;
+};
+
+struct DecodeKey {
+  int B, chunk, nchunks;
+  const void *tokens, *logits, *next;
+  bool operator==(const DecodeKey& o) const {
+    return B == o.B && chunk == o.chunk && nchunks == o.nchunks && tokens == o.tokens &&
+           logits == o.logits && next == o.next;
+  }
+};
+struct DecodeGraph {
+  DecodeKey key;
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+constexpr size_t MAX_GRAPHS = 32;
+
+struct TimedLaunch {
+  const char* label;
+  hipEvent_t a, b;
 };
 
 template <class T>
@@ -86,7 +111,6 @@ struct fs_model {
   int32_t* d_slot = nullptr;
   float* part = nullptr;
   int max_chunks = 0;
-  uint32_t* counters = nullptr;   // [max_seqs * nkv] attention + 1 lm_head
   float* lm_pv = nullptr;
   int32_t* lm_pi = nullptr;
   float* logits_tmp = nullptr;    // [max_seqs, V] when the caller passes none
@@ -95,13 +119,33 @@ struct fs_model {
   hipEvent_t stage_ev[STAGE_RING] = {};
   bool stage_used[STAGE_RING] = {};
   int stage_next = 0;
+  // decode steps replay captured graphs, one per launch configuration
+  hipStream_t cap_stream = nullptr;
+  std::vector<DecodeGraph> graphs;
+  bool use_graphs = true;
+  // measurement hook: per-launch event pairs, labelled by step
+  bool timing = false;
+  std::vector<TimedLaunch> timed;
+  std::vector<hipEvent_t> ev_free;
+
+  void drop_graphs() {
+    for (auto& g : graphs) {
+      hipGraphExecDestroy(g.exec);
+      hipGraphDestroy(g.graph);
+    }
+    graphs.clear();
+  }
 
   ~fs_model() {
     hipDeviceSynchronize();
+    drop_graphs();
+    if (cap_stream) hipStreamDestroy(cap_stream);
+    for (auto& t : timed) { hipEventDestroy(t.a); hipEventDestroy(t.b); }
+    for (auto e : ev_free) hipEventDestroy(e);
     hipFree(wblob); hipFree(nblob); hipFree(kcache); hipFree(vcache);
     hipFree(rope_cos); hipFree(rope_sin);
     hipFree(x); hipFree(xn); hipFree(qkv); hipFree(qr); hipFree(attn); hipFree(hbuf);
-    hipFree(d_pos); hipFree(d_slot); hipFree(part); hipFree(counters);
+    hipFree(d_pos); hipFree(d_slot); hipFree(part);
     hipFree(lm_pv); hipFree(lm_pi); hipFree(logits_tmp);
     for (int i = 0; i < STAGE_RING; ++i)
       if (stage_ev[i]) hipEventDestroy(stage_ev[i]);
@@ -111,9 +155,37 @@ struct fs_model {
 
 namespace {
 
+hipEvent_t take_event(fs_model* m) {
+  if (!m->ev_free.empty()) {
+    hipEvent_t e = m->ev_free.back();
+    m->ev_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Enqueues one kernel launch; in timing mode brackets it with events.
+#define LAUNCH(m, label, s, expr)                                     \
+  do {                                                                \
+    hipEvent_t a_ = nullptr;                                          \
+    if ((m)->timing && (a_ = take_event(m)) != nullptr)               \
+      HIP_TRY(hipEventRecord(a_, s));                                 \
+    HIP_TRY(expr);                                                    \
+    if (a_ != nullptr) {                                              \
+      hipEvent_t b_ = take_event(m);                                  \
+      if (b_ != nullptr) {                                            \
+        HIP_TRY(hipEventRecord(b_, s));                               \
+        (m)->timed.push_back({label, a_, b_});                        \
+      }                                                               \
+    }                                                                 \
+  } while (0)
+
 fs_status ensure_rows(fs_model* m, long long rows, hipStream_t s) {
   if (rows <= m->scratch_rows) return FS_OK;
   HIP_TRY(hipStreamSynchronize(s));
+  m->drop_graphs();   // captured graphs point at the old buffers
   hipFree(m->x); hipFree(m->xn); hipFree(m->qkv); hipFree(m->qr); hipFree(m->attn); hipFree(m->hbuf);
   m->x = nullptr; m->xn = m->qkv = m->qr = m->attn = m->hbuf = nullptr;
   m->scratch_rows = 0;
@@ -167,32 +239,35 @@ fs_status head(fs_model* m, const float* xrows, int rows, int ldx, float* logits
     p.w = m->embed; p.N = c.vocab; p.K = c.hidden;
     p.a = xrows; p.lda = ldx; p.M = rows;
     p.gamma = m->final_norm; p.eps = c.rms_eps;
-    p.logits = logits; p.ldo = c.vocab; p.next = next;
+    p.logits = logits; p.ldo = c.vocab;
     p.part_val = m->lm_pv; p.part_idx = m->lm_pi;
-    p.counter = m->counters + (size_t)c.max_seqs * c.n_kv_heads;
-    HIP_TRY(gemv(m->dt, EPI_LOGITS, p, s));
+    LAUNCH(m, "head", s, gemv(m->dt, EPI_LOGITS, p, s));
+    if (next)
+      LAUNCH(m, "argmax", s, argmax_partials(m->lm_pv, m->lm_pi, gemv_logits_blocks(c.vocab, c.hidden), rows,
+                                             next, s));
     return FS_OK;
   }
-  float* lg = logits;
-  if (lg == nullptr) {
-    if (m->logits_tmp == nullptr &&
-        dalloc(&m->logits_tmp, (size_t)c.max_seqs * c.vocab * sizeof(float)) != hipSuccess)
-      return fail(FS_ERR_OOM, "logits scratch allocation failed");
-    lg = m->logits_tmp;
-  }
+  float* lg = logits != nullptr ? logits : m->logits_tmp;   // logits_tmp allocated by the caller
   if (m->dt == DT_BF16) {
-    HIP_TRY(rmsnorm(xrows, rows, c.hidden, ldx, m->final_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s));
-    HIP_TRY(gemm_bf16(GEPI_STORE_F32, m->xn, c.hidden, m->embed, c.hidden, lg, c.vocab, rows, c.vocab,
-                      c.hidden, s));
+    LAUNCH(m, "norm", s, rmsnorm(xrows, rows, c.hidden, ldx, m->final_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s));
+    LAUNCH(m, "head", s, gemm_bf16(GEPI_STORE_F32, m->xn, c.hidden, m->embed, c.hidden, lg, c.vocab, rows,
+                                   c.vocab, c.hidden, s));
   } else {
     GemvParams p{};
     p.w = m->embed; p.N = c.vocab; p.K = c.hidden;
     p.a = xrows; p.lda = ldx; p.M = rows;
     p.gamma = m->final_norm; p.eps = c.rms_eps;
     p.out = lg; p.ldo = c.vocab;
-    HIP_TRY(gemv(m->dt, EPI_STORE, p, s));
+    LAUNCH(m, "head", s, gemv(m->dt, EPI_STORE, p, s));
   }
-  if (next) HIP_TRY(argmax_rows(lg, rows, c.vocab, c.vocab, next, s));
+  if (next) LAUNCH(m, "argmax", s, argmax_rows(lg, rows, c.vocab, c.vocab, next, s));
+  return FS_OK;
+}
+
+fs_status ensure_logits_tmp(fs_model* m) {
+  if (m->logits_tmp == nullptr &&
+      dalloc(&m->logits_tmp, (size_t)m->cfg.max_seqs * m->cfg.vocab * sizeof(float)) != hipSuccess)
+    return fail(FS_ERR_OOM, "logits scratch allocation failed");
   return FS_OK;
 }
 
@@ -207,24 +282,24 @@ fs_status block_skinny(fs_model* m, const LayerW& L, int rows, Attn&& attention,
   p.w = L.wqkv; p.N = m->qkv_w; p.K = c.hidden;
   p.a = m->x; p.lda = c.hidden; p.M = rows; p.gamma = L.attn_norm;
   p.out = (float*)m->qkv; p.ldo = m->qkv_w;
-  HIP_TRY(gemv(m->dt, EPI_STORE, p, s));
+  LAUNCH(m, "qkv", s, gemv(m->dt, EPI_STORE, p, s));
   fs_status st = attention();
   if (st != FS_OK) return st;
   // output projection + residual
   p.w = L.wo; p.N = c.hidden; p.K = m->qw;
   p.a = (const float*)m->attn; p.lda = m->qw; p.gamma = nullptr;
   p.out = m->x; p.ldo = c.hidden;
-  HIP_TRY(gemv(m->dt, EPI_RESID, p, s));
+  LAUNCH(m, "o_proj", s, gemv(m->dt, EPI_RESID, p, s));
   // RMSNorm + gate/up + SwiGLU
   p.w = L.wgu; p.N = c.ffn; p.K = c.hidden;
   p.a = m->x; p.lda = c.hidden; p.gamma = L.mlp_norm;
   p.out = (float*)m->hbuf; p.ldo = c.ffn;
-  HIP_TRY(gemv(m->dt, EPI_SWIGLU, p, s));
+  LAUNCH(m, "gate_up", s, gemv(m->dt, EPI_SWIGLU, p, s));
   // down projection + residual
   p.w = L.wdown; p.N = c.hidden; p.K = c.ffn;
   p.a = (const float*)m->hbuf; p.lda = c.ffn; p.gamma = nullptr;
   p.out = m->x; p.ldo = c.hidden;
-  HIP_TRY(gemv(m->dt, EPI_RESID, p, s));
+  LAUNCH(m, "down", s, gemv(m->dt, EPI_RESID, p, s));
   return FS_OK;
 }
 
@@ -238,16 +313,18 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
   // rounding it to bf16 alone moves the logits by about as much as the whole
   // error budget, while the MLP input tolerates plain bf16.
   void* xn_lo = (char*)m->xn + (size_t)rows * c.hidden * 2;
-  HIP_TRY(rmsnorm(m->x, rows, c.hidden, c.hidden, L.attn_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s, xn_lo));
-  HIP_TRY(gemm_bf16(qkv_f32 ? GEPI_STORE_F32 : GEPI_STORE_BF16, m->xn, c.hidden, L.wqkv, c.hidden,
-                    m->qkv, m->qkv_w, rows, m->qkv_w, c.hidden, s, xn_lo));
+  LAUNCH(m, "norm", s, rmsnorm(m->x, rows, c.hidden, c.hidden, L.attn_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s, xn_lo));
+  LAUNCH(m, "qkv", s, gemm_bf16(qkv_f32 ? GEPI_STORE_F32 : GEPI_STORE_BF16, m->xn, c.hidden, L.wqkv, c.hidden,
+                                m->qkv, m->qkv_w, rows, m->qkv_w, c.hidden, s, xn_lo));
   fs_status st = attention();
   if (st != FS_OK) return st;
-  HIP_TRY(gemm_bf16(GEPI_RESID_F32, m->attn, m->qw, L.wo, m->qw, m->x, c.hidden, rows, c.hidden, m->qw, s));
-  HIP_TRY(rmsnorm(m->x, rows, c.hidden, c.hidden, L.mlp_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s));
-  HIP_TRY(gemm_bf16(GEPI_SWIGLU_BF16, m->xn, c.hidden, L.wgu, c.hidden, m->hbuf, c.ffn, rows, 2 * c.ffn,
-                    c.hidden, s));
-  HIP_TRY(gemm_bf16(GEPI_RESID_F32, m->hbuf, c.ffn, L.wdown, c.ffn, m->x, c.hidden, rows, c.hidden, c.ffn, s));
+  LAUNCH(m, "o_proj", s, gemm_bf16(GEPI_RESID_F32, m->attn, m->qw, L.wo, m->qw, m->x, c.hidden, rows, c.hidden,
+                                   m->qw, s));
+  LAUNCH(m, "norm", s, rmsnorm(m->x, rows, c.hidden, c.hidden, L.mlp_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s));
+  LAUNCH(m, "gate_up", s, gemm_bf16(GEPI_SWIGLU_BF16, m->xn, c.hidden, L.wgu, c.hidden, m->hbuf, c.ffn, rows,
+                                    2 * c.ffn, c.hidden, s));
+  LAUNCH(m, "down", s, gemm_bf16(GEPI_RESID_F32, m->hbuf, c.ffn, L.wdown, c.ffn, m->x, c.hidden, rows, c.hidden,
+                                 c.ffn, s));
   return FS_OK;
 }
 
@@ -370,15 +447,18 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   if (dalloc(&m->d_pos, (size_t)c.max_seqs * 4) != hipSuccess ||
       dalloc(&m->d_slot, (size_t)c.max_seqs * 4) != hipSuccess ||
       dalloc(&m->part, (size_t)c.max_seqs * c.n_heads * m->max_chunks * (c.head_dim + 2) * 4) != hipSuccess ||
-      dalloc(&m->counters, ((size_t)c.max_seqs * c.n_kv_heads + 1) * 4) != hipSuccess ||
       dalloc(&m->lm_pv, (size_t)GEMV_LOGITS_MAX_M * lm_blocks * 4) != hipSuccess ||
       dalloc(&m->lm_pi, (size_t)GEMV_LOGITS_MAX_M * lm_blocks * 4) != hipSuccess)
     return bail(FS_ERR_OOM, "decode scratch allocation failed");
-  chk(hipMemsetAsync(m->counters, 0, ((size_t)c.max_seqs * c.n_kv_heads + 1) * 4, s));
   if (hipHostMalloc((void**)&m->stage, sizeof(int32_t) * 2 * c.max_seqs * STAGE_RING, hipHostMallocDefault) !=
       hipSuccess)
     return bail(FS_ERR_OOM, "pinned staging allocation failed");
   for (int i = 0; i < STAGE_RING; ++i) chk(hipEventCreateWithFlags(&m->stage_ev[i], hipEventDisableTiming));
+  chk(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
+  {
+    const char* env = std::getenv("FS_DECODE_GRAPHS");
+    if (env != nullptr && env[0] == '0') m->use_graphs = false;
+  }
   chk(hipStreamSynchronize(s));
   if (e != hipSuccess) return bail(FS_ERR_HIP, std::string("model setup failed: ") + hipGetErrorString(e));
   m->slot_len.assign(c.max_seqs, 0);
@@ -409,7 +489,8 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
   if (T > (1LL << 31) / std::max(m->qkv_w, c.ffn)) return fail(FS_ERR_UNSUPPORTED, "B*S too large");
   if ((st = ensure_rows(m, T, s)) != FS_OK) return st;
   if ((st = stage_ints(m, nullptr, slots, B, s)) != FS_OK) return st;
-  HIP_TRY(embed(m->embed, m->dt, tokens, (int)T, c.hidden, c.vocab, m->x, s));
+  if (m->timing) LAUNCH(m, "gate", s, spin_wait(TIMING_GATE_US, s));
+  LAUNCH(m, "embed", s, embed(m->embed, m->dt, tokens, (int)T, c.hidden, c.vocab, m->x, s));
   const bool skinny = (m->dt == DT_F32) || T <= SKINNY_MAX_ROWS;
   const int act_dt = skinny ? DT_F32 : DT_BF16;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -424,14 +505,14 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
       r.cos_t = m->rope_cos; r.sin_t = m->rope_sin; r.slots = m->d_slot;
       r.T = (int)T; r.S_per = S; r.nq = c.n_heads; r.nkv = c.n_kv_heads; r.d = c.head_dim;
       r.slot_stride = m->slot_stride; r.head_stride = m->head_stride;
-      HIP_TRY(rope_kv(r, s));
+      LAUNCH(m, "rope_kv", s, rope_kv(r, s));
       AttnPrefillParams a{};
       a.q = m->qr; a.q_dt = act_dt; a.kcache = kc; a.vcache = vc; a.kv_dt = m->dt;
       a.out = m->attn; a.o_dt = act_dt; a.slots = m->d_slot;
       a.B = B; a.S = S; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim;
       a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
       a.scale = 1.0f / std::sqrt((float)c.head_dim);
-      HIP_TRY(skinny ? attn_prefill_vec(a, s) : attn_prefill(a, s));
+      LAUNCH(m, "attn", s, skinny ? attn_prefill_vec(a, s) : attn_prefill(a, s));
       return FS_OK;
     };
     st = skinny ? block_skinny(m, L, (int)T, attention, s) : block_gemm(m, L, (int)T, false, attention, s);
@@ -442,6 +523,38 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
   if (st != FS_OK) return st;
   for (int b = 0; b < B; ++b) m->slot_len[slots[b]] = S;
   return FS_OK;
+}
+
+// Every kernel of one decode step, in order, on stream s.
+static fs_status enqueue_decode(fs_model* m, const int32_t* tokens, int B, float* logits, int32_t* next,
+                                int chunk, int nchunks, hipStream_t s) {
+  const fs_config& c = m->cfg;
+  if (m->timing) LAUNCH(m, "gate", s, spin_wait(TIMING_GATE_US, s));
+  LAUNCH(m, "embed", s, embed(m->embed, m->dt, tokens, B, c.hidden, c.vocab, m->x, s));
+  const bool skinny = (m->dt == DT_F32) || B <= SKINNY_MAX_ROWS;
+  fs_status st = FS_OK;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& L = m->layers[l];
+    char* kc = (char*)m->kcache + (size_t)l * m->layer_stride * m->esz;
+    char* vc = (char*)m->vcache + (size_t)l * m->layer_stride * m->esz;
+    auto attention = [&]() -> fs_status {
+      AttnDecodeParams a{};
+      a.qkv = (const float*)m->qkv; a.kcache = kc; a.vcache = vc; a.kv_dt = m->dt;
+      a.gq = L.q_norm; a.gk = L.k_norm; a.eps = c.rms_eps;
+      a.cos_t = m->rope_cos; a.sin_t = m->rope_sin; a.positions = m->d_pos; a.slots = m->d_slot;
+      a.part = m->part;
+      a.B = B; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim; a.chunk = chunk; a.nchunks = nchunks;
+      a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
+      a.scale = 1.0f / std::sqrt((float)c.head_dim);
+      LAUNCH(m, "attn", s, attn_decode(a, s));
+      LAUNCH(m, "combine", s, attn_combine(m->part, m->d_pos, B, c.n_heads, c.head_dim, chunk, nchunks,
+                                           m->attn, skinny ? DT_F32 : DT_BF16, s));
+      return FS_OK;
+    };
+    st = skinny ? block_skinny(m, L, B, attention, s) : block_gemm(m, L, B, true, attention, s);
+    if (st != FS_OK) return st;
+  }
+  return head(m, m->x, B, c.hidden, logits, next, s);
 }
 
 fs_status fs_decode_step(fs_model* m, const int32_t* tokens, const int32_t* positions, const int32_t* slots,
@@ -465,37 +578,81 @@ fs_status fs_decode_step(fs_model* m, const int32_t* tokens, const int32_t* posi
   }
   hipStream_t s = (hipStream_t)stream;
   if ((st = ensure_rows(m, B, s)) != FS_OK) return st;
+  if (B > GEMV_LOGITS_MAX_M && logits == nullptr && (st = ensure_logits_tmp(m)) != FS_OK) return st;
   if ((st = stage_ints(m, positions, slots, B, s)) != FS_OK) return st;
-  // split-K chunking of the context: enough workgroups to cover the chip
+  // split-K chunking of the context: enough workgroups to cover the chip.  The
+  // chunk count is rounded up to a power of two (chunks past a sequence's end
+  // exit at once) so one captured graph serves many consecutive positions.
   int chunk = 32;
   while (chunk < 256 && (long long)((maxn + chunk - 1) / chunk) * c.n_kv_heads * B > 1024) chunk *= 2;
-  const int nchunks = (maxn + chunk - 1) / chunk;
+  int nchunks = 1;
+  while (nchunks < (maxn + chunk - 1) / chunk) nchunks *= 2;
+  nchunks = std::min(nchunks, (c.max_ctx + chunk - 1) / chunk);
   if (nchunks > m->max_chunks) return fail(FS_ERR_HIP, "internal: chunk count exceeds scratch");
-  HIP_TRY(embed(m->embed, m->dt, tokens, B, c.hidden, c.vocab, m->x, s));
-  const bool skinny = (m->dt == DT_F32) || B <= SKINNY_MAX_ROWS;
-  for (int l = 0; l < c.n_layers; ++l) {
-    const LayerW& L = m->layers[l];
-    char* kc = (char*)m->kcache + (size_t)l * m->layer_stride * m->esz;
-    char* vc = (char*)m->vcache + (size_t)l * m->layer_stride * m->esz;
-    auto attention = [&]() -> fs_status {
-      AttnDecodeParams a{};
-      a.qkv = (const float*)m->qkv; a.kcache = kc; a.vcache = vc; a.kv_dt = m->dt;
-      a.gq = L.q_norm; a.gk = L.k_norm; a.eps = c.rms_eps;
-      a.cos_t = m->rope_cos; a.sin_t = m->rope_sin; a.positions = m->d_pos; a.slots = m->d_slot;
-      a.out = m->attn; a.o_dt = skinny ? DT_F32 : DT_BF16;
-      a.part = m->part; a.counters = m->counters;
-      a.B = B; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim; a.chunk = chunk; a.nchunks = nchunks;
-      a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
-      a.scale = 1.0f / std::sqrt((float)c.head_dim);
-      HIP_TRY(attn_decode(a, s));
-      return FS_OK;
-    };
-    st = skinny ? block_skinny(m, L, B, attention, s) : block_gemm(m, L, B, true, attention, s);
-    if (st != FS_OK) return st;
+  if (!m->use_graphs || m->timing) {
+    if ((st = enqueue_decode(m, tokens, B, logits, next, chunk, nchunks, s)) != FS_OK) return st;
+  } else {
+    const DecodeKey key{B, chunk, nchunks, tokens, logits, next};
+    DecodeGraph* g = nullptr;
+    for (auto& e : m->graphs)
+      if (e.key == key) { g = &e; break; }
+    if (g == nullptr) {
+      if (m->graphs.size() >= MAX_GRAPHS) {
+        HIP_TRY(hipStreamSynchronize(s));
+        m->drop_graphs();
+      }
+      DecodeGraph ng{key, nullptr, nullptr};
+      HIP_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeRelaxed));
+      st = enqueue_decode(m, tokens, B, logits, next, chunk, nchunks, m->cap_stream);
+      const hipError_t ec = hipStreamEndCapture(m->cap_stream, &ng.graph);
+      if (st != FS_OK) {
+        if (ng.graph) hipGraphDestroy(ng.graph);
+        return st;
+      }
+      if (ec != hipSuccess) return fail(FS_ERR_HIP, std::string("graph capture failed: ") + hipGetErrorString(ec));
+      const hipError_t ei = hipGraphInstantiate(&ng.exec, ng.graph, nullptr, nullptr, 0);
+      if (ei != hipSuccess) {
+        hipGraphDestroy(ng.graph);
+        return fail(FS_ERR_HIP, std::string("graph instantiate failed: ") + hipGetErrorString(ei));
+      }
+      m->graphs.push_back(ng);
+      g = &m->graphs.back();
+    }
+    HIP_TRY(hipGraphLaunch(g->exec, s));
   }
-  st = head(m, m->x, B, c.hidden, logits, next, s);
-  if (st != FS_OK) return st;
   for (int i = 0; i < B; ++i) m->slot_len[slots[i]] = positions[i] + 1;
+  return FS_OK;
+}
+
+fs_status fs_timing(fs_model* m, int32_t enable) {
+  g_err.clear();
+  if (m == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL model");
+  HIP_TRY(hipDeviceSynchronize());
+  for (auto& t : m->timed) {
+    m->ev_free.push_back(t.a);
+    m->ev_free.push_back(t.b);
+  }
+  m->timed.clear();
+  m->timing = enable != 0;
+  return FS_OK;
+}
+
+fs_status fs_timing_read(fs_model* m, const char* label, double* total_ms, int64_t* launches) {
+  g_err.clear();
+  if (m == nullptr || label == nullptr || total_ms == nullptr || launches == nullptr)
+    return fail(FS_ERR_INVALID_ARG, "NULL argument");
+  double tot = 0.0;
+  int64_t n = 0;
+  for (auto& t : m->timed) {
+    if (std::strcmp(t.label, label) != 0) continue;
+    HIP_TRY(hipEventSynchronize(t.b));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, t.a, t.b));
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
   return FS_OK;
 }
 

@@ -13,8 +13,8 @@
 //
 // Decode kernel: one workgroup per (sequence, KV head, context chunk).  It
 // also normalises and rotates the new token's q and k and appends k, v to
-// the cache (fused), and the last workgroup of each (sequence, KV head)
-// combines the chunk partials (split-K flash decoding).
+// the cache (fused), and writes the chunk's partial softmax state; the
+// partials are combined by the consumer (split-K flash decoding).
 #include "common.h"
 #include "kernels.h"
 
@@ -113,7 +113,7 @@ __device__ __forceinline__ void attend(SoftState<REP, D / 16>& st, const float (
 }
 
 // ------------------------------------------------------------------ decode
-template <typename KV, int D, int REP, typename TO>
+template <typename KV, int D, int REP>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams p) {
   constexpr int DP = D / 16;
   constexpr int HALF = D / 2;
@@ -121,7 +121,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
   __shared__ float knew[D], vnew[D];
   __shared__ float sm[4][REP], sl[4][REP];
   __shared__ float so[4][REP][D];
-  __shared__ bool last;
 
   const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -132,7 +131,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
   const int c0 = c * p.chunk;
   if (c0 >= n) return;                                  // chunk past this sequence
   const int c1 = min(c0 + p.chunk, n);
-  const int nvalid = (n + p.chunk - 1) / p.chunk;
   const int W = (p.nq + 2 * p.nkv) * D;
   const float* row = p.qkv + (size_t)b * W;
   const size_t kvoff = (size_t)slot * p.slot_stride + (size_t)j * p.head_stride;
@@ -201,7 +199,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
   }
   __syncthreads();
 
-  TO* out = reinterpret_cast<TO*>(p.out) + (size_t)b * p.nq * D;
   for (int idx = tid; idx < REP * D; idx += 256) {
     const int r = idx / D, e = idx % D;
     float M = sm[0][r];
@@ -215,51 +212,83 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
       O += so[w][r][e] * a;
     }
     const int h = j * REP + r;
-    if (nvalid == 1) {
-      out[h * D + e] = from_f32<TO>(O / L);
-    } else {
-      float* pr = p.part + (((size_t)b * p.nq + h) * p.nchunks + c) * (D + 2);
-      pr[e] = O;
-      if (e == 0) { pr[D] = M; pr[D + 1] = L; }
-    }
+    float* pr = p.part + (((size_t)b * p.nq + h) * p.nchunks + c) * (D + 2);
+    pr[e] = O;
+    if (e == 0) { pr[D] = M; pr[D + 1] = L; }
   }
-  if (nvalid == 1) return;
-
-  // ---- split-K combine by the last chunk workgroup of this (sequence, KV head)
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t done = atomicAdd(p.counters + (size_t)b * p.nkv + j, 1u);
-    last = (done == (uint32_t)(nvalid - 1));
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  for (int idx = tid; idx < REP * D; idx += 256) {
-    const int r = idx / D, e = idx % D;
-    const int h = j * REP + r;
-    const float* pr = p.part + ((size_t)b * p.nq + h) * p.nchunks * (D + 2);
-    float M = -INFINITY;
-    for (int cc = 0; cc < nvalid; ++cc) M = fmaxf(M, pr[cc * (D + 2) + D]);
-    float L = 0.f, O = 0.f;
-    for (int cc = 0; cc < nvalid; ++cc) {
-      const float a = exp2f(pr[cc * (D + 2) + D] - M);
-      L += pr[cc * (D + 2) + D + 1] * a;
-      O += pr[cc * (D + 2) + e] * a;
-    }
-    out[h * D + e] = from_f32<TO>(O / L);
-  }
-  if (tid == 0) p.counters[(size_t)b * p.nkv + j] = 0u;
 }
 
-template <typename KV, int D, typename TO>
+// Combines the chunk partials of each (sequence, query head): one wave per
+// pair.  Every load of the first 32 chunks is issued at once (the chunk
+// maxima and sums by lane, the output slices for each lane's d/64 elements),
+// so a short context costs a single memory round trip; longer contexts loop.
+template <typename TO, int D>
+__global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ part,
+                                                          const int32_t* __restrict__ positions, int nq,
+                                                          int chunk, int nchunks, TO* __restrict__ out) {
+  constexpr int ST = D + 2, NE = D / 64, CB = 32;
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const float* pr = part + ((size_t)b * nq + h) * nchunks * ST;
+  const int nvalid = (positions[b] + chunk) / chunk;
+  float M = -INFINITY, L = 0.f, o[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) o[e] = 0.f;
+  for (int c0 = 0; c0 < nvalid; c0 += CB) {
+    const int n = min(CB, nvalid - c0);
+    // lane c < n holds chunk c0 + c's max and sum; every lane holds its output slice of each chunk
+    const float mc = (lane < n) ? pr[(size_t)(c0 + lane) * ST + D] : -INFINITY;
+    const float lc = (lane < n) ? pr[(size_t)(c0 + lane) * ST + D + 1] : 0.f;
+    float ov[CB][NE];
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+#pragma unroll
+      for (int e = 0; e < NE; ++e) ov[i][e] = (i < n) ? pr[(size_t)(c0 + i) * ST + lane + 64 * e] : 0.f;
+    const float mb = wave_max(mc);
+    const float mn = fmaxf(M, mb);
+    const float corr = (M == -INFINITY) ? 0.f : exp2f(M - mn);
+    const float wl = (lane < n) ? exp2f(mc - mn) : 0.f;
+    L = L * corr + wave_sum(lc * wl);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) o[e] *= corr;
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const float wi = __shfl(wl, i);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) o[e] = fmaf(wi, ov[i][e], o[e]);
+    }
+    M = mn;
+  }
+  const float invL = 1.f / L;
+  TO* orow = out + ((size_t)b * nq + h) * D;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) orow[lane + 64 * e] = from_f32<TO>(o[e] * invL);
+}
+
+hipError_t attn_combine(const float* part, const int32_t* positions, int B, int nq, int d, int chunk,
+                        int nchunks, void* out, int o_dt, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  const dim3 grid(nq, B);
+  if (d == 128 && o_dt == DT_BF16)
+    attn_combine_kernel<bf16, 128><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (bf16*)out);
+  else if (d == 128)
+    attn_combine_kernel<float, 128><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (float*)out);
+  else if (d == 64 && o_dt == DT_BF16)
+    attn_combine_kernel<bf16, 64><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (bf16*)out);
+  else if (d == 64)
+    attn_combine_kernel<float, 64><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (float*)out);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <typename KV, int D>
 static hipError_t decode_rep(const AttnDecodeParams& p, hipStream_t s) {
   const dim3 grid(p.nchunks, p.nkv, p.B);
   switch (p.nq / p.nkv) {
-    case 1: attn_decode_kernel<KV, D, 1, TO><<<grid, 256, 0, s>>>(p); break;
-    case 2: attn_decode_kernel<KV, D, 2, TO><<<grid, 256, 0, s>>>(p); break;
-    case 4: attn_decode_kernel<KV, D, 4, TO><<<grid, 256, 0, s>>>(p); break;
-    case 8: attn_decode_kernel<KV, D, 8, TO><<<grid, 256, 0, s>>>(p); break;
+    case 1: attn_decode_kernel<KV, D, 1><<<grid, 256, 0, s>>>(p); break;
+    case 2: attn_decode_kernel<KV, D, 2><<<grid, 256, 0, s>>>(p); break;
+    case 4: attn_decode_kernel<KV, D, 4><<<grid, 256, 0, s>>>(p); break;
+    case 8: attn_decode_kernel<KV, D, 8><<<grid, 256, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -268,18 +297,11 @@ static hipError_t decode_rep(const AttnDecodeParams& p, hipStream_t s) {
 hipError_t attn_decode(const AttnDecodeParams& p, hipStream_t s) {
   if (p.B <= 0) return hipSuccess;
   if (p.kv_dt == DT_BF16) {
-    if (p.o_dt == DT_BF16) {
-      if (p.d == 128) return decode_rep<bf16, 128, bf16>(p, s);
-      if (p.d == 64) return decode_rep<bf16, 64, bf16>(p, s);
-    } else {
-      if (p.d == 128) return decode_rep<bf16, 128, float>(p, s);
-      if (p.d == 64) return decode_rep<bf16, 64, float>(p, s);
-    }
+    if (p.d == 128) return decode_rep<bf16, 128>(p, s);
+    if (p.d == 64) return decode_rep<bf16, 64>(p, s);
   } else {
-    if (p.o_dt == DT_F32) {
-      if (p.d == 128) return decode_rep<float, 128, float>(p, s);
-      if (p.d == 64) return decode_rep<float, 64, float>(p, s);
-    }
+    if (p.d == 128) return decode_rep<float, 128>(p, s);
+    if (p.d == 64) return decode_rep<float, 64>(p, s);
   }
   return hipErrorInvalidValue;
 }

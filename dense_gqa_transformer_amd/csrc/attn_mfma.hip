@@ -4,31 +4,42 @@
 // diagonal, softmax of q.k/sqrt(d)); flash-style tiling so the S x S score
 // matrix never leaves registers.
 //
-// One workgroup = 4 waves = 128 queries of one query head; each wave owns 32
-// queries.  Key/value tiles of 64 positions are staged in LDS: K row-major
-// [key][d], V transposed [d][key].  Each wave computes the transposed scores
-// S^T = K . Q^T (keys on rows, its 32 queries on columns) with
-// v_mfma_f32_32x32x16_bf16, so every lane owns one query column: the row
-// max / sum of the online softmax is a reduction over the lane's own
-// registers plus one exchange with the lane 32 away.  The probabilities then
-// feed O^T += V^T . P^T straight from the accumulator registers: for a
-// 16-key step, lane half h holds keys {4h..4h+3, 8+4h..8+4h+3} in its
-// registers, and the V^T fragment is read with the same key order, so A and
-// B agree on k whatever order the unit reduces in.
+// One workgroup = HPW query heads of one KV group x 128 queries, 4 waves per
+// head; each wave owns 32 queries.  The heads of a group share every
+// key/value tile, staged once in LDS: K row-major [key][d], V transposed
+// [d][key].  The next tile is fetched into registers while the current one is
+// being used.  Each wave computes the transposed scores S^T = K . Q^T (keys on
+// rows, its 32 queries on columns) with v_mfma_f32_32x32x16_bf16, so every
+// lane owns one query column: the softmax max / sum is a reduction over the
+// lane's own registers plus one exchange with the lane 32 away.  The
+// probabilities then feed O^T += V^T . P^T straight from the accumulator
+// registers: for a 16-key step, lane half h holds keys {4h..4h+3,
+// 8+4h..8+4h+3} in its registers, and the V^T fragment is read in the same
+// key order, so A and B agree on k whatever order the unit reduces in.
+//
+// Softmax in base 2 with a lazily updated running max: the reference max only
+// moves when a score exceeds it by more than 2^8, so the rescale of the
+// output accumulators is almost never executed; the result is exact either
+// way since the final division uses the matching sum.
 #include "common.h"
 #include "kernels.h"
 
 namespace fsk {
 
 static constexpr float LOG2E_M = 1.4426950408889634f;
+static constexpr float LAZY_MAX = 8.0f;   // log2 of the largest un-rescaled p
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(const AttnPrefillParams p) {
+template <int D, int HPW>
+__global__ __launch_bounds__(256 * HPW) void attn_prefill_mfma_kernel(const AttnPrefillParams p) {
   constexpr int BQ = 128, BKV = 64;
+  constexpr int NT = 256 * HPW;     // threads
   constexpr int LDK = D + 8;        // K tile row stride (elements)
   constexpr int LDV = BKV + 8;      // V^T tile row stride (elements)
   constexpr int KS = D / 16;        // k-steps of the score product
   constexpr int DB = D / 32;        // 32-row blocks of O^T
+  constexpr int CH = BKV * D / 8;   // 16-byte chunks per K (or V) tile
+  constexpr int CPT = CH / NT;      // chunks per thread
+  static_assert(CPT >= 1 && CH % NT == 0, "tile / thread mismatch");
   __shared__ __attribute__((aligned(16))) bf16 Ks[BKV * LDK];
   __shared__ __attribute__((aligned(16))) bf16 Vt[D * LDV];
 
@@ -36,11 +47,11 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(const AttnPrefil
   const int col = lane & 31, half = lane >> 5;
   const int S = p.S;
   const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;   // longest tiles first
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int rep = p.nq / p.nkv;
-  const int j = h / rep;
+  const int b = blockIdx.z;
+  const int h = blockIdx.y * HPW + (wid >> 2);            // this wave's query head
+  const int j = h / (p.nq / p.nkv);
   const int q0 = qt * BQ;
-  const int wq0 = q0 + wid * 32;
+  const int wq0 = q0 + (wid & 3) * 32;
   const int myq = wq0 + col;
   const int slot = p.slots[b];
   const size_t kvoff = (size_t)slot * p.slot_stride + (size_t)j * p.head_stride;
@@ -56,7 +67,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(const AttnPrefil
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + half * 8);
   }
-  const float qscale = p.scale * LOG2E_M;
+  const float c2 = p.scale * LOG2E_M;   // raw score -> base-2 exponent
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[DB];
 #pragma unroll
@@ -64,35 +75,46 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(const AttnPrefil
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
-  const int kend = min(q0 + BQ, S);
-  constexpr int KCH = BKV * D / 8;            // 16-byte chunks per tile
-  for (int k0 = 0; k0 < kend; k0 += BKV) {
-    __syncthreads();                          // previous tile fully consumed
-    // K: coalesced rows;  V: lanes take consecutive keys so the transposed
-    // 2-byte LDS writes of one instruction land in consecutive halfwords
+  // register staging of one K/V tile: K chunks row-major (coalesced), V
+  // chunks with consecutive keys per lane so the transposed 2-byte LDS writes
+  // of one instruction land in consecutive halfwords
+  u32x4 rk[CPT];
+  bf16x8 rv[CPT];
+  auto fetch = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < KCH / 256; ++i) {
-      const int id = tid + 256 * i;
-      {
-        const int key = id / (D / 8), c8 = (id % (D / 8)) * 8;
-        u32x4 v = u32x4{0, 0, 0, 0};
-        if (k0 + key < S) v = *reinterpret_cast<const u32x4*>(kg + (size_t)(k0 + key) * D + c8);
-        *reinterpret_cast<u32x4*>(&Ks[key * LDK + c8]) = v;
-      }
-      {
-        const int key = id % BKV, c8 = (id / BKV) * 8;
-        bf16x8 v;
-        if (k0 + key < S) {
-          v = *reinterpret_cast<const bf16x8*>(vg + (size_t)(k0 + key) * D + c8);
-        } else {
+    for (int i = 0; i < CPT; ++i) {
+      const int id = tid + NT * i;
+      const int kk = id / (D / 8), kc = (id % (D / 8)) * 8;
+      rk[i] = (k0 + kk < S) ? *reinterpret_cast<const u32x4*>(kg + (size_t)(k0 + kk) * D + kc)
+                            : u32x4{0, 0, 0, 0};
+      const int vk = id % BKV, vc = (id / BKV) * 8;
+      if (k0 + vk < S) {
+        rv[i] = *reinterpret_cast<const bf16x8*>(vg + (size_t)(k0 + vk) * D + vc);
+      } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (bf16)0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Vt[(c8 + e) * LDV + key] = v[e];
+        for (int e = 0; e < 8; ++e) rv[i][e] = (bf16)0.f;
       }
     }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int id = tid + NT * i;
+      const int kk = id / (D / 8), kc = (id % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&Ks[kk * LDK + kc]) = rk[i];
+      const int vk = id % BKV, vc = (id / BKV) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[(vc + e) * LDV + vk] = rv[i][e];
+    }
+  };
+
+  const int kend = min(q0 + BQ, S);
+  fetch(0);
+  for (int k0 = 0; k0 < kend; k0 += BKV) {
+    __syncthreads();                          // every wave is done with the previous tile
+    stash();
     __syncthreads();
+    if (k0 + BKV < kend) fetch(k0 + BKV);     // next tile in flight during this one
     if (k0 > wq0 + 31) continue;              // every query of this wave precedes the tile
 
     // ---- S^T for keys k0 + 32*kb + (8*(r/4) + 4*half + r%4), query myq
@@ -107,38 +129,42 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(const AttnPrefil
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
     }
-    // ---- scale, causal mask, online softmax (base 2)
-    const bool diag = (k0 + BKV - 1 > wq0);   // tile reaches past some query of this wave
+    // ---- causal mask (only on tiles that reach past this wave's first query)
+    if (k0 + BKV - 1 > wq0) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+          if (key > myq || key >= S) s[kb][r] = -INFINITY;
+        }
+    }
+    // ---- tile max (raw units), lazily moved running max (base-2 units)
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-        float v = s[kb][r] * qscale;
-        if (diag && (key > myq || key >= S)) v = -INFINITY;
-        s[kb][r] = v;
-        mt = fmaxf(mt, v);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m_run, mt);        // finite: key 0 <= every query, seen in tile 0
-    const float corr = exp2f(m_run - mn);
+      for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[kb][r], s[kb][r + 1]));
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
+    if (mt > m_run + LAZY_MAX) {             // rare after the first tile
+      const float corr = exp2f(m_run - mt);
+      l_run *= corr;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+      m_run = mt;
+    }
     float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = exp2f(s[kb][r] - mn);
+        const float e = exp2f(fmaf(s[kb][r], c2, -m_run));
         s[kb][r] = e;
         ls += e;
       }
-    ls += __shfl_xor(ls, 32);
-    l_run = l_run * corr + ls;
-    m_run = mn;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+    l_run += ls + __shfl_xor(ls, 32);
 
     // ---- O^T += V^T . P^T over four 16-key steps
 #pragma unroll
@@ -177,16 +203,24 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(const AttnPrefil
   }
 }
 
+template <int D>
+static hipError_t launch_mfma(const AttnPrefillParams& p, hipStream_t s) {
+  const int rep = p.nq / p.nkv;
+  if (rep % 2 == 0) {
+    const dim3 grid((p.S + 127) / 128, p.nq / 2, p.B);
+    attn_prefill_mfma_kernel<D, 2><<<grid, 512, 0, s>>>(p);
+  } else {
+    const dim3 grid((p.S + 127) / 128, p.nq, p.B);
+    attn_prefill_mfma_kernel<D, 1><<<grid, 256, 0, s>>>(p);
+  }
+  return hipGetLastError();
+}
+
 hipError_t attn_prefill(const AttnPrefillParams& p, hipStream_t s) {
   if (p.B <= 0 || p.S <= 0) return hipSuccess;
   const bool bf = p.q_dt == DT_BF16 && p.kv_dt == DT_BF16 && p.o_dt == DT_BF16;
   if (!bf || (p.d != 128 && p.d != 64)) return attn_prefill_vec(p, s);
-  const dim3 grid((p.S + 127) / 128, p.nq, p.B);
-  if (p.d == 128)
-    attn_prefill_mfma_kernel<128><<<grid, 256, 0, s>>>(p);
-  else
-    attn_prefill_mfma_kernel<64><<<grid, 256, 0, s>>>(p);
-  return hipGetLastError();
+  return p.d == 128 ? launch_mfma<128>(p, s) : launch_mfma<64>(p, s);
 }
 
 }  // namespace fsk

@@ -1,12 +1,15 @@
 // Bandwidth-bound GEMV for the decode path and other calls with few rows.
 //
 // y[m, n] = sum_k W[n, k] * a[m, k], with W stored [out, in] ("Coming back to
-// Failed Star", First sitting, item 3).  Each workgroup stages its activation
-// rows in LDS (optionally RMS-normalised, fused prologue), then each wave
-// streams RPW weight rows with 16-byte loads, lane l covering the 8-element
-// chunks l, l+64, l+128, ...  The cross-lane sum is a wave64 shuffle tree.
+// Failed Star", First sitting, item 3).  Each wave streams RPW weight rows
+// with 16-byte loads, lane l covering the 8-element chunks l, l+64, l+128, ...
+// of every row, so the 64 lanes of a wave together span the whole reduction
+// length: the RMSNorm of the activation row (fused prologue) is one wave sum,
+// with no LDS staging or workgroup barrier.  Weight loads are issued before
+// anything else and the next row group is fetched while the current one is
+// reduced.  The cross-lane dot-product sum is a wave64 shuffle tree.
 // Epilogues: plain store, residual add, SwiGLU on paired gate/up rows, and
-// lm_head logits with a block argmax reduced by the last workgroup.
+// lm_head logits with a per-workgroup argmax (reduced by argmax_partials).
 #include "common.h"
 #include "kernels.h"
 
@@ -54,55 +57,19 @@ __device__ __forceinline__ int weight_row(int slot_row, int& feature) {
 
 template <typename W, int EPI, int MB, int CPL, int RPW>
 __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) {
-  extern __shared__ float lds[];          // [MB][K] activations, then 2*16 reduce scratch
+  // activations held in registers when they fit (always for one row)
+  constexpr bool XREG = (MB * CPL <= 8);
   const int K = p.K;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int m0 = blockIdx.y * MB;
   const int mcount = min(MB, p.M - m0);
-  float* red = lds + MB * K;
-
-  // ---- prologue: stage (and optionally RMS-normalise) the activation rows
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    const bool live = m < mcount;
-    const float* arow = p.a + (size_t)(m0 + (live ? m : 0)) * p.lda;
-    float ss = 0.f;
-    for (int k = tid; k < K; k += GEMV_THREADS) {
-      const float v = live ? arow[k] : 0.f;
-      lds[m * K + k] = v;
-      ss += v * v;
-    }
-    if (p.gamma != nullptr) {
-      ss = wave_sum(ss);
-      if (lane == 0) red[m * 4 + wid] = ss;
-    }
-  }
-  if (p.gamma != nullptr) {
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      const float ss = red[m * 4] + red[m * 4 + 1] + red[m * 4 + 2] + red[m * 4 + 3];
-      const float inv = rsqrtf(ss / (float)K + p.eps);
-      for (int k = tid; k < K; k += GEMV_THREADS) lds[m * K + k] *= inv * p.gamma[k];
-    }
-  }
-  __syncthreads();
-
   const W* __restrict__ w = reinterpret_cast<const W*>(p.w);
   const int nchunk = K >> 3;
   const int slots_total = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;   // weight rows to cover
   const int rows_per_block = GEMV_WAVES * RPW * p.groups;
 
-  float best_v[MB];
-  int best_i[MB];
-#pragma unroll
-  for (int m = 0; m < MB; ++m) { best_v[m] = 0.f; best_i[m] = -1; }
-
-  for (int g = 0; g < p.groups; ++g) {
+  auto load_group = [&](int g, Raw<W> (&raw)[CPL][RPW]) {
     const int rbase = blockIdx.x * rows_per_block + (g * GEMV_WAVES + wid) * RPW;
-    if (rbase >= slots_total) break;
-    // ---- issue every weight load of this row group first
-    Raw<W> raw[CPL][RPW];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = lane + 64 * j;
@@ -116,7 +83,60 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
           raw_zero(raw[j][i]);
       }
     }
-    // ---- multiply-accumulate against the staged activations
+  };
+  Raw<W> ra[CPL][RPW], rb[CPL][RPW];
+  load_group(0, ra);          // weights first: their latency covers the prologue
+
+  // ---- prologue: per-row RMSNorm scale from this wave's own slices
+  float inv[MB];
+  float xv[XREG ? MB : 1][XREG ? CPL : 1][8];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const float* arow = p.a + (size_t)(m0 + min(m, mcount - 1)) * p.lda;
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      float v[8];
+      if (c < nchunk) load8(arow + c * 8, v);
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+      if (XREG) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[XREG ? m : 0][XREG ? j : 0][e] = v[e];
+      }
+    }
+    inv[m] = (p.gamma != nullptr) ? rsqrtf(wave_sum(ss) / (float)K + p.eps) : 1.f;
+  }
+  if (XREG && p.gamma != nullptr) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      float g[8];
+      if (c < nchunk) load8(p.gamma + c * 8, g);
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) g[e] = 0.f;
+      }
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[XREG ? m : 0][XREG ? j : 0][e] *= inv[m] * g[e];
+    }
+  }
+
+  float best_v[MB];
+  int best_i[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) { best_v[m] = 0.f; best_i[m] = -1; }
+
+  auto compute = [&](int g, const Raw<W> (&raw)[CPL][RPW]) {
+    const int rbase = blockIdx.x * rows_per_block + (g * GEMV_WAVES + wid) * RPW;
+    if (rbase >= slots_total) return;
     float acc[RPW][MB];
 #pragma unroll
     for (int i = 0; i < RPW; ++i)
@@ -125,22 +145,34 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = lane + 64 * j;
-      if (c < nchunk) {
+      if (c >= nchunk) continue;
+      float gam[8];
+      if (!XREG) {
+        if (p.gamma != nullptr) load8(p.gamma + c * 8, gam);
+        else {
 #pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          const float4 a0 = *reinterpret_cast<const float4*>(lds + m * K + c * 8);
-          const float4 a1 = *reinterpret_cast<const float4*>(lds + m * K + c * 8 + 4);
+          for (int e = 0; e < 8; ++e) gam[e] = 1.f;
+        }
+      }
 #pragma unroll
-          for (int i = 0; i < RPW; ++i) {
-            float wv[8];
-            raw_f32(raw[j][i], wv);
-            float s = acc[i][m];
-            s = fmaf(wv[0], a0.x, s); s = fmaf(wv[1], a0.y, s);
-            s = fmaf(wv[2], a0.z, s); s = fmaf(wv[3], a0.w, s);
-            s = fmaf(wv[4], a1.x, s); s = fmaf(wv[5], a1.y, s);
-            s = fmaf(wv[6], a1.z, s); s = fmaf(wv[7], a1.w, s);
-            acc[i][m] = s;
-          }
+      for (int m = 0; m < MB; ++m) {
+        float a[8];
+        if (XREG) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[e] = xv[XREG ? m : 0][XREG ? j : 0][e];
+        } else {
+          load8(p.a + (size_t)(m0 + min(m, mcount - 1)) * p.lda + c * 8, a);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[e] *= inv[m] * gam[e];
+        }
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+          float wv[8];
+          raw_f32(raw[j][i], wv);
+          float s = acc[i][m];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s = fmaf(wv[e], a[e], s);
+          acc[i][m] = s;
         }
       }
     }
@@ -149,7 +181,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
 #pragma unroll
       for (int m = 0; m < MB; ++m) acc[i][m] = wave_sum(acc[i][m]);
 
-    // ---- epilogue (lane 0 of each wave holds the sums)
+    // ---- epilogue (every lane holds the sums; lane 0 writes)
     if (lane == 0) {
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
@@ -176,20 +208,28 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
         }
       }
     }
+  };
+
+  // ping-pong over row groups with statically indexed register buffers
+  for (int g = 0; g < p.groups; g += 2) {
+    if (g + 1 < p.groups) load_group(g + 1, rb);
+    compute(g, ra);
+    if (g + 1 >= p.groups) break;
+    if (g + 2 < p.groups) load_group(g + 2, ra);
+    compute(g + 1, rb);
   }
 
   if (EPI == EPI_LOGITS) {
-    // block-level best per row, then the last block reduces all blocks
+    // block-level best per row; argmax_partials reduces the blocks afterwards
     __shared__ float bvs[GEMV_WAVES][MB];
     __shared__ int bis[GEMV_WAVES][MB];
-    __shared__ bool last;
     if (lane == 0) {
 #pragma unroll
       for (int m = 0; m < MB; ++m) { bvs[wid][m] = best_v[m]; bis[wid][m] = best_i[m]; }
     }
     __syncthreads();
-    if (tid < MB) {
-      const int m = tid;
+    if ((int)threadIdx.x < mcount) {
+      const int m = threadIdx.x;
       float bv = bvs[0][m];
       int bi = bis[0][m];
       for (int ww = 1; ww < GEMV_WAVES; ++ww)
@@ -197,40 +237,36 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
       p.part_val[(size_t)m * gridDim.x + blockIdx.x] = bv;
       p.part_idx[(size_t)m * gridDim.x + blockIdx.x] = bi;
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t done = atomicAdd(p.counter, 1u);
-      last = (done == gridDim.x - 1);
-    }
-    __syncthreads();
-    if (last) {
-      __threadfence();
-      for (int m = 0; m < mcount; ++m) {
-        float bv = 0.f;
-        int bi = -1;
-        for (int b = tid; b < (int)gridDim.x; b += GEMV_THREADS) {
-          const float v = __builtin_nontemporal_load(p.part_val + (size_t)m * gridDim.x + b);
-          const int i = __builtin_nontemporal_load(p.part_idx + (size_t)m * gridDim.x + b);
-          if (better(v, i, bv, bi)) { bv = v; bi = i; }
-        }
+  }
+}
+
+// Final step of the LOGITS epilogue: one workgroup per row reduces the
+// per-block (value, index) bests to the greedy ID.
+__global__ __launch_bounds__(256) void argmax_partials_kernel(const float* __restrict__ pv,
+                                                              const int32_t* __restrict__ pi, int nblocks,
+                                                              int32_t* __restrict__ next) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  float bv = 0.f;
+  int bi = -1;
+  for (int b = tid; b < nblocks; b += 256) {
+    const float v = pv[(size_t)m * nblocks + b];
+    const int i = pi[(size_t)m * nblocks + b];
+    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const float ov = __shfl_xor(bv, o);
-          const int oi = __shfl_xor(bi, o);
-          if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-        }
-        if (lane == 0) { bvs[wid][0] = bv; bis[wid][0] = bi; }
-        __syncthreads();
-        if (tid == 0) {
-          for (int ww = 1; ww < GEMV_WAVES; ++ww)
-            if (better(bvs[ww][0], bis[ww][0], bv, bi)) { bv = bvs[ww][0]; bi = bis[ww][0]; }
-          if (p.next) p.next[m0 + m] = bi;
-        }
-        __syncthreads();
-      }
-      if (tid == 0) *p.counter = 0u;
-    }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if (lane == 0) { sv[wid] = bv; si[wid] = bi; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int ww = 1; ww < 4; ++ww)
+      if (better(sv[ww], si[ww], bv, bi)) { bv = sv[ww]; bi = si[ww]; }
+    next[m] = bi;
   }
 }
 
@@ -263,8 +299,7 @@ static hipError_t launch_gemv(GemvParams p, hipStream_t s) {
   const int gx = (slots_total + rows_per_group * groups - 1) / (rows_per_group * groups);
   p.groups = groups;
   const int gy = (p.M + MB - 1) / MB;
-  const size_t lds = (size_t)MB * p.K * sizeof(float) + MB * 4 * sizeof(float);
-  gemv_kernel<W, EPI, MB, CPL, RPW><<<dim3(gx, gy), GEMV_THREADS, lds, s>>>(p);
+  gemv_kernel<W, EPI, MB, CPL, RPW><<<dim3(gx, gy), GEMV_THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -285,6 +320,13 @@ static hipError_t dispatch_mb(GemvParams p, hipStream_t s) {
   if (p.M == 1) return dispatch_cpl<W, EPI, 1>(p, s);
   if (EPI == EPI_LOGITS && p.M > GEMV_LOGITS_MAX_M) return hipErrorInvalidValue;
   return dispatch_cpl<W, EPI, 4>(p, s);
+}
+
+hipError_t argmax_partials(const float* pv, const int32_t* pi, int nblocks, int M, int32_t* next,
+                           hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  argmax_partials_kernel<<<M, 256, 0, s>>>(pv, pi, nblocks, next);
+  return hipGetLastError();
 }
 
 hipError_t gemv(int dt, int epi, GemvParams p, hipStream_t s) {

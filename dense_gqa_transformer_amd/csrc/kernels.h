@@ -19,6 +19,8 @@ hipError_t rmsnorm(const float* x, int T, int H, int ldx, const float* g, float 
                    void* out, int out_dt, int ldo, hipStream_t s, void* lo = nullptr);
 // dst[i] = float(src[i])
 hipError_t convert_f32(const void* src, int dt, float* dst, size_t n, hipStream_t s);
+// A one-wave kernel that waits about `us` microseconds of device wall clock.
+hipError_t spin_wait(int us, hipStream_t s);
 // Packs gate/up [I, H] into blocks of 32 gate rows followed by the matching 32 up rows.
 hipError_t pack_gate_up(const void* gate, const void* up, int dt, int I, int H, void* dst,
                         hipStream_t s);
@@ -41,11 +43,14 @@ struct GemvParams {
   int32_t* next;       // optional [M]: greedy IDs
   float* part_val;     // [M * gemv_logits_blocks] per-block best values
   int32_t* part_idx;   // [M * gemv_logits_blocks] per-block best indices
-  uint32_t* counter;   // one zeroed counter; the last block resets it
   int groups;          // set by the launcher
 };
 hipError_t gemv(int dt, int epi, GemvParams p, hipStream_t s);
+// Number of workgroups (and per-row partials) the LOGITS epilogue uses.
 int gemv_logits_blocks(int N, int K);
+// next[m] = best of the nblocks (value, index) partials of row m.
+hipError_t argmax_partials(const float* pv, const int32_t* pi, int nblocks, int M, int32_t* next,
+                           hipStream_t s);
 
 // ---------------------------------------------------------------- MFMA GEMM (bf16)
 enum GemmEpi { GEPI_STORE_BF16 = 0, GEPI_RESID_F32 = 1, GEPI_SWIGLU_BF16 = 2, GEPI_STORE_F32 = 3 };
@@ -92,8 +97,9 @@ hipError_t attn_prefill(const AttnPrefillParams& p, hipStream_t s);      // MFMA
 hipError_t attn_prefill_vec(const AttnPrefillParams& p, hipStream_t s);  // vector path, any dtype
 
 // Decode: one new token per sequence, split over context chunks, with the
-// q/k RMSNorm + RoPE + KV append of the new token fused in, and the partial
-// results combined by the last workgroup of each (sequence, KV head).
+// q/k RMSNorm + RoPE + KV append of the new token fused in.  Each workgroup
+// writes its chunk's partial (unnormalised o[d], running max m, sum l) for
+// the query heads of its KV head; attn_combine merges them.
 struct AttnDecodeParams {
   const float* qkv;            // [B, (nq+2nkv)*d] fp32 (raw projections)
   void* kcache; void* vcache; int kv_dt;
@@ -101,14 +107,15 @@ struct AttnDecodeParams {
   const float* cos_t; const float* sin_t;
   const int32_t* positions;    // device [B]
   const int32_t* slots;        // device [B]
-  void* out; int o_dt;         // [B, nq*d]
-  float* part;                 // [B, nq, nchunks, d + 2]
-  uint32_t* counters;          // [B, nkv], zeroed; self-resetting
+  float* part;                 // [B, nq, nchunks, d + 2]: o[0..d), m, l (base-2 softmax)
   int B, nq, nkv, d, chunk, nchunks;
   long long slot_stride, head_stride;
   float scale;
 };
 hipError_t attn_decode(const AttnDecodeParams& p, hipStream_t s);
+// out[b, h*d + e] from the chunk partials of sequence b (chunks 0..positions[b]/chunk).
+hipError_t attn_combine(const float* part, const int32_t* positions, int B, int nq, int d, int chunk,
+                        int nchunks, void* out, int o_dt, hipStream_t s);
 
 // ---------------------------------------------------------------- argmax
 // out[b] = greedy ID of row b of logits [B, V] (row stride ldl).

@@ -98,6 +98,18 @@ hipError_t convert_f32(const void* src, int dt, float* dst, size_t n, hipStream_
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ timing gate
+// Waits a bounded time on the device wall clock (100 MHz on this target).
+__global__ void spin_wait_kernel(long long ticks) {
+  const long long t0 = wall_clock64();
+  while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(8);
+}
+
+hipError_t spin_wait(int us, hipStream_t s) {
+  spin_wait_kernel<<<1, 64, 0, s>>>((long long)us * 100);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ gate/up packing
 template <typename W>
 __global__ void pack_gate_up_kernel(const W* __restrict__ gate, const W* __restrict__ up, int H,

@@ -109,6 +109,17 @@ class Model:
     def slot_length(self, slot: int) -> int:
         return int(self._lib.fs_slot_length(self._h, slot))
 
+    def timing(self, enable: bool) -> None:
+        """Starts (clearing old records) or stops per-launch event timing."""
+        check(self._lib.fs_timing(self._h, 1 if enable else 0))
+
+    def timing_read(self, label: str):
+        """(total milliseconds, launches) recorded for one step label."""
+        ms = ctypes.c_double()
+        n = ctypes.c_int64()
+        check(self._lib.fs_timing_read(self._h, label.encode(), ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
+
     def kv_read(self, layer: int, slot: int, kv_head: int, pos0: int, n: int,
                 stream: Optional[torch.cuda.Stream] = None):
         k = torch.empty((n, self.shape.head_dim), dtype=self.torch_dtype, device=self.device)

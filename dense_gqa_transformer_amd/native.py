@@ -82,6 +82,11 @@ def load() -> ctypes.CDLL:
     lib.fs_slot_length.restype = i32
     lib.fs_kv_read.argtypes = [P, i32, i32, i32, i32, i32, P, P, P]
     lib.fs_kv_read.restype = ctypes.c_int
+    lib.fs_timing.argtypes = [P, i32]
+    lib.fs_timing.restype = ctypes.c_int
+    lib.fs_timing_read.argtypes = [P, ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(ctypes.c_int64)]
+    lib.fs_timing_read.restype = ctypes.c_int
     lib.fs_last_error.argtypes = []
     lib.fs_last_error.restype = ctypes.c_char_p
     _lib = lib

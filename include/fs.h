@@ -138,6 +138,19 @@ int32_t fs_slot_length(const fs_model *m, int32_t slot);
 fs_status fs_kv_read(const fs_model *m, int32_t layer, int32_t slot, int32_t kv_head,
                      int32_t pos0, int32_t n, void *k_out, void *v_out, void *stream);
 
+/* Measurement hook.  fs_timing(m, 1) waits for the device, clears earlier
+ * records and starts recording: every kernel this model launches is then
+ * bracketed by a pair of HIP events on the call's stream, labelled with the
+ * step it implements ("embed", "norm", "qkv", "rope_kv", "attn", "combine",
+ * "o_proj", "gate_up", "down", "head", "argmax"), and decode steps run
+ * without graph replay.  fs_timing(m, 0) stops recording (records are kept
+ * until the next fs_timing call).  Errors: INVALID_ARG for a NULL model. */
+fs_status fs_timing(fs_model *m, int32_t enable);
+
+/* Sum of the recorded launch intervals of one label: *total_ms (milliseconds)
+ * and *launches.  Waits for the recorded events.  Errors: INVALID_ARG. */
+fs_status fs_timing_read(fs_model *m, const char *label, double *total_ms, int64_t *launches);
+
 /* Message of the last error on this thread ("" if none); valid until the
  * next fs_* call on this thread. */
 const char *fs_last_error(void);

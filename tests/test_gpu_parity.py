@@ -349,3 +349,43 @@ def test_decode_bs64_ragged():
     ids = nxt.cpu().numpy()
     assert np.all((ids >= 0) & (ids < shape.vocab))
     assert [model.slot_length(i) for i in range(B)] == [lens[i] + wl.decode_steps for i in range(B)]
+
+
+# ------------------------------------------------------------------ graph replay and timing hook
+def test_graph_replay_matches_eager(monkeypatch):
+    # decode steps replayed from captured graphs give the same bits as eager launches
+    shape = synth.QWEN3_0P6B
+    toks = synth.tokens(909, shape.vocab, (1, 40))
+    res = {}
+    for mode in ("1", "0"):
+        monkeypatch.setenv("FS_DECODE_GRAPHS", mode)
+        model = make_model(shape, max_seqs=1, max_ctx=128)
+        lg = model.prefill(dev_tokens(toks), [0])
+        nxt = torch.empty((1,), dtype=torch.int32, device="cuda")
+        from dense_gqa_transformer_amd.model import argmax
+        argmax(lg, out=nxt)
+        logits = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda")
+        outs = []
+        for k in range(40):                    # crosses a chunk-count boundary (graph re-capture)
+            model.decode_step(nxt, [40 + k], [0], logits=logits, next_ids=nxt)
+            torch.cuda.synchronize()            # eager host work between replays
+            outs.append(logits.cpu().numpy()[0].copy())
+        res[mode] = np.stack(outs)
+        model.close()
+    np.testing.assert_array_equal(res["1"], res["0"])
+
+
+def test_timing_hook_labels(big):
+    shape, model = big
+    toks = synth.tokens(31, shape.vocab, (1, 20))
+    model.prefill(dev_tokens(toks), [0])
+    model.timing(True)
+    nxt = torch.tensor([5], dtype=torch.int32, device="cuda")
+    for k in range(3):
+        model.decode_step(nxt, [20 + k], [0], next_ids=nxt)
+    torch.cuda.synchronize()
+    for lab, per_step in (("qkv", 28), ("attn", 28), ("o_proj", 28), ("gate_up", 28), ("down", 28),
+                          ("head", 1), ("argmax", 1), ("embed", 1)):
+        ms, n = model.timing_read(lab)
+        assert n == 3 * per_step and ms > 0, lab
+    model.timing(False)
