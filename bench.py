@@ -8,10 +8,11 @@ fs_decode_step whose greedy output is fed back on the device, at positions
 4 x 4096 tokens.
 
 Also reported:
-  roofline     -- the dominant decode kernel: algorithmic bytes per launch over
-                  its average launch time (HIP events on the library's stream,
-                  from a pass with per-launch timing switched on), against
-                  8 TB/s HBM;
+  roofline     -- the dominant decode kernel (largest per-step time): its
+                  algorithmic bytes per launch over its average launch time,
+                  measured with HIP events on the library's stream while its
+                  28 per-layer launches replay back to back in a graph,
+                  against 8 TB/s HBM;
   prefill      -- prefill tok/s and the MFMA roofline of its dominant kernel;
   cpu_baseline -- the CPU oracle on a bounded sample of the same decode workload.
 
@@ -155,26 +156,15 @@ def main():
     ctx_avg = P + (steps + 1) / 2.0
     hbm_frac = decode_bytes_per_step(shape, ctx_avg) / (dt / steps) / HBM_PEAK
 
-    # per-kernel times of the same steps (events around every launch, no graph)
-    lg = model.prefill(tok, [2])
-    argmax(lg, out=nxt)
-    torch.cuda.synchronize()
-    model.timing(True)
-    nt = min(steps, 64)
-    for k in range(nt):
-        model.decode_step(nxt, [P + k], [2], next_ids=nxt)
-    torch.cuda.synchronize()
-    labels = ("embed", "qkv", "attn", "combine", "o_proj", "gate_up", "down", "head", "argmax")
-    per = {}
-    for lab in labels:
-        ms, n = model.timing_read(lab)
-        if n:
-            per[lab] = (ms, n)
-    model.timing(False)
-    dom = max(per, key=lambda k: per[k][0])
-    avg_s = per[dom][0] / per[dom][1] / 1e3
-    ctx_t = P + (nt + 1) / 2.0
-    bytes_launch = decode_label_bytes(shape, dom, ctx_t)
+    # per-launch duration of each decode kernel class, replayed back to back in
+    # a graph over the 28 layers' own weights (HIP events on the library's stream)
+    per_launch = {}
+    for lab in ("qkv", "attn", "combine", "o_proj", "gate_up", "down", "head"):
+        per_launch[lab] = model.kernel_bench(lab, reps=20, slot=4, position=P + steps // 2)
+    launches = {lab: (1 if lab == "head" else shape.n_layers) for lab in per_launch}
+    dom = max(per_launch, key=lambda k: per_launch[k] * launches[k])
+    avg_s = per_launch[dom] * 1e-6
+    bytes_launch = decode_label_bytes(shape, dom, P + steps // 2 + 1)
     achieved = bytes_launch / avg_s
     out = {
         "metric": "decode tok/s @bs1 (0.6B shape, bf16 weights + bf16 KV cache)",
@@ -197,7 +187,7 @@ def main():
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
                      "traffic": None, "avg_launch_us": round(avg_s * 1e6, 3),
                      "bytes_per_launch": int(bytes_launch)},
-        "decode_kernel_us_per_step": {k: round(v[0] * 1e3 / nt, 2) for k, v in per.items()},
+        "decode_us_per_launch": {k: round(v, 3) for k, v in per_launch.items()},
     }
 
     if not args.no_prefill:

@@ -624,6 +624,98 @@ fs_status fs_decode_step(fs_model* m, const int32_t* tokens, const int32_t* posi
   return FS_OK;
 }
 
+fs_status fs_kernel_bench(fs_model* m, const char* label, int32_t slot, int32_t position, int32_t reps,
+                          double* avg_us, void* stream) {
+  g_err.clear();
+  if (m == nullptr || label == nullptr || avg_us == nullptr || reps <= 0)
+    return fail(FS_ERR_INVALID_ARG, "NULL argument or reps <= 0");
+  const fs_config& c = m->cfg;
+  const bool is_attn = std::strcmp(label, "attn") == 0;
+  if ((is_attn || std::strcmp(label, "combine") == 0) && (slot < 0 || slot >= c.max_seqs || position < 0 || position >= c.max_ctx))
+    return fail(FS_ERR_INVALID_ARG, "bad slot or position");
+  if (c.n_layers == 0 && std::strcmp(label, "head") != 0) return fail(FS_ERR_INVALID_ARG, "model has no layers");
+  hipStream_t s = (hipStream_t)stream;
+  fs_status st = ensure_rows(m, 1, s);
+  if (st != FS_OK) return st;
+  int32_t pos_h[1] = {position}, slot_h[1] = {is_attn ? slot : 0};
+  if ((st = stage_ints(m, pos_h, slot_h, 1, s)) != FS_OK) return st;
+  int chunk = 32;
+  while (chunk < 256 && (long long)((position + chunk) / chunk) * c.n_kv_heads > 1024) chunk *= 2;
+  const int nchunks = (position + chunk) / chunk;
+  // one launch per layer (the layer's own weights), `reps` passes over the layers
+  auto launch_one = [&](int l, hipStream_t ls) -> fs_status {
+    const LayerW& L = m->layers[l];
+    GemvParams p{};
+    p.eps = c.rms_eps; p.M = 1;
+    if (std::strcmp(label, "qkv") == 0) {
+      p.w = L.wqkv; p.N = m->qkv_w; p.K = c.hidden; p.a = m->x; p.lda = c.hidden; p.gamma = L.attn_norm;
+      p.out = (float*)m->qkv; p.ldo = m->qkv_w;
+      HIP_TRY(gemv(m->dt, EPI_STORE, p, ls));
+    } else if (std::strcmp(label, "o_proj") == 0) {
+      p.w = L.wo; p.N = c.hidden; p.K = m->qw; p.a = (const float*)m->attn; p.lda = m->qw;
+      p.out = m->x; p.ldo = c.hidden;
+      HIP_TRY(gemv(m->dt, EPI_RESID, p, ls));
+    } else if (std::strcmp(label, "gate_up") == 0) {
+      p.w = L.wgu; p.N = c.ffn; p.K = c.hidden; p.a = m->x; p.lda = c.hidden; p.gamma = L.mlp_norm;
+      p.out = (float*)m->hbuf; p.ldo = c.ffn;
+      HIP_TRY(gemv(m->dt, EPI_SWIGLU, p, ls));
+    } else if (std::strcmp(label, "down") == 0) {
+      p.w = L.wdown; p.N = c.hidden; p.K = c.ffn; p.a = (const float*)m->hbuf; p.lda = c.ffn;
+      p.out = m->x; p.ldo = c.hidden;
+      HIP_TRY(gemv(m->dt, EPI_RESID, p, ls));
+    } else if (std::strcmp(label, "head") == 0) {
+      p.w = m->embed; p.N = c.vocab; p.K = c.hidden; p.a = m->x; p.lda = c.hidden; p.gamma = m->final_norm;
+      p.ldo = c.vocab; p.part_val = m->lm_pv; p.part_idx = m->lm_pi;
+      HIP_TRY(gemv(m->dt, EPI_LOGITS, p, ls));
+    } else if (is_attn) {
+      AttnDecodeParams a{};
+      a.qkv = (const float*)m->qkv;
+      a.kcache = (char*)m->kcache + (size_t)l * m->layer_stride * m->esz;
+      a.vcache = (char*)m->vcache + (size_t)l * m->layer_stride * m->esz;
+      a.kv_dt = m->dt; a.gq = L.q_norm; a.gk = L.k_norm; a.eps = c.rms_eps;
+      a.cos_t = m->rope_cos; a.sin_t = m->rope_sin; a.positions = m->d_pos; a.slots = m->d_slot;
+      a.part = m->part; a.B = 1; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim;
+      a.chunk = chunk; a.nchunks = nchunks; a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
+      a.scale = 1.0f / std::sqrt((float)c.head_dim);
+      HIP_TRY(attn_decode(a, ls));
+    } else if (std::strcmp(label, "combine") == 0) {
+      HIP_TRY(attn_combine(m->part, m->d_pos, 1, c.n_heads, c.head_dim, chunk, nchunks, m->attn, DT_F32, ls));
+    } else {
+      return fail(FS_ERR_INVALID_ARG, std::string("unknown label ") + label);
+    }
+    return FS_OK;
+  };
+  const int per_pass = std::strcmp(label, "head") == 0 ? 1 : c.n_layers;
+  hipGraph_t g = nullptr;
+  hipGraphExec_t ge = nullptr;
+  HIP_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeRelaxed));
+  for (int l = 0; l < per_pass && st == FS_OK; ++l) st = launch_one(l, m->cap_stream);
+  const hipError_t ec = hipStreamEndCapture(m->cap_stream, &g);
+  if (st != FS_OK) { if (g) hipGraphDestroy(g); return st; }
+  if (ec != hipSuccess) return fail(FS_ERR_HIP, "capture failed");
+  if (hipGraphInstantiate(&ge, g, nullptr, nullptr, 0) != hipSuccess) {
+    hipGraphDestroy(g);
+    return fail(FS_ERR_HIP, "instantiate failed");
+  }
+  hipEvent_t a = nullptr, b = nullptr;
+  hipError_t e = hipEventCreate(&a);
+  if (e == hipSuccess) e = hipEventCreate(&b);
+  if (e == hipSuccess) e = hipGraphLaunch(ge, s);                 // warm
+  if (e == hipSuccess) e = hipEventRecord(a, s);
+  for (int r = 0; r < reps && e == hipSuccess; ++r) e = hipGraphLaunch(ge, s);
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  if (e == hipSuccess) e = hipEventSynchronize(b);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+  if (a) hipEventDestroy(a);
+  if (b) hipEventDestroy(b);
+  hipGraphExecDestroy(ge);
+  hipGraphDestroy(g);
+  if (e != hipSuccess) return fail(FS_ERR_HIP, std::string("kernel bench failed: ") + hipGetErrorString(e));
+  *avg_us = (double)ms * 1e3 / ((double)reps * per_pass);
+  return FS_OK;
+}
+
 fs_status fs_timing(fs_model* m, int32_t enable) {
   g_err.clear();
   if (m == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL model");

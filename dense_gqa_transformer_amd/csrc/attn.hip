@@ -35,6 +35,40 @@ template <> __device__ __forceinline__ void loadn<float, 4>(const float* p, floa
   o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
 }
 
+// Raw (unconverted) loads of d/16 elements, so a batch of them can be in
+// flight before any is used.
+template <typename KV, int N> struct RawKV;
+template <> struct RawKV<bf16, 8> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void get(float* o) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[2 * i] = __uint_as_float(v[i] << 16); o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u); }
+  }
+};
+template <> struct RawKV<bf16, 4> {
+  uint2 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void get(float* o) const {
+    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+};
+template <> struct RawKV<float, 8> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p); b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void get(float* o) const {
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+};
+template <> struct RawKV<float, 4> {
+  float4 a;
+  __device__ __forceinline__ void load(const float* p) { a = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void get(float* o) const { o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; }
+};
+
 template <int REP, int DP>
 struct SoftState {
   float m[REP], l[REP], o[REP][DP];
@@ -122,6 +156,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
   __shared__ float sm[4][REP], sl[4][REP];
   __shared__ float so[4][REP][D];
 
+  constexpr int NPRE = 2;                               // key rows per lane fetched up front
   const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int grp = lane >> 4, li = lane & 15;
@@ -137,6 +172,19 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
   KV* kb = reinterpret_cast<KV*>(p.kcache) + kvoff;
   KV* vb = reinterpret_cast<KV*>(p.vcache) + kvoff;
   const float qscale = p.scale * LOG2E;
+  const bool has_new = (pos >= c0 && pos < c1);
+
+  // ---- this lane's first key/value rows go out before anything else; the
+  //      q/k projections and RoPE tables below are fetched in the same round
+  //      trip.  (Row `pos` is not written yet: it is taken from LDS below.)
+  const int ufirst = c0 + wid * 4 + grp;
+  RawKV<KV, DP> pk[NPRE], pv[NPRE];
+#pragma unroll
+  for (int i = 0; i < NPRE; ++i) {
+    const int u = min(ufirst + 16 * i, c1 - 1);
+    pk[i].load(kb + (size_t)u * D + li * DP);
+    pv[i].load(vb + (size_t)u * D + li * DP);
+  }
 
   // ---- q heads of this group: RMSNorm over d, RoPE at pos, pre-scale
   for (int r = wid; r < REP; r += 4) {
@@ -144,30 +192,32 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
     const bool on = lane < HALF;
     float x0 = on ? row[h * D + lane] : 0.f;
     float x1 = on ? row[h * D + lane + HALF] : 0.f;
+    const float cs = on ? p.cos_t[(size_t)pos * HALF + lane] : 0.f;
+    const float sn = on ? p.sin_t[(size_t)pos * HALF + lane] : 0.f;
     const float inv = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)D + p.eps);
     if (on) {
       x0 *= inv * p.gq[lane];
       x1 *= inv * p.gq[lane + HALF];
-      const float cs = p.cos_t[(size_t)pos * HALF + lane], sn = p.sin_t[(size_t)pos * HALF + lane];
       qs[r][lane] = (x0 * cs - x1 * sn) * qscale;
       qs[r][lane + HALF] = (x1 * cs + x0 * sn) * qscale;
     }
   }
   // ---- the new token's k, v if it falls in this chunk: normalise, rotate, append
-  const bool has_new = (pos >= c0 && pos < c1);
   if (has_new && wid == 3) {
     const bool on = lane < HALF;
     const float* kr = row + p.nq * D + j * D;
     const float* vr = row + (p.nq + p.nkv) * D + j * D;
     float x0 = on ? kr[lane] : 0.f;
     float x1 = on ? kr[lane + HALF] : 0.f;
+    const float va = on ? vr[lane] : 0.f, vbv = on ? vr[lane + HALF] : 0.f;
+    const float cs = on ? p.cos_t[(size_t)pos * HALF + lane] : 0.f;
+    const float sn = on ? p.sin_t[(size_t)pos * HALF + lane] : 0.f;
     const float inv = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)D + p.eps);
     if (on) {
       x0 *= inv * p.gk[lane];
       x1 *= inv * p.gk[lane + HALF];
-      const float cs = p.cos_t[(size_t)pos * HALF + lane], sn = p.sin_t[(size_t)pos * HALF + lane];
       const KV k0 = from_f32<KV>(x0 * cs - x1 * sn), k1 = from_f32<KV>(x1 * cs + x0 * sn);
-      const KV v0 = from_f32<KV>(vr[lane]), v1 = from_f32<KV>(vr[lane + HALF]);
+      const KV v0 = from_f32<KV>(va), v1 = from_f32<KV>(vbv);
       kb[(size_t)pos * D + lane] = k0;
       kb[(size_t)pos * D + lane + HALF] = k1;
       vb[(size_t)pos * D + lane] = v0;
@@ -186,7 +236,48 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
 
   SoftState<REP, DP> st;
   st.init();
-  attend<KV, D, REP>(st, q, kb, vb, c0 + wid * 4, c1, 16, grp, li, has_new ? pos : -1, knew, vnew);
+  const int u_new = has_new ? pos : -1;
+  auto fold = [&](int u, const float* k, const float* v) {
+    float sc[REP];
+#pragma unroll
+    for (int r = 0; r < REP; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < DP; ++e) acc = fmaf(q[r][e], k[e], acc);
+      sc[r] = group_sum<16>(acc);
+    }
+    if (u < c1) st.add(sc, v);
+  };
+  // positions ufirst + 16*i; the trip count is uniform across the wave so the
+  // 16-lane shuffles stay converged
+#pragma unroll
+  for (int i = 0; i < NPRE; ++i) {
+    const int base = c0 + wid * 4 + 16 * i;
+    if (base >= c1) break;
+    const int u = ufirst + 16 * i;
+    float k[DP], v[DP];
+    if (u == u_new) {
+#pragma unroll
+      for (int e = 0; e < DP; ++e) { k[e] = knew[li * DP + e]; v[e] = vnew[li * DP + e]; }
+    } else {
+      pk[i].get(k);
+      pv[i].get(v);
+    }
+    fold(u, k, v);
+  }
+  for (int base = c0 + wid * 4 + 16 * NPRE; base < c1; base += 16) {
+    const int u = base + grp;
+    const int uu = min(u, c1 - 1);
+    float k[DP], v[DP];
+    if (uu == u_new) {
+#pragma unroll
+      for (int e = 0; e < DP; ++e) { k[e] = knew[li * DP + e]; v[e] = vnew[li * DP + e]; }
+    } else {
+      loadn<KV, DP>(kb + (size_t)uu * D + li * DP, k);
+      loadn<KV, DP>(vb + (size_t)uu * D + li * DP, v);
+    }
+    fold(u, k, v);
+  }
   st.merge_xor(16);
   st.merge_xor(32);
   if (lane < 16) {

@@ -120,6 +120,14 @@ class Model:
         check(self._lib.fs_timing_read(self._h, label.encode(), ctypes.byref(ms), ctypes.byref(n)))
         return ms.value, n.value
 
+    def kernel_bench(self, label: str, reps: int = 20, slot: int = 0, position: int = 0,
+                     stream: Optional[torch.cuda.Stream] = None) -> float:
+        """Microseconds per launch of one decode kernel class replayed over all layers."""
+        us = ctypes.c_double()
+        check(self._lib.fs_kernel_bench(self._h, label.encode(), slot, position, reps, ctypes.byref(us),
+                                        _stream_ptr(stream)))
+        return us.value
+
     def kv_read(self, layer: int, slot: int, kv_head: int, pos0: int, n: int,
                 stream: Optional[torch.cuda.Stream] = None):
         k = torch.empty((n, self.shape.head_dim), dtype=self.torch_dtype, device=self.device)

@@ -151,6 +151,22 @@ fs_status fs_timing(fs_model *m, int32_t enable);
  * and *launches.  Waits for the recorded events.  Errors: INVALID_ARG. */
 fs_status fs_timing_read(fs_model *m, const char *label, double *total_ms, int64_t *launches);
 
+/* Measurement hook: average duration of one decode-shaped (batch 1) launch
+ * of the kernel that implements `label` ("qkv", "attn", "combine", "o_proj",
+ * "gate_up", "down" or "head"), as it runs inside a decode step: one launch per layer,
+ * each with that layer's weights, captured back to back in a graph and
+ * replayed `reps` times between two HIP events on `stream` (so the figure
+ * includes the per-launch dispatch cost of graph replay).  *avg_us receives
+ * microseconds per launch.  The call overwrites the model's activation
+ * scratch; "attn" also reads context 0..position of `slot` and writes K/V row
+ * `position` of that slot with values derived from the scratch, so use a
+ * slot that holds nothing of value ("combine" merges the partials of a
+ * context of position+1).  Other labels ignore slot and position.
+ * Synchronous.  Errors: INVALID_ARG (unknown label, bad slot/position,
+ * reps <= 0), HIP. */
+fs_status fs_kernel_bench(fs_model *m, const char *label, int32_t slot, int32_t position,
+                          int32_t reps, double *avg_us, void *stream);
+
 /* Message of the last error on this thread ("" if none); valid until the
  * next fs_* call on this thread. */
 const char *fs_last_error(void);

@@ -12,7 +12,7 @@ def test_library_exports_every_declared_symbol():
     names = native.header_functions()
     assert set(names) == {"fs_model_create", "fs_model_destroy", "fs_prefill", "fs_decode_step",
                           "fs_argmax", "fs_slot_length", "fs_kv_read", "fs_last_error",
-                          "fs_timing", "fs_timing_read"}
+                          "fs_timing", "fs_timing_read", "fs_kernel_bench"}
     for n in names:
         assert hasattr(lib, n), n
 

@@ -389,3 +389,22 @@ def test_timing_hook_labels(big):
         ms, n = model.timing_read(lab)
         assert n == 3 * per_step and ms > 0, lab
     model.timing(False)
+
+
+def test_kernel_bench_hook_leaves_decode_intact(big):
+    shape, model = big
+    toks = synth.tokens(57, shape.vocab, (1, 33))
+    ref = model.prefill(dev_tokens(toks), [0]).cpu().numpy()[0]
+    for lab in ("qkv", "attn", "combine", "o_proj", "gate_up", "down", "head"):
+        us = model.kernel_bench(lab, reps=2, slot=5, position=100)
+        assert 0.0 < us < 10000.0, lab
+    from dense_gqa_transformer_amd import native
+    with pytest.raises(native.FsError):
+        model.kernel_bench("nope", reps=1)
+    # the slot's state is untouched: decoding continues to match the uncached pass
+    logits = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda")
+    t = int(np.argmax(ref))
+    model.decode_step(dev_tokens([t]), [33], [0], logits=logits)
+    full = np.concatenate([toks[0], [t]]).astype(np.int32)
+    un = model.prefill(dev_tokens(full[None, :]), [1]).cpu().numpy()[0]
+    check_logits(logits.cpu().numpy()[0], un, TOL["bf16"], "decode after kernel_bench")
