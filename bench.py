@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=48)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only one 4 x 4096 prefill (for hardware-counter passes) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: --gpus must be 1 "
@@ -132,6 +134,15 @@ def main():
     w = synth.make_weights(shape, 0)
     model = Model(shape, w, max_seqs=5, max_ctx=4096)
     dev = torch.device("cuda")
+    if args.prefill_only:
+        pw = synth.workload("prefill_0p6b_4x4096")
+        ptok = torch.from_numpy(np.stack(pw.prompts).astype(np.int32)).to(dev)
+        logits = torch.empty((4, shape.vocab), dtype=torch.float32, device=dev)
+        t0 = time.perf_counter()
+        model.prefill(ptok, [0, 1, 2, 3], logits=logits)
+        torch.cuda.synchronize()
+        print(json.dumps({"prefill_only_ms": round((time.perf_counter() - t0) * 1e3, 3)}), flush=True)
+        return
     tok = torch.from_numpy(prompt[None, :].astype(np.int32)).to(dev)
     nxt = torch.empty((1,), dtype=torch.int32, device=dev)
     P = len(prompt)

@@ -164,7 +164,7 @@ def test_decode_from_empty_slot_and_error_paths():
 def big():
     shape = synth.QWEN3_0P6B
     _flush("building 0.6B model")
-    return shape, make_model(shape, max_seqs=6, max_ctx=1024)
+    return shape, make_model(shape, max_seqs=6, max_ctx=1152)
 
 
 def test_scorer_6_tokens(big):
@@ -183,9 +183,10 @@ def test_scorer_6_tokens(big):
         assert ref[g] >= kth - 2 * TOL["bf16"]
 
 
-@pytest.mark.parametrize("S", [1, 3, 5, 130])
+@pytest.mark.parametrize("S", [1, 3, 5, 130, 1100])
 def test_prefill_lengths_both_paths(big, S):
-    # S <= 4 runs the GEMV path, larger S the MFMA GEMM path (ragged tail at 130)
+    # S <= 4 runs the GEMV path, larger S the MFMA GEMM path (128-row tiles, ragged
+    # tail at 130; 256-row tiles with a 76-row tail at 1100)
     shape, model = big
     toks = synth.tokens(500 + S, shape.vocab, (1, S))
     ref = oracle_for(shape).forward(toks[0])
