@@ -34,11 +34,13 @@ __global__ __launch_bounds__(256 * HPW) void attn_prefill_mfma_kernel(const Attn
   constexpr int BQ = 128, BKV = 64;
   constexpr int NT = 256 * HPW;     // threads
   constexpr int LDK = D + 8;        // K tile row stride (elements)
-  constexpr int LDV = BKV + 8;      // V^T tile row stride (elements)
+  constexpr int LDV = BKV + 4;      // V^T tile row stride (elements): 136 B, 8-byte aligned, spreads rows over banks
   constexpr int KS = D / 16;        // k-steps of the score product
   constexpr int DB = D / 32;        // 32-row blocks of O^T
   constexpr int CH = BKV * D / 8;   // 16-byte chunks per K (or V) tile
   constexpr int CPT = CH / NT;      // chunks per thread
+  constexpr int VP = (BKV / 2) * (D / 8);   // V key-pair chunks per tile
+  constexpr int VPT = (VP + NT - 1) / NT;   // per thread
   static_assert(CPT >= 1 && CH % NT == 0, "tile / thread mismatch");
   __shared__ __attribute__((aligned(16))) bf16 Ks[BKV * LDK];
   __shared__ __attribute__((aligned(16))) bf16 Vt[D * LDV];
@@ -75,11 +77,11 @@ __global__ __launch_bounds__(256 * HPW) void attn_prefill_mfma_kernel(const Attn
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
-  // register staging of one K/V tile: K chunks row-major (coalesced), V
-  // chunks with consecutive keys per lane so the transposed 2-byte LDS writes
-  // of one instruction land in consecutive halfwords
+  // register staging of one K/V tile: K chunks row-major (coalesced); V as
+  // pairs of consecutive keys per lane (same 8 columns), so the transposed
+  // LDS writes are dwords and one instruction covers 32 consecutive dwords
   u32x4 rk[CPT];
-  bf16x8 rv[CPT];
+  u32x4 rv[VPT][2];
   auto fetch = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
@@ -87,13 +89,15 @@ __global__ __launch_bounds__(256 * HPW) void attn_prefill_mfma_kernel(const Attn
       const int kk = id / (D / 8), kc = (id % (D / 8)) * 8;
       rk[i] = (k0 + kk < S) ? *reinterpret_cast<const u32x4*>(kg + (size_t)(k0 + kk) * D + kc)
                             : u32x4{0, 0, 0, 0};
-      const int vk = id % BKV, vc = (id / BKV) * 8;
-      if (k0 + vk < S) {
-        rv[i] = *reinterpret_cast<const bf16x8*>(vg + (size_t)(k0 + vk) * D + vc);
-      } else {
+    }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rv[i][e] = (bf16)0.f;
-      }
+    for (int i = 0; i < VPT; ++i) {
+      const int id = min(tid + NT * i, VP - 1);            // BKV/2 key pairs x D/8 column chunks
+      const int vk = (id % (BKV / 2)) * 2, vc = (id / (BKV / 2)) * 8;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        rv[i][t] = (k0 + vk + t < S) ? *reinterpret_cast<const u32x4*>(vg + (size_t)(k0 + vk + t) * D + vc)
+                                     : u32x4{0, 0, 0, 0};
     }
   };
   auto stash = [&]() {
@@ -102,9 +106,18 @@ __global__ __launch_bounds__(256 * HPW) void attn_prefill_mfma_kernel(const Attn
       const int id = tid + NT * i;
       const int kk = id / (D / 8), kc = (id % (D / 8)) * 8;
       *reinterpret_cast<u32x4*>(&Ks[kk * LDK + kc]) = rk[i];
-      const int vk = id % BKV, vc = (id / BKV) * 8;
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[(vc + e) * LDV + vk] = rv[i][e];
+    for (int i = 0; i < VPT; ++i) {
+      const int id = tid + NT * i;
+      if (id >= VP) break;
+      const int vk = (id % (BKV / 2)) * 2, vc = (id / (BKV / 2)) * 8;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {                        // columns vc + 2q and vc + 2q + 1
+        const uint32_t a = rv[i][0][q], b = rv[i][1][q];
+        *reinterpret_cast<uint32_t*>(&Vt[(vc + 2 * q) * LDV + vk]) = (a & 0xffffu) | (b << 16);
+        *reinterpret_cast<uint32_t*>(&Vt[(vc + 2 * q + 1) * LDV + vk]) = (a >> 16) | (b & 0xffff0000u);
+      }
     }
   };
 
@@ -120,24 +133,27 @@ __global__ __launch_bounds__(256 * HPW) void attn_prefill_mfma_kernel(const Attn
     // ---- S^T for keys k0 + 32*kb + (8*(r/4) + 4*half + r%4), query myq
     f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + col) * LDK + ks * 16 + half * 8]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-      }
+    for (int ks = 0; ks < KS; ++ks) {                  // two independent accumulator chains
+      bf16x8 a[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        a[kb] = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + col) * LDK + ks * 16 + half * 8]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qf[ks], s[kb], 0, 0, 0);
     }
-    // ---- causal mask (only on tiles that reach past this wave's first query)
+    // ---- causal mask (only on tiles that reach past this wave's first query):
+    //      key offset within the tile is a per-register constant
     if (k0 + BKV - 1 > wq0) {
+      const int lim = min(myq, S - 1) - k0 - half * 4;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          if (key > myq || key >= S) s[kb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + (r >> 2) * 8 + (r & 3) > lim) s[kb][r] = -INFINITY;
     }
     // ---- tile max (raw units), lazily moved running max (base-2 units)
     float mt = -INFINITY;
@@ -147,7 +163,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_prefill_mfma_kernel(const Attn
       for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[kb][r], s[kb][r + 1]));
     mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
     if (mt > m_run + LAZY_MAX) {             // rare after the first tile
-      const float corr = exp2f(m_run - mt);
+      const float corr = __builtin_amdgcn_exp2f(m_run - mt);
       l_run *= corr;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -160,7 +176,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_prefill_mfma_kernel(const Attn
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = exp2f(fmaf(s[kb][r], c2, -m_run));
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -m_run));
         s[kb][r] = e;
         ls += e;
       }
