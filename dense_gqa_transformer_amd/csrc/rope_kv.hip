@@ -1,6 +1,5 @@
 // Per-head q/k RMSNorm + rotate-half RoPE + KV-cache write for a batch of
-// prompt tokens.  One wave per (token, head); lane l holds the RoPE pair
-// (l, l + d/2), so the rotation is lane-local and the norm is one wave sum.
+// prompt tokens.
 //
 // q/k RMSNorm over head_dim with one shared weight per projection, applied
 // before RoPE (Qwen3 layout); RoPE pairs (i, i + d/2) rotated by
@@ -12,70 +11,110 @@
 
 namespace fsk {
 
-template <typename TI, typename TQ, typename KV>
+// D/16 lanes per (token, head): lane `sub` holds elements [8 sub, 8 sub + 8)
+// and the matching RoPE partners [d/2 + 8 sub, ...), so every access is a
+// 16-byte vector and the rotation stays lane-local; 64/(D/16) heads per wave.
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> {
+  static __device__ __forceinline__ void load(const bf16* p, float* o) { load8(p, o); }
+  static __device__ __forceinline__ void store(bf16* p, const float* v) {
+    u32x4 u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = __builtin_bit_cast(uint16_t, (bf16)v[2 * i]);
+      const uint32_t hi = __builtin_bit_cast(uint16_t, (bf16)v[2 * i + 1]);
+      u[i] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(p) = u;
+  }
+};
+template <> struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float* p, float* o) { load8(p, o); }
+  static __device__ __forceinline__ void store(float* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+template <typename TI, typename TQ, typename KV, int D>
 __global__ __launch_bounds__(256) void rope_kv_kernel(const RopeKvParams p) {
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int LPH = D / 16, HALF = D / 2;
+  const int lane = threadIdx.x & 63, sub = lane % LPH;
   const int nh = p.nq + p.nkv;
-  const long long item = (long long)blockIdx.x * 4 + wid;
-  if (item >= (long long)p.T * nh) return;
-  const int t = (int)(item / nh), hh = (int)(item % nh);
-  const int d = p.d, half = d >> 1;
+  const long long item = ((long long)blockIdx.x * 256 + threadIdx.x) / LPH;
+  const bool live = item < (long long)p.T * nh;
+  const long long it = live ? item : 0;
+  const int t = (int)(it / nh), hh = (int)(it % nh);
   const int b = t / p.S_per, pos = t % p.S_per;
-  const int slot = p.slots[b];
-  const int W = (p.nq + 2 * p.nkv) * d;
+  const int W = (p.nq + 2 * p.nkv) * D;
   const TI* row = reinterpret_cast<const TI*>(p.qkv) + (size_t)t * W;
-  const bool on = lane < half;
   const bool is_q = hh < p.nq;
   const int j = hh - p.nq;
-  const TI* src = is_q ? row + hh * d : row + p.nq * d + j * d;
-  float x0 = on ? to_f32(src[lane]) : 0.f;
-  float x1 = on ? to_f32(src[lane + half]) : 0.f;
-  const float ss = wave_sum(x0 * x0 + x1 * x1);
-  const float inv = rsqrtf(ss / (float)d + p.eps);
+  const TI* src = is_q ? row + hh * D : row + p.nq * D + j * D;
+  float x0[8], x1[8];
+  Vec8<TI>::load(src + sub * 8, x0);
+  Vec8<TI>::load(src + HALF + sub * 8, x1);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = fmaf(x0[e], x0[e], fmaf(x1[e], x1[e], ss));
+  ss = group_sum<LPH>(ss);
+  if (!live) return;
+  const float inv = rsqrtf(ss / (float)D + p.eps);
   const float* g = is_q ? p.gq : p.gk;
-  if (on) {
-    x0 = x0 * inv * g[lane];
-    x1 = x1 * inv * g[lane + half];
-    const float c = p.cos_t[(size_t)pos * half + lane];
-    const float s = p.sin_t[(size_t)pos * half + lane];
-    const float y0 = x0 * c - x1 * s;
-    const float y1 = x1 * c + x0 * s;
-    if (is_q) {
-      TQ* q = reinterpret_cast<TQ*>(p.qout) + (size_t)t * p.nq * d + hh * d;
-      q[lane] = from_f32<TQ>(y0);
-      q[lane + half] = from_f32<TQ>(y1);
-    } else {
-      const size_t off = (size_t)slot * p.slot_stride + (size_t)j * p.head_stride + (size_t)pos * d;
-      KV* k = reinterpret_cast<KV*>(p.kcache) + off;
-      k[lane] = from_f32<KV>(y0);
-      k[lane + half] = from_f32<KV>(y1);
-      const TI* vs = row + (p.nq + p.nkv) * d + j * d;
-      KV* v = reinterpret_cast<KV*>(p.vcache) + off;
-      v[lane] = from_f32<KV>(to_f32(vs[lane]));
-      v[lane + half] = from_f32<KV>(to_f32(vs[lane + half]));
-    }
+  float g0[8], g1[8], cs[8], sn[8];
+  load8(g + sub * 8, g0);
+  load8(g + HALF + sub * 8, g1);
+  load8(p.cos_t + (size_t)pos * HALF + sub * 8, cs);
+  load8(p.sin_t + (size_t)pos * HALF + sub * 8, sn);
+  float y0[8], y1[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float a = x0[e] * inv * g0[e], c = x1[e] * inv * g1[e];
+    y0[e] = a * cs[e] - c * sn[e];
+    y1[e] = c * cs[e] + a * sn[e];
   }
+  if (is_q) {
+    TQ* q = reinterpret_cast<TQ*>(p.qout) + (size_t)t * p.nq * D + hh * D;
+    Vec8<TQ>::store(q + sub * 8, y0);
+    Vec8<TQ>::store(q + HALF + sub * 8, y1);
+  } else {
+    const int slot = p.slots[b];
+    const size_t off = (size_t)slot * p.slot_stride + (size_t)j * p.head_stride + (size_t)pos * D;
+    KV* k = reinterpret_cast<KV*>(p.kcache) + off;
+    Vec8<KV>::store(k + sub * 8, y0);
+    Vec8<KV>::store(k + HALF + sub * 8, y1);
+    const TI* vs = row + (p.nq + p.nkv) * D + j * D;
+    float v0[8], v1[8];
+    Vec8<TI>::load(vs + sub * 8, v0);
+    Vec8<TI>::load(vs + HALF + sub * 8, v1);
+    KV* v = reinterpret_cast<KV*>(p.vcache) + off;
+    Vec8<KV>::store(v + sub * 8, v0);
+    Vec8<KV>::store(v + HALF + sub * 8, v1);
+  }
+}
+
+template <typename TI, typename TQ, typename KV>
+static hipError_t launch_rope(const RopeKvParams& p, hipStream_t s) {
+  const long long lanes = (long long)p.T * (p.nq + p.nkv) * (p.d / 16);
+  const int blocks = (int)((lanes + 255) / 256);
+  if (p.d == 128)
+    rope_kv_kernel<TI, TQ, KV, 128><<<blocks, 256, 0, s>>>(p);
+  else if (p.d == 64)
+    rope_kv_kernel<TI, TQ, KV, 64><<<blocks, 256, 0, s>>>(p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t rope_kv(const RopeKvParams& p, hipStream_t s) {
   if (p.T <= 0) return hipSuccess;
-  if (p.d > 128 || (p.d & 1)) return hipErrorInvalidValue;
-  const long long items = (long long)p.T * (p.nq + p.nkv);
-  const int blocks = (int)((items + 3) / 4);
   if (p.kv_dt == DT_BF16) {
-    if (p.in_dt == DT_BF16 && p.q_dt == DT_BF16)
-      rope_kv_kernel<bf16, bf16, bf16><<<blocks, 256, 0, s>>>(p);
-    else if (p.in_dt == DT_F32 && p.q_dt == DT_F32)
-      rope_kv_kernel<float, float, bf16><<<blocks, 256, 0, s>>>(p);
-    else
-      return hipErrorInvalidValue;
-  } else {
-    if (p.in_dt == DT_F32 && p.q_dt == DT_F32)
-      rope_kv_kernel<float, float, float><<<blocks, 256, 0, s>>>(p);
-    else
-      return hipErrorInvalidValue;
+    if (p.in_dt == DT_BF16 && p.q_dt == DT_BF16) return launch_rope<bf16, bf16, bf16>(p, s);
+    if (p.in_dt == DT_F32 && p.q_dt == DT_F32) return launch_rope<float, float, bf16>(p, s);
+  } else if (p.in_dt == DT_F32 && p.q_dt == DT_F32) {
+    return launch_rope<float, float, float>(p, s);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fsk
