@@ -1,0 +1,328 @@
+// Large bf16 MFMA GEMM for the prefill projections and MLP: 256x256 output
+// tile per workgroup of 4 waves (2 x 2, 128x128 per wave = 4x4 blocks of
+// v_mfma_f32_32x32x16_bf16), operands streamed from HBM straight into LDS.
+//
+// C[M, N] = A[M, K] . B[N, K]^T with both operands K-contiguous: A holds
+// activation rows, B a weight stored [out, in] ("Coming back to Failed Star",
+// First sitting, item 3).  fp32 accumulation.
+//
+// Pipeline.  K is consumed in stages of 32.  Each stage's A and B tiles
+// (2 x 16 KB) are fetched with global_load_lds (16 B per lane, the 64 lanes of
+// one instruction fill 1 KB of LDS contiguously), so no VGPR staging and no
+// ds_write instructions are spent on them.  Four stage buffers form a ring:
+// while the waves multiply stage k, stages k+1..k+3 are in flight.  The
+// buffers are four distinct LDS objects and the K loop is unrolled by four, so
+// every access names its buffer statically; the compiler's tracking of LDS DMA
+// then needs no blanket vmcnt(0) before each fragment read, and the one wait
+// per stage is the explicit vmcnt(16) (this wave's loads for stage k+1 done)
+// before the stage's single barrier.
+//
+// Bank conflicts.  A stage row is 32 bf16 = 64 B (four 16-B chunks).  Row R
+// stores its k-chunk c at chunk slot c ^ ((R >> 2) & 3): the 16 rows a
+// quarter-wave fragment read touches then cover all 64 banks once.  The DMA
+// side picks, for each LDS slot, the global chunk that belongs there.
+//
+// Fragments.  MFMA operand "A" is the weight fragment and operand "B" the
+// activation fragment, so lane l of a 32x32 result holds activation row
+// (l % 32) and four consecutive output columns 8*(r/4) + 4*(l/32) + (0..3) in
+// registers r..r+3.  The epilogue writes those quads into LDS (reused once the
+// K loop has drained) with an XOR-swizzled row layout and streams whole rows
+// back to HBM in 16-B chunks.
+#include "common.h"
+#include "kernels.h"
+
+namespace fsk {
+
+namespace {
+
+constexpr int DK = 32;                  // K per stage
+constexpr int TILE = 256;               // output tile edge
+constexpr int STAGE = 2 * TILE * DK;    // bf16 elements per stage: A rows then B rows (32 KB)
+
+__shared__ __attribute__((aligned(1024))) bf16 g_stage0[STAGE];
+__shared__ __attribute__((aligned(1024))) bf16 g_stage1[STAGE];
+__shared__ __attribute__((aligned(1024))) bf16 g_stage2[STAGE];
+__shared__ __attribute__((aligned(1024))) bf16 g_stage3[STAGE];
+
+template <int S> __device__ __forceinline__ bf16* stage_buf() {
+  return S == 0 ? g_stage0 : S == 1 ? g_stage1 : S == 2 ? g_stage2 : g_stage3;
+}
+__device__ __forceinline__ char* wave_region(int w) {
+  return reinterpret_cast<char*>(w == 0 ? g_stage0 : w == 1 ? g_stage1 : w == 2 ? g_stage2 : g_stage3);
+}
+
+template <int V> struct Ic { static constexpr int value = V; };
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt low bits [3:0], high bits [15:14];
+// expcnt [6:4]; lgkmcnt [11:8]).
+constexpr int WAIT_VM16_LGKM0 = (1 << 14) | 0x70;   // vmcnt(16) lgkmcnt(0)
+constexpr int WAIT_VM0_LGKM0 = 0x70;                // vmcnt(0) lgkmcnt(0)
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+}  // namespace
+
+template <int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ A_lo,
+                     const bf16* __restrict__ B, int ldb, void* __restrict__ out, int ldc,
+                     int M, int N, int K, int tiles_n, int nblocks) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid >> 1, wn = wid & 1;
+  // XCD-aware renumbering: the hardware deals workgroups round-robin over the
+  // 8 XCDs; consecutive tiles (sharing A rows / B rows) go to one XCD's L2.
+  int bid = blockIdx.x;
+  if ((nblocks & 7) == 0) bid = (bid & 7) * (nblocks >> 3) + (bid >> 3);
+  const int n0 = (bid % tiles_n) * TILE, m0 = (bid / tiles_n) * TILE;
+
+  // DMA assignment: wave w, instruction j fills tile rows (4w + j)*16 + lane/4
+  // (chunk slot lane % 4).  Rows past M / N re-read the last valid row; their
+  // results are never stored.
+  const int lr = lane >> 2;
+  const int kc = (lane & 3) ^ ((lr >> 2) & 3);
+  const bf16* pa[4];
+  const bf16* pl[4];
+  const bf16* pb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ra = min(m0 + wid * 64 + j * 16 + lr, M - 1);
+    const int rb = min(n0 + wid * 64 + j * 16 + lr, N - 1);
+    pa[j] = A + (size_t)ra * lda + kc * 8;
+    pl[j] = (A_lo != nullptr ? A_lo : A) + (size_t)ra * lda + kc * 8;
+    pb[j] = B + (size_t)rb * ldb + kc * 8;
+  }
+  const int nk0 = K / DK;
+  const int nk = (A_lo != nullptr) ? 2 * nk0 : nk0;   // a multiple of 4
+
+  auto issue = [&](auto Sc, int st) {
+    bf16* L = stage_buf<decltype(Sc)::value>();
+    const bool lo = st >= nk0;
+    const int k0 = (lo ? st - nk0 : st) * DK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_global_load_lds((lo ? pl[j] : pa[j]) + k0, L + (wid * 4 + j) * 16 * DK, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(pb[j] + k0, L + TILE * DK + (wid * 4 + j) * 16 * DK, 16, 0, 0);
+    }
+  };
+
+  const int lrow = lane & 31;
+  const int sw = (lrow >> 2) & 3;
+  const int aoff = (wm * 128 + lrow) * DK, boff = TILE * DK + (wn * 128 + lrow) * DK;
+  const int so0 = ((lane >> 5) ^ sw) * 8, so1 = ((2 + (lane >> 5)) ^ sw) * 8;
+  bf16x8 fa[2][4], fb[2][4];
+  auto fread = [&](auto Sc, int set, int q) {
+    const bf16* L = stage_buf<decltype(Sc)::value>();
+    const int so = q ? so1 : so0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[set][i] = *reinterpret_cast<const bf16x8*>(L + aoff + i * 32 * DK + so);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(L + boff + j * 32 * DK + so);
+  };
+  f32x16 acc[4][4];   // [n block][m block]
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
+  auto mm = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[j][i], 0, 0, 0);
+  };
+
+  issue(Ic<0>{}, 0);
+  issue(Ic<1>{}, min(1, nk - 1));
+  issue(Ic<2>{}, min(2, nk - 1));
+  __builtin_amdgcn_s_waitcnt(WAIT_VM16_LGKM0);
+  lds_barrier();
+  fread(Ic<0>{}, 0, 0);
+
+  // One stage: the loads of stage kt+3 (into the buffer read in stage kt-1),
+  // then the two 16-wide K halves; the second half's fragments come from the
+  // next stage, read after the barrier that publishes it.  Past the end the
+  // ring re-reads the last stage into buffers nobody reads again, which keeps
+  // the vmcnt bookkeeping uniform.
+  auto step = [&](auto Cc, int kt) {
+    constexpr int C = decltype(Cc)::value;
+    issue(Ic<(C + 3) & 3>{}, min(kt + 3, nk - 1));
+    fread(Ic<C>{}, 1, 1);
+    mm(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(WAIT_VM16_LGKM0);
+    lds_barrier();
+    fread(Ic<(C + 1) & 3>{}, 0, 0);
+    mm(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  };
+  for (int kt = 0; kt < nk; kt += 4) {
+    step(Ic<0>{}, kt);
+    step(Ic<1>{}, kt + 1);
+    step(Ic<2>{}, kt + 2);
+    step(Ic<3>{}, kt + 3);
+  }
+
+  // ---- epilogue: drain the ring, then each wave stages its 128x128 block in
+  // its own 32 KB of LDS and writes whole rows.
+  __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
+  lds_barrier();
+  char* R = wave_region(wid);
+  const int hl = lane >> 5;                 // which quad of the 8-column group
+  const int mrow0 = m0 + wm * 128;
+  const int ncol0 = n0 + wn * 128;
+
+  if (EPI == GEPI_STORE_BF16) {
+    // 128 rows x 256 B; 16-B chunk c of row m at slot c ^ (m & 15)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = i * 32 + lrow;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[j][i][4 * g + e];
+          const int c = j * 4 + g;
+          *reinterpret_cast<bf16x4*>(R + m * 256 + ((c ^ (m & 15)) << 4) + hl * 8) = v;
+        }
+    }
+    bf16* o = reinterpret_cast<bf16*>(out);
+    const int c = lane & 15;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int m = it * 4 + (lane >> 4);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(R + m * 256 + ((c ^ (m & 15)) << 4));
+      const int gm = mrow0 + m, gn = ncol0 + c * 8;
+      if (gm < M && gn < N) *reinterpret_cast<u32x4*>(o + (size_t)gm * ldc + gn) = v;
+    }
+  } else if (EPI == GEPI_SWIGLU_BF16) {
+    // the wave's 128 packed columns are two [32 gate | 32 up] pairs -> 64 outputs;
+    // 128 rows x 128 B, chunk c of row m at slot c ^ (m & 7)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = i * 32 + lrow;
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = (bf16)(silu(acc[2 * p][i][4 * g + e]) * acc[2 * p + 1][i][4 * g + e]);
+          const int c = p * 4 + g;
+          *reinterpret_cast<bf16x4*>(R + m * 128 + ((c ^ (m & 7)) << 4) + hl * 8) = v;
+        }
+    }
+    bf16* o = reinterpret_cast<bf16*>(out);
+    const int c = lane & 7;
+    const int f0 = ncol0 / 2, nf = N / 2;
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int m = it * 8 + (lane >> 3);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(R + m * 128 + ((c ^ (m & 7)) << 4));
+      const int gm = mrow0 + m, f = f0 + c * 8;
+      if (gm < M && f < nf) *reinterpret_cast<u32x4*>(o + (size_t)gm * ldc + f) = v;
+    }
+  } else {
+    // fp32 (STORE_F32 / RESID_F32): two passes of 64 rows x 512 B;
+    // 16-B chunk c of row m at slot c ^ (m & 31)
+    float* o = reinterpret_cast<float*>(out);
+    const int c = lane & 31;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * h + ii;
+        const int m = ii * 32 + lrow;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * g + e];
+            const int cc = j * 8 + 2 * g + hl;
+            *reinterpret_cast<f32x4*>(R + m * 512 + ((cc ^ (m & 31)) << 4)) = v;
+          }
+      }
+      const int gn = ncol0 + c * 4, gnc = min(gn, N - 4);
+      for (int it0 = 0; it0 < 32; it0 += 8) {
+        // the residual reads of 8 rows go out together (clamped addresses are
+        // always valid), then the sums are stored where the row is in range
+        f32x4 old[8];
+        if (EPI == GEPI_RESID_F32) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int gmc = min(mrow0 + h * 64 + (it0 + u) * 2 + (lane >> 5), M - 1);
+            old[u] = *reinterpret_cast<const f32x4*>(o + (size_t)gmc * ldc + gnc);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int m = (it0 + u) * 2 + (lane >> 5);
+          f32x4 v = *reinterpret_cast<const f32x4*>(R + m * 512 + ((c ^ (m & 31)) << 4));
+          const int gm = mrow0 + h * 64 + m;
+          if (EPI == GEPI_RESID_F32) v += old[u];
+          if (gm < M && gn < N) *reinterpret_cast<f32x4*>(o + (size_t)gm * ldc + gn) = v;
+        }
+      }
+    }
+  }
+}
+
+// Usable when K is a multiple of 128, rows are 16-B aligned and the problem
+// has enough 256x256 tiles to fill the chip; otherwise the caller picks
+// another kernel.
+bool gemm_dma_ok(int epi, const void* A, int lda, const void* B, int ldb, const void* out, int ldc,
+                 int M, int N, int K, const void* A_lo) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || N % 8 != 0) return false;
+  if (lda % 8 || ldb % 8 || ldc % 8) return false;
+  const uintptr_t al = (uintptr_t)A | (uintptr_t)B | (uintptr_t)out | (uintptr_t)A_lo;
+  if (al & 15) return false;
+  if (epi == GEPI_SWIGLU_BF16 && N % 64 != 0) return false;
+  const long long tiles = (long long)((M + TILE - 1) / TILE) * ((N + TILE - 1) / TILE);
+  return M >= 1024 && tiles >= 256;
+}
+
+hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc,
+                    int M, int N, int K, hipStream_t s, const void* A_lo) {
+  const int tn = (N + TILE - 1) / TILE, tm = (M + TILE - 1) / TILE;
+  const int nb = tn * tm;
+  const bf16* a = (const bf16*)A;
+  const bf16* b = (const bf16*)B;
+  const bf16* al = (const bf16*)A_lo;
+  switch (epi) {
+    case GEPI_STORE_BF16:
+      gemm_dma_kernel<GEPI_STORE_BF16><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb);
+      break;
+    case GEPI_RESID_F32:
+      gemm_dma_kernel<GEPI_RESID_F32><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb);
+      break;
+    case GEPI_SWIGLU_BF16:
+      gemm_dma_kernel<GEPI_SWIGLU_BF16><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb);
+      break;
+    case GEPI_STORE_F32:
+      gemm_dma_kernel<GEPI_STORE_F32><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fsk

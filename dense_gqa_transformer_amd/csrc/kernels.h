@@ -62,6 +62,12 @@ enum GemmEpi { GEPI_STORE_BF16 = 0, GEPI_RESID_F32 = 1, GEPI_SWIGLU_BF16 = 2, GE
 // remainder pass reusing each B tile (keeps activations near fp32 precision).
 hipError_t gemm_bf16(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc,
                      int M, int N, int K, hipStream_t s, const void* A_lo = nullptr);
+// The large-problem kernel behind gemm_bf16 (256x256 tiles, operands streamed
+// into LDS by DMA): gemm_dma_ok says whether it applies to a call.
+bool gemm_dma_ok(int epi, const void* A, int lda, const void* B, int ldb, const void* out, int ldc,
+                 int M, int N, int K, const void* A_lo);
+hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc,
+                    int M, int N, int K, hipStream_t s, const void* A_lo);
 
 // ---------------------------------------------------------------- q/k norm + RoPE + KV write
 // For T tokens: token t belongs to sequence t / S_per (slot slots[t / S_per]) at
