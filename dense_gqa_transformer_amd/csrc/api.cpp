@@ -498,7 +498,17 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
     char* kc = (char*)m->kcache + (size_t)l * m->layer_stride * m->esz;
     char* vc = (char*)m->vcache + (size_t)l * m->layer_stride * m->esz;
     auto attention = [&]() -> fs_status {
+      AttnPrefillParams a{};
+      a.q = m->qr; a.q_dt = act_dt; a.kcache = kc; a.vcache = vc; a.kv_dt = m->dt;
+      a.out = m->attn; a.o_dt = act_dt; a.slots = m->d_slot;
+      a.B = B; a.S = S; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim;
+      a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
+      a.scale = 1.0f / std::sqrt((float)c.head_dim);
+      // the head_dim-128 kernel takes q pre-multiplied by scale * log2(e)
+      const bool fa = !skinny && attn_prefill_fa_ok(a);
+      a.q_prescale = fa ? a.scale * 1.4426950408889634f : 1.0f;
       RopeKvParams r{};
+      r.qscale = a.q_prescale;
       r.qkv = m->qkv; r.in_dt = act_dt; r.qout = m->qr; r.q_dt = act_dt;
       r.kcache = kc; r.vcache = vc; r.kv_dt = m->dt;
       r.gq = L.q_norm; r.gk = L.k_norm; r.eps = c.rms_eps;
@@ -506,13 +516,7 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
       r.T = (int)T; r.S_per = S; r.nq = c.n_heads; r.nkv = c.n_kv_heads; r.d = c.head_dim;
       r.slot_stride = m->slot_stride; r.head_stride = m->head_stride;
       LAUNCH(m, "rope_kv", s, rope_kv(r, s));
-      AttnPrefillParams a{};
-      a.q = m->qr; a.q_dt = act_dt; a.kcache = kc; a.vcache = vc; a.kv_dt = m->dt;
-      a.out = m->attn; a.o_dt = act_dt; a.slots = m->d_slot;
-      a.B = B; a.S = S; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim;
-      a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
-      a.scale = 1.0f / std::sqrt((float)c.head_dim);
-      LAUNCH(m, "attn", s, skinny ? attn_prefill_vec(a, s) : attn_prefill(a, s));
+      LAUNCH(m, "attn", s, skinny ? attn_prefill_vec(a, s) : fa ? attn_prefill_fa(a, s) : attn_prefill(a, s));
       return FS_OK;
     };
     st = skinny ? block_skinny(m, L, (int)T, attention, s) : block_gemm(m, L, (int)T, false, attention, s);

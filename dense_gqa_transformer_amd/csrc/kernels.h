@@ -84,6 +84,7 @@ struct RopeKvParams {
   int T, S_per, nq, nkv, d;
   long long slot_stride;                    // elements per (layer, slot)
   long long head_stride;                    // elements per KV head (= max_ctx * d)
+  float qscale;                             // factor applied to q' before it is stored (1: none)
 };
 hipError_t rope_kv(const RopeKvParams& p, hipStream_t s);
 
@@ -98,9 +99,16 @@ struct AttnPrefillParams {
   int B, S, nq, nkv, d;
   long long slot_stride, head_stride;
   float scale;
+  float q_prescale;            // factor already applied to q (attn_prefill_fa expects scale*log2(e))
 };
 hipError_t attn_prefill(const AttnPrefillParams& p, hipStream_t s);      // MFMA path when bf16
 hipError_t attn_prefill_vec(const AttnPrefillParams& p, hipStream_t s);  // vector path, any dtype
+// head_dim 128, bf16, even query heads per KV head: 64 queries per wave, K/V
+// tiles streamed into LDS by DMA (the kernel behind attn_prefill for that case)
+// With that kernel q is stored pre-multiplied by scale*log2(e) (RopeKvParams.qscale,
+// AttnPrefillParams.q_prescale); the other attention kernels take q unscaled.
+bool attn_prefill_fa_ok(const AttnPrefillParams& p);
+hipError_t attn_prefill_fa(const AttnPrefillParams& p, hipStream_t s);
 
 // Decode: one new token per sequence, split over context chunks, with the
 // q/k RMSNorm + RoPE + KV append of the new token fused in.  Each workgroup

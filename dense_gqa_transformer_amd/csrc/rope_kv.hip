@@ -74,6 +74,8 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const RopeKvParams p) {
     y1[e] = c * cs[e] + a * sn[e];
   }
   if (is_q) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { y0[e] *= p.qscale; y1[e] *= p.qscale; }
     TQ* q = reinterpret_cast<TQ*>(p.qout) + (size_t)t * p.nq * D + hh * D;
     Vec8<TQ>::store(q + sub * 8, y0);
     Vec8<TQ>::store(q + HALF + sub * 8, y1);
