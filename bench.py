@@ -14,6 +14,8 @@ Also reported:
                   28 per-layer launches replay back to back in a graph,
                   against 8 TB/s HBM;
   prefill      -- prefill tok/s and the MFMA roofline of its dominant kernel;
+  traffic      -- (in each roofline) HBM bytes per launch from the committed
+                  counter summary, while the kernel sources are unchanged;
   cpu_baseline -- the CPU oracle on a bounded sample of the same decode workload.
 
 Prints one JSON line.  Inputs are seeded synthetic weights and tokens
@@ -105,6 +107,24 @@ def cpu_baseline(wl, w, steps):
                       f"512-token prompt (float64 NumPy oracle; prefill untimed)"}
 
 
+def measured_traffic(key):
+    """HBM bytes per launch of one kernel from the committed counter summary
+    (profiles/traffic.json: rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a plain
+    copy), or None when no figure exists or the kernel's sources changed since."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(root, "profiles", "traffic.json")) as f:
+            ent = json.load(f)["kernels"][key]
+        h = hashlib.sha256()
+        for src in ent["sources"]:
+            with open(os.path.join(root, src), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return int(ent["traffic_bytes"]) if h.hexdigest() == ent["sources_sha256"] else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +135,9 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=48)
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only one 4 x 4096 prefill (for hardware-counter passes) and exit")
+    ap.add_argument("--copy-cal", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB device buffer 4 times and exit: the plain copy of known "
+                         "size that calibrates the FETCH_SIZE / WRITE_SIZE byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: --gpus must be 1 "
@@ -123,6 +146,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_cal > 0:
+        n = args.copy_cal << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_cal_bytes": n, "copies": 4}), flush=True)
+        return
 
     import synth
     from dense_gqa_transformer_amd.model import Model, argmax
@@ -196,7 +229,7 @@ def main():
         "decode_hbm_frac_step": round(hbm_frac, 4),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved / 1e9, 1),
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
-                     "traffic": None, "avg_launch_us": round(avg_s * 1e6, 3),
+                     "traffic": measured_traffic("decode." + dom), "avg_launch_us": round(avg_s * 1e6, 3),
                      "bytes_per_launch": int(bytes_launch)},
         "decode_us_per_launch": {k: round(v, 3) for k, v in per_launch.items()},
     }
@@ -237,7 +270,7 @@ def main():
             "mfma_frac_gemms": round(gemm_flops / gemm_time / MFMA_BF16_PEAK, 4),
             "roofline": {"bound": "mfma", "kernel": pdom, "achieved": round(pach / 1e12, 1),
                          "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s", "frac": round(pach / MFMA_BF16_PEAK, 4),
-                         "traffic": None, "avg_launch_us": round(pavg * 1e6, 1)},
+                         "traffic": measured_traffic("prefill." + pdom), "avg_launch_us": round(pavg * 1e6, 1)},
             "kernel_ms_per_pass": {k: round(v[0], 3) for k, v in pper.items()},
         }
 
