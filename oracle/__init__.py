@@ -6,3 +6,4 @@ import this package; the GPU library never does.
 from .oracle import (Oracle, rms_norm, rope, rope_cos_sin, silu, softmax_rows,
                      gqa_attention, linear, greedy_argmax, greedy_argmax_fast,
                      top_k, top2_gap, param_count, tensor_count)
+from . import sampling

@@ -134,6 +134,20 @@ def tokens(seed: int, vocab: int, size) -> np.ndarray:
     return rng.integers(0, vocab, size=size).astype(np.int32)
 
 
+def uniforms(seed: int, size) -> np.ndarray:
+    """Uniform draws on [0, 1) as float32 (the random numbers a sampler consumes)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    u = rng.random(size=size, dtype=np.float64)
+    return np.minimum(u, np.nextafter(np.float32(1), np.float32(0))).astype(np.float32)
+
+
+def logit_rows(seed: int, rows: int, vocab: int, std: float = 0.64) -> np.ndarray:
+    """Synthetic fp32 logit rows ~ N(0, std^2), the spread the 0.6B-shape
+    random-init model produces."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (rng.standard_normal((rows, vocab), dtype=np.float32) * np.float32(std)).astype(np.float32)
+
+
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
