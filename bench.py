@@ -274,6 +274,26 @@ def main():
             "kernel_ms_per_pass": {k: round(v[0], 3) for k, v in pper.items()},
         }
 
+    # seeded sampling of one lm_head row (temperature -> top-k -> top-p -> draw)
+    srow = torch.from_numpy(synth.logit_rows(900, 1, shape.vocab)).to(dev)
+    su = torch.from_numpy(synth.uniforms(901, 1)).to(dev)
+    sout = torch.empty((1,), dtype=torch.int32, device=dev)
+    samp = {}
+    for name, (T, k, p) in {"t0.8_k50_p0.9": (0.8, 50, 0.9), "t1.0_k0_p0.95": (1.0, 0, 0.95)}.items():
+        for _ in range(5):
+            model.sample(srow, T, k, p, su, out=sout)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(50):
+            model.sample(srow, T, k, p, su, out=sout)
+        e1.record()
+        torch.cuda.synchronize()
+        us_call = e0.elapsed_time(e1) / 50 * 1e3
+        passes = 8 if p < 1.0 else 6          # row reads: 3 count + 1-3 mass + kept-sum passes, + final block
+        samp[name] = {"us_per_call": round(us_call, 2), "row_bytes_read": passes * shape.vocab * 4}
+    out["sampling"] = {"workload": f"one fp32 logits row of {shape.vocab}, batch 1", **samp}
+
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, w, args.cpu_steps)
     print(json.dumps(out), flush=True)

@@ -114,6 +114,7 @@ struct fs_model {
   float* lm_pv = nullptr;
   int32_t* lm_pi = nullptr;
   float* logits_tmp = nullptr;    // [max_seqs, V] when the caller passes none
+  SampleRowScratch* sample_scr = nullptr;   // [max_seqs], on the first fs_sample
   // pinned staging of per-call host arrays
   int32_t* stage = nullptr;       // [STAGE_RING][2 * max_seqs]
   hipEvent_t stage_ev[STAGE_RING] = {};
@@ -146,7 +147,7 @@ struct fs_model {
     hipFree(rope_cos); hipFree(rope_sin);
     hipFree(x); hipFree(xn); hipFree(qkv); hipFree(qr); hipFree(attn); hipFree(hbuf);
     hipFree(d_pos); hipFree(d_slot); hipFree(part);
-    hipFree(lm_pv); hipFree(lm_pi); hipFree(logits_tmp);
+    hipFree(lm_pv); hipFree(lm_pi); hipFree(logits_tmp); hipFree(sample_scr);
     for (int i = 0; i < STAGE_RING; ++i)
       if (stage_ev[i]) hipEventDestroy(stage_ev[i]);
     if (stage) hipHostFree(stage);
@@ -757,6 +758,37 @@ fs_status fs_argmax(const float* logits, int32_t B, int32_t V, int32_t* out, voi
   if (logits == nullptr || out == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL argument");
   if (B <= 0 || V <= 0) return fail(FS_ERR_INVALID_ARG, "B and V must be positive");
   HIP_TRY(argmax_rows(logits, B, V, V, out, (hipStream_t)stream));
+  return FS_OK;
+}
+
+fs_status fs_sample(fs_model* m, const float* logits, int32_t B, int32_t V, const fs_sampling* sp,
+                    const float* u, int32_t* out, void* stream) {
+  g_err.clear();
+  if (m == nullptr || logits == nullptr || sp == nullptr || out == nullptr)
+    return fail(FS_ERR_INVALID_ARG, "NULL argument");
+  if (B <= 0 || B > m->cfg.max_seqs) return fail(FS_ERR_INVALID_ARG, "B out of range");
+  if (V <= 0) return fail(FS_ERR_INVALID_ARG, "V must be positive");
+  const float T = sp->temperature;
+  if (!(T >= 0.f) || !std::isfinite(T)) return fail(FS_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+  if (sp->top_k < 0) return fail(FS_ERR_INVALID_ARG, "top_k must be >= 0");
+  if (!(sp->top_p > 0.f && sp->top_p <= 1.f)) return fail(FS_ERR_INVALID_ARG, "top_p must be in (0, 1]");
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0.f) {
+    HIP_TRY(argmax_rows(logits, B, V, V, out, s));
+    return FS_OK;
+  }
+  if (u == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL u");
+  if (m->sample_scr == nullptr &&
+      dalloc(&m->sample_scr, (size_t)m->cfg.max_seqs * sizeof(SampleRowScratch)) != hipSuccess)
+    return fail(FS_ERR_OOM, "sampling scratch allocation failed");
+  SampleParams p{};
+  p.logits = logits; p.ld = V; p.B = B; p.V = V;
+  p.G = std::min(SAMPLE_MAX_BLOCKS, std::max(1, (V + 2047) / 2048));
+  p.slice = (V + p.G - 1) / p.G;
+  p.sc = 1.4426950408889634f / T;
+  p.top_k = sp->top_k; p.top_p = sp->top_p;
+  p.u = u; p.out = out; p.scr = m->sample_scr;
+  HIP_TRY(sample_rows(p, s));
   return FS_OK;
 }
 

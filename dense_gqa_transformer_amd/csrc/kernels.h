@@ -135,4 +135,27 @@ hipError_t attn_combine(const float* part, const int32_t* positions, int B, int 
 // out[b] = greedy ID of row b of logits [B, V] (row stride ldl).
 hipError_t argmax_rows(const float* logits, int B, int V, int ldl, int32_t* out, hipStream_t s);
 
+// ---------------------------------------------------------------- sampling
+// Per-row scratch of the sampler (count and mass histograms of the three radix
+// levels, max key, finite count, per-block kept mass).
+constexpr int SAMPLE_MAX_BLOCKS = 128;
+struct SampleRowScratch {
+  uint32_t c1[4096], c2[4096], c3[256];
+  float m1[4096], m2[4096], m3[256];
+  uint32_t maxkey, nfinite;
+  float bsum[SAMPLE_MAX_BLOCKS];
+};
+struct SampleParams {
+  const float* logits; long long ld;   // rows of logits, ld elements apart
+  int B, V, G, slice;                  // G blocks of `slice` token IDs per row
+  float sc;                            // log2(e) / temperature (temperature > 0)
+  int top_k; float top_p;              // 0 = no top-k limit; top_p in (0, 1]
+  const float* u;                      // device [B], uniform in [0, 1)
+  int32_t* out;                        // device [B]
+  SampleRowScratch* scr;               // device [B]
+};
+// temperature -> top-k -> top-p -> renormalise -> draw for B rows; -1 for a row
+// without a finite logit.
+hipError_t sample_rows(const SampleParams& p, hipStream_t s);
+
 }  // namespace fsk

@@ -1,0 +1,343 @@
+// Seeded sampling of a logits row: temperature -> top-k -> top-p ->
+// renormalise -> draw ("Coming back to Failed Star", section "Next: one
+// complete deterministic generation arc": the sampling arc with an explicit
+// filter order; "ferrite", What it does: temperature, top-k, top-p).
+//
+// Rules (the pages fix only the order): finite logits only; top-k keeps every
+// logit >= the k-th largest (ties at the cut all kept, k = 0 no limit); top-p
+// keeps every token at least as probable as the one at which the ranked
+// cumulative mass of the top-k set first reaches p; the kept probabilities are
+// renormalised and the caller's uniform u is mapped through their cumulative
+// distribution in increasing token ID.
+//
+// No sort.  Logits map to order-preserving 32-bit keys; the top-k cut is the
+// k-th largest key, found by a three-level radix select (12 + 12 + 8 bits) on
+// count histograms; the top-p cut is the largest key whose tail mass reaches
+// p * Z_k, found the same way on histograms of probability mass
+// 2^((x - max) log2(e) / T).  The draw sums the kept mass per block of token
+// IDs, then one workgroup walks the block sums and the chosen block's IDs.
+// Every pass is one launch over (blocks of IDs) x (rows); each block re-derives
+// the digits chosen so far from the previous passes' global histograms, so no
+// sequential step runs between launches.
+#include "common.h"
+#include "kernels.h"
+
+namespace fsk {
+
+namespace {
+
+constexpr int NT = 256;      // threads per block
+constexpr int NB1 = 4096;    // bins, levels 1 and 2 (12 bits each)
+constexpr int NB3 = 256;     // bins, level 3 (8 bits)
+
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float keyf(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+__device__ __forceinline__ bool finite(float f) { return (__float_as_uint(f) & 0x7f800000u) != 0x7f800000u; }
+
+// Inclusive prefix over the NT threads of a block (Hillis-Steele in LDS, a
+// fixed order, so every block computes bit-identical results).  Returns this
+// thread's inclusive sum; *before receives the previous thread's inclusive
+// sum (0 for thread 0) and *total the block total, so neighbouring intervals
+// [before, inclusive] meet exactly.
+template <typename T>
+__device__ T block_inclusive(T v, T* before, T* total) {
+  __shared__ T buf[NT];
+  const int t = threadIdx.x;
+  buf[t] = v;
+  __syncthreads();
+  for (int o = 1; o < NT; o <<= 1) {
+    const T add = t >= o ? buf[t - o] : T(0);
+    __syncthreads();
+    buf[t] += add;
+    __syncthreads();
+  }
+  const T inc = buf[t];
+  *before = t > 0 ? buf[t - 1] : T(0);
+  *total = buf[NT - 1];
+  __syncthreads();
+  return inc;
+}
+
+// Descending-order selection over a histogram of nb bins (count or mass):
+// the bin b where the bins above b hold < target and b brings the total to
+// >= target, and target minus what lies above.  When rounding leaves the
+// total short of target, the lowest non-empty bin.  Called by all NT threads;
+// every thread gets the result.
+template <typename T>
+__device__ void select_desc(const T* h, int nb, T target, int* out_bin, T* out_rem) {
+  __shared__ int sbin;
+  __shared__ T srem;
+  const int t = threadIdx.x;
+  const int w = nb / NT;                      // bins per thread (16 or 1)
+  const int hi = nb - t * w;                  // thread t owns bins [hi - w, hi), read downward
+  T s = 0;
+  for (int i = 1; i <= w; ++i) s += h[hi - i];
+  if (t == 0) sbin = -1;
+  __syncthreads();
+  T above, total;
+  const T upto = block_inclusive<T>(s, &above, &total);
+  if (above < target && upto >= target) {     // exactly one thread's interval holds target
+    T a = above, last_a = above;
+    int last = -1;
+    for (int i = 1; i <= w; ++i) {
+      const T v = h[hi - i];
+      if (v > 0) {
+        last = hi - i;
+        last_a = a;
+        if (a + v >= target) break;
+      }
+      a += v;
+    }
+    if (last >= 0) { sbin = last; srem = target - last_a; }
+  }
+  __syncthreads();
+  if (sbin < 0 && t == 0) {                   // total fell short: lowest non-empty bin
+    int b = 0;
+    for (int i = 0; i < nb; ++i) if (h[i] > 0) { b = i; break; }
+    sbin = b;
+    srem = h[b];
+  }
+  __syncthreads();
+  *out_bin = sbin;
+  *out_rem = srem;
+  __syncthreads();
+}
+
+// Sum of a histogram in a fixed order (identical in every block)
+template <typename T>
+__device__ T hist_total(const T* h, int nb) {
+  const int w = nb / NT;
+  T s = 0;
+  for (int i = 0; i < w; ++i) s += h[threadIdx.x * w + i];
+  T before, total;
+  block_inclusive<T>(s, &before, &total);
+  return total;
+}
+
+// the top-k cut (a full key) from the three count histograms
+__device__ uint32_t topk_key(const SampleRowScratch* sc, int top_k) {
+  const uint32_t nf = sc->nfinite;
+  const uint32_t k = (top_k <= 0 || (uint32_t)top_k > nf) ? nf : (uint32_t)top_k;
+  int b1, b2, b3;
+  uint32_t r1, r2, r3;
+  select_desc<uint32_t>(sc->c1, NB1, k, &b1, &r1);
+  select_desc<uint32_t>(sc->c2, NB1, r1, &b2, &r2);
+  select_desc<uint32_t>(sc->c3, NB3, r2, &b3, &r3);
+  (void)r3;
+  return ((uint32_t)b1 << 20) | ((uint32_t)b2 << 8) | (uint32_t)b3;
+}
+
+// the top-p cut (a full key) from the three mass histograms
+__device__ uint32_t topp_key(const SampleRowScratch* sc, float top_p) {
+  const float z = hist_total<float>(sc->m1, NB1);
+  int b1, b2, b3;
+  float r1, r2, r3;
+  select_desc<float>(sc->m1, NB1, top_p * z, &b1, &r1);
+  select_desc<float>(sc->m2, NB1, r1, &b2, &r2);
+  select_desc<float>(sc->m3, NB3, r2, &b3, &r3);
+  (void)r3;
+  return ((uint32_t)b1 << 20) | ((uint32_t)b2 << 8) | (uint32_t)b3;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(NT) void sample_zero_kernel(SampleRowScratch* scr) {
+  SampleRowScratch* sc = scr + blockIdx.x;
+  uint32_t* p = reinterpret_cast<uint32_t*>(sc);
+  const int n = (int)(sizeof(SampleRowScratch) / 4);
+  for (int i = threadIdx.x; i < n; i += NT) p[i] = 0u;
+}
+
+// mode 0: level-1 count histogram (+ max key, finite count)
+// mode 1: level-2 count histogram;  mode 2: level-3 count histogram
+// mode 3..5: mass histograms of levels 1..3 over keys >= the top-k cut
+// mode 6: kept mass of this block (keys >= the final cut)
+template <int MODE>
+__global__ __launch_bounds__(NT) void sample_pass_kernel(const SampleParams p) {
+  const int row = blockIdx.y;
+  SampleRowScratch* sc = p.scr + row;
+  if (MODE > 0 && sc->nfinite == 0) return;
+  const float* x = p.logits + (size_t)row * p.ld;
+  const int i0 = blockIdx.x * p.slice, i1 = min(i0 + p.slice, p.V);
+  constexpr bool MASS = MODE >= 3 && MODE <= 5;
+  constexpr int NB = (MODE == 2 || MODE == 5) ? NB3 : NB1;
+  __shared__ uint32_t hc[NB1];
+  __shared__ float hm[NB1];
+  __shared__ uint32_t smax, scount;
+  __shared__ float ssum;
+
+  // digits chosen by earlier passes
+  uint32_t pre = 0, kcut = 0, cut = 0;
+  int pshift = 0;
+  float xmax = 0.f;
+  if (MODE == 1 || MODE == 2) {
+    int b1, b2;
+    uint32_t r1, r2;
+    const uint32_t nf = sc->nfinite;
+    const uint32_t k = (p.top_k <= 0 || (uint32_t)p.top_k > nf) ? nf : (uint32_t)p.top_k;
+    select_desc<uint32_t>(sc->c1, NB1, k, &b1, &r1);
+    if (MODE == 1) { pre = (uint32_t)b1; pshift = 20; }
+    else { select_desc<uint32_t>(sc->c2, NB1, r1, &b2, &r2); pre = ((uint32_t)b1 << 12) | (uint32_t)b2; pshift = 8; }
+    (void)r2;
+  }
+  if (MODE >= 3) {
+    kcut = topk_key(sc, p.top_k);
+    xmax = keyf(sc->maxkey);
+  }
+  if (MODE == 4 || MODE == 5) {
+    const float z = hist_total<float>(sc->m1, NB1);
+    int b1, b2;
+    float r1, r2;
+    select_desc<float>(sc->m1, NB1, p.top_p * z, &b1, &r1);
+    if (MODE == 4) { pre = (uint32_t)b1; pshift = 20; }
+    else { select_desc<float>(sc->m2, NB1, r1, &b2, &r2); pre = ((uint32_t)b1 << 12) | (uint32_t)b2; pshift = 8; }
+    (void)r2;
+  }
+  if (MODE == 6) cut = (p.top_p < 1.f) ? topp_key(sc, p.top_p) : kcut;
+
+  for (int b = threadIdx.x; b < NB; b += NT) { hc[b] = 0u; hm[b] = 0.f; }
+  if (threadIdx.x == 0) { smax = 0u; scount = 0u; ssum = 0.f; }
+  __syncthreads();
+  uint32_t lmax = 0u, lcnt = 0u;
+  float lsum = 0.f;
+  for (int i = i0 + threadIdx.x; i < i1; i += NT) {
+    const float v = x[i];
+    if (!finite(v)) continue;
+    const uint32_t key = fkey(v);
+    if (MODE == 0) {
+      atomicAdd(&hc[key >> 20], 1u);
+      lmax = max(lmax, key);
+      ++lcnt;
+    } else if (MODE == 1 || MODE == 2) {
+      if ((key >> pshift) == pre) atomicAdd(&hc[MODE == 1 ? ((key >> 8) & 0xfffu) : (key & 0xffu)], 1u);
+    } else {
+      if (key < kcut) continue;
+      const float e = __builtin_amdgcn_exp2f((v - xmax) * p.sc);
+      if (MODE == 3) atomicAdd(&hm[key >> 20], e);
+      else if (MODE == 4 || MODE == 5) {
+        if ((key >> pshift) == pre) atomicAdd(&hm[MODE == 4 ? ((key >> 8) & 0xfffu) : (key & 0xffu)], e);
+      } else if (key >= cut) {
+        lsum += e;
+      }
+    }
+  }
+  if (MODE == 0) {
+    atomicMax(&smax, lmax);
+    atomicAdd(&scount, lcnt);
+  }
+  if (MODE == 6) atomicAdd(&ssum, lsum);
+  __syncthreads();
+  if (MODE == 6) {
+    if (threadIdx.x == 0) sc->bsum[blockIdx.x] = ssum;
+    return;
+  }
+  uint32_t* gc = MODE == 0 ? sc->c1 : MODE == 1 ? sc->c2 : sc->c3;
+  float* gm = MODE == 3 ? sc->m1 : MODE == 4 ? sc->m2 : sc->m3;
+  for (int b = threadIdx.x; b < NB; b += NT) {
+    if (MASS) { if (hm[b] != 0.f) atomicAdd(&gm[b], hm[b]); }
+    else if (hc[b] != 0u) atomicAdd(&gc[b], hc[b]);
+  }
+  if (MODE == 0 && threadIdx.x == 0) {
+    atomicMax(&sc->maxkey, smax);
+    atomicAdd(&sc->nfinite, scount);
+  }
+}
+
+// One workgroup per row: walk the block sums to the block holding u * Z, then
+// that block's token IDs in order to the token.
+__global__ __launch_bounds__(NT) void sample_final_kernel(const SampleParams p) {
+  const int row = blockIdx.x;
+  SampleRowScratch* sc = p.scr + row;
+  if (sc->nfinite == 0) {
+    if (threadIdx.x == 0) p.out[row] = -1;
+    return;
+  }
+  const uint32_t kcut = topk_key(sc, p.top_k);
+  const uint32_t cut = (p.top_p < 1.f) ? topp_key(sc, p.top_p) : kcut;
+  __shared__ int sblk;
+  __shared__ float sbefore, starget;
+  if (threadIdx.x == 0) {
+    float tot = 0.f;
+    for (int g = 0; g < p.G; ++g) tot += sc->bsum[g];
+    const float target = p.u[row] * tot;
+    // first block whose cumulative mass exceeds target; if rounding never
+    // lets it, the last non-empty block
+    float acc = 0.f, before = 0.f;
+    int blk = 0;
+    for (int g = 0; g < p.G; ++g) {
+      const float sg = sc->bsum[g];
+      if (sg > 0.f) {
+        blk = g;
+        before = acc;
+        if (acc + sg > target) break;
+      }
+      acc += sg;
+    }
+    sblk = blk;
+    sbefore = before;
+    starget = target;
+  }
+  __syncthreads();
+  const float* x = p.logits + (size_t)row * p.ld;
+  const float xmax = keyf(sc->maxkey);
+  const int i0 = sblk * p.slice, i1 = min(i0 + p.slice, p.V);
+  // each thread takes a contiguous run of IDs
+  const int per = (p.slice + NT - 1) / NT;
+  const int a0 = i0 + threadIdx.x * per, a1 = min(a0 + per, i1);
+  float mine = 0.f;
+  for (int i = a0; i < a1; ++i) {
+    const float v = x[i];
+    if (finite(v) && fkey(v) >= cut) mine += __builtin_amdgcn_exp2f((v - xmax) * p.sc);
+  }
+  __shared__ float runs[NT];
+  runs[threadIdx.x] = mine;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float acc = sbefore, before = sbefore;
+    int who = 0;
+    for (int t = 0; t < NT; ++t) {
+      if (runs[t] > 0.f) {
+        who = t;
+        before = acc;
+        if (acc + runs[t] > starget) break;
+      }
+      acc += runs[t];
+    }
+    const int b0 = i0 + who * per, b1 = min(b0 + per, i1);
+    int pick = -1;
+    acc = before;
+    for (int i = b0; i < b1; ++i) {
+      const float v = x[i];
+      if (!(finite(v) && fkey(v) >= cut)) continue;
+      pick = i;
+      acc += __builtin_amdgcn_exp2f((v - xmax) * p.sc);
+      if (acc > starget) break;
+    }
+    p.out[row] = pick;
+  }
+}
+
+hipError_t sample_rows(const SampleParams& p, hipStream_t s) {
+  if (p.B <= 0) return hipSuccess;
+  if (p.G <= 0 || p.G > SAMPLE_MAX_BLOCKS) return hipErrorInvalidValue;
+  const dim3 grid(p.G, p.B);
+  sample_zero_kernel<<<p.B, NT, 0, s>>>(p.scr);
+  sample_pass_kernel<0><<<grid, NT, 0, s>>>(p);
+  sample_pass_kernel<1><<<grid, NT, 0, s>>>(p);
+  sample_pass_kernel<2><<<grid, NT, 0, s>>>(p);
+  sample_pass_kernel<3><<<grid, NT, 0, s>>>(p);   // m1: Z_k, needed by the draw too
+  if (p.top_p < 1.f) {
+    sample_pass_kernel<4><<<grid, NT, 0, s>>>(p);
+    sample_pass_kernel<5><<<grid, NT, 0, s>>>(p);
+  }
+  sample_pass_kernel<6><<<grid, NT, 0, s>>>(p);
+  sample_final_kernel<<<p.B, NT, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace fsk

@@ -128,6 +128,22 @@ class Model:
                                         _stream_ptr(stream)))
         return us.value
 
+    def sample(self, logits: torch.Tensor, temperature: float, top_k: int = 0, top_p: float = 1.0,
+               u: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+               stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """One token per row of fp32 logits [B, V]: temperature -> top-k -> top-p ->
+        renormalise -> draw with the caller's uniforms u [B] (fp32 in [0, 1))."""
+        assert logits.dtype == torch.float32 and logits.is_contiguous() and logits.dim() == 2
+        B, V = logits.shape
+        if out is None:
+            out = torch.empty((B,), dtype=torch.int32, device=logits.device)
+        if u is not None:
+            assert u.dtype == torch.float32 and u.is_contiguous() and u.numel() >= B
+        sp = native.FsSampling(float(temperature), int(top_k), float(top_p))
+        check(self._lib.fs_sample(self._h, _ptr(logits), B, V, ctypes.byref(sp),
+                                  _ptr(u) if u is not None else None, _ptr(out), _stream_ptr(stream)))
+        return out
+
     def kv_read(self, layer: int, slot: int, kv_head: int, pos0: int, n: int,
                 stream: Optional[torch.cuda.Stream] = None):
         k = torch.empty((n, self.shape.head_dim), dtype=self.torch_dtype, device=self.device)

@@ -47,6 +47,10 @@ class FsWeights(ctypes.Structure):
                 ("layers", ctypes.POINTER(FsLayerWeights))]
 
 
+class FsSampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float)]
+
+
 class FsError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -78,6 +82,8 @@ def load() -> ctypes.CDLL:
     lib.fs_decode_step.restype = ctypes.c_int
     lib.fs_argmax.argtypes = [P, i32, i32, P, P]
     lib.fs_argmax.restype = ctypes.c_int
+    lib.fs_sample.argtypes = [P, P, i32, i32, ctypes.POINTER(FsSampling), P, P, P]
+    lib.fs_sample.restype = ctypes.c_int
     lib.fs_slot_length.argtypes = [P, i32]
     lib.fs_slot_length.restype = i32
     lib.fs_kv_read.argtypes = [P, i32, i32, i32, i32, i32, P, P, P]

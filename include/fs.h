@@ -129,6 +129,31 @@ fs_status fs_decode_step(fs_model *m, const int32_t *tokens, const int32_t *posi
  * -1 if the row holds no finite value.  Errors: INVALID_ARG for NULL or B, V <= 0. */
 fs_status fs_argmax(const float *logits, int32_t B, int32_t V, int32_t *out, void *stream);
 
+/* Parameters of the sampling chain temperature -> top-k -> top-p ->
+ * renormalise -> draw ("Coming back to Failed Star", section "Next": the
+ * sampling arc with an explicit filter order; "ferrite", What it does). */
+typedef struct {
+    float temperature;   /* > 0 samples; 0 selects greedily (the fs_argmax rule) */
+    int32_t top_k;       /* keep logits >= the k-th largest (ties kept); 0 = no limit */
+    float top_p;         /* in (0, 1]: keep tokens at least as probable as the one at which
+                            the ranked mass of the top-k set first reaches top_p; 1 = keep all */
+} fs_sampling;
+
+/* Draws one token per row of logits.
+ *   logits: device fp32 [B, V]; u: device fp32 [B], uniform draws in [0, 1)
+ *           supplied by the caller (e.g. from a seeded generator; ignored when
+ *           temperature is 0); out: device int32 [B].
+ * Only finite logits take part.  The kept probabilities (computed in fp32 as
+ * 2^((x - max) log2(e) / temperature)) are renormalised and u is mapped
+ * through their cumulative distribution in increasing token ID: out[b] is the
+ * first kept ID whose cumulative probability exceeds u[b]; -1 for a row with
+ * no finite logit.  Uses the model's sampling scratch (allocated on the first
+ * call, rows up to cfg.max_seqs); calls on one model must not overlap.
+ * Errors: INVALID_ARG (NULL pointer, B outside [1, max_seqs], V <= 0,
+ * temperature < 0 or not finite, top_k < 0, top_p outside (0, 1]), OOM, HIP. */
+fs_status fs_sample(fs_model *m, const float *logits, int32_t B, int32_t V,
+                    const fs_sampling *sampling, const float *u, int32_t *out, void *stream);
+
 /* Current length (positions filled) of a slot, or -1 for a bad handle/slot. */
 int32_t fs_slot_length(const fs_model *m, int32_t slot);
 

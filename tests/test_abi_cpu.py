@@ -12,7 +12,7 @@ def test_library_exports_every_declared_symbol():
     names = native.header_functions()
     assert set(names) == {"fs_model_create", "fs_model_destroy", "fs_prefill", "fs_decode_step",
                           "fs_argmax", "fs_slot_length", "fs_kv_read", "fs_last_error",
-                          "fs_timing", "fs_timing_read", "fs_kernel_bench"}
+                          "fs_timing", "fs_timing_read", "fs_kernel_bench", "fs_sample"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -29,6 +29,8 @@ def test_argument_errors_without_device():
     assert lib.fs_decode_step(None, None, None, None, 1, None, None, None) == native.FS_ERR_INVALID_ARG
     assert lib.fs_kv_read(None, 0, 0, 0, 0, 1, None, None, None) == native.FS_ERR_INVALID_ARG
     assert lib.fs_timing(None, 1) == native.FS_ERR_INVALID_ARG
+    sp = native.FsSampling(1.0, 0, 1.0)
+    assert lib.fs_sample(None, fake, 1, 10, ctypes.byref(sp), fake, fake, None) == native.FS_ERR_INVALID_ARG
 
 
 def _cfg(**kw):
