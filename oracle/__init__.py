@@ -7,3 +7,4 @@ from .oracle import (Oracle, rms_norm, rope, rope_cos_sin, silu, softmax_rows,
                      gqa_attention, linear, greedy_argmax, greedy_argmax_fast,
                      top_k, top2_gap, param_count, tensor_count)
 from . import sampling
+from . import generate
