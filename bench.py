@@ -274,6 +274,17 @@ def main():
             "kernel_ms_per_pass": {k: round(v[0], 3) for k, v in pper.items()},
         }
 
+    # the library's generation loop on the same prompt (greedy, one host check per token)
+    gen_n = 64
+    model.generate(prompt, 4, slot=2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gids, gwhy = model.generate(prompt, gen_n, slot=2)
+    gdt = time.perf_counter() - t0
+    out["generate"] = {"workload": f"fs_generate, greedy, {P}-token prompt, {gen_n} new tokens (prefill included)",
+                       "tokens": len(gids), "stop_reason": gwhy, "ms": round(gdt * 1e3, 2),
+                       "tok_s_incl_prefill": round(len(gids) / gdt, 1)}
+
     # seeded sampling of one lm_head row (temperature -> top-k -> top-p -> draw)
     srow = torch.from_numpy(synth.logit_rows(900, 1, shape.vocab)).to(dev)
     su = torch.from_numpy(synth.uniforms(901, 1)).to(dev)

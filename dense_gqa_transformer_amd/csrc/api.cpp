@@ -115,6 +115,8 @@ struct fs_model {
   int32_t* lm_pi = nullptr;
   float* logits_tmp = nullptr;    // [max_seqs, V] when the caller passes none
   SampleRowScratch* sample_scr = nullptr;   // [max_seqs], on the first fs_sample
+  int32_t* gen_tok = nullptr;     // device int32 [1]: the token fs_generate feeds back
+  int32_t* gen_host = nullptr;    // pinned int32 [1]: its host copy
   // pinned staging of per-call host arrays
   int32_t* stage = nullptr;       // [STAGE_RING][2 * max_seqs]
   hipEvent_t stage_ev[STAGE_RING] = {};
@@ -151,6 +153,8 @@ struct fs_model {
     for (int i = 0; i < STAGE_RING; ++i)
       if (stage_ev[i]) hipEventDestroy(stage_ev[i]);
     if (stage) hipHostFree(stage);
+    if (gen_host) hipHostFree(gen_host);
+    hipFree(gen_tok);
   }
 };
 
@@ -790,6 +794,64 @@ fs_status fs_sample(fs_model* m, const float* logits, int32_t B, int32_t V, cons
   p.u = u; p.out = out; p.scr = m->sample_scr;
   HIP_TRY(sample_rows(p, s));
   return FS_OK;
+}
+
+fs_status fs_generate(fs_model* m, const int32_t* prompt, int32_t S, int32_t slot, const fs_generation* g,
+                      int32_t* out_ids, int32_t* n_out, int32_t* stop_reason, void* stream) {
+  g_err.clear();
+  if (m == nullptr || prompt == nullptr || g == nullptr || n_out == nullptr || stop_reason == nullptr)
+    return fail(FS_ERR_INVALID_ARG, "NULL argument");
+  *n_out = 0;
+  *stop_reason = FS_STOP_NONE;
+  const fs_config& c = m->cfg;
+  if (g->max_new_tokens < 0) return fail(FS_ERR_INVALID_ARG, "max_new_tokens must be >= 0");
+  if (g->n_eos < 0 || (g->n_eos > 0 && g->eos_ids == nullptr)) return fail(FS_ERR_INVALID_ARG, "bad EOS set");
+  if (S <= 0) return fail(FS_ERR_INVALID_ARG, "empty prompt (S <= 0)");
+  if (S > c.max_ctx) return fail(FS_ERR_CAPACITY, "prompt longer than max_ctx");
+  if (slot < 0 || slot >= c.max_seqs) return fail(FS_ERR_INVALID_ARG, "slot out of range");
+  const bool sampled = g->sampling != nullptr && g->sampling->temperature != 0.f;
+  if (g->max_new_tokens > 0 && out_ids == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL out_ids");
+  if (sampled && g->uniforms == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL uniforms");
+  if (g->max_new_tokens == 0) {                 // zero budget: no forward pass at all
+    *stop_reason = FS_STOP_BUDGET;
+    return FS_OK;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  fs_status st;
+  if ((st = ensure_logits_tmp(m)) != FS_OK) return st;
+  if (m->gen_tok == nullptr && dalloc(&m->gen_tok, sizeof(int32_t)) != hipSuccess)
+    return fail(FS_ERR_OOM, "token buffer allocation failed");
+  if (m->gen_host == nullptr &&
+      hipHostMalloc((void**)&m->gen_host, sizeof(int32_t), hipHostMallocDefault) != hipSuccess)
+    return fail(FS_ERR_OOM, "pinned token buffer allocation failed");
+  float* lg = m->logits_tmp;
+  if ((st = fs_prefill(m, prompt, 1, S, &slot, lg, stream)) != FS_OK) return st;
+  for (int i = 0;; ++i) {
+    // select token i (greedy after a decode step comes fused with the lm_head)
+    if (sampled) {
+      if ((st = fs_sample(m, lg, 1, c.vocab, g->sampling, g->uniforms + i, m->gen_tok, stream)) != FS_OK) return st;
+    } else if (i == 0) {
+      HIP_TRY(argmax_rows(lg, 1, c.vocab, c.vocab, m->gen_tok, s));
+    }
+    HIP_TRY(hipMemcpyAsync(m->gen_host, m->gen_tok, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    const int32_t tok = *m->gen_host;
+    if (tok < 0) return fail(FS_ERR_UNSUPPORTED, "no finite logit at step " + std::to_string(i));
+    bool eos = false;
+    for (int e = 0; e < g->n_eos; ++e) eos = eos || g->eos_ids[e] == tok;
+    if (eos) {
+      if (g->include_stop_id) out_ids[(*n_out)++] = tok;
+      *stop_reason = FS_STOP_EOS;
+      return FS_OK;
+    }
+    out_ids[(*n_out)++] = tok;
+    if (*n_out == g->max_new_tokens) { *stop_reason = FS_STOP_BUDGET; return FS_OK; }
+    const int32_t pos = S + i;
+    if (pos >= c.max_ctx) { *stop_reason = FS_STOP_CONTEXT; return FS_OK; }
+    if ((st = fs_decode_step(m, m->gen_tok, &pos, &slot, 1, sampled ? lg : nullptr,
+                             sampled ? nullptr : m->gen_tok, stream)) != FS_OK)
+      return st;
+  }
 }
 
 fs_status fs_kv_read(const fs_model* m, int32_t layer, int32_t slot, int32_t kv_head, int32_t pos0, int32_t n,

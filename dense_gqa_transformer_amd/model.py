@@ -144,6 +144,29 @@ class Model:
                                   _ptr(u) if u is not None else None, _ptr(out), _stream_ptr(stream)))
         return out
 
+    def generate(self, prompt, max_new_tokens: int, eos_ids=(), include_stop_id: bool = False,
+                 sampling=None, uniforms: Optional[torch.Tensor] = None, slot: int = 0,
+                 stream: Optional[torch.cuda.Stream] = None):
+        """Generation for one sequence (fs_generate).  prompt: int32 token IDs
+        (host array or device tensor); sampling = (temperature, top_k, top_p) or
+        None for greedy, with uniforms fp32 [max_new_tokens] on the device.
+        Returns (ids, stop_reason)."""
+        if isinstance(prompt, torch.Tensor):
+            pt = prompt.to(device=self.device, dtype=torch.int32).contiguous().view(-1)
+        else:
+            pt = torch.from_numpy(np.ascontiguousarray(np.asarray(prompt, dtype=np.int32))).to(self.device)
+        eos = int_array(eos_ids) if len(eos_ids) else None
+        sp = native.FsSampling(*[float(sampling[0]), int(sampling[1]), float(sampling[2])]) if sampling else None
+        g = native.FsGeneration(int(max_new_tokens), eos, len(eos_ids), int(bool(include_stop_id)),
+                                ctypes.pointer(sp) if sp is not None else None,
+                                uniforms.data_ptr() if uniforms is not None else None)
+        out = (ctypes.c_int32 * max(1, int(max_new_tokens)))()
+        n = ctypes.c_int32()
+        why = ctypes.c_int32()
+        check(self._lib.fs_generate(self._h, _ptr(pt), int(pt.numel()), int(slot), ctypes.byref(g), out,
+                                    ctypes.byref(n), ctypes.byref(why), _stream_ptr(stream)))
+        return [int(out[i]) for i in range(n.value)], int(why.value)
+
     def kv_read(self, layer: int, slot: int, kv_head: int, pos0: int, n: int,
                 stream: Optional[torch.cuda.Stream] = None):
         k = torch.empty((n, self.shape.head_dim), dtype=self.torch_dtype, device=self.device)

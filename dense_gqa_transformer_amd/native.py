@@ -51,6 +51,15 @@ class FsSampling(ctypes.Structure):
     _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float)]
 
 
+class FsGeneration(ctypes.Structure):
+    _fields_ = [("max_new_tokens", ctypes.c_int32), ("eos_ids", ctypes.POINTER(ctypes.c_int32)),
+                ("n_eos", ctypes.c_int32), ("include_stop_id", ctypes.c_int32),
+                ("sampling", ctypes.POINTER(FsSampling)), ("uniforms", ctypes.c_void_p)]
+
+
+FS_STOP_NONE, FS_STOP_EOS, FS_STOP_BUDGET, FS_STOP_CONTEXT = 0, 1, 2, 3
+
+
 class FsError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -84,6 +93,9 @@ def load() -> ctypes.CDLL:
     lib.fs_argmax.restype = ctypes.c_int
     lib.fs_sample.argtypes = [P, P, i32, i32, ctypes.POINTER(FsSampling), P, P, P]
     lib.fs_sample.restype = ctypes.c_int
+    lib.fs_generate.argtypes = [P, P, i32, i32, ctypes.POINTER(FsGeneration), ctypes.POINTER(i32),
+                                ctypes.POINTER(i32), ctypes.POINTER(i32), P]
+    lib.fs_generate.restype = ctypes.c_int
     lib.fs_slot_length.argtypes = [P, i32]
     lib.fs_slot_length.restype = i32
     lib.fs_kv_read.argtypes = [P, i32, i32, i32, i32, i32, P, P, P]

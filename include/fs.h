@@ -154,6 +154,47 @@ typedef struct {
 fs_status fs_sample(fs_model *m, const float *logits, int32_t B, int32_t V,
                     const fs_sampling *sampling, const float *u, int32_t *out, void *stream);
 
+/* Why fs_generate stopped. */
+typedef enum {
+    FS_STOP_NONE = 0,
+    FS_STOP_EOS = 1,       /* the selected token is in the EOS set */
+    FS_STOP_BUDGET = 2,    /* max_new_tokens tokens are out (or the budget was 0) */
+    FS_STOP_CONTEXT = 3    /* the last token would be forwarded at position max_ctx */
+} fs_stop_reason;
+
+/* Settings of one generation. */
+typedef struct {
+    int32_t max_new_tokens;        /* >= 0; 0 returns at once without any forward pass */
+    const int32_t *eos_ids;        /* host int32 [n_eos]: the explicit EOS set (may be empty) */
+    int32_t n_eos;
+    int32_t include_stop_id;       /* nonzero: the EOS ID that stops the loop is returned as the last ID */
+    const fs_sampling *sampling;   /* NULL or temperature 0: greedy (the fs_argmax rule) */
+    const float *uniforms;         /* device fp32 [max_new_tokens] when sampling: token i draws with uniforms[i] */
+} fs_generation;
+
+/* Greedy or sampled generation for one sequence, under the contract the
+ * pages ask to settle first ("Coming back to Failed Star", section "Next:
+ * one complete deterministic generation arc"): raw token IDs, no implicit
+ * BOS; an explicit EOS set; a token budget that may be zero; never a forward
+ * pass at a position >= max_ctx; distinct stop reasons.
+ *   prompt: device int32 [S], S >= 1; slot: the sequence's slot (reset, as by
+ *   fs_prefill); out_ids: host int32 [max_new_tokens]; *n_out: IDs written;
+ *   *stop_reason: an fs_stop_reason.
+ * Token i is selected from the logits of position S-1+i.  After selecting it:
+ * an EOS ID stops the loop (FS_STOP_EOS; appended only with include_stop_id);
+ * otherwise the ID is appended; a full budget stops (FS_STOP_BUDGET); if the
+ * token's own position S+i is >= max_ctx it cannot be forwarded and the loop
+ * stops with the token kept (FS_STOP_CONTEXT); else one decode step (graph
+ * replay) forwards it.  The host reads each 4-byte token back to check the
+ * stop rules.  Synchronous.
+ * Errors: INVALID_ARG (NULL pointer, S <= 0, bad slot, max_new_tokens < 0,
+ * n_eos < 0, bad sampling parameters); CAPACITY (S > max_ctx); UNSUPPORTED
+ * (a step's logits hold no finite value: the loop stops, *n_out and
+ * *stop_reason = FS_STOP_NONE describe what was produced); OOM, HIP. */
+fs_status fs_generate(fs_model *m, const int32_t *prompt, int32_t S, int32_t slot,
+                      const fs_generation *gen, int32_t *out_ids, int32_t *n_out,
+                      int32_t *stop_reason, void *stream);
+
 /* Current length (positions filled) of a slot, or -1 for a bad handle/slot. */
 int32_t fs_slot_length(const fs_model *m, int32_t slot);
 

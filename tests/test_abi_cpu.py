@@ -12,7 +12,7 @@ def test_library_exports_every_declared_symbol():
     names = native.header_functions()
     assert set(names) == {"fs_model_create", "fs_model_destroy", "fs_prefill", "fs_decode_step",
                           "fs_argmax", "fs_slot_length", "fs_kv_read", "fs_last_error",
-                          "fs_timing", "fs_timing_read", "fs_kernel_bench", "fs_sample"}
+                          "fs_timing", "fs_timing_read", "fs_kernel_bench", "fs_sample", "fs_generate"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -31,6 +31,11 @@ def test_argument_errors_without_device():
     assert lib.fs_timing(None, 1) == native.FS_ERR_INVALID_ARG
     sp = native.FsSampling(1.0, 0, 1.0)
     assert lib.fs_sample(None, fake, 1, 10, ctypes.byref(sp), fake, fake, None) == native.FS_ERR_INVALID_ARG
+    g = native.FsGeneration(4, None, 0, 0, None, None)
+    n, why = ctypes.c_int32(), ctypes.c_int32()
+    out = (ctypes.c_int32 * 4)()
+    assert lib.fs_generate(None, fake, 3, 0, ctypes.byref(g), out, ctypes.byref(n), ctypes.byref(why),
+                           None) == native.FS_ERR_INVALID_ARG
 
 
 def _cfg(**kw):
