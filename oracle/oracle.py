@@ -37,6 +37,12 @@ layout); RoPE rotates the pairs (i, i + d/2) by ``p * theta^(-2i/d)``; the
 attention scale is ``1/sqrt(head_dim)``; query head h reads KV head
 ``h // (n_heads / n_kv_heads)``; the mask is causal and includes the diagonal;
 ``silu(z) = z / (1 + exp(-z))``; a row with no finite logit selects -1.
+The gated-attention variant ("ferrite", section "What it does": gated
+attention output, partial rotate-half RoPE on 64 of 256 dims, and the fix of
+its q/gate split to the per-head interleaved layout): wq rows hold, head by
+head, the query then the gate; the head's attention output is multiplied by
+``sigmoid(gate)`` before the output projection; only the first ``rope_dim``
+dims of q and k rotate, with angles ``p * theta^(-2i/rope_dim)``.
 
 Every function is pinned by tests in ``tests/test_oracle_pins.py``.
 """
@@ -74,16 +80,19 @@ def rope_cos_sin(positions: np.ndarray, head_dim: int, theta: float, dtype):
     return np.cos(ang).astype(dtype), np.sin(ang).astype(dtype)
 
 
-def rope(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
+def rope(x: np.ndarray, positions: np.ndarray, theta: float, rot_dim: Optional[int] = None) -> np.ndarray:
     """Rotate-half RoPE on ``x[S, heads, d]`` at ``positions[S]``.
 
-    The pair (x_i, x_{i+d/2}) is rotated by angle p*theta^(-2i/d):
-    (x_i cos a - x_{i+d/2} sin a,  x_{i+d/2} cos a + x_i sin a).
+    The pair (x_i, x_{i+r/2}) is rotated by angle p*theta^(-2i/r):
+    (x_i cos a - x_{i+r/2} sin a,  x_{i+r/2} cos a + x_i sin a), for the first
+    ``r = rot_dim`` dims (default all of d); dims r..d-1 pass through.
     RoPE is named in "Failed Star (fs)", section "How it's built"; the
-    rotate-half pairing is the convention "ferrite", section "What it does",
-    names for its attention blocks.
+    rotate-half pairing, and rotating only 64 of 256 head dims, are what
+    "ferrite", section "What it does", describes for its attention blocks.
     """
     d = x.shape[-1]
+    if rot_dim is not None and rot_dim != d:
+        return np.concatenate([rope(x[..., :rot_dim], positions, theta), x[..., rot_dim:]], axis=-1)
     half = d // 2
     cos, sin = rope_cos_sin(positions, d, theta, x.dtype)
     cos = cos[:, None, :]
@@ -91,6 +100,11 @@ def rope(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
     x1 = x[..., :half]
     x2 = x[..., half:]
     return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    """Logistic function 1 / (1 + e^-z), the output gate of gated attention."""
+    return 1.0 / (1.0 + np.exp(-z))
 
 
 def silu(z: np.ndarray) -> np.ndarray:
@@ -167,17 +181,28 @@ class Oracle:
         s = x.shape[0]
         # attention half
         xn = rms_norm(x, w["attn_norm"], sh.rms_eps)
-        q = linear(xn, w["wq"]).reshape(s, sh.n_heads, sh.head_dim)
+        qp = linear(xn, w["wq"])
+        gate = None
+        if getattr(sh, "attn_gate", False):
+            # per-head interleaved [query | gate] rows ("ferrite", What it does)
+            qg = qp.reshape(s, sh.n_heads, 2, sh.head_dim)
+            q, gate = qg[:, :, 0, :], qg[:, :, 1, :]
+        else:
+            q = qp.reshape(s, sh.n_heads, sh.head_dim)
         k = linear(xn, w["wk"]).reshape(s, sh.n_kv_heads, sh.head_dim)
         v = linear(xn, w["wv"]).reshape(s, sh.n_kv_heads, sh.head_dim)
-        q = rope(rms_norm(q, w["q_norm"], sh.rms_eps), pos, sh.rope_theta)
-        k = rope(rms_norm(k, w["k_norm"], sh.rms_eps), pos, sh.rope_theta)
+        rot = getattr(sh, "rope_dim", 0) or sh.head_dim
+        q = rope(rms_norm(q, w["q_norm"], sh.rms_eps), pos, sh.rope_theta, rot)
+        k = rope(rms_norm(k, w["k_norm"], sh.rms_eps), pos, sh.rope_theta, rot)
         if k_past is not None and k_past.shape[0] > 0:
             k_all = np.concatenate([k_past, k], axis=0)
             v_all = np.concatenate([v_past, v], axis=0)
         else:
             k_all, v_all = k, v
-        a = gqa_attention(q, k_all, v_all, pos).reshape(s, sh.q_width)
+        a = gqa_attention(q, k_all, v_all, pos)
+        if gate is not None:
+            a = a * sigmoid(gate)
+        a = a.reshape(s, sh.q_width)
         x = x + linear(a, w["wo"])
         if dump is not None:
             dump[f"layer{li}.q"] = q

@@ -47,10 +47,21 @@ class ModelShape:
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
     dtype: str = BF16
+    rope_dim: int = 0          # rotated dims per head (0: all of head_dim)
+    attn_gate: bool = False    # q projection carries a per-head output gate
 
     @property
     def q_width(self) -> int:
         return self.n_heads * self.head_dim
+
+    @property
+    def rot_dim(self) -> int:
+        return self.rope_dim or self.head_dim
+
+    @property
+    def q_proj_width(self) -> int:
+        """Rows of wq: per head the query, then (gated) its gate, interleaved by head."""
+        return self.q_width * (2 if self.attn_gate else 1)
 
     @property
     def kv_width(self) -> int:
@@ -59,7 +70,7 @@ class ModelShape:
     def layer_shapes(self) -> Dict[str, tuple]:
         h, q, kv, i, d = self.hidden, self.q_width, self.kv_width, self.ffn, self.head_dim
         return {
-            "attn_norm": (h,), "wq": (q, h), "wk": (kv, h), "wv": (kv, h),
+            "attn_norm": (h,), "wq": (self.q_proj_width, h), "wk": (kv, h), "wv": (kv, h),
             "q_norm": (d,), "k_norm": (d,), "wo": (h, q), "mlp_norm": (h,),
             "w_gate": (i, h), "w_up": (i, h), "w_down": (h, i),
         }
@@ -71,6 +82,13 @@ TINY = ModelShape(n_layers=2, hidden=256, n_heads=4, n_kv_heads=2, head_dim=64,
 # Qwen3-0.6B shape, bf16 weights.
 QWEN3_0P6B = ModelShape(n_layers=28, hidden=1024, n_heads=16, n_kv_heads=8,
                         head_dim=128, ffn=3072, vocab=151936, dtype=BF16)
+# The gated attention variant ("ferrite", What it does): 8 query / 2 KV heads
+# of width 256, rotate-half RoPE on 64 of the 256 dims, a sigmoid gate on each
+# head's output carried by the q projection (per-head interleaved [q | gate]).
+GATED_TINY = ModelShape(n_layers=2, hidden=512, n_heads=8, n_kv_heads=2, head_dim=256,
+                        ffn=1024, vocab=4096, dtype=F32, rope_dim=64, attn_gate=True)
+GATED_BF16 = ModelShape(n_layers=2, hidden=512, n_heads=8, n_kv_heads=2, head_dim=256,
+                        ffn=1024, vocab=4096, dtype=BF16, rope_dim=64, attn_gate=True)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -173,6 +191,10 @@ def workload(name: str) -> Workload:
     prefill_0p6b_4x4096  : 0.6B bf16, four 4096-token prompts, last-token logits
     decode_0p6b_bs64     : 0.6B bf16, 64 prompts of ragged length in
                            [256, 4096], 128 decode steps each
+    gated_tiny_fp32      : gated-attention variant (fp32), one 16-token prompt,
+                           16 decode steps
+    gated_bf16           : gated-attention variant (bf16), two 160-token
+                           prompts, 16 decode steps
     """
     if name == "tiny_fp32":
         t = tokens(101, TINY.vocab, (1, 16))
@@ -192,11 +214,17 @@ def workload(name: str) -> Workload:
         prompts = tuple(rng.integers(0, QWEN3_0P6B.vocab, size=int(n)).astype(np.int32)
                         for n in lens)
         return Workload(name, QWEN3_0P6B, prompts, 128)
+    if name == "gated_tiny_fp32":
+        t = tokens(107, GATED_TINY.vocab, (1, 16))
+        return Workload(name, GATED_TINY, (t[0],), 16)
+    if name == "gated_bf16":
+        t = tokens(108, GATED_BF16.vocab, (2, 160))
+        return Workload(name, GATED_BF16, (t[0], t[1]), 16)
     raise KeyError(name)
 
 
 WORKLOADS = ("tiny_fp32", "scorer_0p6b", "decode_0p6b_bs1",
-             "prefill_0p6b_4x4096", "decode_0p6b_bs64")
+             "prefill_0p6b_4x4096", "decode_0p6b_bs64", "gated_tiny_fp32", "gated_bf16")
 
 
 def small_shape(**kw) -> ModelShape:
