@@ -86,6 +86,9 @@ struct fs_model {
   int dt = 0;
   size_t esz = 0;
   int qkv_w = 0, qw = 0, kvw = 0;
+  int qpw = 0;          // rows of the q (+ gate) projection
+  int rot = 0;          // rotated dims per head
+  int gated = 0;        // attention output gate carried by the q projection
   // weights
   void* wblob = nullptr;
   float* nblob = nullptr;
@@ -354,7 +357,11 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   const int rep = c.n_heads / c.n_kv_heads;
   if (rep != 1 && rep != 2 && rep != 4 && rep != 8)
     return fail(FS_ERR_UNSUPPORTED, "n_heads / n_kv_heads must be 1, 2, 4 or 8");
-  if (c.head_dim != 64 && c.head_dim != 128) return fail(FS_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c.head_dim != 64 && c.head_dim != 128 && c.head_dim != 256)
+    return fail(FS_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
+  if (c.rope_dim < 0 || c.rope_dim > c.head_dim || c.rope_dim % 16 != 0)
+    return fail(FS_ERR_UNSUPPORTED, "rope_dim must be 0 or a multiple of 16 up to head_dim");
+  if (c.attn_gate != 0 && c.attn_gate != 1) return fail(FS_ERR_INVALID_ARG, "attn_gate must be 0 or 1");
   if (c.hidden % 64 != 0 || c.ffn % 64 != 0)
     return fail(FS_ERR_UNSUPPORTED, "hidden and ffn must be multiples of 64");
   if (!cpl_ok(c.hidden) || !cpl_ok(c.ffn) || !cpl_ok(c.n_heads * c.head_dim))
@@ -378,7 +385,10 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   m->esz = dt_size(c.dtype);
   m->qw = c.n_heads * c.head_dim;
   m->kvw = c.n_kv_heads * c.head_dim;
-  m->qkv_w = m->qw + 2 * m->kvw;
+  m->rot = c.rope_dim > 0 ? c.rope_dim : c.head_dim;
+  m->gated = c.attn_gate;
+  m->qpw = m->qw * (m->gated ? 2 : 1);          // q (+ gate) projection rows
+  m->qkv_w = m->qpw + 2 * m->kvw;
   const size_t H = c.hidden, I = c.ffn, V = c.vocab, es = m->esz;
   const size_t per_layer = ((size_t)m->qkv_w * H + H * m->qw + 2 * I * H + H * I) * es;
   const size_t wbytes = V * H * es + per_layer * c.n_layers;
@@ -402,10 +412,10 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
     const fs_layer_weights& src = w->layers[l];
     LayerW& L = m->layers[l];
     L.wqkv = wp; wp += (size_t)m->qkv_w * H * es;
-    chk(hipMemcpyAsync(L.wqkv, src.wq, (size_t)m->qw * H * es, hipMemcpyDeviceToDevice, s));
-    chk(hipMemcpyAsync((char*)L.wqkv + (size_t)m->qw * H * es, src.wk, (size_t)m->kvw * H * es,
+    chk(hipMemcpyAsync(L.wqkv, src.wq, (size_t)m->qpw * H * es, hipMemcpyDeviceToDevice, s));
+    chk(hipMemcpyAsync((char*)L.wqkv + (size_t)m->qpw * H * es, src.wk, (size_t)m->kvw * H * es,
                        hipMemcpyDeviceToDevice, s));
-    chk(hipMemcpyAsync((char*)L.wqkv + (size_t)(m->qw + m->kvw) * H * es, src.wv, (size_t)m->kvw * H * es,
+    chk(hipMemcpyAsync((char*)L.wqkv + (size_t)(m->qpw + m->kvw) * H * es, src.wv, (size_t)m->kvw * H * es,
                        hipMemcpyDeviceToDevice, s));
     L.wo = wp; wp += H * m->qw * es;
     chk(hipMemcpyAsync(L.wo, src.wo, H * m->qw * es, hipMemcpyDeviceToDevice, s));
@@ -432,12 +442,12 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   if (dalloc(&m->kcache, kvbytes) != hipSuccess || dalloc(&m->vcache, kvbytes) != hipSuccess)
     return bail(FS_ERR_OOM, "KV cache allocation failed");
 
-  // RoPE tables: angle p * theta^(-2i/d) in double, cos/sin stored as fp32
-  const int half = c.head_dim / 2;
+  // RoPE tables: angle p * theta^(-2i/r) (r = rotated dims) in double, cos/sin stored as fp32
+  const int half = m->rot / 2;
   std::vector<float> hc((size_t)c.max_ctx * half), hs((size_t)c.max_ctx * half);
   for (int p = 0; p < c.max_ctx; ++p)
     for (int i = 0; i < half; ++i) {
-      const double ang = (double)p * std::pow((double)c.rope_theta, -2.0 * i / (double)c.head_dim);
+      const double ang = (double)p * std::pow((double)c.rope_theta, -2.0 * i / (double)m->rot);
       hc[(size_t)p * half + i] = (float)std::cos(ang);
       hs[(size_t)p * half + i] = (float)std::sin(ang);
     }
@@ -514,6 +524,7 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
       a.q_prescale = fa ? a.scale * 1.4426950408889634f : 1.0f;
       RopeKvParams r{};
       r.qscale = a.q_prescale;
+      r.rot = m->rot; r.gated = m->gated;
       r.qkv = m->qkv; r.in_dt = act_dt; r.qout = m->qr; r.q_dt = act_dt;
       r.kcache = kc; r.vcache = vc; r.kv_dt = m->dt;
       r.gq = L.q_norm; r.gk = L.k_norm; r.eps = c.rms_eps;
@@ -522,6 +533,8 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
       r.slot_stride = m->slot_stride; r.head_stride = m->head_stride;
       LAUNCH(m, "rope_kv", s, rope_kv(r, s));
       LAUNCH(m, "attn", s, skinny ? attn_prefill_vec(a, s) : fa ? attn_prefill_fa(a, s) : attn_prefill(a, s));
+      if (m->gated)
+        LAUNCH(m, "attn_gate", s, attn_gate(m->attn, act_dt, m->qkv, act_dt, (int)T, c.n_heads, c.head_dim, m->qkv_w, s));
       return FS_OK;
     };
     st = skinny ? block_skinny(m, L, (int)T, attention, s) : block_gemm(m, L, (int)T, false, attention, s);
@@ -555,9 +568,13 @@ static fs_status enqueue_decode(fs_model* m, const int32_t* tokens, int B, float
       a.B = B; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim; a.chunk = chunk; a.nchunks = nchunks;
       a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
       a.scale = 1.0f / std::sqrt((float)c.head_dim);
+      a.rot = m->rot; a.gated = m->gated;
       LAUNCH(m, "attn", s, attn_decode(a, s));
       LAUNCH(m, "combine", s, attn_combine(m->part, m->d_pos, B, c.n_heads, c.head_dim, chunk, nchunks,
                                            m->attn, skinny ? DT_F32 : DT_BF16, s));
+      if (m->gated)
+        LAUNCH(m, "attn_gate", s, attn_gate(m->attn, skinny ? DT_F32 : DT_BF16, m->qkv, DT_F32, B, c.n_heads,
+                                       c.head_dim, m->qkv_w, s));
       return FS_OK;
     };
     st = skinny ? block_skinny(m, L, B, attention, s) : block_gemm(m, L, B, true, attention, s);
@@ -686,6 +703,7 @@ fs_status fs_kernel_bench(fs_model* m, const char* label, int32_t slot, int32_t 
       a.part = m->part; a.B = 1; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim;
       a.chunk = chunk; a.nchunks = nchunks; a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
       a.scale = 1.0f / std::sqrt((float)c.head_dim);
+      a.rot = m->rot; a.gated = m->gated;
       HIP_TRY(attn_decode(a, ls));
     } else if (std::strcmp(label, "combine") == 0) {
       HIP_TRY(attn_combine(m->part, m->d_pos, 1, c.n_heads, c.head_dim, chunk, nchunks, m->attn, DT_F32, ls));

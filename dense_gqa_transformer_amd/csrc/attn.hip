@@ -12,9 +12,11 @@
 // Group states merge exactly: m = max, l and o rescaled by 2^(m_g - m).
 //
 // Decode kernel: one workgroup per (sequence, KV head, context chunk).  It
-// also normalises and rotates the new token's q and k and appends k, v to
-// the cache (fused), and writes the chunk's partial softmax state; the
-// partials are combined by the consumer (split-K flash decoding).
+// also normalises and rotates the new token's q and k (rotate-half on the
+// first `rot` dims; q rows interleaved with gate rows when the variant is
+// gated) and appends k, v to the cache (fused), and writes the chunk's
+// partial softmax state; the partials are combined by the consumer (split-K
+// flash decoding).
 #include "common.h"
 #include "kernels.h"
 
@@ -34,6 +36,9 @@ template <> __device__ __forceinline__ void loadn<float, 4>(const float* p, floa
   const float4 a = *reinterpret_cast<const float4*>(p);
   o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
 }
+
+template <> __device__ __forceinline__ void loadn<bf16, 16>(const bf16* p, float* o) { load8(p, o); load8(p + 8, o + 8); }
+template <> __device__ __forceinline__ void loadn<float, 16>(const float* p, float* o) { load8(p, o); load8(p + 8, o + 8); }
 
 // Raw (unconverted) loads of d/16 elements, so a batch of them can be in
 // flight before any is used.
@@ -68,6 +73,43 @@ template <> struct RawKV<float, 4> {
   __device__ __forceinline__ void load(const float* p) { a = *reinterpret_cast<const float4*>(p); }
   __device__ __forceinline__ void get(float* o) const { o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; }
 };
+
+template <typename KV> struct RawKV<KV, 16> {
+  RawKV<KV, 8> a, b;
+  __device__ __forceinline__ void load(const KV* p) { a.load(p); b.load(p + 8); }
+  __device__ __forceinline__ void get(float* o) const { a.get(o); b.get(o + 8); }
+};
+
+// RMSNorm over d with weight g, then rotate-half RoPE on the first `rot`
+// dims (pairs (i, i + rot/2), angles from the table rows cs / sn of length
+// rot/2), times `mul`, into y[0..D).  One wave: lane holds elements lane + 64i;
+// a rotated element also reads its partner from x.
+template <int D>
+__device__ __forceinline__ void norm_rope_wave(const float* x, const float* g, const float* cs, const float* sn,
+                                               int rot, float eps, float mul, int lane, float* y) {
+  constexpr int NE = D / 64;
+  float v[NE];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    v[i] = x[lane + 64 * i];
+    ss = fmaf(v[i], v[i], ss);
+  }
+  const float inv = rsqrtf(wave_sum(ss) / (float)D + eps);
+  const int rh = rot >> 1;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int e = lane + 64 * i;
+    float a = v[i] * inv * g[e];
+    if (e < rot) {
+      const bool lo = e < rh;
+      const int pe = lo ? e + rh : e - rh, fi = lo ? e : e - rh;
+      const float b = x[pe] * inv * g[pe];
+      a = lo ? a * cs[fi] - b * sn[fi] : a * cs[fi] + b * sn[fi];
+    }
+    y[e] = a * mul;
+  }
+}
 
 template <int REP, int DP>
 struct SoftState {
@@ -150,7 +192,6 @@ __device__ __forceinline__ void attend(SoftState<REP, D / 16>& st, const float (
 template <typename KV, int D, int REP>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams p) {
   constexpr int DP = D / 16;
-  constexpr int HALF = D / 2;
   __shared__ float qs[REP][D];
   __shared__ float knew[D], vnew[D];
   __shared__ float sm[4][REP], sl[4][REP];
@@ -166,7 +207,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
   const int c0 = c * p.chunk;
   if (c0 >= n) return;                                  // chunk past this sequence
   const int c1 = min(c0 + p.chunk, n);
-  const int W = (p.nq + 2 * p.nkv) * D;
+  const int qmul = p.gated ? 2 : 1;                      // q rows interleaved with gate rows
+  const int W = (p.nq * qmul + 2 * p.nkv) * D;
   const float* row = p.qkv + (size_t)b * W;
   const size_t kvoff = (size_t)slot * p.slot_stride + (size_t)j * p.head_stride;
   KV* kb = reinterpret_cast<KV*>(p.kcache) + kvoff;
@@ -187,43 +229,25 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
   }
 
   // ---- q heads of this group: RMSNorm over d, RoPE at pos, pre-scale
+  const float* cs_row = p.cos_t + (size_t)pos * (p.rot >> 1);
+  const float* sn_row = p.sin_t + (size_t)pos * (p.rot >> 1);
   for (int r = wid; r < REP; r += 4) {
     const int h = j * REP + r;
-    const bool on = lane < HALF;
-    float x0 = on ? row[h * D + lane] : 0.f;
-    float x1 = on ? row[h * D + lane + HALF] : 0.f;
-    const float cs = on ? p.cos_t[(size_t)pos * HALF + lane] : 0.f;
-    const float sn = on ? p.sin_t[(size_t)pos * HALF + lane] : 0.f;
-    const float inv = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)D + p.eps);
-    if (on) {
-      x0 *= inv * p.gq[lane];
-      x1 *= inv * p.gq[lane + HALF];
-      qs[r][lane] = (x0 * cs - x1 * sn) * qscale;
-      qs[r][lane + HALF] = (x1 * cs + x0 * sn) * qscale;
-    }
+    norm_rope_wave<D>(row + (size_t)h * D * qmul, p.gq, cs_row, sn_row, p.rot, p.eps, qscale, lane, qs[r]);
   }
   // ---- the new token's k, v if it falls in this chunk: normalise, rotate, append
   if (has_new && wid == 3) {
-    const bool on = lane < HALF;
-    const float* kr = row + p.nq * D + j * D;
-    const float* vr = row + (p.nq + p.nkv) * D + j * D;
-    float x0 = on ? kr[lane] : 0.f;
-    float x1 = on ? kr[lane + HALF] : 0.f;
-    const float va = on ? vr[lane] : 0.f, vbv = on ? vr[lane + HALF] : 0.f;
-    const float cs = on ? p.cos_t[(size_t)pos * HALF + lane] : 0.f;
-    const float sn = on ? p.sin_t[(size_t)pos * HALF + lane] : 0.f;
-    const float inv = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)D + p.eps);
-    if (on) {
-      x0 *= inv * p.gk[lane];
-      x1 *= inv * p.gk[lane + HALF];
-      const KV k0 = from_f32<KV>(x0 * cs - x1 * sn), k1 = from_f32<KV>(x1 * cs + x0 * sn);
-      const KV v0 = from_f32<KV>(va), v1 = from_f32<KV>(vbv);
-      kb[(size_t)pos * D + lane] = k0;
-      kb[(size_t)pos * D + lane + HALF] = k1;
-      vb[(size_t)pos * D + lane] = v0;
-      vb[(size_t)pos * D + lane + HALF] = v1;
-      knew[lane] = to_f32(k0); knew[lane + HALF] = to_f32(k1);
-      vnew[lane] = to_f32(v0); vnew[lane + HALF] = to_f32(v1);
+    const float* kr = row + (size_t)p.nq * D * qmul + j * D;
+    const float* vr = kr + (size_t)p.nkv * D;
+    norm_rope_wave<D>(kr, p.gk, cs_row, sn_row, p.rot, p.eps, 1.f, lane, knew);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      const int e = lane + 64 * i;
+      const KV kk = from_f32<KV>(knew[e]), vv = from_f32<KV>(vr[e]);
+      kb[(size_t)pos * D + e] = kk;
+      vb[(size_t)pos * D + e] = vv;
+      knew[e] = to_f32(kk);
+      vnew[e] = to_f32(vv);
     }
   }
   __syncthreads();
@@ -363,6 +387,10 @@ hipError_t attn_combine(const float* part, const int32_t* positions, int B, int 
     attn_combine_kernel<bf16, 128><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (bf16*)out);
   else if (d == 128)
     attn_combine_kernel<float, 128><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (float*)out);
+  else if (d == 256 && o_dt == DT_BF16)
+    attn_combine_kernel<bf16, 256><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (bf16*)out);
+  else if (d == 256)
+    attn_combine_kernel<float, 256><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (float*)out);
   else if (d == 64 && o_dt == DT_BF16)
     attn_combine_kernel<bf16, 64><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (bf16*)out);
   else if (d == 64)
@@ -390,9 +418,11 @@ hipError_t attn_decode(const AttnDecodeParams& p, hipStream_t s) {
   if (p.kv_dt == DT_BF16) {
     if (p.d == 128) return decode_rep<bf16, 128>(p, s);
     if (p.d == 64) return decode_rep<bf16, 64>(p, s);
+    if (p.d == 256) return decode_rep<bf16, 256>(p, s);
   } else {
     if (p.d == 128) return decode_rep<float, 128>(p, s);
     if (p.d == 64) return decode_rep<float, 64>(p, s);
+    if (p.d == 256) return decode_rep<float, 256>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -439,6 +469,8 @@ static hipError_t prefill_vec(const AttnPrefillParams& p, hipStream_t s) {
     attn_prefill_vec_kernel<TQ, KV, 128, TO><<<grid, 256, 0, s>>>(p);
   else if (p.d == 64)
     attn_prefill_vec_kernel<TQ, KV, 64, TO><<<grid, 256, 0, s>>>(p);
+  else if (p.d == 256)
+    attn_prefill_vec_kernel<TQ, KV, 256, TO><<<grid, 256, 0, s>>>(p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

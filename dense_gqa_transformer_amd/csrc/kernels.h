@@ -85,8 +85,15 @@ struct RopeKvParams {
   long long slot_stride;                    // elements per (layer, slot)
   long long head_stride;                    // elements per KV head (= max_ctx * d)
   float qscale;                             // factor applied to q' before it is stored (1: none)
+  int rot;                                  // rotated dims per head (pairs (i, i + rot/2))
+  int gated;                                // q rows interleaved with gate rows per head
 };
 hipError_t rope_kv(const RopeKvParams& p, hipStream_t s);
+
+// Gated attention output: a[t, h*d + e] *= sigmoid(qkv[t, 2h*d + d + e]) for
+// T rows (a of a_dt, [T, nq*d]; qkv of qkv_dt, rows of width ldq).
+hipError_t attn_gate(void* a, int a_dt, const void* qkv, int qkv_dt, int T, int nq, int d, int ldq,
+                     hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 // Prefill: causal attention of T = B*S queries against their slot's cache
@@ -125,6 +132,8 @@ struct AttnDecodeParams {
   int B, nq, nkv, d, chunk, nchunks;
   long long slot_stride, head_stride;
   float scale;
+  int rot;                     // rotated dims per head
+  int gated;                   // q rows interleaved with gate rows per head
 };
 hipError_t attn_decode(const AttnDecodeParams& p, hipStream_t s);
 // out[b, h*d + e] from the chunk partials of sequence b (chunks 0..positions[b]/chunk).

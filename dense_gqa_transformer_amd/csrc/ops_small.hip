@@ -1,5 +1,7 @@
 // Small bandwidth-bound kernels: embedding gather, RMSNorm, dtype widening,
 // gate/up packing and row argmax.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -162,6 +164,39 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ 
 hipError_t argmax_rows(const float* logits, int B, int V, int ldl, int32_t* out, hipStream_t s) {
   if (B <= 0) return hipSuccess;
   argmax_kernel<<<B, 1024, 0, s>>>(logits, V, ldl, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- attention output gate
+// a[t, h*d + e] *= sigmoid(qkv[t, 2h*d + d + e]): the gated-attention variant's
+// per-head output gate, read from the gate rows the q projection interleaves
+// with each head's query rows ("ferrite", What it does).
+template <typename TA, typename TG>
+__global__ __launch_bounds__(256) void attn_gate_kernel(TA* __restrict__ a, const TG* __restrict__ qkv, int T,
+                                                        int nq, int d, int ldq) {
+  const long long n = (long long)T * nq * d;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const int t = (int)(i / ((long long)nq * d));
+    const int r = (int)(i % ((long long)nq * d));
+    const int h = r / d, e = r % d;
+    const float g = to_f32(qkv[(size_t)t * ldq + (size_t)(2 * h + 1) * d + e]);
+    a[i] = from_f32<TA>(to_f32(a[i]) / (1.f + __expf(-g)));
+  }
+}
+
+hipError_t attn_gate(void* a, int a_dt, const void* qkv, int qkv_dt, int T, int nq, int d, int ldq,
+                     hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const long long n = (long long)T * nq * d;
+  const int blocks = (int)std::min<long long>((n + 255) / 256, 4096);
+  if (a_dt == DT_BF16 && qkv_dt == DT_BF16)
+    attn_gate_kernel<bf16, bf16><<<blocks, 256, 0, s>>>((bf16*)a, (const bf16*)qkv, T, nq, d, ldq);
+  else if (a_dt == DT_BF16 && qkv_dt == DT_F32)
+    attn_gate_kernel<bf16, float><<<blocks, 256, 0, s>>>((bf16*)a, (const float*)qkv, T, nq, d, ldq);
+  else if (a_dt == DT_F32 && qkv_dt == DT_F32)
+    attn_gate_kernel<float, float><<<blocks, 256, 0, s>>>((float*)a, (const float*)qkv, T, nq, d, ldq);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -52,7 +52,8 @@ class Model:
         self.vocab = shape.vocab
         self.cfg = FsConfig(shape.n_layers, shape.hidden, shape.n_heads, shape.n_kv_heads,
                             shape.head_dim, shape.ffn, shape.vocab, float(shape.rms_eps),
-                            float(shape.rope_theta), self.dtype, int(max_seqs), int(max_ctx))
+                            float(shape.rope_theta), self.dtype, int(max_seqs), int(max_ctx),
+                            int(getattr(shape, "rope_dim", 0)), int(bool(getattr(shape, "attn_gate", False))))
         with torch.cuda.device(self.device):
             keep = []
 

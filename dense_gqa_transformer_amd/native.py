@@ -35,7 +35,8 @@ class FsConfig(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
                 ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("max_seqs", ctypes.c_int32), ("max_ctx", ctypes.c_int32)]
+                ("max_seqs", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
+                ("rope_dim", ctypes.c_int32), ("attn_gate", ctypes.c_int32)]
 
 
 class FsLayerWeights(ctypes.Structure):

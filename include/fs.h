@@ -64,12 +64,21 @@ typedef struct {
   float rms_eps, rope_theta;
   int32_t dtype;             /* fs_dtype */
   int32_t max_seqs, max_ctx;
+  /* Gated-attention variant ("ferrite", What it does: gated attention output,
+   * rotate-half RoPE on 64 of 256 head dims, q/gate split per head). */
+  int32_t rope_dim;          /* rotated dims per head: 0 = all of head_dim; else a multiple of 16 <= head_dim */
+  int32_t attn_gate;         /* 0 or 1: wq also carries a sigmoid gate per head */
 } fs_config;
 
 /* One layer's weights, device pointers of cfg.dtype, row-major [out, in]:
  *   attn_norm [hidden], wq [n_heads*head_dim, hidden], wk/wv [n_kv_heads*head_dim, hidden],
  *   q_norm/k_norm [head_dim] (shared by all heads), wo [hidden, n_heads*head_dim],
- *   mlp_norm [hidden], w_gate/w_up [ffn, hidden], w_down [hidden, ffn]. */
+ *   mlp_norm [hidden], w_gate/w_up [ffn, hidden], w_down [hidden, ffn].
+ * With attn_gate, wq is [2*n_heads*head_dim, hidden]: head h's query rows
+ * [2h*head_dim, (2h+1)*head_dim) then its gate rows [(2h+1)*head_dim,
+ * (2h+2)*head_dim); the head's attention output is multiplied by
+ * sigmoid(gate) before wo.  Only the first rope_dim dims of q and k rotate,
+ * by p * rope_theta^(-2i/rope_dim), pairs (i, i + rope_dim/2). */
 typedef struct {
   const void *attn_norm, *wq, *wk, *wv, *q_norm, *k_norm, *wo,
              *mlp_norm, *w_gate, *w_up, *w_down;
@@ -208,7 +217,7 @@ fs_status fs_kv_read(const fs_model *m, int32_t layer, int32_t slot, int32_t kv_
  * records and starts recording: every kernel this model launches is then
  * bracketed by a pair of HIP events on the call's stream, labelled with the
  * step it implements ("embed", "norm", "qkv", "rope_kv", "attn", "combine",
- * "o_proj", "gate_up", "down", "head", "argmax"), and decode steps run
+ * "attn_gate", "o_proj", "gate_up", "down", "head", "argmax"), and decode steps run
  * without graph replay.  fs_timing(m, 0) stops recording (records are kept
  * until the next fs_timing call).  Errors: INVALID_ARG for a NULL model. */
 fs_status fs_timing(fs_model *m, int32_t enable);

@@ -40,7 +40,8 @@ def test_argument_errors_without_device():
 
 def _cfg(**kw):
     base = dict(n_layers=1, hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn=768, vocab=4096,
-                rms_eps=1e-6, rope_theta=1e6, dtype=native.FS_F32, max_seqs=1, max_ctx=32)
+                rms_eps=1e-6, rope_theta=1e6, dtype=native.FS_F32, max_seqs=1, max_ctx=32,
+                rope_dim=0, attn_gate=0)
     base.update(kw)
     return native.FsConfig(*[base[f] for f, _ in native.FsConfig._fields_])
 
