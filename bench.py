@@ -125,6 +125,50 @@ def measured_traffic(key):
     return int(ent["traffic_bytes"]) if h.hexdigest() == ent["sources_sha256"] else None
 
 
+def gated_variant_bench(dev, Model):
+    """bs1 decode and a 1 x 1024 prefill of the gated-attention variant at the
+    0.6B shape's widths (8 query / 2 KV heads of width 256, RoPE on 64 dims,
+    sigmoid output gate), bf16 weights and KV."""
+    import numpy as np
+    import torch
+
+    import synth
+    gs = synth.GATED_0P6B
+    gw = synth.make_weights(gs, 0)
+    gm = Model(gs, gw, max_seqs=1, max_ctx=1024)
+    del gw
+    prompt = synth.tokens(110, gs.vocab, 512)
+    tok = torch.from_numpy(prompt[None, :].astype(np.int32)).to(dev)
+    lg = gm.prefill(tok, [0])
+    nxt = torch.argmax(lg, dim=1).to(torch.int32)
+    P, steps = len(prompt), 64
+    for k in range(4):
+        gm.decode_step(nxt, [P + k], [0], next_ids=nxt)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        gm.decode_step(nxt, [P + 4 + k], [0], next_ids=nxt)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    ctx = P + 4 + steps // 2
+    wbytes = 2 * (gs.vocab * gs.hidden + gs.n_layers * (gs.q_proj_width * gs.hidden + 2 * gs.kv_width * gs.hidden +
+                                                      gs.hidden * gs.q_width + 3 * gs.ffn * gs.hidden))
+    kvbytes = gs.n_layers * 2 * gs.kv_width * 2 * ctx
+    ptok = torch.from_numpy(synth.tokens(111, gs.vocab, (1, 1024)).astype(np.int32)).to(dev)
+    gm.prefill(ptok, [0])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gm.prefill(ptok, [0])
+    torch.cuda.synchronize()
+    pdt = time.perf_counter() - t0
+    gm.close()
+    return {"workload": "gated-attention variant, 28 layers, hidden 1024, 8 query / 2 KV heads x 256 "
+                        "(RoPE on 64 dims), ffn 3072, vocab 151936, bf16; bs1 decode from a 512-token prompt",
+            "decode_tok_s": round(1.0 / dt, 1), "ms_per_step": round(dt * 1e3, 4),
+            "decode_hbm_frac_step": round((wbytes + kvbytes) / dt / 8e12, 4),
+            "prefill_1x1024_tok_s": round(1024 / pdt, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +328,8 @@ def main():
     out["generate"] = {"workload": f"fs_generate, greedy, {P}-token prompt, {gen_n} new tokens (prefill included)",
                        "tokens": len(gids), "stop_reason": gwhy, "ms": round(gdt * 1e3, 2),
                        "tok_s_incl_prefill": round(len(gids) / gdt, 1)}
+
+    out["gated_variant"] = gated_variant_bench(dev, Model)
 
     # seeded sampling of one lm_head row (temperature -> top-k -> top-p -> draw)
     srow = torch.from_numpy(synth.logit_rows(900, 1, shape.vocab)).to(dev)

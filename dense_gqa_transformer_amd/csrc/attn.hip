@@ -82,32 +82,36 @@ template <typename KV> struct RawKV<KV, 16> {
 
 // RMSNorm over d with weight g, then rotate-half RoPE on the first `rot`
 // dims (pairs (i, i + rot/2), angles from the table rows cs / sn of length
-// rot/2), times `mul`, into y[0..D).  One wave: lane holds elements lane + 64i;
-// a rotated element also reads its partner from x.
+// rot/2), times `mul`.  One wave: lane holds elements lane + 64i (returned
+// in y[i]); a rotated element also reads its partner from x.
 template <int D>
 __device__ __forceinline__ void norm_rope_wave(const float* x, const float* g, const float* cs, const float* sn,
-                                               int rot, float eps, float mul, int lane, float* y) {
+                                               int rot, float eps, float mul, int lane, float (&y)[D / 64]) {
   constexpr int NE = D / 64;
-  float v[NE];
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < NE; ++i) {
-    v[i] = x[lane + 64 * i];
-    ss = fmaf(v[i], v[i], ss);
-  }
-  const float inv = rsqrtf(wave_sum(ss) / (float)D + eps);
   const int rh = rot >> 1;
+  // every load first (one memory round trip): the element, its rotation
+  // partner, both weights and the angle
+  float v[NE], vp[NE], gv[NE], gp[NE], c[NE], sv[NE];
 #pragma unroll
   for (int i = 0; i < NE; ++i) {
     const int e = lane + 64 * i;
-    float a = v[i] * inv * g[e];
-    if (e < rot) {
-      const bool lo = e < rh;
-      const int pe = lo ? e + rh : e - rh, fi = lo ? e : e - rh;
-      const float b = x[pe] * inv * g[pe];
-      a = lo ? a * cs[fi] - b * sn[fi] : a * cs[fi] + b * sn[fi];
-    }
-    y[e] = a * mul;
+    const bool r = e < rot, lo = e < rh;
+    const int pe = r ? (lo ? e + rh : e - rh) : e, fi = r ? (lo ? e : e - rh) : 0;
+    v[i] = x[e];
+    vp[i] = x[pe];
+    gv[i] = g[e];
+    gp[i] = g[pe];
+    c[i] = r ? cs[fi] : 1.f;
+    sv[i] = r ? (lo ? -sn[fi] : sn[fi]) : 0.f;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) ss = fmaf(v[i], v[i], ss);
+  const float inv = rsqrtf(wave_sum(ss) / (float)D + eps);
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const float a = v[i] * inv * gv[i], b = vp[i] * inv * gp[i];
+    y[i] = (a * c[i] + b * sv[i]) * mul;
   }
 }
 
@@ -233,21 +237,27 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
   const float* sn_row = p.sin_t + (size_t)pos * (p.rot >> 1);
   for (int r = wid; r < REP; r += 4) {
     const int h = j * REP + r;
-    norm_rope_wave<D>(row + (size_t)h * D * qmul, p.gq, cs_row, sn_row, p.rot, p.eps, qscale, lane, qs[r]);
+    float y[D / 64];
+    norm_rope_wave<D>(row + (size_t)h * D * qmul, p.gq, cs_row, sn_row, p.rot, p.eps, qscale, lane, y);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) qs[r][lane + 64 * i] = y[i];
   }
   // ---- the new token's k, v if it falls in this chunk: normalise, rotate, append
   if (has_new && wid == 3) {
     const float* kr = row + (size_t)p.nq * D * qmul + j * D;
     const float* vr = kr + (size_t)p.nkv * D;
-    norm_rope_wave<D>(kr, p.gk, cs_row, sn_row, p.rot, p.eps, 1.f, lane, knew);
+    float vv[D / 64], y[D / 64];
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) vv[i] = vr[lane + 64 * i];
+    norm_rope_wave<D>(kr, p.gk, cs_row, sn_row, p.rot, p.eps, 1.f, lane, y);
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) {
       const int e = lane + 64 * i;
-      const KV kk = from_f32<KV>(knew[e]), vv = from_f32<KV>(vr[e]);
+      const KV kk = from_f32<KV>(y[i]), vk = from_f32<KV>(vv[i]);
       kb[(size_t)pos * D + e] = kk;
-      vb[(size_t)pos * D + e] = vv;
+      vb[(size_t)pos * D + e] = vk;
       knew[e] = to_f32(kk);
-      vnew[e] = to_f32(vv);
+      vnew[e] = to_f32(vk);
     }
   }
   __syncthreads();

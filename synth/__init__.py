@@ -89,6 +89,9 @@ GATED_TINY = ModelShape(n_layers=2, hidden=512, n_heads=8, n_kv_heads=2, head_di
                         ffn=1024, vocab=4096, dtype=F32, rope_dim=64, attn_gate=True)
 GATED_BF16 = ModelShape(n_layers=2, hidden=512, n_heads=8, n_kv_heads=2, head_dim=256,
                         ffn=1024, vocab=4096, dtype=BF16, rope_dim=64, attn_gate=True)
+# The same attention at the 0.6B shape's other widths (for measurement).
+GATED_0P6B = ModelShape(n_layers=28, hidden=1024, n_heads=8, n_kv_heads=2, head_dim=256,
+                        ffn=3072, vocab=151936, dtype=BF16, rope_dim=64, attn_gate=True)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
