@@ -89,6 +89,34 @@ __device__ __forceinline__ void norm_rope_wave(const float* x, const float* g, c
                                                int rot, float eps, float mul, int lane, float (&y)[D / 64]) {
   constexpr int NE = D / 64;
   const int rh = rot >> 1;
+  if constexpr (NE >= 2) {
+    if (rot == D) {
+      // full rotation: element i's partner is element i +- NE/2 of the same lane
+      constexpr int H = NE / 2;
+      float v[NE], gv[NE], c[H], sv[H];
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        v[i] = x[lane + 64 * i];
+        gv[i] = g[lane + 64 * i];
+      }
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        c[i] = cs[lane + 64 * i];
+        sv[i] = sn[lane + 64 * i];
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < NE; ++i) ss = fmaf(v[i], v[i], ss);
+      const float inv = rsqrtf(wave_sum(ss) / (float)D + eps);
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float a = v[i] * inv * gv[i], b = v[i + H] * inv * gv[i + H];
+        y[i] = (a * c[i] - b * sv[i]) * mul;
+        y[i + H] = (b * c[i] + a * sv[i]) * mul;
+      }
+      return;
+    }
+  }
   // every load first (one memory round trip): the element, its rotation
   // partner, both weights and the angle
   float v[NE], vp[NE], gv[NE], gp[NE], c[NE], sv[NE];
