@@ -8,3 +8,4 @@ from .oracle import (Oracle, rms_norm, rope, rope_cos_sin, sigmoid, silu, softma
                      top_k, top2_gap, param_count, tensor_count)
 from . import sampling
 from . import generate
+from . import quant
