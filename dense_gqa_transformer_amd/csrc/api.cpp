@@ -49,6 +49,8 @@ constexpr int STAGE_RING = 64;
 struct LayerW {
   void *wqkv, *wo, *wgu, *wdown;
   float *attn_norm, *q_norm, *k_norm, *mlp_norm;
+  // int8 weights: one scale per weight row (null otherwise)
+  float *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sdown = nullptr;
 };
 
 struct DecodeKey {
@@ -89,10 +91,14 @@ struct fs_model {
   int qpw = 0;          // rows of the q (+ gate) projection
   int rot = 0;          // rotated dims per head
   int gated = 0;        // attention output gate carried by the q projection
+  int wdt = 0;          // storage of the matrices: dt, or DT_I8 (codes + row scales)
   // weights
   void* wblob = nullptr;
   float* nblob = nullptr;
+  float* sblob = nullptr;         // int8 row scales
+  void* wconv = nullptr;          // bf16 copy of one layer matrix's codes (MFMA operand)
   void* embed = nullptr;
+  float* embed_scale = nullptr;
   float* final_norm = nullptr;
   std::vector<LayerW> layers;
   // KV cache [layer][slot][kv_head][pos][d]
@@ -148,7 +154,7 @@ struct fs_model {
     if (cap_stream) hipStreamDestroy(cap_stream);
     for (auto& t : timed) { hipEventDestroy(t.a); hipEventDestroy(t.b); }
     for (auto e : ev_free) hipEventDestroy(e);
-    hipFree(wblob); hipFree(nblob); hipFree(kcache); hipFree(vcache);
+    hipFree(wblob); hipFree(nblob); hipFree(sblob); hipFree(wconv); hipFree(kcache); hipFree(vcache);
     hipFree(rope_cos); hipFree(rope_sin);
     hipFree(x); hipFree(xn); hipFree(qkv); hipFree(qr); hipFree(attn); hipFree(hbuf);
     hipFree(d_pos); hipFree(d_slot); hipFree(part);
@@ -244,29 +250,30 @@ fs_status head(fs_model* m, const float* xrows, int rows, int ldx, float* logits
   const fs_config& c = m->cfg;
   if (rows <= GEMV_LOGITS_MAX_M) {
     GemvParams p{};
-    p.w = m->embed; p.N = c.vocab; p.K = c.hidden;
+    p.w = m->embed; p.wscale = m->embed_scale; p.N = c.vocab; p.K = c.hidden;
     p.a = xrows; p.lda = ldx; p.M = rows;
     p.gamma = m->final_norm; p.eps = c.rms_eps;
     p.logits = logits; p.ldo = c.vocab;
     p.part_val = m->lm_pv; p.part_idx = m->lm_pi;
-    LAUNCH(m, "head", s, gemv(m->dt, EPI_LOGITS, p, s));
+    LAUNCH(m, "head", s, gemv(m->wdt, EPI_LOGITS, p, s));
     if (next)
-      LAUNCH(m, "argmax", s, argmax_partials(m->lm_pv, m->lm_pi, gemv_logits_blocks(c.vocab, c.hidden), rows,
-                                             next, s));
+      LAUNCH(m, "argmax", s, argmax_partials(m->lm_pv, m->lm_pi, gemv_logits_blocks(m->wdt, c.vocab, c.hidden),
+                                             rows, next, s));
     return FS_OK;
   }
   float* lg = logits != nullptr ? logits : m->logits_tmp;   // logits_tmp allocated by the caller
-  if (m->dt == DT_BF16) {
+  if (m->wdt == DT_BF16) {
     LAUNCH(m, "norm", s, rmsnorm(xrows, rows, c.hidden, ldx, m->final_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s));
     LAUNCH(m, "head", s, gemm_bf16(GEPI_STORE_F32, m->xn, c.hidden, m->embed, c.hidden, lg, c.vocab, rows,
                                    c.vocab, c.hidden, s));
   } else {
+    // fp32 and int8 heads: GEMV over row groups (int8 codes stream once per 4 rows)
     GemvParams p{};
-    p.w = m->embed; p.N = c.vocab; p.K = c.hidden;
+    p.w = m->embed; p.wscale = m->embed_scale; p.N = c.vocab; p.K = c.hidden;
     p.a = xrows; p.lda = ldx; p.M = rows;
     p.gamma = m->final_norm; p.eps = c.rms_eps;
     p.out = lg; p.ldo = c.vocab;
-    LAUNCH(m, "head", s, gemv(m->dt, EPI_STORE, p, s));
+    LAUNCH(m, "head", s, gemv(m->wdt, EPI_STORE, p, s));
   }
   if (next) LAUNCH(m, "argmax", s, argmax_rows(lg, rows, c.vocab, c.vocab, next, s));
   return FS_OK;
@@ -287,27 +294,27 @@ fs_status block_skinny(fs_model* m, const LayerW& L, int rows, Attn&& attention,
   GemvParams p{};
   p.eps = c.rms_eps;
   // Q/K/V projection with the input RMSNorm fused in
-  p.w = L.wqkv; p.N = m->qkv_w; p.K = c.hidden;
+  p.w = L.wqkv; p.wscale = L.sqkv; p.N = m->qkv_w; p.K = c.hidden;
   p.a = m->x; p.lda = c.hidden; p.M = rows; p.gamma = L.attn_norm;
   p.out = (float*)m->qkv; p.ldo = m->qkv_w;
-  LAUNCH(m, "qkv", s, gemv(m->dt, EPI_STORE, p, s));
+  LAUNCH(m, "qkv", s, gemv(m->wdt, EPI_STORE, p, s));
   fs_status st = attention();
   if (st != FS_OK) return st;
   // output projection + residual
-  p.w = L.wo; p.N = c.hidden; p.K = m->qw;
+  p.w = L.wo; p.wscale = L.so; p.N = c.hidden; p.K = m->qw;
   p.a = (const float*)m->attn; p.lda = m->qw; p.gamma = nullptr;
   p.out = m->x; p.ldo = c.hidden;
-  LAUNCH(m, "o_proj", s, gemv(m->dt, EPI_RESID, p, s));
+  LAUNCH(m, "o_proj", s, gemv(m->wdt, EPI_RESID, p, s));
   // RMSNorm + gate/up + SwiGLU
-  p.w = L.wgu; p.N = c.ffn; p.K = c.hidden;
+  p.w = L.wgu; p.wscale = L.sgu; p.N = c.ffn; p.K = c.hidden;
   p.a = m->x; p.lda = c.hidden; p.gamma = L.mlp_norm;
   p.out = (float*)m->hbuf; p.ldo = c.ffn;
-  LAUNCH(m, "gate_up", s, gemv(m->dt, EPI_SWIGLU, p, s));
+  LAUNCH(m, "gate_up", s, gemv(m->wdt, EPI_SWIGLU, p, s));
   // down projection + residual
-  p.w = L.wdown; p.N = c.hidden; p.K = c.ffn;
+  p.w = L.wdown; p.wscale = L.sdown; p.N = c.hidden; p.K = c.ffn;
   p.a = (const float*)m->hbuf; p.lda = c.ffn; p.gamma = nullptr;
   p.out = m->x; p.ldo = c.hidden;
-  LAUNCH(m, "down", s, gemv(m->dt, EPI_RESID, p, s));
+  LAUNCH(m, "down", s, gemv(m->wdt, EPI_RESID, p, s));
   return FS_OK;
 }
 
@@ -321,18 +328,41 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
   // rounding it to bf16 alone moves the logits by about as much as the whole
   // error budget, while the MLP input tolerates plain bf16.
   void* xn_lo = (char*)m->xn + (size_t)rows * c.hidden * 2;
+  // int8 weights: each matrix's codes are widened to bf16 (exact) into wconv
+  // just before its GEMM, and the row scales are applied per output column
+  const bool q8 = (m->wdt == DT_I8);
+  const void* wb = L.wqkv;
+  if (q8) {
+    LAUNCH(m, "wconv", s, codes_to_bf16((const int8_t*)L.wqkv, (size_t)m->qkv_w * c.hidden, m->wconv, s));
+    wb = m->wconv;
+  }
   LAUNCH(m, "norm", s, rmsnorm(m->x, rows, c.hidden, c.hidden, L.attn_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s, xn_lo));
-  LAUNCH(m, "qkv", s, gemm_bf16(qkv_f32 ? GEPI_STORE_F32 : GEPI_STORE_BF16, m->xn, c.hidden, L.wqkv, c.hidden,
-                                m->qkv, m->qkv_w, rows, m->qkv_w, c.hidden, s, xn_lo));
+  LAUNCH(m, "qkv", s, gemm_bf16(qkv_f32 ? GEPI_STORE_F32 : GEPI_STORE_BF16, m->xn, c.hidden, wb, c.hidden,
+                                m->qkv, m->qkv_w, rows, m->qkv_w, c.hidden, s, xn_lo, L.sqkv));
   fs_status st = attention();
   if (st != FS_OK) return st;
-  LAUNCH(m, "o_proj", s, gemm_bf16(GEPI_RESID_F32, m->attn, m->qw, L.wo, m->qw, m->x, c.hidden, rows, c.hidden,
-                                   m->qw, s));
+  wb = L.wo;
+  if (q8) {
+    LAUNCH(m, "wconv", s, codes_to_bf16((const int8_t*)L.wo, (size_t)c.hidden * m->qw, m->wconv, s));
+    wb = m->wconv;
+  }
+  LAUNCH(m, "o_proj", s, gemm_bf16(GEPI_RESID_F32, m->attn, m->qw, wb, m->qw, m->x, c.hidden, rows, c.hidden,
+                                   m->qw, s, nullptr, L.so));
+  wb = L.wgu;
+  if (q8) {
+    LAUNCH(m, "wconv", s, codes_to_bf16((const int8_t*)L.wgu, (size_t)2 * c.ffn * c.hidden, m->wconv, s));
+    wb = m->wconv;
+  }
   LAUNCH(m, "norm", s, rmsnorm(m->x, rows, c.hidden, c.hidden, L.mlp_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s));
-  LAUNCH(m, "gate_up", s, gemm_bf16(GEPI_SWIGLU_BF16, m->xn, c.hidden, L.wgu, c.hidden, m->hbuf, c.ffn, rows,
-                                    2 * c.ffn, c.hidden, s));
-  LAUNCH(m, "down", s, gemm_bf16(GEPI_RESID_F32, m->hbuf, c.ffn, L.wdown, c.ffn, m->x, c.hidden, rows, c.hidden,
-                                 c.ffn, s));
+  LAUNCH(m, "gate_up", s, gemm_bf16(GEPI_SWIGLU_BF16, m->xn, c.hidden, wb, c.hidden, m->hbuf, c.ffn, rows,
+                                    2 * c.ffn, c.hidden, s, nullptr, L.sgu));
+  wb = L.wdown;
+  if (q8) {
+    LAUNCH(m, "wconv", s, codes_to_bf16((const int8_t*)L.wdown, (size_t)c.hidden * c.ffn, m->wconv, s));
+    wb = m->wconv;
+  }
+  LAUNCH(m, "down", s, gemm_bf16(GEPI_RESID_F32, m->hbuf, c.ffn, wb, c.ffn, m->x, c.hidden, rows, c.hidden,
+                                 c.ffn, s, nullptr, L.sdown));
   return FS_OK;
 }
 
@@ -362,6 +392,8 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   if (c.rope_dim < 0 || c.rope_dim > c.head_dim || c.rope_dim % 16 != 0)
     return fail(FS_ERR_UNSUPPORTED, "rope_dim must be 0 or a multiple of 16 up to head_dim");
   if (c.attn_gate != 0 && c.attn_gate != 1) return fail(FS_ERR_INVALID_ARG, "attn_gate must be 0 or 1");
+  if (c.weight_format != FS_WEIGHTS_DTYPE && c.weight_format != FS_WEIGHTS_I8_ROW)
+    return fail(FS_ERR_UNSUPPORTED, "unknown weight_format");
   if (c.hidden % 64 != 0 || c.ffn % 64 != 0)
     return fail(FS_ERR_UNSUPPORTED, "hidden and ffn must be multiples of 64");
   if (!cpl_ok(c.hidden) || !cpl_ok(c.ffn) || !cpl_ok(c.n_heads * c.head_dim))
@@ -369,12 +401,19 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return fail(FS_ERR_INVALID_ARG, "bad rms_eps or rope_theta");
   if (w->embed == nullptr || w->final_norm == nullptr || (c.n_layers > 0 && w->layers == nullptr))
     return fail(FS_ERR_INVALID_ARG, "NULL weight pointer");
+  const bool q8 = (c.weight_format == FS_WEIGHTS_I8_ROW);
   for (int l = 0; l < c.n_layers; ++l) {
     const fs_layer_weights& L = w->layers[l];
     const void* ps[] = {L.attn_norm, L.wq, L.wk, L.wv, L.q_norm, L.k_norm, L.wo, L.mlp_norm, L.w_gate, L.w_up, L.w_down};
     for (const void* p : ps)
       if (p == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL weight pointer in layer " + std::to_string(l));
+    // the quantizer reads matrices in 16-byte vectors
+    const void* mats[] = {L.wq, L.wk, L.wv, L.wo, L.w_down};
+    for (const void* p : mats)
+      if (q8 && ((uintptr_t)p & 15))
+        return fail(FS_ERR_INVALID_ARG, "int8 weights need 16-byte aligned matrices (layer " + std::to_string(l) + ")");
   }
+  if (q8 && ((uintptr_t)w->embed & 15)) return fail(FS_ERR_INVALID_ARG, "int8 weights need a 16-byte aligned embed");
   hipStream_t s = (hipStream_t)stream;
   int device = 0;
   HIP_TRY(hipGetDevice(&device));
@@ -389,40 +428,77 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   m->gated = c.attn_gate;
   m->qpw = m->qw * (m->gated ? 2 : 1);          // q (+ gate) projection rows
   m->qkv_w = m->qpw + 2 * m->kvw;
-  const size_t H = c.hidden, I = c.ffn, V = c.vocab, es = m->esz;
-  const size_t per_layer = ((size_t)m->qkv_w * H + H * m->qw + 2 * I * H + H * I) * es;
-  const size_t wbytes = V * H * es + per_layer * c.n_layers;
+  m->wdt = q8 ? DT_I8 : m->dt;
+  const size_t H = c.hidden, I = c.ffn, V = c.vocab, es = m->esz, wes = dt_size(m->wdt);
+  const size_t per_layer = ((size_t)m->qkv_w * H + H * m->qw + 2 * I * H + H * I) * wes;
+  const size_t wbytes = V * H * wes + per_layer * c.n_layers;
   const size_t nfloats = H + (size_t)c.n_layers * (2 * H + 2 * c.head_dim);
+  // int8 row scales: each matrix's run starts on a 64-float (256 B) boundary
+  auto rup = [](size_t n) { return (n + 63) / 64 * 64; };
+  const size_t sfloats = q8 ? rup(V) + (size_t)c.n_layers * (rup(m->qkv_w) + rup(H) + rup(2 * I) + rup(H)) : 0;
+  void* pack_tmp = nullptr;       // packed gate/up of one layer before quantization
   auto bail = [&](fs_status st, const std::string& msg) {
+    hipFree(pack_tmp);
     delete m;
     return fail(st, msg);
   };
   if (dalloc(&m->wblob, wbytes) != hipSuccess) return bail(FS_ERR_OOM, "weight allocation failed");
   if (dalloc(&m->nblob, nfloats * 4) != hipSuccess) return bail(FS_ERR_OOM, "norm allocation failed");
+  if (q8) {
+    if (dalloc(&m->sblob, sfloats * 4) != hipSuccess || dalloc(&pack_tmp, 2 * I * H * es) != hipSuccess)
+      return bail(FS_ERR_OOM, "int8 scale allocation failed");
+    if (m->dt == DT_BF16) {
+      const size_t most = std::max(std::max((size_t)m->qkv_w * H, H * m->qw), std::max(2 * I * H, H * I));
+      if (dalloc(&m->wconv, most * 2) != hipSuccess) return bail(FS_ERR_OOM, "int8 operand allocation failed");
+    }
+  }
   char* wp = (char*)m->wblob;
   float* np = m->nblob;
+  float* sp = m->sblob;
   hipError_t e = hipSuccess;
   auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
-  m->embed = wp; wp += V * H * es;
-  chk(hipMemcpyAsync(m->embed, w->embed, V * H * es, hipMemcpyDeviceToDevice, s));
+  // a [rows, cols] matrix of cfg.dtype into dst: copied, or quantized with its
+  // scales taken from the scale blob
+  auto put = [&](const void* src, int rows, int cols, void* dst, float** scale) {
+    if (!q8) {
+      chk(hipMemcpyAsync(dst, src, (size_t)rows * cols * es, hipMemcpyDeviceToDevice, s));
+      return;
+    }
+    if (*scale == nullptr) *scale = sp;     // the matrix's run of scales starts here
+    chk(quantize_rows(src, m->dt, rows, cols, (int8_t*)dst, sp, s));
+    sp += rows;
+  };
+  auto close_run = [&](float* start) {
+    if (q8) sp = start + rup((size_t)(sp - start));
+  };
+  m->embed = wp; wp += V * H * wes;
+  put(w->embed, (int)V, (int)H, m->embed, &m->embed_scale);
+  close_run(m->embed_scale);
   m->final_norm = np; np += H;
   chk(convert_f32(w->final_norm, m->dt, m->final_norm, H, s));
   m->layers.resize(c.n_layers);
   for (int l = 0; l < c.n_layers; ++l) {
     const fs_layer_weights& src = w->layers[l];
     LayerW& L = m->layers[l];
-    L.wqkv = wp; wp += (size_t)m->qkv_w * H * es;
-    chk(hipMemcpyAsync(L.wqkv, src.wq, (size_t)m->qpw * H * es, hipMemcpyDeviceToDevice, s));
-    chk(hipMemcpyAsync((char*)L.wqkv + (size_t)m->qpw * H * es, src.wk, (size_t)m->kvw * H * es,
-                       hipMemcpyDeviceToDevice, s));
-    chk(hipMemcpyAsync((char*)L.wqkv + (size_t)(m->qpw + m->kvw) * H * es, src.wv, (size_t)m->kvw * H * es,
-                       hipMemcpyDeviceToDevice, s));
-    L.wo = wp; wp += H * m->qw * es;
-    chk(hipMemcpyAsync(L.wo, src.wo, H * m->qw * es, hipMemcpyDeviceToDevice, s));
-    L.wgu = wp; wp += 2 * I * H * es;
-    chk(pack_gate_up(src.w_gate, src.w_up, m->dt, (int)I, (int)H, L.wgu, s));
-    L.wdown = wp; wp += H * I * es;
-    chk(hipMemcpyAsync(L.wdown, src.w_down, H * I * es, hipMemcpyDeviceToDevice, s));
+    L.wqkv = wp; wp += (size_t)m->qkv_w * H * wes;
+    put(src.wq, m->qpw, (int)H, L.wqkv, &L.sqkv);
+    put(src.wk, m->kvw, (int)H, (char*)L.wqkv + (size_t)m->qpw * H * wes, &L.sqkv);
+    put(src.wv, m->kvw, (int)H, (char*)L.wqkv + (size_t)(m->qpw + m->kvw) * H * wes, &L.sqkv);
+    close_run(L.sqkv);
+    L.wo = wp; wp += H * m->qw * wes;
+    put(src.wo, (int)H, m->qw, L.wo, &L.so);
+    close_run(L.so);
+    L.wgu = wp; wp += 2 * I * H * wes;
+    if (q8) {
+      chk(pack_gate_up(src.w_gate, src.w_up, m->dt, (int)I, (int)H, pack_tmp, s));
+      put(pack_tmp, 2 * (int)I, (int)H, L.wgu, &L.sgu);
+      close_run(L.sgu);
+    } else {
+      chk(pack_gate_up(src.w_gate, src.w_up, m->dt, (int)I, (int)H, L.wgu, s));
+    }
+    L.wdown = wp; wp += H * I * wes;
+    put(src.w_down, (int)H, (int)I, L.wdown, &L.sdown);
+    close_run(L.sdown);
     L.attn_norm = np; np += H;
     L.mlp_norm = np; np += H;
     L.q_norm = np; np += c.head_dim;
@@ -458,7 +534,7 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
 
   // decode scratch
   m->max_chunks = (c.max_ctx + 31) / 32;
-  const int lm_blocks = gemv_logits_blocks(c.vocab, c.hidden);
+  const int lm_blocks = gemv_logits_blocks(m->wdt, c.vocab, c.hidden);
   if (dalloc(&m->d_pos, (size_t)c.max_seqs * 4) != hipSuccess ||
       dalloc(&m->d_slot, (size_t)c.max_seqs * 4) != hipSuccess ||
       dalloc(&m->part, (size_t)c.max_seqs * c.n_heads * m->max_chunks * (c.head_dim + 2) * 4) != hipSuccess ||
@@ -476,6 +552,8 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   }
   chk(hipStreamSynchronize(s));
   if (e != hipSuccess) return bail(FS_ERR_HIP, std::string("model setup failed: ") + hipGetErrorString(e));
+  hipFree(pack_tmp);
+  pack_tmp = nullptr;
   m->slot_len.assign(c.max_seqs, 0);
   *out = m;
   return FS_OK;
@@ -505,7 +583,7 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
   if ((st = ensure_rows(m, T, s)) != FS_OK) return st;
   if ((st = stage_ints(m, nullptr, slots, B, s)) != FS_OK) return st;
   if (m->timing) LAUNCH(m, "gate", s, spin_wait(TIMING_GATE_US, s));
-  LAUNCH(m, "embed", s, embed(m->embed, m->dt, tokens, (int)T, c.hidden, c.vocab, m->x, s));
+  LAUNCH(m, "embed", s, embed(m->embed, m->wdt, tokens, (int)T, c.hidden, c.vocab, m->x, s, m->embed_scale));
   const bool skinny = (m->dt == DT_F32) || T <= SKINNY_MAX_ROWS;
   const int act_dt = skinny ? DT_F32 : DT_BF16;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -552,7 +630,7 @@ static fs_status enqueue_decode(fs_model* m, const int32_t* tokens, int B, float
                                 int chunk, int nchunks, hipStream_t s) {
   const fs_config& c = m->cfg;
   if (m->timing) LAUNCH(m, "gate", s, spin_wait(TIMING_GATE_US, s));
-  LAUNCH(m, "embed", s, embed(m->embed, m->dt, tokens, B, c.hidden, c.vocab, m->x, s));
+  LAUNCH(m, "embed", s, embed(m->embed, m->wdt, tokens, B, c.hidden, c.vocab, m->x, s, m->embed_scale));
   const bool skinny = (m->dt == DT_F32) || B <= SKINNY_MAX_ROWS;
   fs_status st = FS_OK;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -674,25 +752,25 @@ fs_status fs_kernel_bench(fs_model* m, const char* label, int32_t slot, int32_t 
     GemvParams p{};
     p.eps = c.rms_eps; p.M = 1;
     if (std::strcmp(label, "qkv") == 0) {
-      p.w = L.wqkv; p.N = m->qkv_w; p.K = c.hidden; p.a = m->x; p.lda = c.hidden; p.gamma = L.attn_norm;
+      p.w = L.wqkv; p.wscale = L.sqkv; p.N = m->qkv_w; p.K = c.hidden; p.a = m->x; p.lda = c.hidden; p.gamma = L.attn_norm;
       p.out = (float*)m->qkv; p.ldo = m->qkv_w;
-      HIP_TRY(gemv(m->dt, EPI_STORE, p, ls));
+      HIP_TRY(gemv(m->wdt, EPI_STORE, p, ls));
     } else if (std::strcmp(label, "o_proj") == 0) {
-      p.w = L.wo; p.N = c.hidden; p.K = m->qw; p.a = (const float*)m->attn; p.lda = m->qw;
+      p.w = L.wo; p.wscale = L.so; p.N = c.hidden; p.K = m->qw; p.a = (const float*)m->attn; p.lda = m->qw;
       p.out = m->x; p.ldo = c.hidden;
-      HIP_TRY(gemv(m->dt, EPI_RESID, p, ls));
+      HIP_TRY(gemv(m->wdt, EPI_RESID, p, ls));
     } else if (std::strcmp(label, "gate_up") == 0) {
-      p.w = L.wgu; p.N = c.ffn; p.K = c.hidden; p.a = m->x; p.lda = c.hidden; p.gamma = L.mlp_norm;
+      p.w = L.wgu; p.wscale = L.sgu; p.N = c.ffn; p.K = c.hidden; p.a = m->x; p.lda = c.hidden; p.gamma = L.mlp_norm;
       p.out = (float*)m->hbuf; p.ldo = c.ffn;
-      HIP_TRY(gemv(m->dt, EPI_SWIGLU, p, ls));
+      HIP_TRY(gemv(m->wdt, EPI_SWIGLU, p, ls));
     } else if (std::strcmp(label, "down") == 0) {
-      p.w = L.wdown; p.N = c.hidden; p.K = c.ffn; p.a = (const float*)m->hbuf; p.lda = c.ffn;
+      p.w = L.wdown; p.wscale = L.sdown; p.N = c.hidden; p.K = c.ffn; p.a = (const float*)m->hbuf; p.lda = c.ffn;
       p.out = m->x; p.ldo = c.hidden;
-      HIP_TRY(gemv(m->dt, EPI_RESID, p, ls));
+      HIP_TRY(gemv(m->wdt, EPI_RESID, p, ls));
     } else if (std::strcmp(label, "head") == 0) {
-      p.w = m->embed; p.N = c.vocab; p.K = c.hidden; p.a = m->x; p.lda = c.hidden; p.gamma = m->final_norm;
+      p.w = m->embed; p.wscale = m->embed_scale; p.N = c.vocab; p.K = c.hidden; p.a = m->x; p.lda = c.hidden; p.gamma = m->final_norm;
       p.ldo = c.vocab; p.part_val = m->lm_pv; p.part_idx = m->lm_pi;
-      HIP_TRY(gemv(m->dt, EPI_LOGITS, p, ls));
+      HIP_TRY(gemv(m->wdt, EPI_LOGITS, p, ls));
     } else if (is_attn) {
       AttnDecodeParams a{};
       a.qkv = (const float*)m->qkv;
@@ -780,6 +858,18 @@ fs_status fs_argmax(const float* logits, int32_t B, int32_t V, int32_t* out, voi
   if (logits == nullptr || out == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL argument");
   if (B <= 0 || V <= 0) return fail(FS_ERR_INVALID_ARG, "B and V must be positive");
   HIP_TRY(argmax_rows(logits, B, V, V, out, (hipStream_t)stream));
+  return FS_OK;
+}
+
+fs_status fs_quantize_rows_i8(const void* src, int32_t dtype, int32_t rows, int32_t cols, int8_t* codes,
+                              float* scales, void* stream) {
+  g_err.clear();
+  if (src == nullptr || codes == nullptr || scales == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+  if (dtype != FS_F32 && dtype != FS_BF16) return fail(FS_ERR_UNSUPPORTED, "unknown dtype");
+  if (rows <= 0 || cols <= 0 || cols % 8 != 0) return fail(FS_ERR_INVALID_ARG, "rows, cols must be > 0, cols % 8 == 0");
+  if (((uintptr_t)src & 15) || ((uintptr_t)codes & 7) || ((uintptr_t)scales & 3))
+    return fail(FS_ERR_INVALID_ARG, "misaligned src (16 B), codes (8 B) or scales (4 B)");
+  HIP_TRY(quantize_rows(src, dtype, rows, cols, codes, scales, (hipStream_t)stream));
   return FS_OK;
 }
 

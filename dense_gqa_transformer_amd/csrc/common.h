@@ -56,6 +56,12 @@ __device__ __forceinline__ void load8(const float* p, float* out) {
   out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
+// The four signed 8-bit codes packed in a 32-bit word, as fp32 (exact).
+__device__ __forceinline__ void codes4(uint32_t w, float* out) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) out[b] = (float)(int)(int8_t)(uint8_t)(w >> (8 * b));
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // (value, index) ordering for greedy selection: larger finite value wins,

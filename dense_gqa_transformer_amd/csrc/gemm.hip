@@ -27,7 +27,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16* __restrict__
                                                         const bf16* __restrict__ B, int ldb,
                                                         void* __restrict__ out, int ldc,
                                                         int M, int N, int K,
-                                                        const bf16* __restrict__ A_lo) {
+                                                        const bf16* __restrict__ A_lo,
+                                                        const float* __restrict__ colscale) {
   __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDK];
   __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * LDK];
 
@@ -108,7 +109,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16* __restrict__
         // the wave's 64 columns are [32 gate | matching 32 up] of the packed matrix
         if (n0 + wn * 64 >= N) continue;
         const int f = (n0 + wn * 64) / 2 + col_in;
-        const float g = acc[i][0][r], u = acc[i][1][r];
+        float g = acc[i][0][r], u = acc[i][1][r];
+        if (colscale != nullptr) {
+          g *= colscale[n0 + wn * 64 + col_in];
+          u *= colscale[n0 + wn * 64 + 32 + col_in];
+        }
         reinterpret_cast<bf16*>(out)[(size_t)row * ldc + f] = (bf16)(silu(g) * u);
       } else {
 #pragma unroll
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16* __restrict__
           const int col = n0 + wn * 64 + j * 32 + col_in;
           if (col >= N) continue;
           const size_t o = (size_t)row * ldc + col;
-          const float v = acc[i][j][r];
+          const float v = colscale != nullptr ? acc[i][j][r] * colscale[col] : acc[i][j][r];
           if (EPI == GEPI_STORE_BF16) reinterpret_cast<bf16*>(out)[o] = (bf16)v;
           else if (EPI == GEPI_STORE_F32) reinterpret_cast<float*>(out)[o] = v;
           else reinterpret_cast<float*>(out)[o] += v;
@@ -140,7 +145,8 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(const bf16* __restri
                                                             const bf16* __restrict__ B, int ldb,
                                                             void* __restrict__ out, int ldc,
                                                             int M, int N, int K, const bf16* __restrict__ A_lo,
-                                                            int tiles_n, int nblocks) {
+                                                            int tiles_n, int nblocks,
+                                                            const float* __restrict__ colscale) {
   __shared__ __attribute__((aligned(16))) bf16 As[2][BM2 * LDK];
   __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN2 * LDK];
 
@@ -220,7 +226,11 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(const bf16* __restri
       if (EPI == GEPI_SWIGLU_BF16) {
         if (n0 + wn * 64 >= N) continue;
         const int f = (n0 + wn * 64) / 2 + col_in;
-        const float g = acc[i][0][r], u = acc[i][1][r];
+        float g = acc[i][0][r], u = acc[i][1][r];
+        if (colscale != nullptr) {
+          g *= colscale[n0 + wn * 64 + col_in];
+          u *= colscale[n0 + wn * 64 + 32 + col_in];
+        }
         reinterpret_cast<bf16*>(out)[(size_t)row * ldc + f] = (bf16)(silu(g) * u);
       } else {
 #pragma unroll
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(const bf16* __restri
           const int col = n0 + wn * 64 + j * 32 + col_in;
           if (col >= N) continue;
           const size_t o = (size_t)row * ldc + col;
-          const float v = acc[i][j][r];
+          const float v = colscale != nullptr ? acc[i][j][r] * colscale[col] : acc[i][j][r];
           if (EPI == GEPI_STORE_BF16) reinterpret_cast<bf16*>(out)[o] = (bf16)v;
           else if (EPI == GEPI_STORE_F32) reinterpret_cast<float*>(out)[o] = v;
           else reinterpret_cast<float*>(out)[o] += v;
@@ -240,18 +250,18 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(const bf16* __restri
 
 template <int EPI>
 static void launch_big(const bf16* a, int lda, const bf16* b, int ldb, void* out, int ldc, int M, int N, int K,
-                       const bf16* alo, hipStream_t s) {
+                       const bf16* alo, const float* cs, hipStream_t s) {
   const int tn = (N + BN2 - 1) / BN2, tm = (M + BM2 - 1) / BM2;
-  gemm_bf16_big_kernel<EPI><<<tn * tm, 512, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, alo, tn, tn * tm);
+  gemm_bf16_big_kernel<EPI><<<tn * tm, 512, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, alo, tn, tn * tm, cs);
 }
 
 hipError_t gemm_bf16(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc,
-                     int M, int N, int K, hipStream_t s, const void* A_lo) {
+                     int M, int N, int K, hipStream_t s, const void* A_lo, const float* colscale) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % BK != 0) return hipErrorInvalidValue;
   if (epi == GEPI_SWIGLU_BF16 && N % 64 != 0) return hipErrorInvalidValue;
   if (gemm_dma_ok(epi, A, lda, B, ldb, out, ldc, M, N, K, A_lo))
-    return gemm_dma(epi, A, lda, B, ldb, out, ldc, M, N, K, s, A_lo);
+    return gemm_dma(epi, A, lda, B, ldb, out, ldc, M, N, K, s, A_lo, colscale);
   const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
   const bf16* a = (const bf16*)A;
   const bf16* b = (const bf16*)B;
@@ -259,19 +269,19 @@ hipError_t gemm_bf16(int epi, const void* A, int lda, const void* B, int ldb, vo
   // large problems: 256x256 tiles once there are enough of them to fill the chip
   if (M >= 1024 && (long long)((M + BM2 - 1) / BM2) * ((N + BN2 - 1) / BN2) >= 256) {
     switch (epi) {
-      case GEPI_STORE_BF16: launch_big<GEPI_STORE_BF16>(a, lda, b, ldb, out, ldc, M, N, K, alo, s); break;
-      case GEPI_RESID_F32: launch_big<GEPI_RESID_F32>(a, lda, b, ldb, out, ldc, M, N, K, alo, s); break;
-      case GEPI_SWIGLU_BF16: launch_big<GEPI_SWIGLU_BF16>(a, lda, b, ldb, out, ldc, M, N, K, alo, s); break;
-      case GEPI_STORE_F32: launch_big<GEPI_STORE_F32>(a, lda, b, ldb, out, ldc, M, N, K, alo, s); break;
+      case GEPI_STORE_BF16: launch_big<GEPI_STORE_BF16>(a, lda, b, ldb, out, ldc, M, N, K, alo, colscale, s); break;
+      case GEPI_RESID_F32: launch_big<GEPI_RESID_F32>(a, lda, b, ldb, out, ldc, M, N, K, alo, colscale, s); break;
+      case GEPI_SWIGLU_BF16: launch_big<GEPI_SWIGLU_BF16>(a, lda, b, ldb, out, ldc, M, N, K, alo, colscale, s); break;
+      case GEPI_STORE_F32: launch_big<GEPI_STORE_F32>(a, lda, b, ldb, out, ldc, M, N, K, alo, colscale, s); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
   switch (epi) {
-    case GEPI_STORE_BF16: gemm_bf16_kernel<GEPI_STORE_BF16><<<grid, 256, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, (const bf16*)A_lo); break;
-    case GEPI_RESID_F32: gemm_bf16_kernel<GEPI_RESID_F32><<<grid, 256, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, (const bf16*)A_lo); break;
-    case GEPI_SWIGLU_BF16: gemm_bf16_kernel<GEPI_SWIGLU_BF16><<<grid, 256, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, (const bf16*)A_lo); break;
-    case GEPI_STORE_F32: gemm_bf16_kernel<GEPI_STORE_F32><<<grid, 256, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, (const bf16*)A_lo); break;
+    case GEPI_STORE_BF16: gemm_bf16_kernel<GEPI_STORE_BF16><<<grid, 256, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, (const bf16*)A_lo, colscale); break;
+    case GEPI_RESID_F32: gemm_bf16_kernel<GEPI_RESID_F32><<<grid, 256, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, (const bf16*)A_lo, colscale); break;
+    case GEPI_SWIGLU_BF16: gemm_bf16_kernel<GEPI_SWIGLU_BF16><<<grid, 256, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, (const bf16*)A_lo, colscale); break;
+    case GEPI_STORE_F32: gemm_bf16_kernel<GEPI_STORE_F32><<<grid, 256, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, (const bf16*)A_lo, colscale); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -66,7 +66,7 @@ template <int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ A_lo,
                      const bf16* __restrict__ B, int ldb, void* __restrict__ out, int ldc,
-                     int M, int N, int K, int tiles_n, int nblocks) {
+                     int M, int N, int K, int tiles_n, int nblocks, const float* __restrict__ colscale) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid >> 1, wn = wid & 1;
@@ -184,6 +184,20 @@ void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict
   const int hl = lane >> 5;                 // which quad of the 8-column group
   const int mrow0 = m0 + wm * 128;
   const int ncol0 = n0 + wn * 128;
+  if (colscale != nullptr) {
+    // per-column scale; columns past N (clamped reads) are never stored
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = min(ncol0 + 32 * j + 8 * g + 4 * hl, N - 4);
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(colscale + n);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[j][i][4 * g + e] *= sc[e];
+      }
+  }
 
   if (EPI == GEPI_STORE_BF16) {
     // 128 rows x 256 B; 16-B chunk c of row m at slot c ^ (m & 15)
@@ -300,7 +314,8 @@ bool gemm_dma_ok(int epi, const void* A, int lda, const void* B, int ldb, const 
 }
 
 hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc,
-                    int M, int N, int K, hipStream_t s, const void* A_lo) {
+                    int M, int N, int K, hipStream_t s, const void* A_lo, const float* colscale) {
+  if (colscale != nullptr && ((uintptr_t)colscale & 15)) return hipErrorInvalidValue;
   const int tn = (N + TILE - 1) / TILE, tm = (M + TILE - 1) / TILE;
   const int nb = tn * tm;
   const bf16* a = (const bf16*)A;
@@ -308,16 +323,16 @@ hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, voi
   const bf16* al = (const bf16*)A_lo;
   switch (epi) {
     case GEPI_STORE_BF16:
-      gemm_dma_kernel<GEPI_STORE_BF16><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb);
+      gemm_dma_kernel<GEPI_STORE_BF16><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
       break;
     case GEPI_RESID_F32:
-      gemm_dma_kernel<GEPI_RESID_F32><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb);
+      gemm_dma_kernel<GEPI_RESID_F32><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
       break;
     case GEPI_SWIGLU_BF16:
-      gemm_dma_kernel<GEPI_SWIGLU_BF16><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb);
+      gemm_dma_kernel<GEPI_SWIGLU_BF16><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
       break;
     case GEPI_STORE_F32:
-      gemm_dma_kernel<GEPI_STORE_F32><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb);
+      gemm_dma_kernel<GEPI_STORE_F32><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
       break;
     default:
       return hipErrorInvalidValue;

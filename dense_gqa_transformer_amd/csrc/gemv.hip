@@ -10,6 +10,8 @@
 // reduced.  The cross-lane dot-product sum is a wave64 shuffle tree.
 // Epilogues: plain store, residual add, SwiGLU on paired gate/up rows, and
 // lm_head logits with a per-workgroup argmax (reduced by argmax_partials).
+// Int8 weights (one scale per row) stream 16 codes per lane per load; each
+// row's dot product is multiplied by its scale before the epilogue.
 #include "common.h"
 #include "kernels.h"
 
@@ -18,9 +20,11 @@ namespace fsk {
 static constexpr int GEMV_THREADS = 256;
 static constexpr int GEMV_WAVES = 4;
 
+// One lane's chunk of a weight row: CE consecutive elements.
 template <typename W> struct Raw;
-template <> struct Raw<bf16> { u32x4 v; };
-template <> struct Raw<float> { f32x4 a, b; };
+template <> struct Raw<bf16> { static constexpr int CE = 8; u32x4 v; };
+template <> struct Raw<float> { static constexpr int CE = 8; f32x4 a, b; };
+template <> struct Raw<int8_t> { static constexpr int CE = 16; u32x4 v; };
 
 __device__ __forceinline__ void raw_load(const bf16* p, Raw<bf16>& r) {
   r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -29,6 +33,10 @@ __device__ __forceinline__ void raw_load(const float* p, Raw<float>& r) {
   r.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
   r.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
 }
+__device__ __forceinline__ void raw_load(const int8_t* p, Raw<int8_t>& r) {
+  r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void raw_zero(Raw<int8_t>& r) { r.v = u32x4{0, 0, 0, 0}; }
 __device__ __forceinline__ void raw_zero(Raw<bf16>& r) { r.v = u32x4{0, 0, 0, 0}; }
 __device__ __forceinline__ void raw_zero(Raw<float>& r) { r.a = f32x4{0, 0, 0, 0}; r.b = r.a; }
 __device__ __forceinline__ void raw_f32(const Raw<bf16>& r, float* o) {
@@ -37,6 +45,16 @@ __device__ __forceinline__ void raw_f32(const Raw<bf16>& r, float* o) {
     o[2 * i] = __uint_as_float(r.v[i] << 16);
     o[2 * i + 1] = __uint_as_float(r.v[i] & 0xffff0000u);
   }
+}
+__device__ __forceinline__ void raw_f32(const Raw<int8_t>& r, float* o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) codes4(r.v[i], o + 4 * i);
+}
+// CE consecutive activations (fp32)
+template <int CE>
+__device__ __forceinline__ void load_act(const float* p, float* o) {
+#pragma unroll
+  for (int h = 0; h < CE / 8; ++h) load8(p + 8 * h, o + 8 * h);
 }
 __device__ __forceinline__ void raw_f32(const Raw<float>& r, float* o) {
   o[0] = r.a[0]; o[1] = r.a[1]; o[2] = r.a[2]; o[3] = r.a[3];
@@ -57,14 +75,16 @@ __device__ __forceinline__ int weight_row(int slot_row, int& feature) {
 
 template <typename W, int EPI, int MB, int CPL, int RPW>
 __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) {
+  constexpr int CE = Raw<W>::CE;
+  constexpr bool QUANT = (CE == 16);
   // activations held in registers when they fit (always for one row)
-  constexpr bool XREG = (MB * CPL <= 8);
+  constexpr bool XREG = (MB * CPL * CE <= 64);
   const int K = p.K;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int m0 = blockIdx.y * MB;
   const int mcount = min(MB, p.M - m0);
   const W* __restrict__ w = reinterpret_cast<const W*>(p.w);
-  const int nchunk = K >> 3;
+  const int nchunk = K / CE;
   const int slots_total = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;   // weight rows to cover
   const int rows_per_block = GEMV_WAVES * RPW * p.groups;
 
@@ -78,7 +98,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
         int f;
         const int r = weight_row<EPI>(rbase + i, f);
         if (c < nchunk && rbase + i < slots_total)
-          raw_load(w + (size_t)r * K + c * 8, raw[j][i]);
+          raw_load(w + (size_t)r * K + c * CE, raw[j][i]);
         else
           raw_zero(raw[j][i]);
       }
@@ -89,7 +109,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
 
   // ---- prologue: per-row RMSNorm scale from this wave's own slices
   float inv[MB];
-  float xv[XREG ? MB : 1][XREG ? CPL : 1][8];
+  float xv[XREG ? MB : 1][XREG ? CPL : 1][CE];
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const float* arow = p.a + (size_t)(m0 + min(m, mcount - 1)) * p.lda;
@@ -97,17 +117,17 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = lane + 64 * j;
-      float v[8];
-      if (c < nchunk) load8(arow + c * 8, v);
+      float v[CE];
+      if (c < nchunk) load_act<CE>(arow + c * CE, v);
       else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        for (int e = 0; e < CE; ++e) v[e] = 0.f;
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+      for (int e = 0; e < CE; ++e) ss = fmaf(v[e], v[e], ss);
       if (XREG) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xv[XREG ? m : 0][XREG ? j : 0][e] = v[e];
+        for (int e = 0; e < CE; ++e) xv[XREG ? m : 0][XREG ? j : 0][e] = v[e];
       }
     }
     inv[m] = (p.gamma != nullptr) ? rsqrtf(wave_sum(ss) / (float)K + p.eps) : 1.f;
@@ -116,16 +136,16 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = lane + 64 * j;
-      float g[8];
-      if (c < nchunk) load8(p.gamma + c * 8, g);
+      float g[CE];
+      if (c < nchunk) load_act<CE>(p.gamma + c * CE, g);
       else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) g[e] = 0.f;
+        for (int e = 0; e < CE; ++e) g[e] = 0.f;
       }
 #pragma unroll
       for (int m = 0; m < MB; ++m)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xv[XREG ? m : 0][XREG ? j : 0][e] *= inv[m] * g[e];
+        for (int e = 0; e < CE; ++e) xv[XREG ? m : 0][XREG ? j : 0][e] *= inv[m] * g[e];
     }
   }
 
@@ -146,32 +166,32 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
     for (int j = 0; j < CPL; ++j) {
       const int c = lane + 64 * j;
       if (c >= nchunk) continue;
-      float gam[8];
+      float gam[CE];
       if (!XREG) {
-        if (p.gamma != nullptr) load8(p.gamma + c * 8, gam);
+        if (p.gamma != nullptr) load_act<CE>(p.gamma + c * CE, gam);
         else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) gam[e] = 1.f;
+          for (int e = 0; e < CE; ++e) gam[e] = 1.f;
         }
       }
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
-        float a[8];
+        float a[CE];
         if (XREG) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) a[e] = xv[XREG ? m : 0][XREG ? j : 0][e];
+          for (int e = 0; e < CE; ++e) a[e] = xv[XREG ? m : 0][XREG ? j : 0][e];
         } else {
-          load8(p.a + (size_t)(m0 + min(m, mcount - 1)) * p.lda + c * 8, a);
+          load_act<CE>(p.a + (size_t)(m0 + min(m, mcount - 1)) * p.lda + c * CE, a);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) a[e] *= inv[m] * gam[e];
+          for (int e = 0; e < CE; ++e) a[e] *= inv[m] * gam[e];
         }
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
-          float wv[8];
+          float wv[CE];
           raw_f32(raw[j][i], wv);
           float s = acc[i][m];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s = fmaf(wv[e], a[e], s);
+          for (int e = 0; e < CE; ++e) s = fmaf(wv[e], a[e], s);
           acc[i][m] = s;
         }
       }
@@ -183,6 +203,16 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
 
     // ---- epilogue (every lane holds the sums; lane 0 writes)
     if (lane == 0) {
+      if (QUANT) {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+          int f;
+          const int r = weight_row<EPI>(min(rbase + i, slots_total - 1), f);
+          const float sc = p.wscale[r];
+#pragma unroll
+          for (int m = 0; m < MB; ++m) acc[i][m] *= sc;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         const int sr = rbase + i;
@@ -271,8 +301,9 @@ __global__ __launch_bounds__(256) void argmax_partials_kernel(const float* __res
 }
 
 // ------------------------------------------------------------------ launcher
-static int cpl_for(int K) {
-  const int c = (K / 8 + 63) / 64;
+// chunks per lane for a reduction length K in chunks of ce elements
+static int cpl_for(int K, int ce) {
+  const int c = (K / ce + 63) / 64;
   if (c <= 1) return 1;
   if (c <= 2) return 2;
   if (c <= 4) return 4;
@@ -281,17 +312,23 @@ static int cpl_for(int K) {
   return -1;
 }
 
-int gemv_logits_blocks(int N, int K) {
-  const int cpl = cpl_for(K);
-  const int rpw = cpl <= 2 ? 4 : 2;
-  const int rows_per_group = GEMV_WAVES * rpw;
+// rows per wave: short rows (one chunk per lane) four at a time, longer ones
+// two, which keeps the decode projections at 128-384 workgroups
+static constexpr int rpw_for(bool quant, int cpl) {
+  return quant ? (cpl <= 1 ? 4 : 2) : (cpl <= 2 ? 4 : 2);
+}
+
+int gemv_logits_blocks(int dt, int N, int K) {
+  const bool q = (dt == DT_I8);
+  const int cpl = cpl_for(K, q ? 16 : 8);
+  const int rows_per_group = GEMV_WAVES * rpw_for(q, cpl);
   const int groups = 8;
   return (N + rows_per_group * groups - 1) / (rows_per_group * groups);
 }
 
 template <typename W, int EPI, int MB, int CPL>
 static hipError_t launch_gemv(GemvParams p, hipStream_t s) {
-  constexpr int RPW = (CPL <= 2) ? 4 : 2;
+  constexpr int RPW = rpw_for(Raw<W>::CE == 16, CPL);
   const int slots_total = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
   const int rows_per_group = GEMV_WAVES * RPW;
   int groups = 1;
@@ -305,7 +342,7 @@ static hipError_t launch_gemv(GemvParams p, hipStream_t s) {
 
 template <typename W, int EPI, int MB>
 static hipError_t dispatch_cpl(GemvParams p, hipStream_t s) {
-  switch (cpl_for(p.K)) {
+  switch (cpl_for(p.K, Raw<W>::CE)) {
     case 1: return launch_gemv<W, EPI, MB, 1>(p, s);
     case 2: return launch_gemv<W, EPI, MB, 2>(p, s);
     case 4: return launch_gemv<W, EPI, MB, 4>(p, s);
@@ -332,6 +369,16 @@ hipError_t argmax_partials(const float* pv, const int32_t* pi, int nblocks, int 
 hipError_t gemv(int dt, int epi, GemvParams p, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (p.K % 8 != 0) return hipErrorInvalidValue;
+  if (dt == DT_I8) {
+    if (p.K % 16 != 0 || p.wscale == nullptr) return hipErrorInvalidValue;
+    switch (epi) {
+      case EPI_STORE: return dispatch_mb<int8_t, EPI_STORE>(p, s);
+      case EPI_RESID: return dispatch_mb<int8_t, EPI_RESID>(p, s);
+      case EPI_SWIGLU: return dispatch_mb<int8_t, EPI_SWIGLU>(p, s);
+      case EPI_LOGITS: return dispatch_mb<int8_t, EPI_LOGITS>(p, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (dt == DT_BF16) {
     switch (epi) {
       case EPI_STORE: return dispatch_mb<bf16, EPI_STORE>(p, s);

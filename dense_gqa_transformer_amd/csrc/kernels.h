@@ -5,14 +5,22 @@
 
 namespace fsk {
 
-enum Dt { DT_F32 = 0, DT_BF16 = 1 };
+// DT_I8: signed 8-bit codes with one fp32 scale per row (weights only)
+enum Dt { DT_F32 = 0, DT_BF16 = 1, DT_I8 = 2 };
 
-inline size_t dt_size(int dt) { return dt == DT_BF16 ? 2 : 4; }
+inline size_t dt_size(int dt) { return dt == DT_BF16 ? 2 : dt == DT_I8 ? 1 : 4; }
 
 // ---------------------------------------------------------------- small ops
-// x[t, :] = E[tok[t], :] widened to fp32 (ids clamped to [0, V)).
+// x[t, :] = E[tok[t], :] widened to fp32 (ids clamped to [0, V)); DT_I8 rows
+// are multiplied by their scale (escale[id]).
 hipError_t embed(const void* E, int dt, const int32_t* tok, int T, int H, int V,
-                 float* x, hipStream_t s);
+                 float* x, hipStream_t s, const float* escale = nullptr);
+// Per-row symmetric int8: scale[r] = max|src[r,:]| / 127, codes = rint(src / scale)
+// (fp32 quotients, ties to even; zero row -> scale 0).  cols % 8 == 0.
+hipError_t quantize_rows(const void* src, int dt, int rows, int cols, int8_t* codes, float* scales,
+                         hipStream_t s);
+// dst[i] = bf16(codes[i]) (exact: |code| <= 127); n % 16 == 0.
+hipError_t codes_to_bf16(const int8_t* codes, size_t n, void* dst, hipStream_t s);
 // out[t, :] = x[t*ldx, :] / sqrt(mean(x^2) + eps) * g; out of out_dt at row stride ldo.
 // lo (bf16 only, optional): the rounding remainder, y - out, also as bf16.
 hipError_t rmsnorm(const float* x, int T, int H, int ldx, const float* g, float eps,
@@ -31,6 +39,7 @@ static constexpr int GEMV_LOGITS_MAX_M = 4;
 
 struct GemvParams {
   const void* w;       // [N, K] of dt (SWIGLU: packed gate/up, 2*N rows, N = ffn)
+  const float* wscale; // DT_I8: per weight row scale (row dot products are multiplied by it)
   int N, K;            // output features, reduction length
   const float* a;      // activations, M rows at stride lda (fp32)
   int lda, M;
@@ -47,7 +56,7 @@ struct GemvParams {
 };
 hipError_t gemv(int dt, int epi, GemvParams p, hipStream_t s);
 // Number of workgroups (and per-row partials) the LOGITS epilogue uses.
-int gemv_logits_blocks(int N, int K);
+int gemv_logits_blocks(int dt, int N, int K);
 // next[m] = best of the nblocks (value, index) partials of row m.
 hipError_t argmax_partials(const float* pv, const int32_t* pi, int nblocks, int M, int32_t* next,
                            hipStream_t s);
@@ -60,14 +69,17 @@ enum GemmEpi { GEPI_STORE_BF16 = 0, GEPI_RESID_F32 = 1, GEPI_SWIGLU_BF16 = 2, GE
 // out[m*ldc + f] = silu(gate_f) * up_f.  Requires K % 64 == 0 (and N % 64 == 0 for SWIGLU).
 // A_lo (optional): a second bf16 operand of A's shape; C = (A + A_lo) . B^T, the
 // remainder pass reusing each B tile (keeps activations near fp32 precision).
+// colscale (optional, fp32 [N]): C[:, n] *= colscale[n] before the epilogue
+// (B holding int8 codes as bf16, colscale their row scales).
 hipError_t gemm_bf16(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc,
-                     int M, int N, int K, hipStream_t s, const void* A_lo = nullptr);
+                     int M, int N, int K, hipStream_t s, const void* A_lo = nullptr,
+                     const float* colscale = nullptr);
 // The large-problem kernel behind gemm_bf16 (256x256 tiles, operands streamed
 // into LDS by DMA): gemm_dma_ok says whether it applies to a call.
 bool gemm_dma_ok(int epi, const void* A, int lda, const void* B, int ldb, const void* out, int ldc,
                  int M, int N, int K, const void* A_lo);
 hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc,
-                    int M, int N, int K, hipStream_t s, const void* A_lo);
+                    int M, int N, int K, hipStream_t s, const void* A_lo, const float* colscale);
 
 // ---------------------------------------------------------------- q/k norm + RoPE + KV write
 // For T tokens: token t belongs to sequence t / S_per (slot slots[t / S_per]) at

@@ -36,12 +36,116 @@ __global__ __launch_bounds__(256) void embed_kernel(const W* __restrict__ E, con
   }
 }
 
-hipError_t embed(const void* E, int dt, const int32_t* tok, int T, int H, int V, float* x, hipStream_t s) {
+// int8 rows: code * the row's scale, rounded to fp32 (the residual stream)
+__global__ __launch_bounds__(256) void embed_i8_kernel(const int8_t* __restrict__ E,
+                                                       const float* __restrict__ escale,
+                                                       const int32_t* __restrict__ tok, int H, int V,
+                                                       float* __restrict__ x) {
+  const int t = blockIdx.x;
+  int id = tok[t];
+  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+  const int8_t* row = E + (size_t)id * H;
+  const float sc = escale[id];
+  float* dst = x + (size_t)t * H;
+  for (int k = threadIdx.x * 8; k < H; k += 256 * 8) {
+    const uint2 w = *reinterpret_cast<const uint2*>(row + k);
+    float v[8];
+    codes4(w.x, v);
+    codes4(w.y, v + 4);
+    *reinterpret_cast<float4*>(dst + k) = make_float4(v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc);
+    *reinterpret_cast<float4*>(dst + k + 4) = make_float4(v[4] * sc, v[5] * sc, v[6] * sc, v[7] * sc);
+  }
+}
+
+hipError_t embed(const void* E, int dt, const int32_t* tok, int T, int H, int V, float* x, hipStream_t s,
+                 const float* escale) {
   if (T <= 0) return hipSuccess;
-  if (dt == DT_BF16)
+  if (dt == DT_I8) {
+    if (escale == nullptr || H % 8 != 0) return hipErrorInvalidValue;
+    embed_i8_kernel<<<T, 256, 0, s>>>((const int8_t*)E, escale, tok, H, V, x);
+  } else if (dt == DT_BF16) {
     embed_kernel<bf16><<<T, 256, 0, s>>>((const bf16*)E, tok, H, V, x);
-  else
+  } else {
     embed_kernel<float><<<T, 256, 0, s>>>((const float*)E, tok, H, V, x);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ int8 rows
+// Per-row symmetric quantization, one wave per row: the row's largest
+// magnitude (wave max), scale = amax / 127 and code = rint(x / scale), both
+// quotients correctly rounded fp32 divisions.  Rows are re-read for the
+// codes (they are a few KB and still in cache).
+template <typename W>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const W* __restrict__ src, int rows, int cols,
+                                                            int8_t* __restrict__ codes,
+                                                            float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const W* row = src + (size_t)r * cols;
+  float amax = 0.f;
+  for (int k = lane * 8; k < cols; k += 64 * 8) {
+    float v[8];
+    load8(row + k, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  }
+  amax = wave_max(amax);
+  const float sc = amax / 127.0f;
+  if (lane == 0) scales[r] = sc;
+  int8_t* out = codes + (size_t)r * cols;
+  for (int k = lane * 8; k < cols; k += 64 * 8) {
+    float v[8];
+    load8(row + k, v);
+    uint32_t w[2] = {0u, 0u};
+    if (sc > 0.f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float q = fminf(fmaxf(rintf(v[e] / sc), -127.f), 127.f);
+        w[e >> 2] |= (uint32_t)(uint8_t)(int8_t)(int)q << (8 * (e & 3));
+      }
+    }
+    *reinterpret_cast<uint2*>(out + k) = make_uint2(w[0], w[1]);
+  }
+}
+
+hipError_t quantize_rows(const void* src, int dt, int rows, int cols, int8_t* codes, float* scales,
+                         hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (cols <= 0 || cols % 8 != 0) return hipErrorInvalidValue;
+  const int blocks = (rows + 3) / 4;
+  if (dt == DT_BF16)
+    quantize_rows_kernel<bf16><<<blocks, 256, 0, s>>>((const bf16*)src, rows, cols, codes, scales);
+  else if (dt == DT_F32)
+    quantize_rows_kernel<float><<<blocks, 256, 0, s>>>((const float*)src, rows, cols, codes, scales);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// Codes as bf16 operands of the MFMA GEMM (integers up to 127 are exact).
+__global__ __launch_bounds__(256) void codes_to_bf16_kernel(const int8_t* __restrict__ codes, size_t n16,
+                                                            bf16* __restrict__ dst) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(codes + i * 16);
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) codes4(w[j], v + 4 * j);
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { a[e] = (bf16)v[e]; b[e] = (bf16)v[8 + e]; }
+    *reinterpret_cast<bf16x8*>(dst + i * 16) = a;
+    *reinterpret_cast<bf16x8*>(dst + i * 16 + 8) = b;
+  }
+}
+
+hipError_t codes_to_bf16(const int8_t* codes, size_t n, void* dst, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (n % 16 != 0) return hipErrorInvalidValue;
+  const size_t n16 = n / 16;
+  const size_t blocks = std::min<size_t>((n16 + 255) / 256, 4096);
+  codes_to_bf16_kernel<<<(unsigned)blocks, 256, 0, s>>>(codes, n16, (bf16*)dst);
   return hipGetLastError();
 }
 

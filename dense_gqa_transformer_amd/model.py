@@ -40,6 +40,8 @@ class Model:
     ``{"embed", "final_norm", "layers": [{attn_norm, wq, ...}]}`` of numpy
     arrays or tensors, ``[out, in]`` row-major.  The values are copied into
     library-owned memory; for bf16 models they must be bf16-representable.
+    ``shape.weight_format == "i8_row"`` has the library store the matrices as
+    int8 codes with one scale per output row (quantized at creation).
     """
 
     def __init__(self, shape, weights: dict, max_seqs: int, max_ctx: int,
@@ -53,7 +55,9 @@ class Model:
         self.cfg = FsConfig(shape.n_layers, shape.hidden, shape.n_heads, shape.n_kv_heads,
                             shape.head_dim, shape.ffn, shape.vocab, float(shape.rms_eps),
                             float(shape.rope_theta), self.dtype, int(max_seqs), int(max_ctx),
-                            int(getattr(shape, "rope_dim", 0)), int(bool(getattr(shape, "attn_gate", False))))
+                            int(getattr(shape, "rope_dim", 0)), int(bool(getattr(shape, "attn_gate", False))),
+                            native.FS_WEIGHTS_I8_ROW if getattr(shape, "weight_format", "dtype") == "i8_row"
+                            else native.FS_WEIGHTS_DTYPE)
         with torch.cuda.device(self.device):
             keep = []
 
@@ -175,6 +179,19 @@ class Model:
         check(self._lib.fs_kv_read(self._h, layer, slot, kv_head, pos0, n, _ptr(k), _ptr(v),
                                    _stream_ptr(stream)))
         return k, v
+
+
+def quantize_rows_i8(src: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
+    """Per-row int8 codes and fp32 scales of a device matrix [rows, cols] (fp32
+    or bf16), by the library's quantizer (fs_quantize_rows_i8)."""
+    lib = native.load()
+    assert src.dim() == 2 and src.is_contiguous() and src.dtype in (torch.float32, torch.bfloat16)
+    rows, cols = src.shape
+    codes = torch.empty((rows, cols), dtype=torch.int8, device=src.device)
+    scales = torch.empty((rows,), dtype=torch.float32, device=src.device)
+    dt = native.FS_BF16 if src.dtype == torch.bfloat16 else native.FS_F32
+    check(lib.fs_quantize_rows_i8(_ptr(src), dt, rows, cols, _ptr(codes), _ptr(scales), _stream_ptr(stream)))
+    return codes, scales
 
 
 def argmax(logits: torch.Tensor, out: Optional[torch.Tensor] = None,

@@ -24,6 +24,8 @@ STATUS_NAMES = {0: "FS_OK", -1: "FS_ERR_INVALID_ARG", -2: "FS_ERR_OOM", -3: "FS_
                 -4: "FS_ERR_CAPACITY", -5: "FS_ERR_UNSUPPORTED"}
 FS_F32 = 0
 FS_BF16 = 1
+FS_WEIGHTS_DTYPE = 0
+FS_WEIGHTS_I8_ROW = 1
 
 LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo",
                 "mlp_norm", "w_gate", "w_up", "w_down")
@@ -36,7 +38,8 @@ class FsConfig(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32),
                 ("max_seqs", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
-                ("rope_dim", ctypes.c_int32), ("attn_gate", ctypes.c_int32)]
+                ("rope_dim", ctypes.c_int32), ("attn_gate", ctypes.c_int32),
+                ("weight_format", ctypes.c_int32)]
 
 
 class FsLayerWeights(ctypes.Structure):
@@ -92,6 +95,8 @@ def load() -> ctypes.CDLL:
     lib.fs_decode_step.restype = ctypes.c_int
     lib.fs_argmax.argtypes = [P, i32, i32, P, P]
     lib.fs_argmax.restype = ctypes.c_int
+    lib.fs_quantize_rows_i8.argtypes = [P, i32, i32, i32, P, P, P]
+    lib.fs_quantize_rows_i8.restype = ctypes.c_int
     lib.fs_sample.argtypes = [P, P, i32, i32, ctypes.POINTER(FsSampling), P, P, P]
     lib.fs_sample.restype = ctypes.c_int
     lib.fs_generate.argtypes = [P, P, i32, i32, ctypes.POINTER(FsGeneration), ctypes.POINTER(i32),

@@ -50,9 +50,22 @@ typedef enum {
 
 typedef enum { FS_F32 = 0, FS_BF16 = 1 } fs_dtype;
 
+/* Storage of the matrices (wq, wk, wv, wo, w_gate, w_up, w_down and the tied
+ * embedding / head).  The low-bit option answers "Milestones", M7 (decide
+ * from measurements whether low-bit weights pay for themselves; "ferrite",
+ * What it does, lists the 8-bit block formats it reads):
+ *   FS_WEIGHTS_DTYPE:  kept in cfg.dtype;
+ *   FS_WEIGHTS_I8_ROW: signed 8-bit codes with one fp32 scale per output row,
+ *     made by fs_model_create from the cfg.dtype weights with the
+ *     fs_quantize_rows_i8 rule.  Products use code * scale exactly (the scale
+ *     multiplies each row's fp32 dot product); the embedding lookup reads the
+ *     same codes, so the head stays tied.  Norm weights, activations and the
+ *     KV cache keep cfg.dtype. */
+typedef enum { FS_WEIGHTS_DTYPE = 0, FS_WEIGHTS_I8_ROW = 1 } fs_weight_format;
+
 /* Model shape and KV capacity.
  *   n_heads % n_kv_heads == 0; query head h reads KV head h / (n_heads/n_kv_heads).
- *   head_dim in {64, 128}; hidden, n_heads*head_dim and ffn multiples of 64.
+ *   head_dim in {64, 128, 256}; hidden, n_heads*head_dim and ffn multiples of 64.
  *   rms_eps: the eps of every RMSNorm, inside the square root.
  *   rope_theta: base of the rotary frequencies theta^(-2i/head_dim).
  *   dtype: element type of every weight, the KV cache, and GEMM operands.
@@ -68,6 +81,7 @@ typedef struct {
    * rotate-half RoPE on 64 of 256 head dims, q/gate split per head). */
   int32_t rope_dim;          /* rotated dims per head: 0 = all of head_dim; else a multiple of 16 <= head_dim */
   int32_t attn_gate;         /* 0 or 1: wq also carries a sigmoid gate per head */
+  int32_t weight_format;     /* fs_weight_format */
 } fs_config;
 
 /* One layer's weights, device pointers of cfg.dtype, row-major [out, in]:
@@ -137,6 +151,18 @@ fs_status fs_decode_step(fs_model *m, const int32_t *tokens, const int32_t *posi
  * exact ties ("Coming back to Failed Star", section "Next", Selection);
  * -1 if the row holds no finite value.  Errors: INVALID_ARG for NULL or B, V <= 0. */
 fs_status fs_argmax(const float *logits, int32_t B, int32_t V, int32_t *out, void *stream);
+
+/* Per-row symmetric int8 quantization (the FS_WEIGHTS_I8_ROW rule).
+ *   src:    device [rows, cols] of dtype (fs_dtype), row-major.
+ *   codes:  device int8 [rows, cols]; scales: device fp32 [rows].
+ * scale[r] = max_k |src[r, k]| / 127 and codes[r, k] = nearest integer to
+ * src[r, k] / scale[r] (ties to even), both quotients correctly rounded fp32;
+ * a row of zeros gets scale 0 and zero codes.  Rows whose largest magnitude
+ * is below the fp32 normal range are outside the rule's contract.
+ * Errors: INVALID_ARG for NULL pointers, rows or cols <= 0, cols % 8 != 0;
+ * UNSUPPORTED for an unknown dtype. */
+fs_status fs_quantize_rows_i8(const void *src, int32_t dtype, int32_t rows, int32_t cols,
+                              int8_t *codes, float *scales, void *stream);
 
 /* Parameters of the sampling chain temperature -> top-k -> top-p ->
  * renormalise -> draw ("Coming back to Failed Star", section "Next": the

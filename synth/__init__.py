@@ -49,6 +49,7 @@ class ModelShape:
     dtype: str = BF16
     rope_dim: int = 0          # rotated dims per head (0: all of head_dim)
     attn_gate: bool = False    # q projection carries a per-head output gate
+    weight_format: str = "dtype"   # "dtype", or "i8_row": int8 codes + one scale per output row
 
     @property
     def q_width(self) -> int:
@@ -92,6 +93,11 @@ GATED_BF16 = ModelShape(n_layers=2, hidden=512, n_heads=8, n_kv_heads=2, head_di
 # The same attention at the 0.6B shape's other widths (for measurement).
 GATED_0P6B = ModelShape(n_layers=28, hidden=1024, n_heads=8, n_kv_heads=2, head_dim=256,
                         ffn=3072, vocab=151936, dtype=BF16, rope_dim=64, attn_gate=True)
+
+
+# Int8 weights (one scale per output row) on the tiny fp32 model and the 0.6B shape.
+TINY_I8 = dataclasses.replace(TINY, weight_format="i8_row")
+QWEN3_0P6B_I8 = dataclasses.replace(QWEN3_0P6B, weight_format="i8_row")
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:

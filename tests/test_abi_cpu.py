@@ -12,7 +12,8 @@ def test_library_exports_every_declared_symbol():
     names = native.header_functions()
     assert set(names) == {"fs_model_create", "fs_model_destroy", "fs_prefill", "fs_decode_step",
                           "fs_argmax", "fs_slot_length", "fs_kv_read", "fs_last_error",
-                          "fs_timing", "fs_timing_read", "fs_kernel_bench", "fs_sample", "fs_generate"}
+                          "fs_timing", "fs_timing_read", "fs_kernel_bench", "fs_sample", "fs_generate",
+                          "fs_quantize_rows_i8"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -36,12 +37,18 @@ def test_argument_errors_without_device():
     out = (ctypes.c_int32 * 4)()
     assert lib.fs_generate(None, fake, 3, 0, ctypes.byref(g), out, ctypes.byref(n), ctypes.byref(why),
                            None) == native.FS_ERR_INVALID_ARG
+    q = lib.fs_quantize_rows_i8
+    assert q(None, native.FS_BF16, 4, 64, fake, fake, None) == native.FS_ERR_INVALID_ARG
+    assert q(fake, 9, 4, 64, fake, fake, None) == native.FS_ERR_UNSUPPORTED
+    assert q(fake, native.FS_BF16, 0, 64, fake, fake, None) == native.FS_ERR_INVALID_ARG
+    assert q(fake, native.FS_BF16, 4, 60, fake, fake, None) == native.FS_ERR_INVALID_ARG
+    assert q(ctypes.c_void_p(0x1008), native.FS_BF16, 4, 64, fake, fake, None) == native.FS_ERR_INVALID_ARG
 
 
 def _cfg(**kw):
     base = dict(n_layers=1, hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn=768, vocab=4096,
                 rms_eps=1e-6, rope_theta=1e6, dtype=native.FS_F32, max_seqs=1, max_ctx=32,
-                rope_dim=0, attn_gate=0)
+                rope_dim=0, attn_gate=0, weight_format=0)
     base.update(kw)
     return native.FsConfig(*[base[f] for f, _ in native.FsConfig._fields_])
 
@@ -55,6 +62,7 @@ def _cfg(**kw):
     (dict(hidden=8192), native.FS_ERR_UNSUPPORTED),
     (dict(max_ctx=0), native.FS_ERR_INVALID_ARG),
     (dict(vocab=0), native.FS_ERR_INVALID_ARG),
+    (dict(weight_format=2), native.FS_ERR_UNSUPPORTED),
 ])
 def test_create_rejects_bad_config(kw, status):
     lib = native.load()
