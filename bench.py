@@ -169,6 +169,87 @@ def gated_variant_bench(dev, Model):
             "prefill_1x1024_tok_s": round(1024 / pdt, 1)}
 
 
+def int8_weights_bench(dev, Model, shape, w, ref_model, prompt):
+    """The low-bit decision's measurements: the 0.6B shape with int8 weights
+    (one scale per output row, quantized by the library from the same bf16
+    weights) against the bf16 model -- speed (bs1 decode, 4 x 4096 prefill),
+    weight memory, and quality (logits of both models on one teacher-forced
+    token stream, the bf16 model choosing the tokens)."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import synth
+    qs = dataclasses.replace(shape, weight_format="i8_row")
+    qm = Model(qs, w, max_seqs=4, max_ctx=4096)
+    H, L, I, V = shape.hidden, shape.n_layers, shape.ffn, shape.vocab
+    rows_cols = [(shape.q_width + 2 * shape.kv_width, H), (H, shape.q_width), (2 * I, H), (H, I)]
+    bf16_w = 2 * (V * H + L * sum(r * c for r, c in rows_cols))
+    int8_w = V * H + 4 * V + L * sum(r * c + 4 * r for r, c in rows_cols)
+    P = len(prompt)
+    tok = torch.from_numpy(prompt[None, :].astype(np.int32)).to(dev)
+    nxt = torch.empty((1,), dtype=torch.int32, device=dev)
+    # speed: bs1 decode from the same 512-token prompt
+    lg = qm.prefill(tok, [1])
+    nxt.copy_(torch.argmax(lg, dim=1).to(torch.int32))
+    for k in range(8):
+        qm.decode_step(nxt, [P + k], [1], next_ids=nxt)
+    qm.prefill(tok, [0])
+    torch.cuda.synchronize()
+    steps = 128
+    t0 = time.perf_counter()
+    for k in range(steps):
+        qm.decode_step(nxt, [P + k], [0], next_ids=nxt)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    ctx = P + (steps + 1) / 2.0
+    other = L * (2 * H + 2 * shape.head_dim) * 2 + 2 * H * 2       # norm weights, embedding row
+    step_bytes = int8_w + other + L * 2 * shape.kv_width * 2 * ctx
+    per_launch = {lab: qm.kernel_bench(lab, reps=20, slot=2, position=P + steps // 2)
+                  for lab in ("qkv", "o_proj", "gate_up", "down", "head")}
+    # speed: 4 x 4096 prefill
+    pw = synth.workload("prefill_0p6b_4x4096")
+    ptok = torch.from_numpy(np.stack(pw.prompts).astype(np.int32)).to(dev)
+    plg = torch.empty((4, V), dtype=torch.float32, device=dev)
+    qm.prefill(ptok, [0, 1, 2, 3], logits=plg)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    qm.prefill(ptok, [0, 1, 2, 3], logits=plg)
+    torch.cuda.synchronize()
+    pdt = time.perf_counter() - t0
+    # quality: one token stream through both models
+    ql = qm.prefill(tok, [0])
+    rl = ref_model.prefill(tok, [3])
+    a, b = torch.empty((1, V), device=dev), torch.empty((1, V), device=dev)
+    diffs, rel, agree = [], [], 0
+    cur_q, cur_r = ql.clone(), rl.clone()
+    n_q = 64
+    for k in range(n_q):
+        d = (cur_q - cur_r).abs().max().item()
+        diffs.append(d)
+        rel.append(((cur_q - cur_r).pow(2).mean().sqrt() / cur_r.pow(2).mean().sqrt()).item())
+        ti = int(torch.argmax(cur_r[0]).item())
+        agree += int(torch.argmax(cur_q[0]).item()) == ti
+        t = torch.tensor([ti], dtype=torch.int32, device=dev)
+        qm.decode_step(t, [P + k], [0], logits=a)
+        ref_model.decode_step(t, [P + k], [3], logits=b)
+        cur_q, cur_r = a.clone(), b.clone()
+    qm.close()
+    return {"workload": "0.6B shape, int8 codes + one fp32 scale per output row for every matrix (tied "
+                        "embedding / head included), bf16 activations and KV; bs1 decode from the same "
+                        "512-token prompt; 4 x 4096 prefill",
+            "decode_tok_s": round(1.0 / dt, 1), "ms_per_step": round(dt * 1e3, 4),
+            "decode_hbm_frac_step": round(step_bytes / dt / HBM_PEAK, 4),
+            "decode_us_per_launch": {k: round(v, 3) for k, v in per_launch.items()},
+            "prefill_4x4096_tok_s": round(4 * 4096 / pdt, 1), "prefill_ms": round(pdt * 1e3, 2),
+            "weight_bytes": {"int8": int(int8_w), "bf16": int(bf16_w)},
+            "quality_vs_bf16": {"positions": n_q, "greedy_agree": agree,
+                                "max_abs_logit_diff": round(max(diffs), 4),
+                                "mean_max_abs_logit_diff": round(float(np.mean(diffs)), 4),
+                                "mean_rel_rms_logit_diff": round(float(np.mean(rel)), 5)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,6 +411,7 @@ def main():
                        "tok_s_incl_prefill": round(len(gids) / gdt, 1)}
 
     out["gated_variant"] = gated_variant_bench(dev, Model)
+    out["int8_weights"] = int8_weights_bench(dev, Model, shape, w, model, prompt)
 
     # seeded sampling of one lm_head row (temperature -> top-k -> top-p -> draw)
     srow = torch.from_numpy(synth.logit_rows(900, 1, shape.vocab)).to(dev)
