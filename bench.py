@@ -260,6 +260,9 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=48)
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only one 4 x 4096 prefill (for hardware-counter passes) and exit")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="run only the 512-token prefill and --steps bs1 decode steps (for hardware-counter "
+                         "passes) and exit")
     ap.add_argument("--copy-cal", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 4 times and exit: the plain copy of known "
                          "size that calibrates the FETCH_SIZE / WRITE_SIZE byte counters")
@@ -304,6 +307,14 @@ def main():
     tok = torch.from_numpy(prompt[None, :].astype(np.int32)).to(dev)
     nxt = torch.empty((1,), dtype=torch.int32, device=dev)
     P = len(prompt)
+    if args.decode_only:
+        argmax(model.prefill(tok, [0]), out=nxt)
+        t0 = time.perf_counter()
+        for k in range(steps):
+            model.decode_step(nxt, [P + k], [0], next_ids=nxt)
+        torch.cuda.synchronize()
+        print(json.dumps({"decode_only_steps": steps, "ms": round((time.perf_counter() - t0) * 1e3, 3)}), flush=True)
+        return
 
     # warmup on slot 1 (also captures the decode graphs used below)
     lg = model.prefill(tok, [1])
