@@ -243,7 +243,7 @@ fs_status fs_kv_read(const fs_model *m, int32_t layer, int32_t slot, int32_t kv_
  * records and starts recording: every kernel this model launches is then
  * bracketed by a pair of HIP events on the call's stream, labelled with the
  * step it implements ("embed", "norm", "qkv", "rope_kv", "attn", "combine",
- * "attn_gate", "o_proj", "gate_up", "down", "head", "argmax"), and decode steps run
+ * "attn_gate", "wconv", "o_proj", "gate_up", "down", "head", "argmax"), and decode steps run
  * without graph replay.  fs_timing(m, 0) stops recording (records are kept
  * until the next fs_timing call).  Errors: INVALID_ARG for a NULL model. */
 fs_status fs_timing(fs_model *m, int32_t enable);
