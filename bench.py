@@ -250,6 +250,112 @@ def int8_weights_bench(dev, Model, shape, w, ref_model, prompt):
                                 "mean_rel_rms_logit_diff": round(float(np.mean(rel)), 5)}}
 
 
+def scorer_bench(dev, model, shape):
+    """The 6-token scorer on the bs1 model: latency of one fs_prefill (last-token
+    logits) and the weight bytes it must move over that time."""
+    import numpy as np
+    import torch
+
+    import synth
+    wl = synth.workload("scorer_0p6b")
+    tok = torch.from_numpy(wl.prompts[0][None, :].astype(np.int32)).to(dev)
+    lg = torch.empty((1, shape.vocab), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        model.prefill(tok, [3], logits=lg)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(20):
+        t0 = time.perf_counter()
+        model.prefill(tok, [3], logits=lg)
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    t = float(np.median(ts))
+    model.timing(True)
+    model.prefill(tok, [3], logits=lg)
+    torch.cuda.synchronize()
+    per = {}
+    for lab in ("embed", "norm", "qkv", "rope_kv", "attn", "o_proj", "gate_up", "down", "head"):
+        ms, n = model.timing_read(lab)
+        if n:
+            per[lab] = round(ms, 4)
+    model.timing(False)
+    return {"workload": "scorer_0p6b: one 6-token prompt, last-token logits (fs_prefill)",
+            "latency_ms_p50": round(t * 1e3, 4), "hbm_frac": round(decode_bytes_per_step(shape, 6) / t / HBM_PEAK, 4),
+            "kernel_ms": per}
+
+
+def batched_decode_bench(dev, Model, w, argmax):
+    """64 sequences of ragged context (uniform in [256, 4096]), prefilled one by
+    one (untimed), then decode steps with B = 64 and next IDs fed back on the
+    device: 2 warmup steps, then the workload's 128 timed steps."""
+    import numpy as np
+    import torch
+
+    import synth
+    wl = synth.workload("decode_0p6b_bs64")
+    shape = wl.shape
+    B, steps, warm = wl.batch, wl.decode_steps, 2
+    lens = np.array([len(p) for p in wl.prompts])
+    m = Model(shape, w, max_seqs=B, max_ctx=int(lens.max()) + warm + steps + 1)
+    nxt = torch.empty((B,), dtype=torch.int32, device=dev)
+    for i, p in enumerate(wl.prompts):
+        lg = m.prefill(torch.from_numpy(p[None, :].astype(np.int32)).to(dev), [i])
+        argmax(lg, out=nxt[i:i + 1])
+    slots = list(range(B))
+    for k in range(warm):
+        m.decode_step(nxt, [int(n) + k for n in lens], slots, next_ids=nxt)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(warm, warm + steps):
+        m.decode_step(nxt, [int(n) + k for n in lens], slots, next_ids=nxt)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    # one more step under the per-launch event hook: time per kernel class
+    m.timing(True)
+    m.decode_step(nxt, [int(n) + warm + steps for n in lens], slots, next_ids=nxt)
+    torch.cuda.synchronize()
+    per = {}
+    for lab in ("embed", "norm", "qkv", "attn", "combine", "o_proj", "gate_up", "down", "head", "argmax"):
+        ms, n = m.timing_read(lab)
+        if n:
+            per[lab] = round(ms, 4)
+    m.timing(False)
+    m.close()
+    kv_per_pos = shape.n_layers * 2 * shape.kv_width * 2
+    wbytes = decode_bytes_per_step(shape, 0)
+    ctx_sum = float(np.sum(lens)) * steps + B * sum(warm + k + 1 for k in range(steps))
+    step_bytes = wbytes + kv_per_pos * ctx_sum / steps + B * kv_per_pos
+    return {"workload": "decode_0p6b_bs64: 64 sequences, contexts uniform in [256, 4096], greedy, next IDs on "
+                        "device; 2 warmup steps then 128 timed",
+            "tok_s": round(B * steps / dt, 1), "ms_per_step": round(dt * 1e3 / steps, 3),
+            "hbm_frac_step": round(step_bytes / (dt / steps) / HBM_PEAK, 4),
+            "bytes_per_step": int(step_bytes), "kernel_ms_per_step": per}
+
+
+def tiny_bench(dev, Model, argmax):
+    """The tiny fp32 model: 16-token prompt, 16 greedy decode steps (launch-bound)."""
+    import numpy as np
+    import torch
+
+    import synth
+    wl = synth.workload("tiny_fp32")
+    m = Model(wl.shape, synth.make_weights(wl.shape, 0), max_seqs=2, max_ctx=64)
+    tok = torch.from_numpy(wl.prompts[0][None, :].astype(np.int32)).to(dev)
+    nxt = torch.empty((1,), dtype=torch.int32, device=dev)
+    P = tok.shape[1]
+    for slot in (1, 0):
+        argmax(m.prefill(tok, [slot]), out=nxt)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(wl.decode_steps):
+            m.decode_step(nxt, [P + k], [slot], next_ids=nxt)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+    m.close()
+    return {"workload": "tiny_fp32: 2 layers, hidden 256, 16-token prompt, 16 greedy decode steps (second run)",
+            "decode_tok_s": round(wl.decode_steps / dt, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,6 +442,18 @@ def main():
     ctx_avg = P + (steps + 1) / 2.0
     hbm_frac = decode_bytes_per_step(shape, ctx_avg) / (dt / steps) / HBM_PEAK
 
+    # per-step latency distribution: the same steps again on slot 2, with an
+    # event after each step on the stream the steps run on
+    lg = model.prefill(tok, [2])
+    argmax(lg, out=nxt)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for k in range(steps):
+        model.decode_step(nxt, [P + k], [2], next_ids=nxt)
+        evs[k + 1].record()
+    torch.cuda.synchronize()
+    step_ms = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(steps)])
+
     # per-launch duration of each decode kernel class, replayed back to back in
     # a graph over the 28 layers' own weights (HIP events on the library's stream)
     per_launch = {}
@@ -363,6 +481,8 @@ def main():
                                "greedy batch-1 decode steps from position 512",
                    "global_batch": 1, "seq_len": P + steps, "parallelism": "none"},
         "decode_hbm_frac_step": round(hbm_frac, 4),
+        "decode_step_ms_p50": round(float(np.percentile(step_ms, 50)), 4),
+        "decode_step_ms_p99": round(float(np.percentile(step_ms, 99)), 4),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved / 1e9, 1),
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
                      "traffic": measured_traffic("decode." + dom), "avg_launch_us": round(avg_s * 1e6, 3),
@@ -421,6 +541,9 @@ def main():
                        "tokens": len(gids), "stop_reason": gwhy, "ms": round(gdt * 1e3, 2),
                        "tok_s_incl_prefill": round(len(gids) / gdt, 1)}
 
+    out["scorer"] = scorer_bench(dev, model, shape)
+    out["batched_decode"] = batched_decode_bench(dev, Model, w, argmax)
+    out["tiny"] = tiny_bench(dev, Model, argmax)
     out["gated_variant"] = gated_variant_bench(dev, Model)
     out["int8_weights"] = int8_weights_bench(dev, Model, shape, w, model, prompt)
 

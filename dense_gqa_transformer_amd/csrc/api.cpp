@@ -39,7 +39,7 @@ fs_status fail(fs_status st, const std::string& msg) {
 
 // Up to this many rows per call the projections run as GEMV (weights streamed
 // once, fp32 activations); above it as MFMA GEMM on bf16 activations.
-constexpr int SKINNY_MAX_ROWS = GEMV_LOGITS_MAX_M;
+constexpr int SKINNY_MAX_ROWS = 8;
 // In timing mode each call starts with a short device-side wait so the host
 // can queue the whole call behind it: the event pairs then bracket kernels
 // that run back to back instead of waiting on the host.

@@ -260,6 +260,8 @@ hipError_t gemm_bf16(int epi, const void* A, int lda, const void* B, int ldb, vo
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % BK != 0) return hipErrorInvalidValue;
   if (epi == GEPI_SWIGLU_BF16 && N % 64 != 0) return hipErrorInvalidValue;
+  if (gemm_skinny_ok(epi, A, lda, B, ldb, M, N, K, A_lo))
+    return gemm_skinny(epi, A, lda, B, ldb, out, ldc, M, N, K, s, A_lo, colscale);
   if (gemm_dma_ok(epi, A, lda, B, ldb, out, ldc, M, N, K, A_lo))
     return gemm_dma(epi, A, lda, B, ldb, out, ldc, M, N, K, s, A_lo, colscale);
   const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);

@@ -1,0 +1,176 @@
+// MFMA GEMM for few activation rows (M <= 64): batched decode steps and short
+// prompts.
+//
+// C[M, N] = A[M, K] . B[N, K]^T as in gemm.hip (B a weight stored [out, in],
+// "Coming back to Failed Star", First sitting, item 3), but shaped for the
+// case where the weight, not the arithmetic, is the cost: a workgroup owns a
+// slab of 32 * NT weight rows and every activation row, so each weight byte is
+// fetched once.  The 4 waves split K four ways and stream their operands
+// straight from global memory into MFMA fragments (no LDS staging); the four
+// partial products meet in LDS for the epilogue.
+//
+// Fragments: for a 64-wide K chunk, lane l supplies row (l % 32) of its 32-row
+// tile and the 32 consecutive k at 32 * (l / 32), eight per
+// v_mfma_f32_32x32x16_bf16 step, identically for both operands, so each
+// product sums every k of the chunk exactly once and each lane reads 64
+// contiguous bytes of a row.  With the weight fragment as the first operand the
+// 32x32 result holds (weight row 8*(r/4) + 4*(l/32) + r%4, activation row
+// l%32) in register r.
+#include "common.h"
+#include "kernels.h"
+
+namespace fsk {
+
+namespace {
+
+constexpr int SK_WAVES = 4;
+
+template <int EPI, int NT, int MT>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16* __restrict__ A, int lda,
+                                                          const bf16* __restrict__ A_lo,
+                                                          const bf16* __restrict__ B, int ldb,
+                                                          void* __restrict__ out, int ldc, int M, int N, int K,
+                                                          const float* __restrict__ colscale) {
+  constexpr int NS = 32 * NT;                 // weight rows (output columns) of this workgroup
+  constexpr int MS = 32 * MT;                 // activation rows covered
+  constexpr int RS = NS + 1;                  // padded LDS row: the partial sums of one activation row
+  __shared__ float red[SK_WAVES][MS * RS];
+
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  const int n0 = blockIdx.x * NS;
+  const int kw = K / SK_WAVES, kb = wid * kw;
+
+  const bf16* bp[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) bp[t] = B + (size_t)min(n0 + 32 * t + r, N - 1) * ldb + kb + 32 * h;
+  const bf16* ap[MT];
+  const bf16* alp[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const size_t row = (size_t)min(32 * i + r, M - 1);
+    ap[i] = A + row * lda + kb + 32 * h;
+    alp[i] = (A_lo != nullptr) ? A_lo + row * lda + kb + 32 * h : nullptr;
+  }
+  const bool lo = (A_lo != nullptr);
+
+  f32x16 acc[NT][MT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[t][i][e] = 0.f;
+
+#pragma unroll 2
+  for (int k = 0; k < kw; k += 64) {
+    bf16x8 bv[NT][4], av[MT][4], alv[MT][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) bv[t][s] = *reinterpret_cast<const bf16x8*>(bp[t] + k + 8 * s);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) av[i][s] = *reinterpret_cast<const bf16x8*>(ap[i] + k + 8 * s);
+    if (lo) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) alv[i][s] = *reinterpret_cast<const bf16x8*>(alp[i] + k + 8 * s);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[t][s], av[i][s], acc[t][i], 0, 0, 0);
+          if (lo) acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[t][s], alv[i][s], acc[t][i], 0, 0, 0);
+        }
+  }
+
+  // ---- the four K quarters meet in LDS: red[w][m * RS + n]
+  float* R = red[wid];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int n = 32 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+        R[(32 * i + r) * RS + n] = acc[t][i][e];
+      }
+  __syncthreads();
+
+  const int rows = min(M, MS);
+  if (EPI == GEPI_SWIGLU_BF16) {
+    // the slab is one packed [32 gate | 32 up] block: 32 output features
+    const int f0 = n0 / 2;
+    for (int idx = threadIdx.x; idx < rows * 32; idx += 256) {
+      const int m = idx >> 5, n = idx & 31;
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int w = 0; w < SK_WAVES; ++w) {
+        g += red[w][m * RS + n];
+        u += red[w][m * RS + 32 + n];
+      }
+      if (colscale != nullptr) {
+        g *= colscale[n0 + n];
+        u *= colscale[n0 + 32 + n];
+      }
+      reinterpret_cast<bf16*>(out)[(size_t)m * ldc + f0 + n] = (bf16)(silu(g) * u);
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < rows * NS; idx += 256) {
+      const int m = idx / NS, n = idx % NS;
+      if (n0 + n >= N) continue;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < SK_WAVES; ++w) v += red[w][m * RS + n];
+      if (colscale != nullptr) v *= colscale[n0 + n];
+      const size_t o = (size_t)m * ldc + n0 + n;
+      if (EPI == GEPI_STORE_BF16) reinterpret_cast<bf16*>(out)[o] = (bf16)v;
+      else if (EPI == GEPI_STORE_F32) reinterpret_cast<float*>(out)[o] = v;
+      else reinterpret_cast<float*>(out)[o] += v;
+    }
+  }
+}
+
+template <int EPI, int NT>
+hipError_t launch_nt(const bf16* a, int lda, const bf16* alo, const bf16* b, int ldb, void* out, int ldc, int M,
+                     int N, int K, const float* cs, hipStream_t s) {
+  const int blocks = (N + 32 * NT - 1) / (32 * NT);
+  if (M <= 32)
+    gemm_skinny_kernel<EPI, NT, 1><<<blocks, 256, 0, s>>>(a, lda, alo, b, ldb, out, ldc, M, N, K, cs);
+  else
+    gemm_skinny_kernel<EPI, NT, 2><<<blocks, 256, 0, s>>>(a, lda, alo, b, ldb, out, ldc, M, N, K, cs);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_skinny_ok(int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+                    const void* A_lo) {
+  if (M <= 0 || M > 64 || N <= 0 || K <= 0 || K % 256 != 0 || N % 32 != 0) return false;
+  if (epi == GEPI_SWIGLU_BF16 && N % 64 != 0) return false;
+  if (lda % 8 || ldb % 8) return false;
+  const uintptr_t al = (uintptr_t)A | (uintptr_t)B | (uintptr_t)A_lo;
+  return (al & 15) == 0;
+}
+
+hipError_t gemm_skinny(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc, int M, int N,
+                       int K, hipStream_t s, const void* A_lo, const float* colscale) {
+  const bf16* a = (const bf16*)A;
+  const bf16* b = (const bf16*)B;
+  const bf16* al = (const bf16*)A_lo;
+  switch (epi) {
+    case GEPI_STORE_BF16: return launch_nt<GEPI_STORE_BF16, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, colscale, s);
+    case GEPI_STORE_F32: return launch_nt<GEPI_STORE_F32, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, colscale, s);
+    case GEPI_RESID_F32: return launch_nt<GEPI_RESID_F32, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, colscale, s);
+    case GEPI_SWIGLU_BF16: return launch_nt<GEPI_SWIGLU_BF16, 2>(a, lda, al, b, ldb, out, ldc, M, N, K, colscale, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fsk

@@ -352,11 +352,18 @@ static hipError_t dispatch_cpl(GemvParams p, hipStream_t s) {
   }
 }
 
+// Rows per workgroup: 1, 4, or 8 (5-8 rows and larger M in groups of 8), so a
+// short prompt streams each weight once.
 template <typename W, int EPI>
 static hipError_t dispatch_mb(GemvParams p, hipStream_t s) {
   if (p.M == 1) return dispatch_cpl<W, EPI, 1>(p, s);
-  if (EPI == EPI_LOGITS && p.M > GEMV_LOGITS_MAX_M) return hipErrorInvalidValue;
-  return dispatch_cpl<W, EPI, 4>(p, s);
+  if (EPI == EPI_LOGITS) {
+    if (p.M > GEMV_LOGITS_MAX_M) return hipErrorInvalidValue;
+    return dispatch_cpl<W, EPI, 4>(p, s);
+  } else {
+    if (p.M <= 4) return dispatch_cpl<W, EPI, 4>(p, s);
+    return dispatch_cpl<W, EPI, 8>(p, s);
+  }
 }
 
 hipError_t argmax_partials(const float* pv, const int32_t* pi, int nblocks, int M, int32_t* next,

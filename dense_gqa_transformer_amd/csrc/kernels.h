@@ -80,6 +80,12 @@ bool gemm_dma_ok(int epi, const void* A, int lda, const void* B, int ldb, const 
                  int M, int N, int K, const void* A_lo);
 hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc,
                     int M, int N, int K, hipStream_t s, const void* A_lo, const float* colscale);
+// The few-rows kernel behind gemm_bf16 (M <= 64, K % 256 == 0, N % 32 == 0):
+// one weight slab per workgroup, K split over its waves, each weight read once.
+bool gemm_skinny_ok(int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
+                    const void* A_lo);
+hipError_t gemm_skinny(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc, int M, int N,
+                       int K, hipStream_t s, const void* A_lo, const float* colscale);
 
 // ---------------------------------------------------------------- q/k norm + RoPE + KV write
 // For T tokens: token t belongs to sequence t / S_per (slot slots[t / S_per]) at

@@ -6,7 +6,7 @@ dims) against the oracle.
 Shapes GATED_TINY (fp32, tolerance 1e-4) and GATED_BF16 (bf16, 2e-2), seeded
 random-init weights and uniform-random tokens.  Covers the prefill (fp32 vector
 path; bf16 GEMM path with the head_dim-256 vector attention), teacher-forced
-decode at batch 2 (GEMV path) and batch 6 (GEMM path), and the cached K of
+decode at batch 2 (GEMV path) and batch 10 (GEMM path), and the cached K of
 layer 0 (only its first 64 dims rotate).
 """
 import numpy as np
@@ -56,7 +56,7 @@ def test_gated_tiny_fp32_prefill_and_decode():
 def test_gated_bf16_prefill_decode_and_cache():
     wl = synth.workload("gated_bf16")
     shape = wl.shape
-    m = make_model(shape, max_seqs=6, max_ctx=256)
+    m = make_model(shape, max_seqs=10, max_ctx=256)
     orc = O.Oracle(shape, weights(shape))
     try:
         toks = np.stack(wl.prompts)                                   # [2, 160]
@@ -83,25 +83,25 @@ def test_gated_bf16_prefill_decode_and_cache():
                 ref = orc.decode_step(i, nxt[i], pos)
                 check_logits(got[i], ref, TOL["bf16"], f"gated bf16 decode step {k_} row {i}")
                 nxt[i] = O.greedy_argmax(ref)
-        # batch 6 (GEMM path in the decode step): four more sequences, short prompts
-        more = synth.tokens(109, shape.vocab, (4, 24))
-        m.prefill(dev_tokens(more), [2, 3, 4, 5])
+        # batch 10 (GEMM path in the decode step): eight more sequences, short prompts
+        more = synth.tokens(109, shape.vocab, (8, 24))
+        m.prefill(dev_tokens(more), list(range(2, 10)))
         orcs = {}
         cur = {}
-        for i in range(4):
+        for i in range(8):
             o = O.Oracle(shape, weights(shape))
             cur[2 + i] = O.greedy_argmax(o.prefill(0, more[i]))
             orcs[2 + i] = o
-        slots = [0, 1, 2, 3, 4, 5]
+        slots = list(range(10))
         pos0 = toks.shape[1] + wl.decode_steps
-        positions = [pos0, pos0, 24, 24, 24, 24]
-        tokens = nxt + [cur[s] for s in range(2, 6)]
-        out6 = torch.empty((6, shape.vocab), dtype=torch.float32, device="cuda")
-        m.decode_step(dev_tokens(tokens), positions, slots, logits=out6)
-        got = out6.cpu().numpy()
+        positions = [pos0, pos0] + [24] * 8
+        tokens = nxt + [cur[s] for s in range(2, 10)]
+        out10 = torch.empty((10, shape.vocab), dtype=torch.float32, device="cuda")
+        m.decode_step(dev_tokens(tokens), positions, slots, logits=out10)
+        got = out10.cpu().numpy()
         for i in range(2):
-            check_logits(got[i], orc.decode_step(i, tokens[i], positions[i]), TOL["bf16"], f"B=6 row {i}")
-        for s in range(2, 6):
-            check_logits(got[s], orcs[s].decode_step(0, tokens[s], positions[s]), TOL["bf16"], f"B=6 row {s}")
+            check_logits(got[i], orc.decode_step(i, tokens[i], positions[i]), TOL["bf16"], f"B=10 row {i}")
+        for s in range(2, 10):
+            check_logits(got[s], orcs[s].decode_step(0, tokens[s], positions[s]), TOL["bf16"], f"B=10 row {s}")
     finally:
         m.close()

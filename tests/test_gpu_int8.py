@@ -7,9 +7,10 @@ and scales of its quantizer must equal the oracle's bit for bit, and the
 forward pass must match the oracle run on the dequantized weights to the
 usual tolerances: 1e-4 on the tiny fp32 model (GEMV path only), 2e-2 on the
 0.6B shape with greedy IDs exact away from near-ties.  The 0.6B cases cover
-the GEMV path (scorer, bs1 decode with the fused argmax), the MFMA GEMM path
-with the codes widened to bf16 and the scales applied per column (prefill of
-130 and 1100 tokens, a 6-sequence decode step), and the 256x256 DMA GEMM
+the GEMV path (bs1 decode with the fused argmax, a 6-sequence decode step), the
+MFMA GEMM path with the codes widened to bf16 and the scales applied per
+column (the scorer's 6 tokens go through the 8-row GEMV; prefill of 130 and
+1100 tokens, a 10-sequence decode step), and the 256x256 DMA GEMM
 (2 x 4096 prefill, checked through its cached K/V against an oracle prefix).
 """
 import functools
@@ -118,7 +119,7 @@ def test_tiny_fp32_int8_prefill_and_decode():
 def big8():
     shape = synth.QWEN3_0P6B_I8
     _flush("building 0.6B int8 model")
-    m = make_model(shape, max_seqs=6, max_ctx=1152)
+    m = make_model(shape, max_seqs=10, max_ctx=1152)
     _flush("dequantized oracle")
     orc = q_oracle(shape)
     yield shape, m, orc
@@ -155,23 +156,26 @@ def test_0p6b_int8_decode_bs1_and_bs6(big8):
         ref = orc.decode_step(0, tok, pos)
         check_logits(logits.cpu().numpy()[0], ref, TOL["bf16"], f"int8 bs1 decode {k}")
         check_argmax(int(nxt.cpu()[0]), ref, f"int8 bs1 decode {k}")
-    # six sequences in one step: the GEMM path (codes widened to bf16) and the
-    # row-group GEMV head
-    slots = [0, 1, 2, 3, 4, 5]
-    prompts = synth.tokens(612, shape.vocab, (6, 20))
-    m.prefill(dev_tokens(prompts), slots)
-    toks = synth.tokens(613, shape.vocab, 6)
-    out = torch.empty((6, shape.vocab), dtype=torch.float32, device="cuda")
-    nx6 = torch.empty((6,), dtype=torch.int32, device="cuda")
-    m.decode_step(dev_tokens(toks), [20] * 6, slots, logits=out, next_ids=nx6)
-    got = out.cpu().numpy()
-    ids = nx6.cpu().numpy()
-    for i in range(6):
+    # six sequences in one step (the 8-row GEMV and the row-group GEMV head), then
+    # ten (the GEMM path: codes widened to bf16, scales per column)
+    prompts = synth.tokens(612, shape.vocab, (10, 20))
+    toks = synth.tokens(613, shape.vocab, 10)
+    refs = []
+    for i in range(10):
         o = q_oracle(shape)
         o.prefill(0, prompts[i])
-        r = o.decode_step(0, int(toks[i]), 20)
-        check_logits(got[i], r, TOL["bf16"], f"int8 B=6 row {i}")
-        check_argmax(int(ids[i]), r, f"int8 B=6 row {i}")
+        refs.append(o.decode_step(0, int(toks[i]), 20))
+    for B in (6, 10):
+        slots = list(range(B))
+        m.prefill(dev_tokens(prompts[:B]), slots)
+        out = torch.empty((B, shape.vocab), dtype=torch.float32, device="cuda")
+        nx = torch.empty((B,), dtype=torch.int32, device="cuda")
+        m.decode_step(dev_tokens(toks[:B]), [20] * B, slots, logits=out, next_ids=nx)
+        got = out.cpu().numpy()
+        ids = nx.cpu().numpy()
+        for i in range(B):
+            check_logits(got[i], refs[i], TOL["bf16"], f"int8 B={B} row {i}")
+            check_argmax(int(ids[i]), refs[i], f"int8 B={B} row {i}")
 
 
 def test_0p6b_int8_prefill_2x4096_through_the_cache():

@@ -183,10 +183,11 @@ def test_scorer_6_tokens(big):
         assert ref[g] >= kth - 2 * TOL["bf16"]
 
 
-@pytest.mark.parametrize("S", [1, 3, 5, 130, 1100])
+@pytest.mark.parametrize("S", [1, 3, 5, 9, 130, 1100])
 def test_prefill_lengths_both_paths(big, S):
-    # S <= 4 runs the GEMV path, larger S the MFMA GEMM path (128-row tiles, ragged
-    # tail at 130; 256-row tiles with a 76-row tail at 1100)
+    # S <= 8 runs the GEMV path (1, 4 or 8 rows per workgroup), larger S the MFMA
+    # GEMM path (128-row tiles, ragged tails at 9 and 130; 256-row tiles with a
+    # 76-row tail at 1100)
     shape, model = big
     toks = synth.tokens(500 + S, shape.vocab, (1, S))
     ref = oracle_for(shape).forward(toks[0])
