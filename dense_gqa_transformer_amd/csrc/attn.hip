@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
   __shared__ float sm[4][REP], sl[4][REP];
   __shared__ float so[4][REP][D];
 
-  constexpr int NPRE = 2;                               // key rows per lane fetched up front
+  constexpr int NPRE = 2;                               // key rows per lane in flight
   const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int grp = lane >> 4, li = lane & 15;
@@ -310,35 +310,34 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
     }
     if (u < c1) st.add(sc, v);
   };
-  // positions ufirst + 16*i; the trip count is uniform across the wave so the
-  // 16-lane shuffles stay converged
-#pragma unroll
-  for (int i = 0; i < NPRE; ++i) {
+  // positions ufirst + 16*i, i = 0, 1, ...: rows i .. i+NPRE-1 are in flight in
+  // the NPRE register slots, and a slot is refilled with row i+NPRE as soon as
+  // row i is unpacked.  `base` (and so the trip count) is uniform across the
+  // wave, so the 16-lane shuffles stay converged.
+  static_assert(NPRE == 2, "two register slots");
+  auto step = [&](int i, RawKV<KV, DP>& sk, RawKV<KV, DP>& sv) -> bool {
     const int base = c0 + wid * 4 + 16 * i;
-    if (base >= c1) break;
+    if (base >= c1) return false;
     const int u = ufirst + 16 * i;
     float k[DP], v[DP];
     if (u == u_new) {
 #pragma unroll
       for (int e = 0; e < DP; ++e) { k[e] = knew[li * DP + e]; v[e] = vnew[li * DP + e]; }
     } else {
-      pk[i].get(k);
-      pv[i].get(v);
+      sk.get(k);
+      sv.get(v);
+    }
+    if (base + 16 * NPRE < c1) {
+      const int un = min(u + 16 * NPRE, c1 - 1);
+      sk.load(kb + (size_t)un * D + li * DP);
+      sv.load(vb + (size_t)un * D + li * DP);
     }
     fold(u, k, v);
-  }
-  for (int base = c0 + wid * 4 + 16 * NPRE; base < c1; base += 16) {
-    const int u = base + grp;
-    const int uu = min(u, c1 - 1);
-    float k[DP], v[DP];
-    if (uu == u_new) {
-#pragma unroll
-      for (int e = 0; e < DP; ++e) { k[e] = knew[li * DP + e]; v[e] = vnew[li * DP + e]; }
-    } else {
-      loadn<KV, DP>(kb + (size_t)uu * D + li * DP, k);
-      loadn<KV, DP>(vb + (size_t)uu * D + li * DP, v);
-    }
-    fold(u, k, v);
+    return true;
+  };
+  for (int i = 0;; i += 2) {
+    if (!step(i, pk[0], pv[0])) break;
+    if (!step(i + 1, pk[1], pv[1])) break;
   }
   st.merge_xor(16);
   st.merge_xor(32);
