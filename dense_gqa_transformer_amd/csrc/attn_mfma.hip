@@ -5,7 +5,9 @@
 // matrix never leaves registers.
 //
 // One workgroup = HPW query heads of one KV group x 128 queries, 4 waves per
-// head; each wave owns 32 queries.  The heads of a group share every
+// head; each wave owns 32 queries (head_dim 64 / 128: two heads when the group
+// has an even count; head_dim 256: one, its output accumulators take 128
+// registers per lane).  The heads of a group share every
 // key/value tile, staged once in LDS: K row-major [key][d], V transposed
 // [d][key].  The next tile is fetched into registers while the current one is
 // being used.  Each wave computes the transposed scores S^T = K . Q^T (keys on
@@ -222,10 +224,14 @@ __global__ __launch_bounds__(256 * HPW) void attn_prefill_mfma_kernel(const Attn
 template <int D>
 static hipError_t launch_mfma(const AttnPrefillParams& p, hipStream_t s) {
   const int rep = p.nq / p.nkv;
-  if (rep % 2 == 0) {
-    const dim3 grid((p.S + 127) / 128, p.nq / 2, p.B);
-    attn_prefill_mfma_kernel<D, 2><<<grid, 512, 0, s>>>(p);
-  } else {
+  if constexpr (D <= 128) {
+    if (rep % 2 == 0) {
+      const dim3 grid((p.S + 127) / 128, p.nq / 2, p.B);
+      attn_prefill_mfma_kernel<D, 2><<<grid, 512, 0, s>>>(p);
+      return hipGetLastError();
+    }
+  }
+  {
     const dim3 grid((p.S + 127) / 128, p.nq, p.B);
     attn_prefill_mfma_kernel<D, 1><<<grid, 256, 0, s>>>(p);
   }
@@ -235,7 +241,8 @@ static hipError_t launch_mfma(const AttnPrefillParams& p, hipStream_t s) {
 hipError_t attn_prefill(const AttnPrefillParams& p, hipStream_t s) {
   if (p.B <= 0 || p.S <= 0) return hipSuccess;
   const bool bf = p.q_dt == DT_BF16 && p.kv_dt == DT_BF16 && p.o_dt == DT_BF16;
-  if (!bf || (p.d != 128 && p.d != 64)) return attn_prefill_vec(p, s);
+  if (!bf || (p.d != 128 && p.d != 64 && p.d != 256)) return attn_prefill_vec(p, s);
+  if (p.d == 256) return launch_mfma<256>(p, s);    // one head per workgroup (register budget)
   return p.d == 128 ? launch_mfma<128>(p, s) : launch_mfma<64>(p, s);
 }
 
