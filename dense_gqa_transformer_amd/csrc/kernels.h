@@ -171,6 +171,10 @@ struct SampleRowScratch {
   float m1[4096], m2[4096], m3[256];
   uint32_t maxkey, nfinite;
   float bsum[SAMPLE_MAX_BLOCKS];
+  // selections made so far (written by block 0 of the pass that makes them)
+  uint32_t kb1, kr1, kb2, kr2, kcut;   // top-k digits, remaining counts, the full cut key
+  uint32_t pb1, pb2, cut;              // top-p digits and the final cut key
+  float z, pr1, pr2;                   // top-k mass, remaining masses
 };
 struct SampleParams {
   const float* logits; long long ld;   // rows of logits, ld elements apart

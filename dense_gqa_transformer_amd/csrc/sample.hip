@@ -16,9 +16,12 @@
 // p * Z_k, found the same way on histograms of probability mass
 // 2^((x - max) log2(e) / T).  The draw sums the kept mass per block of token
 // IDs, then one workgroup walks the block sums and the chosen block's IDs.
-// Every pass is one launch over (blocks of IDs) x (rows); each block re-derives
-// the digits chosen so far from the previous passes' global histograms, so no
-// sequential step runs between launches.
+// Every pass is one launch over (blocks of IDs) x (rows).  A pass first makes
+// the one selection that the previous pass's histogram allows (every block
+// makes it identically, from the same global histogram in a fixed order;
+// block 0 stores it in the row scratch), then builds the next histogram, so
+// no separate selection step runs between launches and no pass repeats an
+// earlier selection.
 #include "common.h"
 #include "kernels.h"
 
@@ -39,26 +42,32 @@ __device__ __forceinline__ float keyf(uint32_t k) {
 }
 __device__ __forceinline__ bool finite(float f) { return (__float_as_uint(f) & 0x7f800000u) != 0x7f800000u; }
 
-// Inclusive prefix over the NT threads of a block (Hillis-Steele in LDS, a
-// fixed order, so every block computes bit-identical results).  Returns this
-// thread's inclusive sum; *before receives the previous thread's inclusive
-// sum (0 for thread 0) and *total the block total, so neighbouring intervals
-// [before, inclusive] meet exactly.
+// Inclusive prefix over the NT threads of a block: a wave64 shuffle scan, then
+// the four wave totals folded in a fixed order, so every block computes
+// bit-identical results.  Returns this thread's inclusive sum; *before
+// receives the previous thread's inclusive sum (0 for thread 0) and *total the
+// block total, so neighbouring intervals [before, inclusive] meet exactly.
 template <typename T>
 __device__ T block_inclusive(T v, T* before, T* total) {
-  __shared__ T buf[NT];
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int o = 1; o < NT; o <<= 1) {
-    const T add = t >= o ? buf[t - o] : T(0);
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+  static_assert(NT == 256, "four waves");
+  __shared__ T ws[NT / 64];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  T x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-  const T inc = buf[t];
-  *before = t > 0 ? buf[t - 1] : T(0);
-  *total = buf[NT - 1];
+  if (lane == 63) ws[w] = x;
+  __syncthreads();
+  T off = T(0);
+  for (int i = 0; i < w; ++i) off += ws[i];
+  T tot = T(0);
+  for (int i = 0; i < NT / 64; ++i) tot += ws[i];
+  const T inc = x + off;
+  const T prev = __shfl_up(inc, 1);
+  *before = lane > 0 ? prev : off;
+  *total = tot;
   __syncthreads();
   return inc;
 }
@@ -119,31 +128,6 @@ __device__ T hist_total(const T* h, int nb) {
   return total;
 }
 
-// the top-k cut (a full key) from the three count histograms
-__device__ uint32_t topk_key(const SampleRowScratch* sc, int top_k) {
-  const uint32_t nf = sc->nfinite;
-  const uint32_t k = (top_k <= 0 || (uint32_t)top_k > nf) ? nf : (uint32_t)top_k;
-  int b1, b2, b3;
-  uint32_t r1, r2, r3;
-  select_desc<uint32_t>(sc->c1, NB1, k, &b1, &r1);
-  select_desc<uint32_t>(sc->c2, NB1, r1, &b2, &r2);
-  select_desc<uint32_t>(sc->c3, NB3, r2, &b3, &r3);
-  (void)r3;
-  return ((uint32_t)b1 << 20) | ((uint32_t)b2 << 8) | (uint32_t)b3;
-}
-
-// the top-p cut (a full key) from the three mass histograms
-__device__ uint32_t topp_key(const SampleRowScratch* sc, float top_p) {
-  const float z = hist_total<float>(sc->m1, NB1);
-  int b1, b2, b3;
-  float r1, r2, r3;
-  select_desc<float>(sc->m1, NB1, top_p * z, &b1, &r1);
-  select_desc<float>(sc->m2, NB1, r1, &b2, &r2);
-  select_desc<float>(sc->m3, NB3, r2, &b3, &r3);
-  (void)r3;
-  return ((uint32_t)b1 << 20) | ((uint32_t)b2 << 8) | (uint32_t)b3;
-}
-
 }  // namespace
 
 __global__ __launch_bounds__(NT) void sample_zero_kernel(SampleRowScratch* scr) {
@@ -154,9 +138,12 @@ __global__ __launch_bounds__(NT) void sample_zero_kernel(SampleRowScratch* scr) 
 }
 
 // mode 0: level-1 count histogram (+ max key, finite count)
-// mode 1: level-2 count histogram;  mode 2: level-3 count histogram
-// mode 3..5: mass histograms of levels 1..3 over keys >= the top-k cut
-// mode 6: kept mass of this block (keys >= the final cut)
+// mode 1: select the top-k level-1 digit; level-2 count histogram
+// mode 2: select the level-2 digit; level-3 count histogram
+// mode 3: select the level-3 digit (top-k cut); level-1 mass histogram over keys >= it
+// mode 4: select the top-p level-1 digit; level-2 mass histogram
+// mode 5: select the level-2 digit; level-3 mass histogram
+// mode 6: the final cut (top-p level 3, or the top-k cut); kept mass of this block
 template <int MODE>
 __global__ __launch_bounds__(NT) void sample_pass_kernel(const SampleParams p) {
   const int row = blockIdx.y;
@@ -170,35 +157,64 @@ __global__ __launch_bounds__(NT) void sample_pass_kernel(const SampleParams p) {
   __shared__ float hm[NB1];
   __shared__ uint32_t smax, scount;
   __shared__ float ssum;
+  const bool store = blockIdx.x == 0 && threadIdx.x == 0;
 
-  // digits chosen by earlier passes
+  // ---- this pass's selection (earlier ones come from the scratch)
   uint32_t pre = 0, kcut = 0, cut = 0;
   int pshift = 0;
   float xmax = 0.f;
-  if (MODE == 1 || MODE == 2) {
-    int b1, b2;
-    uint32_t r1, r2;
+  if (MODE == 1) {
     const uint32_t nf = sc->nfinite;
     const uint32_t k = (p.top_k <= 0 || (uint32_t)p.top_k > nf) ? nf : (uint32_t)p.top_k;
-    select_desc<uint32_t>(sc->c1, NB1, k, &b1, &r1);
-    if (MODE == 1) { pre = (uint32_t)b1; pshift = 20; }
-    else { select_desc<uint32_t>(sc->c2, NB1, r1, &b2, &r2); pre = ((uint32_t)b1 << 12) | (uint32_t)b2; pshift = 8; }
-    (void)r2;
-  }
-  if (MODE >= 3) {
-    kcut = topk_key(sc, p.top_k);
-    xmax = keyf(sc->maxkey);
-  }
-  if (MODE == 4 || MODE == 5) {
+    int b;
+    uint32_t r;
+    select_desc<uint32_t>(sc->c1, NB1, k, &b, &r);
+    if (store) { sc->kb1 = (uint32_t)b; sc->kr1 = r; }
+    pre = (uint32_t)b;
+    pshift = 20;
+  } else if (MODE == 2) {
+    int b;
+    uint32_t r;
+    const uint32_t b1 = sc->kb1;
+    select_desc<uint32_t>(sc->c2, NB1, sc->kr1, &b, &r);
+    if (store) { sc->kb2 = (uint32_t)b; sc->kr2 = r; }
+    pre = (b1 << 12) | (uint32_t)b;
+    pshift = 8;
+  } else if (MODE == 3) {
+    int b;
+    uint32_t r;
+    select_desc<uint32_t>(sc->c3, NB3, sc->kr2, &b, &r);
+    kcut = (sc->kb1 << 20) | (sc->kb2 << 8) | (uint32_t)b;
+    if (store) sc->kcut = kcut;
+  } else if (MODE == 4) {
     const float z = hist_total<float>(sc->m1, NB1);
-    int b1, b2;
-    float r1, r2;
-    select_desc<float>(sc->m1, NB1, p.top_p * z, &b1, &r1);
-    if (MODE == 4) { pre = (uint32_t)b1; pshift = 20; }
-    else { select_desc<float>(sc->m2, NB1, r1, &b2, &r2); pre = ((uint32_t)b1 << 12) | (uint32_t)b2; pshift = 8; }
-    (void)r2;
+    int b;
+    float r;
+    select_desc<float>(sc->m1, NB1, p.top_p * z, &b, &r);
+    if (store) { sc->z = z; sc->pb1 = (uint32_t)b; sc->pr1 = r; }
+    pre = (uint32_t)b;
+    pshift = 20;
+  } else if (MODE == 5) {
+    int b;
+    float r;
+    const uint32_t b1 = sc->pb1;
+    select_desc<float>(sc->m2, NB1, sc->pr1, &b, &r);
+    if (store) { sc->pb2 = (uint32_t)b; sc->pr2 = r; }
+    pre = (b1 << 12) | (uint32_t)b;
+    pshift = 8;
+  } else if (MODE == 6) {
+    if (p.top_p < 1.f) {
+      int b;
+      float r;
+      select_desc<float>(sc->m3, NB3, sc->pr2, &b, &r);
+      cut = (sc->pb1 << 20) | (sc->pb2 << 8) | (uint32_t)b;
+    } else {
+      cut = sc->kcut;
+    }
+    if (store) sc->cut = cut;
   }
-  if (MODE == 6) cut = (p.top_p < 1.f) ? topp_key(sc, p.top_p) : kcut;
+  if (MODE >= 4) kcut = sc->kcut;
+  if (MODE >= 3) xmax = keyf(sc->maxkey);
 
   for (int b = threadIdx.x; b < NB; b += NT) { hc[b] = 0u; hm[b] = 0.f; }
   if (threadIdx.x == 0) { smax = 0u; scount = 0u; ssum = 0.f; }
@@ -257,20 +273,22 @@ __global__ __launch_bounds__(NT) void sample_final_kernel(const SampleParams p) 
     if (threadIdx.x == 0) p.out[row] = -1;
     return;
   }
-  const uint32_t kcut = topk_key(sc, p.top_k);
-  const uint32_t cut = (p.top_p < 1.f) ? topp_key(sc, p.top_p) : kcut;
+  const uint32_t cut = sc->cut;
+  __shared__ float bs[SAMPLE_MAX_BLOCKS];
   __shared__ int sblk;
   __shared__ float sbefore, starget;
+  if (threadIdx.x < p.G) bs[threadIdx.x] = sc->bsum[threadIdx.x];   // all loads at once
+  __syncthreads();
   if (threadIdx.x == 0) {
     float tot = 0.f;
-    for (int g = 0; g < p.G; ++g) tot += sc->bsum[g];
+    for (int g = 0; g < p.G; ++g) tot += bs[g];
     const float target = p.u[row] * tot;
     // first block whose cumulative mass exceeds target; if rounding never
     // lets it, the last non-empty block
     float acc = 0.f, before = 0.f;
     int blk = 0;
     for (int g = 0; g < p.G; ++g) {
-      const float sg = sc->bsum[g];
+      const float sg = bs[g];
       if (sg > 0.f) {
         blk = g;
         before = acc;
@@ -295,6 +313,8 @@ __global__ __launch_bounds__(NT) void sample_final_kernel(const SampleParams p) 
     if (finite(v) && fkey(v) >= cut) mine += __builtin_amdgcn_exp2f((v - xmax) * p.sc);
   }
   __shared__ float runs[NT];
+  __shared__ int swho;
+  __shared__ float sacc;
   runs[threadIdx.x] = mine;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -308,10 +328,15 @@ __global__ __launch_bounds__(NT) void sample_final_kernel(const SampleParams p) 
       }
       acc += runs[t];
     }
-    const int b0 = i0 + who * per, b1 = min(b0 + per, i1);
+    swho = who;
+    sacc = before;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x == swho) {
+    // the chosen run, walked by the thread that summed it (its IDs are cached)
     int pick = -1;
-    acc = before;
-    for (int i = b0; i < b1; ++i) {
+    float acc = sacc;
+    for (int i = a0; i < a1; ++i) {
       const float v = x[i];
       if (!(finite(v) && fkey(v) >= cut)) continue;
       pick = i;
