@@ -3,12 +3,18 @@
 The main parity suite runs the tiny fp32 model, the 0.6B shape and the gated
 variant; these cases reach the remaining instantiations: grouped-query ratios
 1, 4 and 8 (and 2 with one KV head per pair), head_dim 64, 128 and 256, partial
-RoPE on the base model, and both dtypes.  Each model (2 layers, seeded
+RoPE on the base model, hidden = ffn = 4096 (the widest rows the decode
+GEMV takes), and both dtypes.  Each model (2 layers, seeded
 random-init weights, uniform-random tokens) is checked against the oracle on
 a batched prefill of two prompts (the MFMA GEMM and attention paths for bf16,
 more than 64 rows), a one-token prompt, teacher-forced decode at batch 2 (GEMV)
 and a decode step at batch 12 (the few-row MFMA GEMM for bf16).  Tolerances
-as elsewhere: 1e-4 (fp32), 2e-2 (bf16) on every logit.
+as elsewhere: 1e-4 (fp32), 2e-2 (bf16) on every logit, except that the bf16
+bound scales with the spread of the logits for the hidden-4096 model: its
+logits spread twice as wide as the 0.6B shape's (std 1.31 against 0.64), and
+rounding the oracle's activations on the CPU at the points where the GPU
+path rounds them to bf16 moves its logits by 3.3e-2 max-abs, the error the GPU
+shows.
 """
 import numpy as np
 import pytest
@@ -27,10 +33,13 @@ def _gpu():
     need_gpu()
 
 
-def _shape(nq, nkv, d, dtype, rope_dim=0, hidden=512):
-    return synth.ModelShape(n_layers=2, hidden=hidden, n_heads=nq, n_kv_heads=nkv, head_dim=d, ffn=768,
+def _shape(nq, nkv, d, dtype, rope_dim=0, hidden=512, ffn=768):
+    return synth.ModelShape(n_layers=2, hidden=hidden, n_heads=nq, n_kv_heads=nkv, head_dim=d, ffn=ffn,
                             vocab=2048, dtype=dtype, rope_dim=rope_dim)
 
+
+# bf16 tolerance factor of the cases whose logit spread exceeds the 0.6B shape's
+TOL_SCALE = {"wide_h4096_bf16": 2.0}
 
 CASES = {
     "mha_d64_bf16": _shape(4, 4, 64, synth.BF16, hidden=256),      # ratio 1, odd group: one head per workgroup
@@ -39,6 +48,8 @@ CASES = {
     "mha_d128_bf16": _shape(4, 4, 128, synth.BF16),                # ratio 1 at d 128: MFMA kernel, one head
     "gqa2_d256_bf16": _shape(4, 2, 256, synth.BF16),               # d 256, full rotation
     "rope32_d128_bf16": _shape(8, 4, 128, synth.BF16, rope_dim=32),
+    "wide_h4096_bf16": _shape(32, 8, 128, synth.BF16, hidden=4096, ffn=4096),   # the widest rows the GEMV takes
+    "wide_h4096_f32": _shape(32, 8, 128, synth.F32, hidden=4096, ffn=4096),
     "gqa8_d64_f32": _shape(8, 1, 64, synth.F32),
     "gqa2_d256_f32": _shape(4, 2, 256, synth.F32, rope_dim=64),
 }
@@ -47,7 +58,7 @@ CASES = {
 @pytest.mark.parametrize("name", list(CASES))
 def test_shape_parity(name):
     shape = CASES[name]
-    tol = TOL["f32"] if shape.dtype == synth.F32 else TOL["bf16"]
+    tol = TOL["f32"] if shape.dtype == synth.F32 else TOL["bf16"] * TOL_SCALE.get(name, 1.0)
     seed = 700 + list(CASES).index(name)
     S = 96
     prompts = synth.tokens(seed, shape.vocab, (2, S))
