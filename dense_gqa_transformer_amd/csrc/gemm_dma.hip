@@ -1,6 +1,9 @@
 // Large bf16 MFMA GEMM for the prefill projections and MLP: 256x256 output
-// tile per workgroup of 4 waves (2 x 2, 128x128 per wave = 4x4 blocks of
-// v_mfma_f32_32x32x16_bf16), operands streamed from HBM straight into LDS.
+// tile per workgroup of 8 waves, two per SIMD (2 x 4, 128x64 per wave = 4x2
+// blocks of v_mfma_f32_32x32x16_bf16), operands streamed from HBM straight
+// into LDS.  Two waves per SIMD let one wave's waits for the stage barrier
+// overlap the other's products (measured 3-8% faster than one wave of 128x128
+// per SIMD on the four prefill shapes).
 //
 // C[M, N] = A[M, K] . B[N, K]^T with both operands K-contiguous: A holds
 // activation rows, B a weight stored [out, in] ("Coming back to Failed Star",
@@ -14,8 +17,8 @@
 // buffers are four distinct LDS objects and the K loop is unrolled by four, so
 // every access names its buffer statically; the compiler's tracking of LDS DMA
 // then needs no blanket vmcnt(0) before each fragment read, and the one wait
-// per stage is the explicit vmcnt(16) (this wave's loads for stage k+1 done)
-// before the stage's single barrier.
+// per stage is the explicit vmcnt(8) (this wave's four loads for stage k+1
+// done) before the stage's single barrier.
 //
 // Bank conflicts.  A stage row is 32 bf16 = 64 B (four 16-B chunks).  Row R
 // stores its k-chunk c at chunk slot c ^ ((R >> 2) & 3): the 16 rows a
@@ -47,15 +50,17 @@ __shared__ __attribute__((aligned(1024))) bf16 g_stage3[STAGE];
 template <int S> __device__ __forceinline__ bf16* stage_buf() {
   return S == 0 ? g_stage0 : S == 1 ? g_stage1 : S == 2 ? g_stage2 : g_stage3;
 }
+// 16 KB of LDS for wave w's epilogue: half (w & 1) of stage buffer w >> 1
 __device__ __forceinline__ char* wave_region(int w) {
-  return reinterpret_cast<char*>(w == 0 ? g_stage0 : w == 1 ? g_stage1 : w == 2 ? g_stage2 : g_stage3);
+  char* b = reinterpret_cast<char*>((w >> 1) == 0 ? g_stage0 : (w >> 1) == 1 ? g_stage1 : (w >> 1) == 2 ? g_stage2 : g_stage3);
+  return b + (w & 1) * 16384;
 }
 
 template <int V> struct Ic { static constexpr int value = V; };
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt low bits [3:0], high bits [15:14];
 // expcnt [6:4]; lgkmcnt [11:8]).
-constexpr int WAIT_VM16_LGKM0 = (1 << 14) | 0x70;   // vmcnt(16) lgkmcnt(0)
+constexpr int WAIT_VM8_LGKM0 = 0x78;                // vmcnt(8) lgkmcnt(0)
 constexpr int WAIT_VM0_LGKM0 = 0x70;                // vmcnt(0) lgkmcnt(0)
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -63,65 +68,65 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 }  // namespace
 
 template <int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ A_lo,
-                     const bf16* __restrict__ B, int ldb, void* __restrict__ out, int ldc,
-                     int M, int N, int K, int tiles_n, int nblocks, const float* __restrict__ colscale) {
+                  const bf16* __restrict__ B, int ldb, void* __restrict__ out, int ldc,
+                  int M, int N, int K, int tiles_n, int nblocks, const float* __restrict__ colscale) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid >> 2, wn = wid & 3;
   // XCD-aware renumbering: the hardware deals workgroups round-robin over the
   // 8 XCDs; consecutive tiles (sharing A rows / B rows) go to one XCD's L2.
   int bid = blockIdx.x;
   if ((nblocks & 7) == 0) bid = (bid & 7) * (nblocks >> 3) + (bid >> 3);
   const int n0 = (bid % tiles_n) * TILE, m0 = (bid / tiles_n) * TILE;
 
-  // DMA assignment: wave w, instruction j fills tile rows (4w + j)*16 + lane/4
-  // (chunk slot lane % 4).  Rows past M / N re-read the last valid row; their
-  // results are never stored.
+  // DMA assignment: wave w, instruction j fills tile rows (2w + j)*16 + lane/4
+  // (chunk slot lane % 4) of A and of B.  Rows past M / N re-read the last
+  // valid row; their results are never stored.
   const int lr = lane >> 2;
   const int kc = (lane & 3) ^ ((lr >> 2) & 3);
-  const bf16* pa[4];
-  const bf16* pl[4];
-  const bf16* pb[4];
+  const bf16* pa[2];
+  const bf16* pl[2];
+  const bf16* pb[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ra = min(m0 + wid * 64 + j * 16 + lr, M - 1);
-    const int rb = min(n0 + wid * 64 + j * 16 + lr, N - 1);
+  for (int j = 0; j < 2; ++j) {
+    const int ra = min(m0 + wid * 32 + j * 16 + lr, M - 1);
+    const int rb = min(n0 + wid * 32 + j * 16 + lr, N - 1);
     pa[j] = A + (size_t)ra * lda + kc * 8;
     pl[j] = (A_lo != nullptr ? A_lo : A) + (size_t)ra * lda + kc * 8;
     pb[j] = B + (size_t)rb * ldb + kc * 8;
   }
   const int nk0 = K / DK;
-  const int nk = (A_lo != nullptr) ? 2 * nk0 : nk0;   // a multiple of 4
+  const int nk = (A_lo != nullptr) ? 2 * nk0 : nk0;
 
   auto issue = [&](auto Sc, int st) {
     bf16* L = stage_buf<decltype(Sc)::value>();
     const bool lo = st >= nk0;
     const int k0 = (lo ? st - nk0 : st) * DK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      __builtin_amdgcn_global_load_lds((lo ? pl[j] : pa[j]) + k0, L + (wid * 4 + j) * 16 * DK, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(pb[j] + k0, L + TILE * DK + (wid * 4 + j) * 16 * DK, 16, 0, 0);
+    for (int j = 0; j < 2; ++j) {
+      __builtin_amdgcn_global_load_lds((lo ? pl[j] : pa[j]) + k0, L + (wid * 2 + j) * 16 * DK, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(pb[j] + k0, L + TILE * DK + (wid * 2 + j) * 16 * DK, 16, 0, 0);
     }
   };
 
   const int lrow = lane & 31;
   const int sw = (lrow >> 2) & 3;
-  const int aoff = (wm * 128 + lrow) * DK, boff = TILE * DK + (wn * 128 + lrow) * DK;
+  const int aoff = (wm * 128 + lrow) * DK, boff = TILE * DK + (wn * 64 + lrow) * DK;
   const int so0 = ((lane >> 5) ^ sw) * 8, so1 = ((2 + (lane >> 5)) ^ sw) * 8;
-  bf16x8 fa[2][4], fb[2][4];
+  bf16x8 fa[2][4], fb[2][2];
   auto fread = [&](auto Sc, int set, int q) {
     const bf16* L = stage_buf<decltype(Sc)::value>();
     const int so = q ? so1 : so0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[set][i] = *reinterpret_cast<const bf16x8*>(L + aoff + i * 32 * DK + so);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(L + boff + j * 32 * DK + so);
+    for (int j = 0; j < 2; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(L + boff + j * 32 * DK + so);
   };
-  f32x16 acc[4][4];   // [n block][m block]
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -130,43 +135,42 @@ void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[j][i], 0, 0, 0);
   };
-
-  issue(Ic<0>{}, 0);
-  issue(Ic<1>{}, min(1, nk - 1));
-  issue(Ic<2>{}, min(2, nk - 1));
-  __builtin_amdgcn_s_waitcnt(WAIT_VM16_LGKM0);
-  lds_barrier();
-  fread(Ic<0>{}, 0, 0);
 
   // One stage: the loads of stage kt+3 (into the buffer read in stage kt-1),
   // then the two 16-wide K halves; the second half's fragments come from the
   // next stage, read after the barrier that publishes it.  Past the end the
   // ring re-reads the last stage into buffers nobody reads again, which keeps
   // the vmcnt bookkeeping uniform.
+  issue(Ic<0>{}, 0);
+  issue(Ic<1>{}, min(1, nk - 1));
+  issue(Ic<2>{}, min(2, nk - 1));
+  __builtin_amdgcn_s_waitcnt(WAIT_VM8_LGKM0);
+  lds_barrier();
+  fread(Ic<0>{}, 0, 0);
+
   auto step = [&](auto Cc, int kt) {
     constexpr int C = decltype(Cc)::value;
     issue(Ic<(C + 3) & 3>{}, min(kt + 3, nk - 1));
     fread(Ic<C>{}, 1, 1);
     mm(0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    __builtin_amdgcn_s_waitcnt(WAIT_VM16_LGKM0);
+    __builtin_amdgcn_s_waitcnt(WAIT_VM8_LGKM0);
     lds_barrier();
     fread(Ic<(C + 1) & 3>{}, 0, 0);
     mm(1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 6; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   };
   for (int kt = 0; kt < nk; kt += 4) {
@@ -176,18 +180,18 @@ void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict
     step(Ic<3>{}, kt + 3);
   }
 
-  // ---- epilogue: drain the ring, then each wave stages its 128x128 block in
-  // its own 32 KB of LDS and writes whole rows.
+  // ---- epilogue: drain the ring, then each wave stages its 128x64 block in
+  // its own 16 KB of LDS and writes whole rows.
   __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
   lds_barrier();
   char* R = wave_region(wid);
-  const int hl = lane >> 5;                 // which quad of the 8-column group
+  const int hl = lane >> 5;
   const int mrow0 = m0 + wm * 128;
-  const int ncol0 = n0 + wn * 128;
+  const int ncol0 = n0 + wn * 64;
   if (colscale != nullptr) {
     // per-column scale; columns past N (clamped reads) are never stored
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n = min(ncol0 + 32 * j + 8 * g + 4 * hl, N - 4);
@@ -200,63 +204,58 @@ void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict
   }
 
   if (EPI == GEPI_STORE_BF16) {
-    // 128 rows x 256 B; 16-B chunk c of row m at slot c ^ (m & 15)
+    // 128 rows x 128 B; chunk c of row m at slot c ^ (m & 7)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = i * 32 + lrow;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           bf16x4 v;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[j][i][4 * g + e];
           const int c = j * 4 + g;
-          *reinterpret_cast<bf16x4*>(R + m * 256 + ((c ^ (m & 15)) << 4) + hl * 8) = v;
-        }
-    }
-    bf16* o = reinterpret_cast<bf16*>(out);
-    const int c = lane & 15;
-#pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-      const int m = it * 4 + (lane >> 4);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(R + m * 256 + ((c ^ (m & 15)) << 4));
-      const int gm = mrow0 + m, gn = ncol0 + c * 8;
-      if (gm < M && gn < N) *reinterpret_cast<u32x4*>(o + (size_t)gm * ldc + gn) = v;
-    }
-  } else if (EPI == GEPI_SWIGLU_BF16) {
-    // the wave's 128 packed columns are two [32 gate | 32 up] pairs -> 64 outputs;
-    // 128 rows x 128 B, chunk c of row m at slot c ^ (m & 7)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = i * 32 + lrow;
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = (bf16)(silu(acc[2 * p][i][4 * g + e]) * acc[2 * p + 1][i][4 * g + e]);
-          const int c = p * 4 + g;
           *reinterpret_cast<bf16x4*>(R + m * 128 + ((c ^ (m & 7)) << 4) + hl * 8) = v;
         }
     }
     bf16* o = reinterpret_cast<bf16*>(out);
     const int c = lane & 7;
-    const int f0 = ncol0 / 2, nf = N / 2;
 #pragma unroll 4
     for (int it = 0; it < 16; ++it) {
       const int m = it * 8 + (lane >> 3);
       const u32x4 v = *reinterpret_cast<const u32x4*>(R + m * 128 + ((c ^ (m & 7)) << 4));
+      const int gm = mrow0 + m, gn = ncol0 + c * 8;
+      if (gm < M && gn < N) *reinterpret_cast<u32x4*>(o + (size_t)gm * ldc + gn) = v;
+    }
+  } else if (EPI == GEPI_SWIGLU_BF16) {
+    // the wave's 64 packed columns are one [32 gate | 32 up] pair -> 32 outputs;
+    // 128 rows x 64 B, chunk c of row m at slot c ^ (m & 3)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = i * 32 + lrow;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(silu(acc[0][i][4 * g + e]) * acc[1][i][4 * g + e]);
+        *reinterpret_cast<bf16x4*>(R + m * 64 + ((g ^ (m & 3)) << 4) + hl * 8) = v;
+      }
+    }
+    bf16* o = reinterpret_cast<bf16*>(out);
+    const int c = lane & 3;
+    const int f0 = ncol0 / 2, nf = N / 2;
+#pragma unroll 4
+    for (int it = 0; it < 8; ++it) {
+      const int m = it * 16 + (lane >> 2);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(R + m * 64 + ((c ^ (m & 3)) << 4));
       const int gm = mrow0 + m, f = f0 + c * 8;
       if (gm < M && f < nf) *reinterpret_cast<u32x4*>(o + (size_t)gm * ldc + f) = v;
     }
   } else {
-    // fp32 (STORE_F32 / RESID_F32): two passes of 64 rows x 512 B;
-    // 16-B chunk c of row m at slot c ^ (m & 31)
+    // fp32: two passes of 64 rows x 256 B; chunk cc of row m at slot cc ^ (m & 15)
     float* o = reinterpret_cast<float*>(out);
-    const int c = lane & 31;
+    const int c = lane & 15;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -264,32 +263,30 @@ void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict
         const int i = 2 * h + ii;
         const int m = ii * 32 + lrow;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             f32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * g + e];
             const int cc = j * 8 + 2 * g + hl;
-            *reinterpret_cast<f32x4*>(R + m * 512 + ((cc ^ (m & 31)) << 4)) = v;
+            *reinterpret_cast<f32x4*>(R + m * 256 + ((cc ^ (m & 15)) << 4)) = v;
           }
       }
       const int gn = ncol0 + c * 4, gnc = min(gn, N - 4);
-      for (int it0 = 0; it0 < 32; it0 += 8) {
-        // the residual reads of 8 rows go out together (clamped addresses are
-        // always valid), then the sums are stored where the row is in range
-        f32x4 old[8];
+      for (int it0 = 0; it0 < 16; it0 += 4) {
+        f32x4 old[4];
         if (EPI == GEPI_RESID_F32) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int gmc = min(mrow0 + h * 64 + (it0 + u) * 2 + (lane >> 5), M - 1);
+          for (int u = 0; u < 4; ++u) {
+            const int gmc = min(mrow0 + h * 64 + (it0 + u) * 4 + (lane >> 4), M - 1);
             old[u] = *reinterpret_cast<const f32x4*>(o + (size_t)gmc * ldc + gnc);
           }
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int m = (it0 + u) * 2 + (lane >> 5);
-          f32x4 v = *reinterpret_cast<const f32x4*>(R + m * 512 + ((c ^ (m & 31)) << 4));
+        for (int u = 0; u < 4; ++u) {
+          const int m = (it0 + u) * 4 + (lane >> 4);
+          f32x4 v = *reinterpret_cast<const f32x4*>(R + m * 256 + ((c ^ (m & 15)) << 4));
           const int gm = mrow0 + h * 64 + m;
           if (EPI == GEPI_RESID_F32) v += old[u];
           if (gm < M && gn < N) *reinterpret_cast<f32x4*>(o + (size_t)gm * ldc + gn) = v;
@@ -323,16 +320,16 @@ hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, voi
   const bf16* al = (const bf16*)A_lo;
   switch (epi) {
     case GEPI_STORE_BF16:
-      gemm_dma_kernel<GEPI_STORE_BF16><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
+      gemm_dma_kernel<GEPI_STORE_BF16><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
       break;
     case GEPI_RESID_F32:
-      gemm_dma_kernel<GEPI_RESID_F32><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
+      gemm_dma_kernel<GEPI_RESID_F32><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
       break;
     case GEPI_SWIGLU_BF16:
-      gemm_dma_kernel<GEPI_SWIGLU_BF16><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
+      gemm_dma_kernel<GEPI_SWIGLU_BF16><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
       break;
     case GEPI_STORE_F32:
-      gemm_dma_kernel<GEPI_STORE_F32><<<nb, 256, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
+      gemm_dma_kernel<GEPI_STORE_F32><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
       break;
     default:
       return hipErrorInvalidValue;
