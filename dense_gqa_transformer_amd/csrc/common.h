@@ -19,25 +19,57 @@ template <class T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
+// Cross-lane reductions on DPP row operations (no LDS round trip): within an
+// aligned row of 16 lanes, exchange with lane ^ 1 and lane ^ 2 (quad
+// permutes), then with the mirrored lane of the half row and of the row, so
+// every lane of the row ends with the row's total; whole-wave results add the
+// four row totals read from lanes 0, 16, 32 and 48.  Every lane of the wave
+// (or row) must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);     // quad_perm(1, 0, 3, 2)
+  v += dpp_f<0x4E>(v);     // quad_perm(2, 3, 0, 1)
+  v += dpp_f<0x141>(v);    // row_half_mirror
+  v += dpp_f<0x140>(v);    // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 // Sum over the 64 lanes of a wave (every lane receives the total).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v = row16_sum(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
 // Sum over aligned groups of `W` lanes (W a power of two <= 64).
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
+  if constexpr (W == 16) {
+    return row16_sum(v);
+  } else if constexpr (W == 64) {
+    return wave_sum(v);
+  } else {
 #pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+  }
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = row16_max(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // Loads 8 consecutive elements as fp32 (16 B for bf16, 32 B for fp32).
