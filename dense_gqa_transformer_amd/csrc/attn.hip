@@ -168,19 +168,22 @@ struct SoftState {
       m[r] = mn;
     }
   }
-  // merge with the state held `off` lanes away (xor)
-  __device__ __forceinline__ void merge_xor(int off) {
+  // merge with the state held OFF lanes away (xor; 16 or 32)
+  template <int OFF>
+  __device__ __forceinline__ void merge_xor() {
+    static_assert(OFF == 16 || OFF == 32, "row-pair or half-wave exchange");
+    auto other = [](float v) { return OFF == 16 ? xor16_f(v) : xor32_f(v); };
 #pragma unroll
     for (int r = 0; r < REP; ++r) {
-      const float mo = __shfl_xor(m[r], off);
-      const float lo = __shfl_xor(l[r], off);
+      const float mo = other(m[r]);
+      const float lo = other(l[r]);
       const float mn = fmaxf(m[r], mo);
       const float a = (m[r] == -INFINITY) ? 0.f : exp2f(m[r] - mn);
       const float b = (mo == -INFINITY) ? 0.f : exp2f(mo - mn);
       l[r] = l[r] * a + lo * b;
 #pragma unroll
       for (int e = 0; e < DP; ++e) {
-        const float oo = __shfl_xor(o[r][e], off);
+        const float oo = other(o[r][e]);
         o[r][e] = o[r][e] * a + oo * b;
       }
       m[r] = mn;
@@ -339,8 +342,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
     if (!step(i, pk[0], pv[0])) break;
     if (!step(i + 1, pk[1], pv[1])) break;
   }
-  st.merge_xor(16);
-  st.merge_xor(32);
+  st.template merge_xor<16>();
+  st.template merge_xor<32>();
   if (lane < 16) {
 #pragma unroll
     for (int r = 0; r < REP; ++r) {
@@ -489,8 +492,8 @@ __global__ __launch_bounds__(256) void attn_prefill_vec_kernel(const AttnPrefill
   SoftState<1, DP> st;
   st.init();
   attend<KV, D, 1>(st, q, kb, vb, 0, t + 1, 4, grp, li, -1, nullptr, nullptr);
-  st.merge_xor(16);
-  st.merge_xor(32);
+  st.template merge_xor<16>();
+  st.template merge_xor<32>();
   if (lane < 16) {
     TO* o = reinterpret_cast<TO*>(p.out) + qrow;
     const float inv = 1.f / st.l[0];

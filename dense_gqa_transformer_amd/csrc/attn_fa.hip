@@ -185,7 +185,7 @@ void attn_prefill_fa_kernel(const AttnPrefillParams p, const bf16* __restrict__ 
       mb = fmax3(mb, sv[1][r], sv[1][r + 1]);
     }
     const float mt = fmax3(ma, mb, fmaxf(sv[0][15], sv[1][15]));
-    return fmaxf(mt, __shfl_xor(mt, 32));   // relative to m_run
+    return pair32_max(mt);   // relative to m_run
   };
   // move m_run when the tile's max (relative to it) exceeds FLAZY, or always
   // for the first tile; the unexponentiated tile sv follows the move
@@ -215,7 +215,7 @@ void attn_prefill_fa_kernel(const AttnPrefillParams p, const bf16* __restrict__ 
         ls += e;
         pb[kb * 2 + (r >> 3)][r & 7] = (bf16)e;
       }
-    l_run += ls + __shfl_xor(ls, 32);
+    l_run += pair32_sum(ls);
   };
   // O^T += V^T . P^T over the tile in buffer C
   auto pv = [&](auto Cc) {

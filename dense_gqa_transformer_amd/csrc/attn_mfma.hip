@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_prefill_mfma_kernel(const Attn
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[kb][r], s[kb][r + 1]));
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
+    mt = pair32_max(mt) * c2;
     if (mt > m_run + LAZY_MAX) {             // rare after the first tile
       const float corr = __builtin_amdgcn_exp2f(m_run - mt);
       l_run *= corr;
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_prefill_mfma_kernel(const Attn
         s[kb][r] = e;
         ls += e;
       }
-    l_run += ls + __shfl_xor(ls, 32);
+    l_run += pair32_sum(ls);
 
     // ---- O^T += V^T . P^T over four 16-key steps
 #pragma unroll

@@ -22,9 +22,9 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 // Cross-lane reductions on DPP row operations (no LDS round trip): within an
 // aligned row of 16 lanes, exchange with lane ^ 1 and lane ^ 2 (quad
 // permutes), then with the mirrored lane of the half row and of the row, so
-// every lane of the row ends with the row's total; whole-wave results add the
-// four row totals read from lanes 0, 16, 32 and 48.  Every lane of the wave
-// (or row) must be active.
+// every lane of the row ends with the row's total; whole-wave results then
+// combine row pairs and wave halves with the permlane swaps below.  Every lane
+// of the wave (or row) must be active.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
@@ -43,14 +43,41 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_f<0x140>(v));
   return v;
 }
-__device__ __forceinline__ float lane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+// Across rows, v_permlane16_swap / v_permlane32_swap (gfx950) with both
+// operands v return, in every lane, the two values of its xor-16 (xor-32) pair:
+// first the lower lane's, then the upper lane's.
+struct LanePair { float lo, hi; };
+__device__ __forceinline__ LanePair pair16(float v) {
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(q[0]), __uint_as_float(q[1])};
+}
+__device__ __forceinline__ LanePair pair32(float v) {
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(q[0]), __uint_as_float(q[1])};
+}
+// the value held by lane ^ 16 / lane ^ 32
+__device__ __forceinline__ float xor16_f(float v) {
+  const LanePair p = pair16(v);
+  return (__lane_id() & 16) ? p.lo : p.hi;
+}
+__device__ __forceinline__ float xor32_f(float v) {
+  const LanePair p = pair32(v);
+  return (__lane_id() & 32) ? p.lo : p.hi;
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+  const LanePair p = pair32(v);
+  return p.lo + p.hi;
+}
+__device__ __forceinline__ float pair32_max(float v) {
+  const LanePair p = pair32(v);
+  return fmaxf(p.lo, p.hi);
 }
 
 // Sum over the 64 lanes of a wave (every lane receives the total).
 __device__ __forceinline__ float wave_sum(float v) {
   v = row16_sum(v);
-  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+  const LanePair r = pair16(v);
+  return pair32_sum(r.lo + r.hi);
 }
 
 // Sum over aligned groups of `W` lanes (W a power of two <= 64).
@@ -69,7 +96,8 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float wave_max(float v) {
   v = row16_max(v);
-  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+  const LanePair r = pair16(v);
+  return pair32_max(fmaxf(r.lo, r.hi));
 }
 
 // Loads 8 consecutive elements as fp32 (16 B for bf16, 32 B for fp32).
