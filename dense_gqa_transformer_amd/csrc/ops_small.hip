@@ -153,35 +153,61 @@ hipError_t codes_to_bf16(const int8_t* codes, size_t n, void* dst, hipStream_t s
 // x / sqrt(mean(x^2) + eps) * g over one row ("Failed Star (fs)", How it's built).
 // With `lo` set (bf16 output only) the value is also split: out = bf16(y),
 // lo = bf16(y - out), so that out + lo carries y to about 16 significant bits.
-template <typename O>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int H, int ldx,
+// One wave per row: lane l holds the 16-byte chunks l, l + 64, ... of the row
+// in registers (one read of x), the mean square is one wave sum, and the
+// outputs leave as 8- or 16-byte stores.
+template <typename O, int MAXJ>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int T, int H, int ldx,
                                                       const float* __restrict__ g, float eps,
                                                       O* __restrict__ out, O* __restrict__ lo, int ldo) {
-  __shared__ float sh[4];
-  const float* row = x + (size_t)blockIdx.x * ldx;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= T) return;
+  const float* row = x + (size_t)r * ldx;
+  const int nc = H >> 2;
+  f32x4 v[MAXJ];
   float ss = 0.f;
-  for (int k = threadIdx.x; k < H; k += 256) {
-    float v = row[k];
-    ss += v * v;
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int c = lane + 64 * j;
+    v[j] = (c < nc) ? *reinterpret_cast<const f32x4*>(row + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss = fmaf(v[j][e], v[j][e], ss);
   }
-  ss = block_sum256(ss, sh);
-  const float inv = rsqrtf(ss / (float)H + eps);
-  O* o = out + (size_t)blockIdx.x * ldo;
-  for (int k = threadIdx.x; k < H; k += 256) {
-    const float y = row[k] * inv * g[k];
-    const O hi = from_f32<O>(y);
-    o[k] = hi;
-    if (lo != nullptr) lo[(size_t)blockIdx.x * ldo + k] = from_f32<O>(y - to_f32(hi));
+  const float inv = rsqrtf(wave_sum(ss) / (float)H + eps);
+  O* o = out + (size_t)r * ldo;
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int c = lane + 64 * j;
+    if (c >= nc) break;
+    const f32x4 gg = *reinterpret_cast<const f32x4*>(g + 4 * c);
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = v[j][e] * inv * gg[e];
+    if constexpr (sizeof(O) == 2) {
+      bf16x4 hi, rem;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = (bf16)y[e];
+        rem[e] = (bf16)(y[e] - (float)hi[e]);
+      }
+      *reinterpret_cast<bf16x4*>(o + 4 * c) = hi;
+      if (lo != nullptr) *reinterpret_cast<bf16x4*>(lo + (size_t)r * ldo + 4 * c) = rem;
+    } else {
+      *reinterpret_cast<f32x4*>(o + 4 * c) = f32x4{y[0], y[1], y[2], y[3]};
+    }
   }
 }
 
 hipError_t rmsnorm(const float* x, int T, int H, int ldx, const float* g, float eps, void* out,
                    int out_dt, int ldo, hipStream_t s, void* lo) {
   if (T <= 0) return hipSuccess;
+  if (H % 4 != 0 || H > 4096 || ldx % 4 != 0 || ldo % 4 != 0) return hipErrorInvalidValue;
+  const int blocks = (T + 3) / 4;
   if (out_dt == DT_BF16)
-    rmsnorm_kernel<bf16><<<T, 256, 0, s>>>(x, H, ldx, g, eps, (bf16*)out, (bf16*)lo, ldo);
+    rmsnorm_kernel<bf16, 16><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, (bf16*)lo, ldo);
   else if (lo == nullptr)
-    rmsnorm_kernel<float><<<T, 256, 0, s>>>(x, H, ldx, g, eps, (float*)out, nullptr, ldo);
+    rmsnorm_kernel<float, 16><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (float*)out, nullptr, ldo);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
