@@ -5,10 +5,13 @@
 // registers.
 //
 // Work split.  A workgroup takes 128 queries of the two query heads that share
-// one KV head: 4 waves, one per SIMD; wave w owns 64 queries (two 32-column
-// blocks) of head 2y + w/2.  Owning 64 queries means every K or V fragment a
-// wave reads from LDS feeds two MFMAs, which halves LDS traffic per MFMA
-// compared with 32-query waves.
+// one KV head: 8 waves, two per SIMD; wave w owns 32 queries (one 32-column
+// block) of head 2y + w/4, so the two waves on a SIMD overlap one's
+// exponentials with the other's products.  Each wave reads 32 KB of K and V
+// fragments from LDS per 64-key tile for 32 MFMAs, which puts the tile loop
+// close to the LDS bandwidth (a 64-query wave would halve that traffic but
+// needs about twice the registers, leaving one wave per SIMD, which measured
+// slower).
 //
 // Staging.  The K and V tiles (64 keys x 128 d, 16 KB each) go from HBM
 // straight into LDS with global_load_lds through a ring of four stage buffers
