@@ -155,17 +155,24 @@ struct SoftState {
       for (int e = 0; e < DP; ++e) o[r][e] = 0.f;
     }
   }
-  // fold one key position: s[r] = base-2 score, v = this lane's value slice
+  // fold one key position: s[r] = base-2 score, v = this lane's value slice.
+  // The reference m only moves when a score exceeds it by more than 2^8 (and
+  // on the first position, where m is -inf), so the accumulators are rarely
+  // rescaled; l and o use the same m, so the final o / l is unchanged.
   __device__ __forceinline__ void add(const float* s, const float* v) {
 #pragma unroll
     for (int r = 0; r < REP; ++r) {
-      const float mn = fmaxf(m[r], s[r]);
-      const float corr = exp2f(m[r] - mn);
-      const float pp = exp2f(s[r] - mn);
-      l[r] = l[r] * corr + pp;
+      if (s[r] > m[r] + 8.f) {
+        const float corr = __builtin_amdgcn_exp2f(m[r] - s[r]);   // 0 while m is -inf
+        l[r] *= corr;
 #pragma unroll
-      for (int e = 0; e < DP; ++e) o[r][e] = o[r][e] * corr + pp * v[e];
-      m[r] = mn;
+        for (int e = 0; e < DP; ++e) o[r][e] *= corr;
+        m[r] = s[r];
+      }
+      const float pp = __builtin_amdgcn_exp2f(s[r] - m[r]);
+      l[r] += pp;
+#pragma unroll
+      for (int e = 0; e < DP; ++e) o[r][e] = fmaf(pp, v[e], o[r][e]);
     }
   }
   // merge with the state held OFF lanes away (xor; 16 or 32)
