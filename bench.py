@@ -63,8 +63,11 @@ def decode_label_bytes(shape, label, ctx):
         return V * H * es + 4 * H
     if label == "attn":     # K and V of ctx positions of all KV heads + new k/v written
         return 2 * kvw * es * ctx + 2 * kvw * es + 4 * (qw + 2 * kvw)
-    if label == "combine":  # one (o[d], m, l) partial per 32-position chunk and head, output row
-        return 4 * shape.n_heads * (d + 2) * -(-ctx // 32) + 4 * qw
+    if label == "combine":  # one (o[d], m, l) partial per chunk and head, output row
+        chunk = 32                                   # at most 32 chunks, up to 256 positions each
+        while chunk < 256 and -(-ctx // chunk) > 32:
+            chunk *= 2
+        return 4 * shape.n_heads * (d + 2) * -(-ctx // chunk) + 4 * qw
     return None
 
 
@@ -456,8 +459,16 @@ def main():
 
     # per-launch duration of each decode kernel class, replayed back to back in
     # a graph over the 28 layers' own weights (HIP events on the library's stream)
+    # (the merge launch only where the step at this context runs the split form)
+    model.timing(True)
+    model.decode_step(nxt, [P + steps], [2], next_ids=nxt)
+    torch.cuda.synchronize()
+    merges = model.timing_read("combine")[1]
+    model.timing(False)
     per_launch = {}
     for lab in ("qkv", "attn", "combine", "o_proj", "gate_up", "down", "head"):
+        if lab == "combine" and not merges:
+            continue
         per_launch[lab] = model.kernel_bench(lab, reps=20, slot=4, position=P + steps // 2)
     launches = {lab: (1 if lab == "head" else shape.n_layers) for lab in per_launch}
     dom = max(per_launch, key=lambda k: per_launch[k] * launches[k])

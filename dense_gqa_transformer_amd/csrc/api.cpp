@@ -135,6 +135,10 @@ struct fs_model {
   hipStream_t cap_stream = nullptr;
   std::vector<DecodeGraph> graphs;
   bool use_graphs = true;
+  // decode attention form: 0 chosen per step, 1 always split-K, 2 one pass where it exists
+  int attn_mode = 0;
+  // shortest split-K chunk (positions per workgroup)
+  int min_chunk = 32;
   // measurement hook: per-launch event pairs, labelled by step
   bool timing = false;
   std::vector<TimedLaunch> timed;
@@ -549,6 +553,14 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   {
     const char* env = std::getenv("FS_DECODE_GRAPHS");
     if (env != nullptr && env[0] == '0') m->use_graphs = false;
+    const char* am = std::getenv("FS_DECODE_ATTN");
+    if (am != nullptr && std::strcmp(am, "split") == 0) m->attn_mode = 1;
+    if (am != nullptr && std::strcmp(am, "onepass") == 0) m->attn_mode = 2;
+    const char* mc = std::getenv("FS_DECODE_MIN_CHUNK");
+    if (mc != nullptr) {
+      const int v = std::atoi(mc);
+      if (v == 32 || v == 64 || v == 128 || v == 256) m->min_chunk = v;
+    }
   }
   chk(hipStreamSynchronize(s));
   if (e != hipSuccess) return bail(FS_ERR_HIP, std::string("model setup failed: ") + hipGetErrorString(e));
@@ -625,9 +637,45 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
   return FS_OK;
 }
 
+// How the decode attention covers the context (longest sequence maxn keys).
+// Short contexts at small batch take the one-pass kernel: one 16-wave
+// workgroup per (sequence, KV head) and no merge launch (one CU streams the
+// head's whole context at ~60 GB/s, so this pays only below ~180 keys).
+// Otherwise split-K chunks of at least min_chunk positions, doubled (up to
+// 256) while a sequence would need more than 32 chunks (the merge reads up to
+// 32 partials in one round trip and loops beyond) or the launch would exceed
+// 1024 workgroups; with pow2 the chunk count is rounded up to a power of two
+// (chunks past a sequence's end exit at once) so one captured graph serves
+// many consecutive positions.
+constexpr int ONEPASS_MAX_CTX = 128;
+constexpr int SPLIT_MAX_CHUNKS = 32;
+constexpr int ONEPASS_MAX_GROUPS = 64;      // B * n_kv_heads
+struct AttnSplit {
+  int chunk, nchunks;
+  bool onepass;
+};
+static AttnSplit attn_split(const fs_model* m, int B, int maxn, bool pow2, int mode) {
+  const fs_config& c = m->cfg;
+  const bool can1 = attn_decode_onepass_ok(c.n_heads, c.n_kv_heads, c.head_dim);
+  const bool one = can1 && (mode == 2 || (mode == 0 && maxn <= ONEPASS_MAX_CTX &&
+                                          (long long)B * c.n_kv_heads <= ONEPASS_MAX_GROUPS));
+  if (one) return {0, 1, true};
+  int chunk = m->min_chunk;
+  while (chunk < 256 && ((maxn + chunk - 1) / chunk > SPLIT_MAX_CHUNKS ||
+                         (long long)((maxn + chunk - 1) / chunk) * c.n_kv_heads * B > 1024))
+    chunk *= 2;
+  int nchunks = (maxn + chunk - 1) / chunk;
+  if (pow2) {
+    int p2 = 1;
+    while (p2 < nchunks) p2 *= 2;
+    nchunks = std::min(p2, (c.max_ctx + chunk - 1) / chunk);
+  }
+  return {chunk, nchunks, false};
+}
+
 // Every kernel of one decode step, in order, on stream s.
 static fs_status enqueue_decode(fs_model* m, const int32_t* tokens, int B, float* logits, int32_t* next,
-                                int chunk, int nchunks, hipStream_t s) {
+                                const AttnSplit& sp, hipStream_t s) {
   const fs_config& c = m->cfg;
   if (m->timing) LAUNCH(m, "gate", s, spin_wait(TIMING_GATE_US, s));
   LAUNCH(m, "embed", s, embed(m->embed, m->wdt, tokens, B, c.hidden, c.vocab, m->x, s, m->embed_scale));
@@ -643,13 +691,15 @@ static fs_status enqueue_decode(fs_model* m, const int32_t* tokens, int B, float
       a.gq = L.q_norm; a.gk = L.k_norm; a.eps = c.rms_eps;
       a.cos_t = m->rope_cos; a.sin_t = m->rope_sin; a.positions = m->d_pos; a.slots = m->d_slot;
       a.part = m->part;
-      a.B = B; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim; a.chunk = chunk; a.nchunks = nchunks;
+      a.out = sp.onepass ? m->attn : nullptr; a.o_dt = skinny ? DT_F32 : DT_BF16;
+      a.B = B; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim; a.chunk = sp.chunk; a.nchunks = sp.nchunks;
       a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
       a.scale = 1.0f / std::sqrt((float)c.head_dim);
       a.rot = m->rot; a.gated = m->gated;
       LAUNCH(m, "attn", s, attn_decode(a, s));
-      LAUNCH(m, "combine", s, attn_combine(m->part, m->d_pos, B, c.n_heads, c.head_dim, chunk, nchunks,
-                                           m->attn, skinny ? DT_F32 : DT_BF16, s));
+      if (!sp.onepass)
+        LAUNCH(m, "combine", s, attn_combine(m->part, m->d_pos, B, c.n_heads, c.head_dim, sp.chunk, sp.nchunks,
+                                             m->attn, skinny ? DT_F32 : DT_BF16, s));
       if (m->gated)
         LAUNCH(m, "attn_gate", s, attn_gate(m->attn, skinny ? DT_F32 : DT_BF16, m->qkv, DT_F32, B, c.n_heads,
                                        c.head_dim, m->qkv_w, s));
@@ -684,19 +734,13 @@ fs_status fs_decode_step(fs_model* m, const int32_t* tokens, const int32_t* posi
   if ((st = ensure_rows(m, B, s)) != FS_OK) return st;
   if (B > GEMV_LOGITS_MAX_M && logits == nullptr && (st = ensure_logits_tmp(m)) != FS_OK) return st;
   if ((st = stage_ints(m, positions, slots, B, s)) != FS_OK) return st;
-  // split-K chunking of the context: enough workgroups to cover the chip.  The
-  // chunk count is rounded up to a power of two (chunks past a sequence's end
-  // exit at once) so one captured graph serves many consecutive positions.
-  int chunk = 32;
-  while (chunk < 256 && (long long)((maxn + chunk - 1) / chunk) * c.n_kv_heads * B > 1024) chunk *= 2;
-  int nchunks = 1;
-  while (nchunks < (maxn + chunk - 1) / chunk) nchunks *= 2;
-  nchunks = std::min(nchunks, (c.max_ctx + chunk - 1) / chunk);
-  if (nchunks > m->max_chunks) return fail(FS_ERR_HIP, "internal: chunk count exceeds scratch");
+  const AttnSplit sp = attn_split(m, B, maxn, true, m->attn_mode);
+  if (sp.nchunks > m->max_chunks) return fail(FS_ERR_HIP, "internal: chunk count exceeds scratch");
   if (!m->use_graphs || m->timing) {
-    if ((st = enqueue_decode(m, tokens, B, logits, next, chunk, nchunks, s)) != FS_OK) return st;
+    if ((st = enqueue_decode(m, tokens, B, logits, next, sp, s)) != FS_OK) return st;
   } else {
-    const DecodeKey key{B, chunk, nchunks, tokens, logits, next};
+    // the one-pass form is keyed as chunk 0 and serves every maxn it covers
+    const DecodeKey key{B, sp.chunk, sp.nchunks, tokens, logits, next};
     DecodeGraph* g = nullptr;
     for (auto& e : m->graphs)
       if (e.key == key) { g = &e; break; }
@@ -707,7 +751,7 @@ fs_status fs_decode_step(fs_model* m, const int32_t* tokens, const int32_t* posi
       }
       DecodeGraph ng{key, nullptr, nullptr};
       HIP_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeRelaxed));
-      st = enqueue_decode(m, tokens, B, logits, next, chunk, nchunks, m->cap_stream);
+      st = enqueue_decode(m, tokens, B, logits, next, sp, m->cap_stream);
       const hipError_t ec = hipStreamEndCapture(m->cap_stream, &ng.graph);
       if (st != FS_OK) {
         if (ng.graph) hipGraphDestroy(ng.graph);
@@ -734,7 +778,10 @@ fs_status fs_kernel_bench(fs_model* m, const char* label, int32_t slot, int32_t 
   if (m == nullptr || label == nullptr || avg_us == nullptr || reps <= 0)
     return fail(FS_ERR_INVALID_ARG, "NULL argument or reps <= 0");
   const fs_config& c = m->cfg;
-  const bool is_attn = std::strcmp(label, "attn") == 0;
+  // "attn": the form a batch-1 decode step at this position takes; "attn_split"
+  // and "attn_onepass" force one; "combine": the merge launch of the split form
+  const bool is_attn = std::strcmp(label, "attn") == 0 || std::strcmp(label, "attn_split") == 0 ||
+                       std::strcmp(label, "attn_onepass") == 0;
   if ((is_attn || std::strcmp(label, "combine") == 0) && (slot < 0 || slot >= c.max_seqs || position < 0 || position >= c.max_ctx))
     return fail(FS_ERR_INVALID_ARG, "bad slot or position");
   if (c.n_layers == 0 && std::strcmp(label, "head") != 0) return fail(FS_ERR_INVALID_ARG, "model has no layers");
@@ -743,9 +790,12 @@ fs_status fs_kernel_bench(fs_model* m, const char* label, int32_t slot, int32_t 
   if (st != FS_OK) return st;
   int32_t pos_h[1] = {position}, slot_h[1] = {is_attn ? slot : 0};
   if ((st = stage_ints(m, pos_h, slot_h, 1, s)) != FS_OK) return st;
-  int chunk = 32;
-  while (chunk < 256 && (long long)((position + chunk) / chunk) * c.n_kv_heads > 1024) chunk *= 2;
-  const int nchunks = (position + chunk) / chunk;
+  const int mode = std::strcmp(label, "attn_split") == 0 || std::strcmp(label, "combine") == 0 ? 1
+                   : std::strcmp(label, "attn_onepass") == 0                                   ? 2
+                                                                                               : m->attn_mode;
+  if (mode == 2 && !attn_decode_onepass_ok(c.n_heads, c.n_kv_heads, c.head_dim))
+    return fail(FS_ERR_UNSUPPORTED, "no one-pass decode attention for this head shape");
+  const AttnSplit sp = attn_split(m, 1, position + 1, false, mode);
   // one launch per layer (the layer's own weights), `reps` passes over the layers
   auto launch_one = [&](int l, hipStream_t ls) -> fs_status {
     const LayerW& L = m->layers[l];
@@ -779,12 +829,13 @@ fs_status fs_kernel_bench(fs_model* m, const char* label, int32_t slot, int32_t 
       a.kv_dt = m->dt; a.gq = L.q_norm; a.gk = L.k_norm; a.eps = c.rms_eps;
       a.cos_t = m->rope_cos; a.sin_t = m->rope_sin; a.positions = m->d_pos; a.slots = m->d_slot;
       a.part = m->part; a.B = 1; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim;
-      a.chunk = chunk; a.nchunks = nchunks; a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
+      a.out = sp.onepass ? m->attn : nullptr; a.o_dt = DT_F32;
+      a.chunk = sp.chunk; a.nchunks = sp.nchunks; a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
       a.scale = 1.0f / std::sqrt((float)c.head_dim);
       a.rot = m->rot; a.gated = m->gated;
       HIP_TRY(attn_decode(a, ls));
     } else if (std::strcmp(label, "combine") == 0) {
-      HIP_TRY(attn_combine(m->part, m->d_pos, 1, c.n_heads, c.head_dim, chunk, nchunks, m->attn, DT_F32, ls));
+      HIP_TRY(attn_combine(m->part, m->d_pos, 1, c.n_heads, c.head_dim, sp.chunk, sp.nchunks, m->attn, DT_F32, ls));
     } else {
       return fail(FS_ERR_INVALID_ARG, std::string("unknown label ") + label);
     }

@@ -16,7 +16,11 @@
 // first `rot` dims; q rows interleaved with gate rows when the variant is
 // gated) and appends k, v to the cache (fused), and writes the chunk's
 // partial softmax state; the partials are combined by the consumer (split-K
-// flash decoding).
+// flash decoding).  One-pass form, for short contexts at small batch: one
+// workgroup of 16 waves per (sequence, KV head) walks the whole context, the
+// 16 wave states merge in LDS and the normalised output is written directly,
+// which saves the merge launch (a few microseconds) at the price of streaming
+// each KV head's context through one CU.
 #include "common.h"
 #include "kernels.h"
 
@@ -231,13 +235,17 @@ __device__ __forceinline__ void attend(SoftState<REP, D / 16>& st, const float (
 }
 
 // ------------------------------------------------------------------ decode
-template <typename KV, int D, int REP>
-__global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams p) {
+// ONE: the one-pass form (16 waves, the whole context, output written to
+// p.out); otherwise 4 waves per chunk writing partials.
+template <typename KV, int D, int REP, bool ONE>
+__global__ __launch_bounds__(ONE ? 1024 : 256) void attn_decode_kernel(const AttnDecodeParams p) {
   constexpr int DP = D / 16;
+  constexpr int NW = ONE ? 16 : 4;                      // waves
+  constexpr int STEP = 4 * NW;                          // positions per step of the workgroup
   __shared__ float qs[REP][D];
   __shared__ float knew[D], vnew[D];
-  __shared__ float sm[4][REP], sl[4][REP];
-  __shared__ float so[4][REP][D];
+  __shared__ float sm[NW][REP], sl[NW][REP];
+  __shared__ float so[NW][REP][D];
 
   constexpr int NPRE = 2;                               // key rows per lane in flight
   const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -246,9 +254,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
   const int pos = p.positions[b];
   const int slot = p.slots[b];
   const int n = pos + 1;
-  const int c0 = c * p.chunk;
+  const int c0 = ONE ? 0 : c * p.chunk;
   if (c0 >= n) return;                                  // chunk past this sequence
-  const int c1 = min(c0 + p.chunk, n);
+  const int c1 = ONE ? n : min(c0 + p.chunk, n);
   const int qmul = p.gated ? 2 : 1;                      // q rows interleaved with gate rows
   const int W = (p.nq * qmul + 2 * p.nkv) * D;
   const float* row = p.qkv + (size_t)b * W;
@@ -265,7 +273,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
   RawKV<KV, DP> pk[NPRE], pv[NPRE];
 #pragma unroll
   for (int i = 0; i < NPRE; ++i) {
-    const int u = min(ufirst + 16 * i, c1 - 1);
+    const int u = min(ufirst + STEP * i, c1 - 1);
     pk[i].load(kb + (size_t)u * D + li * DP);
     pv[i].load(vb + (size_t)u * D + li * DP);
   }
@@ -273,7 +281,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
   // ---- q heads of this group: RMSNorm over d, RoPE at pos, pre-scale
   const float* cs_row = p.cos_t + (size_t)pos * (p.rot >> 1);
   const float* sn_row = p.sin_t + (size_t)pos * (p.rot >> 1);
-  for (int r = wid; r < REP; r += 4) {
+  for (int r = wid; r < REP; r += NW) {
     const int h = j * REP + r;
     float y[D / 64];
     norm_rope_wave<D>(row + (size_t)h * D * qmul, p.gq, cs_row, sn_row, p.rot, p.eps, qscale, lane, y);
@@ -281,7 +289,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
     for (int i = 0; i < D / 64; ++i) qs[r][lane + 64 * i] = y[i];
   }
   // ---- the new token's k, v if it falls in this chunk: normalise, rotate, append
-  if (has_new && wid == 3) {
+  if (has_new && wid == NW - 1) {
     const float* kr = row + (size_t)p.nq * D * qmul + j * D;
     const float* vr = kr + (size_t)p.nkv * D;
     float vv[D / 64], y[D / 64];
@@ -320,15 +328,15 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
     }
     if (u < c1) st.add(sc, v);
   };
-  // positions ufirst + 16*i, i = 0, 1, ...: rows i .. i+NPRE-1 are in flight in
+  // positions ufirst + STEP*i, i = 0, 1, ...: rows i .. i+NPRE-1 are in flight in
   // the NPRE register slots, and a slot is refilled with row i+NPRE as soon as
   // row i is unpacked.  `base` (and so the trip count) is uniform across the
   // wave, so the 16-lane shuffles stay converged.
   static_assert(NPRE == 2, "two register slots");
   auto step = [&](int i, RawKV<KV, DP>& sk, RawKV<KV, DP>& sv) -> bool {
-    const int base = c0 + wid * 4 + 16 * i;
+    const int base = c0 + wid * 4 + STEP * i;
     if (base >= c1) return false;
-    const int u = ufirst + 16 * i;
+    const int u = ufirst + STEP * i;
     float k[DP], v[DP];
     if (u == u_new) {
 #pragma unroll
@@ -337,8 +345,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
       sk.get(k);
       sv.get(v);
     }
-    if (base + 16 * NPRE < c1) {
-      const int un = min(u + 16 * NPRE, c1 - 1);
+    if (base + STEP * NPRE < c1) {
+      const int un = min(u + STEP * NPRE, c1 - 1);
       sk.load(kb + (size_t)un * D + li * DP);
       sv.load(vb + (size_t)un * D + li * DP);
     }
@@ -361,22 +369,29 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeParams
   }
   __syncthreads();
 
-  for (int idx = tid; idx < REP * D; idx += 256) {
+  for (int idx = tid; idx < REP * D; idx += 64 * NW) {
     const int r = idx / D, e = idx % D;
     float M = sm[0][r];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm[w][r]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm[w][r]);
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float a = (sm[w][r] == -INFINITY) ? 0.f : exp2f(sm[w][r] - M);
       L += sl[w][r] * a;
       O += so[w][r][e] * a;
     }
     const int h = j * REP + r;
-    float* pr = p.part + (((size_t)b * p.nq + h) * p.nchunks + c) * (D + 2);
-    pr[e] = O;
-    if (e == 0) { pr[D] = M; pr[D + 1] = L; }
+    if constexpr (ONE) {
+      // position 0 is always attended, so L > 0
+      const size_t o = ((size_t)b * p.nq + h) * D + e;
+      if (p.o_dt == DT_BF16) reinterpret_cast<bf16*>(p.out)[o] = (bf16)(O / L);
+      else reinterpret_cast<float*>(p.out)[o] = O / L;
+    } else {
+      float* pr = p.part + (((size_t)b * p.nq + h) * p.nchunks + c) * (D + 2);
+      pr[e] = O;
+      if (e == 0) { pr[D] = M; pr[D + 1] = L; }
+    }
   }
 }
 
@@ -447,21 +462,39 @@ hipError_t attn_combine(const float* part, const int32_t* positions, int B, int 
   return hipGetLastError();
 }
 
+template <typename KV, int D, int REP>
+static void decode_launch(const AttnDecodeParams& p, hipStream_t s) {
+  if constexpr (REP * D <= ATTN_ONEPASS_MAX_REP_D) {
+    if (p.out != nullptr) {
+      attn_decode_kernel<KV, D, REP, true><<<dim3(1, p.nkv, p.B), 1024, 0, s>>>(p);
+      return;
+    }
+  }
+  attn_decode_kernel<KV, D, REP, false><<<dim3(p.nchunks, p.nkv, p.B), 256, 0, s>>>(p);
+}
+
 template <typename KV, int D>
 static hipError_t decode_rep(const AttnDecodeParams& p, hipStream_t s) {
-  const dim3 grid(p.nchunks, p.nkv, p.B);
   switch (p.nq / p.nkv) {
-    case 1: attn_decode_kernel<KV, D, 1><<<grid, 256, 0, s>>>(p); break;
-    case 2: attn_decode_kernel<KV, D, 2><<<grid, 256, 0, s>>>(p); break;
-    case 4: attn_decode_kernel<KV, D, 4><<<grid, 256, 0, s>>>(p); break;
-    case 8: attn_decode_kernel<KV, D, 8><<<grid, 256, 0, s>>>(p); break;
+    case 1: decode_launch<KV, D, 1>(p, s); break;
+    case 2: decode_launch<KV, D, 2>(p, s); break;
+    case 4: decode_launch<KV, D, 4>(p, s); break;
+    case 8: decode_launch<KV, D, 8>(p, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+bool attn_decode_onepass_ok(int nq, int nkv, int d) {
+  if (nkv <= 0 || nq % nkv != 0) return false;
+  const int rep = nq / nkv;
+  return (rep == 1 || rep == 2 || rep == 4 || rep == 8) && (d == 64 || d == 128 || d == 256) &&
+         rep * d <= ATTN_ONEPASS_MAX_REP_D;
+}
+
 hipError_t attn_decode(const AttnDecodeParams& p, hipStream_t s) {
   if (p.B <= 0) return hipSuccess;
+  if (p.out != nullptr && !attn_decode_onepass_ok(p.nq, p.nkv, p.d)) return hipErrorInvalidValue;
   if (p.kv_dt == DT_BF16) {
     if (p.d == 128) return decode_rep<bf16, 128>(p, s);
     if (p.d == 64) return decode_rep<bf16, 64>(p, s);

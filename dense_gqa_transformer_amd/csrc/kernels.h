@@ -147,6 +147,8 @@ struct AttnDecodeParams {
   const int32_t* positions;    // device [B]
   const int32_t* slots;        // device [B]
   float* part;                 // [B, nq, nchunks, d + 2]: o[0..d), m, l (base-2 softmax)
+  void* out;                   // non-null: one pass over the whole context, out[b, h*d + e] in o_dt
+  int o_dt;                    //   (part, chunk and nchunks unused)
   int B, nq, nkv, d, chunk, nchunks;
   long long slot_stride, head_stride;
   float scale;
@@ -154,6 +156,11 @@ struct AttnDecodeParams {
   int gated;                   // q rows interleaved with gate rows per head
 };
 hipError_t attn_decode(const AttnDecodeParams& p, hipStream_t s);
+// The one-pass form exists for (nq/nkv) * d <= ATTN_ONEPASS_MAX_REP_D (its
+// 16-wave workgroup keeps q and the output state of every query head of the
+// group in registers).
+constexpr int ATTN_ONEPASS_MAX_REP_D = 256;
+bool attn_decode_onepass_ok(int nq, int nkv, int d);
 // out[b, h*d + e] from the chunk partials of sequence b (chunks 0..positions[b]/chunk).
 hipError_t attn_combine(const float* part, const int32_t* positions, int B, int nq, int d, int chunk,
                         int nchunks, void* out, int o_dt, hipStream_t s);

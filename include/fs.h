@@ -253,8 +253,12 @@ fs_status fs_timing(fs_model *m, int32_t enable);
 fs_status fs_timing_read(fs_model *m, const char *label, double *total_ms, int64_t *launches);
 
 /* Measurement hook: average duration of one decode-shaped (batch 1) launch
- * of the kernel that implements `label` ("qkv", "attn", "combine", "o_proj",
- * "gate_up", "down" or "head"), as it runs inside a decode step: one launch per layer,
+ * of the kernel that implements `label` ("qkv", "attn", "attn_split",
+ * "attn_onepass", "combine", "o_proj", "gate_up", "down" or "head"), as it
+ * runs inside a decode step.  "attn" is the form of the decode attention a
+ * batch-1 step at this position takes (one pass over the whole context with
+ * no merge launch for short contexts, split-K chunks plus the "combine"
+ * merge otherwise); "attn_split" and "attn_onepass" force one form.  One launch per layer,
  * each with that layer's weights, captured back to back in a graph and
  * replayed `reps` times between two HIP events on `stream` (so the figure
  * includes the per-launch dispatch cost of graph replay).  *avg_us receives
@@ -264,7 +268,8 @@ fs_status fs_timing_read(fs_model *m, const char *label, double *total_ms, int64
  * slot that holds nothing of value ("combine" merges the partials of a
  * context of position+1).  Other labels ignore slot and position.
  * Synchronous.  Errors: INVALID_ARG (unknown label, bad slot/position,
- * reps <= 0), HIP. */
+ * reps <= 0), UNSUPPORTED ("attn_onepass" for a head shape without that
+ * form), HIP. */
 fs_status fs_kernel_bench(fs_model *m, const char *label, int32_t slot, int32_t position,
                           int32_t reps, double *avg_us, void *stream);
 

@@ -353,6 +353,50 @@ def test_decode_bs64_ragged():
     assert [model.slot_length(i) for i in range(B)] == [lens[i] + wl.decode_steps for i in range(B)]
 
 
+# ------------------------------------------------------------------ the two decode attention forms
+@pytest.mark.parametrize("mode", ["split", "onepass"])
+@pytest.mark.parametrize("which", ["tiny_fp32", "0p6b_bf16"])
+def test_decode_attention_forms(monkeypatch, mode, which):
+    # split-K chunks + merge launch, and the one-pass 16-wave workgroup, each
+    # forced for every step: three ragged sequences (1, 37 and 300 tokens of
+    # context on the tiny model, 1, 200 and 1100 on the 0.6B shape, the last
+    # past the context up to which the one-pass form is chosen by itself),
+    # teacher-forced decode at batch 3 and at batch 1, against the oracle
+    shape = synth.TINY if which == "tiny_fp32" else synth.QWEN3_0P6B
+    tol = TOL["f32"] if which == "tiny_fp32" else TOL["bf16"]
+    lens = [1, 37, 300] if which == "tiny_fp32" else [1, 200, 1100]
+    monkeypatch.setenv("FS_DECODE_ATTN", mode)
+    _flush(f"decode attention form {mode} on {which}")
+    model = make_model(shape, max_seqs=3, max_ctx=max(lens) + 8)
+    try:
+        orcs, refs = [], []
+        for i, n in enumerate(lens):
+            toks = synth.tokens(4100 + n, shape.vocab, (1, n))
+            model.prefill(dev_tokens(toks), [i])
+            o = fresh_oracle(shape)
+            refs.append(o.prefill(0, toks[0]))
+            orcs.append(o)
+        out = torch.empty((3, shape.vocab), dtype=torch.float32, device="cuda")
+        nxt = torch.empty((3,), dtype=torch.int32, device="cuda")
+        for k in range(3):
+            toks = [O.greedy_argmax_fast(r) for r in refs]
+            pos = [n + k for n in lens]
+            model.decode_step(dev_tokens(toks), pos, [0, 1, 2], logits=out, next_ids=nxt)
+            got, ids = out.cpu().numpy(), nxt.cpu().numpy()
+            refs = [orcs[i].decode_step(0, toks[i], pos[i]) for i in range(3)]
+            for i in range(3):
+                check_logits(got[i], refs[i], tol, f"{mode} {which} B=3 row {i} step {k}")
+                check_argmax(int(ids[i]), refs[i], f"{mode} {which} B=3 row {i} step {k}")
+        one = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda")
+        for i in range(3):
+            tok = O.greedy_argmax_fast(refs[i])
+            pos = lens[i] + 3
+            model.decode_step(dev_tokens([tok]), [pos], [i], logits=one)
+            check_logits(one.cpu().numpy()[0], orcs[i].decode_step(0, tok, pos), tol, f"{mode} {which} B=1 row {i}")
+    finally:
+        model.close()
+
+
 # ------------------------------------------------------------------ graph replay and timing hook
 def test_graph_replay_matches_eager(monkeypatch):
     # decode steps replayed from captured graphs give the same bits as eager launches
@@ -397,7 +441,7 @@ def test_kernel_bench_hook_leaves_decode_intact(big):
     shape, model = big
     toks = synth.tokens(57, shape.vocab, (1, 33))
     ref = model.prefill(dev_tokens(toks), [0]).cpu().numpy()[0]
-    for lab in ("qkv", "attn", "combine", "o_proj", "gate_up", "down", "head"):
+    for lab in ("qkv", "attn", "attn_split", "attn_onepass", "combine", "o_proj", "gate_up", "down", "head"):
         us = model.kernel_bench(lab, reps=2, slot=5, position=100)
         assert 0.0 < us < 10000.0, lab
     from dense_gqa_transformer_amd import native
