@@ -40,6 +40,11 @@ fs_status fail(fs_status st, const std::string& msg) {
 // Up to this many rows per call the projections run as GEMV (weights streamed
 // once, fp32 activations); above it as MFMA GEMM on bf16 activations.
 constexpr int SKINNY_MAX_ROWS = 8;
+// Few-row (<= 64) O and down projections split K over up to 12 workgroups per
+// 32-column slab (N = hidden gives only hidden / 32 slabs otherwise).
+constexpr int KSPLIT_MAX = 12;
+static_assert(KSPLIT_MAX <= RMSNORM_MAX_PARTS, "the RMSNorm adds every partial");
+constexpr int KSPLIT_MAX_ROWS = 64;
 // In timing mode each call starts with a short device-side wait so the host
 // can queue the whole call behind it: the event pairs then bracket kernels
 // that run back to back instead of waiting on the host.
@@ -120,6 +125,10 @@ struct fs_model {
   int32_t* d_slot = nullptr;
   float* part = nullptr;
   int max_chunks = 0;
+  // split-K partials of the few-row O / down projections, [KSPLIT_MAX][64][hidden];
+  // pend_np > 0: that many partials wait to be added to x by the next RMSNorm
+  float* kpart = nullptr;
+  int pend_np = 0;
   float* lm_pv = nullptr;
   int32_t* lm_pi = nullptr;
   float* logits_tmp = nullptr;    // [max_seqs, V] when the caller passes none
@@ -161,7 +170,7 @@ struct fs_model {
     hipFree(wblob); hipFree(nblob); hipFree(sblob); hipFree(wconv); hipFree(kcache); hipFree(vcache);
     hipFree(rope_cos); hipFree(rope_sin);
     hipFree(x); hipFree(xn); hipFree(qkv); hipFree(qr); hipFree(attn); hipFree(hbuf);
-    hipFree(d_pos); hipFree(d_slot); hipFree(part);
+    hipFree(d_pos); hipFree(d_slot); hipFree(part); hipFree(kpart);
     hipFree(lm_pv); hipFree(lm_pi); hipFree(logits_tmp); hipFree(sample_scr);
     for (int i = 0; i < STAGE_RING; ++i)
       if (stage_ev[i]) hipEventDestroy(stage_ev[i]);
@@ -290,6 +299,42 @@ fs_status ensure_logits_tmp(fs_model* m) {
   return FS_OK;
 }
 
+// Number of K splits for a few-row projection with N = hidden outputs: the
+// smallest that gives >= 192 workgroups, with every wave's share of K a whole
+// number of 64-wide chunks; 1 when the few-row kernel does not take the call.
+int resid_ksplit(const fs_model* m, const void* A, int lda, const void* W, int rows, int K) {
+  const int N = m->cfg.hidden;
+  if (rows > KSPLIT_MAX_ROWS || !gemm_skinny_ok(GEPI_RESID_F32, A, lda, W, K, rows, N, K, nullptr)) return 1;
+  const int slabs = N / 32;
+  for (int ks = 1; ks <= KSPLIT_MAX; ++ks)
+    if (K % (256 * ks) == 0 && slabs * ks >= 192) return ks;
+  return 1;
+}
+
+// out-projection-shaped GEMM (N = hidden) into the residual stream: x += A . W^T.
+// The few-row form splits K over workgroups and leaves its partials pending
+// for the next RMSNorm (norm_in) or flush_partials.
+hipError_t resid_proj(fs_model* m, const void* A, int lda, const void* W, int rows, int K, const float* cs,
+                      hipStream_t s) {
+  const fs_config& c = m->cfg;
+  if (m->pend_np != 0) return hipErrorInvalidValue;       // partials would be overwritten
+  const int ks = resid_ksplit(m, A, lda, W, rows, K);
+  if (ks == 1) return gemm_bf16(GEPI_RESID_F32, A, lda, W, K, m->x, c.hidden, rows, c.hidden, K, s, nullptr, cs);
+  m->pend_np = ks;
+  return gemm_skinny(GEPI_PART_F32, A, lda, W, K, m->kpart, c.hidden, rows, c.hidden, K, s, nullptr, cs, ks);
+}
+
+// RMSNorm of x into xn (bf16, optional remainder), first adding pending partials.
+hipError_t norm_in(fs_model* m, int rows, const float* gamma, void* lo, hipStream_t s) {
+  const fs_config& c = m->cfg;
+  if (m->pend_np == 0)
+    return rmsnorm(m->x, rows, c.hidden, c.hidden, gamma, c.rms_eps, m->xn, DT_BF16, c.hidden, s, lo);
+  const int np = m->pend_np;
+  m->pend_np = 0;
+  return rmsnorm_add(m->x, m->kpart, np, rows, c.hidden, c.hidden, gamma, c.rms_eps, m->xn, DT_BF16, c.hidden, s,
+                     lo);
+}
+
 // One transformer block over `rows` activation rows in the skinny (GEMV) form.
 // attention: a callable that consumes m->qkv (fp32) and fills m->attn (fp32).
 template <class Attn>
@@ -340,7 +385,7 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
     LAUNCH(m, "wconv", s, codes_to_bf16((const int8_t*)L.wqkv, (size_t)m->qkv_w * c.hidden, m->wconv, s));
     wb = m->wconv;
   }
-  LAUNCH(m, "norm", s, rmsnorm(m->x, rows, c.hidden, c.hidden, L.attn_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s, xn_lo));
+  LAUNCH(m, "norm", s, norm_in(m, rows, L.attn_norm, xn_lo, s));
   LAUNCH(m, "qkv", s, gemm_bf16(qkv_f32 ? GEPI_STORE_F32 : GEPI_STORE_BF16, m->xn, c.hidden, wb, c.hidden,
                                 m->qkv, m->qkv_w, rows, m->qkv_w, c.hidden, s, xn_lo, L.sqkv));
   fs_status st = attention();
@@ -350,14 +395,13 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
     LAUNCH(m, "wconv", s, codes_to_bf16((const int8_t*)L.wo, (size_t)c.hidden * m->qw, m->wconv, s));
     wb = m->wconv;
   }
-  LAUNCH(m, "o_proj", s, gemm_bf16(GEPI_RESID_F32, m->attn, m->qw, wb, m->qw, m->x, c.hidden, rows, c.hidden,
-                                   m->qw, s, nullptr, L.so));
+  LAUNCH(m, "o_proj", s, resid_proj(m, m->attn, m->qw, wb, rows, m->qw, L.so, s));
   wb = L.wgu;
   if (q8) {
     LAUNCH(m, "wconv", s, codes_to_bf16((const int8_t*)L.wgu, (size_t)2 * c.ffn * c.hidden, m->wconv, s));
     wb = m->wconv;
   }
-  LAUNCH(m, "norm", s, rmsnorm(m->x, rows, c.hidden, c.hidden, L.mlp_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s));
+  LAUNCH(m, "norm", s, norm_in(m, rows, L.mlp_norm, nullptr, s));
   LAUNCH(m, "gate_up", s, gemm_bf16(GEPI_SWIGLU_BF16, m->xn, c.hidden, wb, c.hidden, m->hbuf, c.ffn, rows,
                                     2 * c.ffn, c.hidden, s, nullptr, L.sgu));
   wb = L.wdown;
@@ -365,8 +409,18 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
     LAUNCH(m, "wconv", s, codes_to_bf16((const int8_t*)L.wdown, (size_t)c.hidden * c.ffn, m->wconv, s));
     wb = m->wconv;
   }
-  LAUNCH(m, "down", s, gemm_bf16(GEPI_RESID_F32, m->hbuf, c.ffn, wb, c.ffn, m->x, c.hidden, rows, c.hidden,
-                                 c.ffn, s, nullptr, L.sdown));
+  LAUNCH(m, "down", s, resid_proj(m, m->hbuf, c.ffn, wb, rows, c.ffn, L.sdown, s));
+  return FS_OK;
+}
+
+// Adds split-K partials still pending to x (rows rows) without normalising.
+fs_status flush_partials(fs_model* m, int rows, hipStream_t s) {
+  if (m->pend_np == 0) return FS_OK;
+  const fs_config& c = m->cfg;
+  const int np = m->pend_np;
+  m->pend_np = 0;
+  LAUNCH(m, "norm", s, rmsnorm_add(m->x, m->kpart, np, rows, c.hidden, c.hidden, nullptr, c.rms_eps, nullptr,
+                                   DT_BF16, c.hidden, s));
   return FS_OK;
 }
 
@@ -542,6 +596,7 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   if (dalloc(&m->d_pos, (size_t)c.max_seqs * 4) != hipSuccess ||
       dalloc(&m->d_slot, (size_t)c.max_seqs * 4) != hipSuccess ||
       dalloc(&m->part, (size_t)c.max_seqs * c.n_heads * m->max_chunks * (c.head_dim + 2) * 4) != hipSuccess ||
+      dalloc(&m->kpart, (size_t)KSPLIT_MAX * KSPLIT_MAX_ROWS * c.hidden * 4) != hipSuccess ||
       dalloc(&m->lm_pv, (size_t)GEMV_LOGITS_MAX_M * lm_blocks * 4) != hipSuccess ||
       dalloc(&m->lm_pi, (size_t)GEMV_LOGITS_MAX_M * lm_blocks * 4) != hipSuccess)
     return bail(FS_ERR_OOM, "decode scratch allocation failed");
@@ -598,6 +653,7 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
   LAUNCH(m, "embed", s, embed(m->embed, m->wdt, tokens, (int)T, c.hidden, c.vocab, m->x, s, m->embed_scale));
   const bool skinny = (m->dt == DT_F32) || T <= SKINNY_MAX_ROWS;
   const int act_dt = skinny ? DT_F32 : DT_BF16;
+  m->pend_np = 0;
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = m->layers[l];
     char* kc = (char*)m->kcache + (size_t)l * m->layer_stride * m->esz;
@@ -630,6 +686,7 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
     st = skinny ? block_skinny(m, L, (int)T, attention, s) : block_gemm(m, L, (int)T, false, attention, s);
     if (st != FS_OK) return st;
   }
+  if ((st = flush_partials(m, (int)T, s)) != FS_OK) return st;
   // last row of each sequence: rows b*S + S-1
   st = head(m, m->x + (size_t)(S - 1) * c.hidden, B, S * c.hidden, logits, nullptr, s);
   if (st != FS_OK) return st;
@@ -681,6 +738,7 @@ static fs_status enqueue_decode(fs_model* m, const int32_t* tokens, int B, float
   LAUNCH(m, "embed", s, embed(m->embed, m->wdt, tokens, B, c.hidden, c.vocab, m->x, s, m->embed_scale));
   const bool skinny = (m->dt == DT_F32) || B <= SKINNY_MAX_ROWS;
   fs_status st = FS_OK;
+  m->pend_np = 0;
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = m->layers[l];
     char* kc = (char*)m->kcache + (size_t)l * m->layer_stride * m->esz;
@@ -708,6 +766,7 @@ static fs_status enqueue_decode(fs_model* m, const int32_t* tokens, int B, float
     st = skinny ? block_skinny(m, L, B, attention, s) : block_gemm(m, L, B, true, attention, s);
     if (st != FS_OK) return st;
   }
+  if ((st = flush_partials(m, B, s)) != FS_OK) return st;
   return head(m, m->x, B, c.hidden, logits, next, s);
 }
 

@@ -39,7 +39,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16* __restrict
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int r = lane & 31, h = lane >> 5;
   const int n0 = blockIdx.x * NS;
-  const int kw = K / SK_WAVES, kb = wid * kw;
+  const int ks = K / (int)gridDim.y;          // K range of this workgroup (split blockIdx.y)
+  const int kw = ks / SK_WAVES, kb = blockIdx.y * ks + wid * kw;
 
   const bf16* bp[NT];
 #pragma unroll
@@ -132,6 +133,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16* __restrict
       const size_t o = (size_t)m * ldc + n0 + n;
       if (EPI == GEPI_STORE_BF16) reinterpret_cast<bf16*>(out)[o] = (bf16)v;
       else if (EPI == GEPI_STORE_F32) reinterpret_cast<float*>(out)[o] = v;
+      else if (EPI == GEPI_PART_F32) reinterpret_cast<float*>(out)[(size_t)blockIdx.y * M * ldc + o] = v;
       else reinterpret_cast<float*>(out)[o] += v;
     }
   }
@@ -139,12 +141,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16* __restrict
 
 template <int EPI, int NT>
 hipError_t launch_nt(const bf16* a, int lda, const bf16* alo, const bf16* b, int ldb, void* out, int ldc, int M,
-                     int N, int K, const float* cs, hipStream_t s) {
-  const int blocks = (N + 32 * NT - 1) / (32 * NT);
+                     int N, int K, const float* cs, int ksplit, hipStream_t s) {
+  const dim3 grid((N + 32 * NT - 1) / (32 * NT), ksplit);
   if (M <= 32)
-    gemm_skinny_kernel<EPI, NT, 1><<<blocks, 256, 0, s>>>(a, lda, alo, b, ldb, out, ldc, M, N, K, cs);
+    gemm_skinny_kernel<EPI, NT, 1><<<grid, 256, 0, s>>>(a, lda, alo, b, ldb, out, ldc, M, N, K, cs);
   else
-    gemm_skinny_kernel<EPI, NT, 2><<<blocks, 256, 0, s>>>(a, lda, alo, b, ldb, out, ldc, M, N, K, cs);
+    gemm_skinny_kernel<EPI, NT, 2><<<grid, 256, 0, s>>>(a, lda, alo, b, ldb, out, ldc, M, N, K, cs);
   return hipGetLastError();
 }
 
@@ -160,15 +162,18 @@ bool gemm_skinny_ok(int epi, const void* A, int lda, const void* B, int ldb, int
 }
 
 hipError_t gemm_skinny(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc, int M, int N,
-                       int K, hipStream_t s, const void* A_lo, const float* colscale) {
+                       int K, hipStream_t s, const void* A_lo, const float* colscale, int ksplit) {
+  if (ksplit < 1 || (ksplit > 1 && epi != GEPI_PART_F32) || K % (256 * ksplit) != 0) return hipErrorInvalidValue;
   const bf16* a = (const bf16*)A;
   const bf16* b = (const bf16*)B;
   const bf16* al = (const bf16*)A_lo;
+  const float* cs = colscale;
   switch (epi) {
-    case GEPI_STORE_BF16: return launch_nt<GEPI_STORE_BF16, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, colscale, s);
-    case GEPI_STORE_F32: return launch_nt<GEPI_STORE_F32, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, colscale, s);
-    case GEPI_RESID_F32: return launch_nt<GEPI_RESID_F32, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, colscale, s);
-    case GEPI_SWIGLU_BF16: return launch_nt<GEPI_SWIGLU_BF16, 2>(a, lda, al, b, ldb, out, ldc, M, N, K, colscale, s);
+    case GEPI_STORE_BF16: return launch_nt<GEPI_STORE_BF16, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, cs, 1, s);
+    case GEPI_STORE_F32: return launch_nt<GEPI_STORE_F32, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, cs, 1, s);
+    case GEPI_RESID_F32: return launch_nt<GEPI_RESID_F32, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, cs, 1, s);
+    case GEPI_PART_F32: return launch_nt<GEPI_PART_F32, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, cs, ksplit, s);
+    case GEPI_SWIGLU_BF16: return launch_nt<GEPI_SWIGLU_BF16, 2>(a, lda, al, b, ldb, out, ldc, M, N, K, cs, 1, s);
     default: return hipErrorInvalidValue;
   }
 }

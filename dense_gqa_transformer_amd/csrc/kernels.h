@@ -25,6 +25,13 @@ hipError_t codes_to_bf16(const int8_t* codes, size_t n, void* dst, hipStream_t s
 // lo (bf16 only, optional): the rounding remainder, y - out, also as bf16.
 hipError_t rmsnorm(const float* x, int T, int H, int ldx, const float* g, float eps,
                    void* out, int out_dt, int ldo, hipStream_t s, void* lo = nullptr);
+// The same after adding np (<= RMSNORM_MAX_PARTS) split-K partials to the residual rows:
+// x[t, :] += parts[0][t, :] + ... + parts[np-1][t, :] (in that order; parts is
+// [np][T][H] dense), written back to x, then normalised into out as above.
+// out may be null (the additions only).
+constexpr int RMSNORM_MAX_PARTS = 16;
+hipError_t rmsnorm_add(float* x, const float* parts, int np, int T, int H, int ldx, const float* g, float eps,
+                       void* out, int out_dt, int ldo, hipStream_t s, void* lo = nullptr);
 // dst[i] = float(src[i])
 hipError_t convert_f32(const void* src, int dt, float* dst, size_t n, hipStream_t s);
 // A one-wave kernel that waits about `us` microseconds of device wall clock.
@@ -62,7 +69,8 @@ hipError_t argmax_partials(const float* pv, const int32_t* pi, int nblocks, int 
                            hipStream_t s);
 
 // ---------------------------------------------------------------- MFMA GEMM (bf16)
-enum GemmEpi { GEPI_STORE_BF16 = 0, GEPI_RESID_F32 = 1, GEPI_SWIGLU_BF16 = 2, GEPI_STORE_F32 = 3 };
+enum GemmEpi { GEPI_STORE_BF16 = 0, GEPI_RESID_F32 = 1, GEPI_SWIGLU_BF16 = 2, GEPI_STORE_F32 = 3,
+               GEPI_PART_F32 = 4 };
 // C[M, N] = A[M, K] . B[N, K]^T; A, B bf16 row-major with K contiguous (lda, ldb);
 // fp32 accumulation.  STORE_*: out[m*ldc + n] = C; RESID_F32: out[m*ldc + n] += C;
 // SWIGLU_BF16: B is packed gate/up (blocks of 32+32 rows, N = 2*ffn) and
@@ -82,10 +90,13 @@ hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, voi
                     int M, int N, int K, hipStream_t s, const void* A_lo, const float* colscale);
 // The few-rows kernel behind gemm_bf16 (M <= 64, K % 256 == 0, N % 32 == 0):
 // one weight slab per workgroup, K split over its waves, each weight read once.
+// PART_F32 (only here): K is also split over ksplit workgroups per slab
+// (K % (256 * ksplit) == 0) and split s stores its partial product at
+// out + s * M * ldc (fp32, [ksplit][M][ldc]); rmsnorm_add sums them.
 bool gemm_skinny_ok(int epi, const void* A, int lda, const void* B, int ldb, int M, int N, int K,
                     const void* A_lo);
 hipError_t gemm_skinny(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc, int M, int N,
-                       int K, hipStream_t s, const void* A_lo, const float* colscale);
+                       int K, hipStream_t s, const void* A_lo, const float* colscale, int ksplit = 1);
 
 // ---------------------------------------------------------------- q/k norm + RoPE + KV write
 // For T tokens: token t belongs to sequence t / S_per (slot slots[t / S_per]) at

@@ -156,6 +156,26 @@ hipError_t codes_to_bf16(const int8_t* codes, size_t n, void* dst, hipStream_t s
 // One wave per row: lane l holds the 16-byte chunks l, l + 64, ... of the row
 // in registers (one read of x), the mean square is one wave sum, and the
 // outputs leave as 8- or 16-byte stores.
+template <typename O>
+__device__ __forceinline__ void norm_store(const f32x4& v, float inv, const float* g, int c, O* o, O* lo) {
+  const f32x4 gg = *reinterpret_cast<const f32x4*>(g + 4 * c);
+  float y[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = v[e] * inv * gg[e];
+  if constexpr (sizeof(O) == 2) {
+    bf16x4 hi, rem;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hi[e] = (bf16)y[e];
+      rem[e] = (bf16)(y[e] - (float)hi[e]);
+    }
+    *reinterpret_cast<bf16x4*>(o + 4 * c) = hi;
+    if (lo != nullptr) *reinterpret_cast<bf16x4*>(lo + 4 * c) = rem;
+  } else {
+    *reinterpret_cast<f32x4*>(o + 4 * c) = f32x4{y[0], y[1], y[2], y[3]};
+  }
+}
+
 template <typename O, int MAXJ>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int T, int H, int ldx,
                                                       const float* __restrict__ g, float eps,
@@ -176,38 +196,90 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
   const float inv = rsqrtf(wave_sum(ss) / (float)H + eps);
   O* o = out + (size_t)r * ldo;
+  O* ol = (lo != nullptr) ? lo + (size_t)r * ldo : nullptr;
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
     const int c = lane + 64 * j;
     if (c >= nc) break;
-    const f32x4 gg = *reinterpret_cast<const f32x4*>(g + 4 * c);
-    float y[4];
+    norm_store<O>(v[j], inv, g, c, o, ol);
+  }
+}
+
+// With split-K partials to add: one workgroup per row, thread t holding the
+// 16-byte chunks t, t + 256, ...; each chunk's np partial loads go out
+// together, the partials are added in order 0..np-1 (so the result does not
+// depend on launch timing) and the row is written back before it is
+// normalised (out == nullptr: the additions only).
+template <typename O>
+__global__ __launch_bounds__(256) void rmsnorm_add_kernel(float* __restrict__ x, int T, int H, int ldx,
+                                                          const float* __restrict__ g, float eps,
+                                                          O* __restrict__ out, O* __restrict__ lo, int ldo,
+                                                          const float* __restrict__ parts, int np) {
+  constexpr int MAXC = 4;                          // H <= 4096
+  __shared__ float red[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  float* row = x + (size_t)r * ldx;
+  const int nc = H >> 2;
+  const size_t pst = (size_t)T * H;
+  const float* prow = parts + (size_t)r * H;
+  f32x4 v[MAXC];
+  float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = v[j][e] * inv * gg[e];
-    if constexpr (sizeof(O) == 2) {
-      bf16x4 hi, rem;
+  for (int j = 0; j < MAXC; ++j) {
+    const int c = tid + 256 * j;
+    v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c < nc) {
+      f32x4 pv[RMSNORM_MAX_PARTS];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi[e] = (bf16)y[e];
-        rem[e] = (bf16)(y[e] - (float)hi[e]);
-      }
-      *reinterpret_cast<bf16x4*>(o + 4 * c) = hi;
-      if (lo != nullptr) *reinterpret_cast<bf16x4*>(lo + (size_t)r * ldo + 4 * c) = rem;
-    } else {
-      *reinterpret_cast<f32x4*>(o + 4 * c) = f32x4{y[0], y[1], y[2], y[3]};
+      for (int q = 0; q < RMSNORM_MAX_PARTS; ++q)
+        if (q < np) pv[q] = *reinterpret_cast<const f32x4*>(prow + q * pst + 4 * c);
+      f32x4 a = *reinterpret_cast<const f32x4*>(row + 4 * c);
+#pragma unroll
+      for (int q = 0; q < RMSNORM_MAX_PARTS; ++q)
+        if (q < np) a += pv[q];
+      *reinterpret_cast<f32x4*>(row + 4 * c) = a;
+      v[j] = a;
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss = fmaf(v[j][e], v[j][e], ss);
+  }
+  if (out == nullptr) return;
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  O* o = out + (size_t)r * ldo;
+  O* ol = (lo != nullptr) ? lo + (size_t)r * ldo : nullptr;
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int c = tid + 256 * j;
+    if (c < nc) norm_store<O>(v[j], inv, g, c, o, ol);
   }
 }
 
 hipError_t rmsnorm(const float* x, int T, int H, int ldx, const float* g, float eps, void* out,
                    int out_dt, int ldo, hipStream_t s, void* lo) {
   if (T <= 0) return hipSuccess;
-  if (H % 4 != 0 || H > 4096 || ldx % 4 != 0 || ldo % 4 != 0) return hipErrorInvalidValue;
+  if (out == nullptr || H % 4 != 0 || H > 4096 || ldx % 4 != 0 || ldo % 4 != 0) return hipErrorInvalidValue;
   const int blocks = (T + 3) / 4;
   if (out_dt == DT_BF16)
     rmsnorm_kernel<bf16, 16><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, (bf16*)lo, ldo);
   else if (lo == nullptr)
     rmsnorm_kernel<float, 16><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (float*)out, nullptr, ldo);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t rmsnorm_add(float* x, const float* parts, int np, int T, int H, int ldx, const float* g, float eps,
+                       void* out, int out_dt, int ldo, hipStream_t s, void* lo) {
+  if (T <= 0) return hipSuccess;
+  if (np <= 0 || np > RMSNORM_MAX_PARTS || parts == nullptr) return hipErrorInvalidValue;
+  if (H % 4 != 0 || H > 4096 || ldx % 4 != 0 || ldo % 4 != 0) return hipErrorInvalidValue;
+  if (out_dt == DT_BF16)
+    rmsnorm_add_kernel<bf16><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, (bf16*)lo, ldo, parts, np);
+  else if (lo == nullptr)
+    rmsnorm_add_kernel<float><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (float*)out, nullptr, ldo, parts, np);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
