@@ -129,6 +129,10 @@ struct fs_model {
   // pend_np > 0: that many partials wait to be added to x by the next RMSNorm
   float* kpart = nullptr;
   int pend_np = 0;
+  // where the decode attention finds this layer's q/k/v projection (m->qkv, or
+  // qkv_np split-K partials in kpart)
+  const float* qkv_src = nullptr;
+  int qkv_np = 1;
   float* lm_pv = nullptr;
   int32_t* lm_pi = nullptr;
   float* logits_tmp = nullptr;    // [max_seqs, V] when the caller passes none
@@ -299,12 +303,11 @@ fs_status ensure_logits_tmp(fs_model* m) {
   return FS_OK;
 }
 
-// Number of K splits for a few-row projection with N = hidden outputs: the
-// smallest that gives >= 192 workgroups, with every wave's share of K a whole
-// number of 64-wide chunks; 1 when the few-row kernel does not take the call.
-int resid_ksplit(const fs_model* m, const void* A, int lda, const void* W, int rows, int K) {
-  const int N = m->cfg.hidden;
-  if (rows > KSPLIT_MAX_ROWS || !gemm_skinny_ok(GEPI_RESID_F32, A, lda, W, K, rows, N, K, nullptr)) return 1;
+// Number of K splits for a few-row projection with N outputs: the smallest
+// that gives >= 192 workgroups, with every wave's share of K a whole number of
+// 64-wide chunks; 1 when the few-row kernel does not take the call.
+int ksplit_for(const void* A, int lda, const void* W, int rows, int N, int K, const void* A_lo) {
+  if (rows > KSPLIT_MAX_ROWS || !gemm_skinny_ok(GEPI_STORE_F32, A, lda, W, K, rows, N, K, A_lo)) return 1;
   const int slabs = N / 32;
   for (int ks = 1; ks <= KSPLIT_MAX; ++ks)
     if (K % (256 * ks) == 0 && slabs * ks >= 192) return ks;
@@ -318,7 +321,7 @@ hipError_t resid_proj(fs_model* m, const void* A, int lda, const void* W, int ro
                       hipStream_t s) {
   const fs_config& c = m->cfg;
   if (m->pend_np != 0) return hipErrorInvalidValue;       // partials would be overwritten
-  const int ks = resid_ksplit(m, A, lda, W, rows, K);
+  const int ks = ksplit_for(A, lda, W, rows, c.hidden, K, nullptr);
   if (ks == 1) return gemm_bf16(GEPI_RESID_F32, A, lda, W, K, m->x, c.hidden, rows, c.hidden, K, s, nullptr, cs);
   m->pend_np = ks;
   return gemm_skinny(GEPI_PART_F32, A, lda, W, K, m->kpart, c.hidden, rows, c.hidden, K, s, nullptr, cs, ks);
@@ -347,6 +350,8 @@ fs_status block_skinny(fs_model* m, const LayerW& L, int rows, Attn&& attention,
   p.a = m->x; p.lda = c.hidden; p.M = rows; p.gamma = L.attn_norm;
   p.out = (float*)m->qkv; p.ldo = m->qkv_w;
   LAUNCH(m, "qkv", s, gemv(m->wdt, EPI_STORE, p, s));
+  m->qkv_src = (const float*)m->qkv;
+  m->qkv_np = 1;
   fs_status st = attention();
   if (st != FS_OK) return st;
   // output projection + residual
@@ -386,8 +391,21 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
     wb = m->wconv;
   }
   LAUNCH(m, "norm", s, norm_in(m, rows, L.attn_norm, xn_lo, s));
-  LAUNCH(m, "qkv", s, gemm_bf16(qkv_f32 ? GEPI_STORE_F32 : GEPI_STORE_BF16, m->xn, c.hidden, wb, c.hidden,
-                                m->qkv, m->qkv_w, rows, m->qkv_w, c.hidden, s, xn_lo, L.sqkv));
+  // decode (fp32 q/k/v): the few-row form splits K and the attention sums the
+  // partials as it loads q/k/v (not for the gated variant, whose gate rows are
+  // read from m->qkv afterwards)
+  const int qks = (qkv_f32 && !m->gated) ? ksplit_for(m->xn, c.hidden, wb, rows, m->qkv_w, c.hidden, xn_lo) : 1;
+  m->qkv_src = (const float*)m->qkv;
+  m->qkv_np = 1;
+  if (qks > 1) {
+    LAUNCH(m, "qkv", s, gemm_skinny(GEPI_PART_F32, m->xn, c.hidden, wb, c.hidden, m->kpart, m->qkv_w, rows,
+                                    m->qkv_w, c.hidden, s, xn_lo, L.sqkv, qks));
+    m->qkv_src = m->kpart;
+    m->qkv_np = qks;
+  } else {
+    LAUNCH(m, "qkv", s, gemm_bf16(qkv_f32 ? GEPI_STORE_F32 : GEPI_STORE_BF16, m->xn, c.hidden, wb, c.hidden,
+                                  m->qkv, m->qkv_w, rows, m->qkv_w, c.hidden, s, xn_lo, L.sqkv));
+  }
   fs_status st = attention();
   if (st != FS_OK) return st;
   wb = L.wo;
@@ -596,7 +614,8 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   if (dalloc(&m->d_pos, (size_t)c.max_seqs * 4) != hipSuccess ||
       dalloc(&m->d_slot, (size_t)c.max_seqs * 4) != hipSuccess ||
       dalloc(&m->part, (size_t)c.max_seqs * c.n_heads * m->max_chunks * (c.head_dim + 2) * 4) != hipSuccess ||
-      dalloc(&m->kpart, (size_t)KSPLIT_MAX * KSPLIT_MAX_ROWS * c.hidden * 4) != hipSuccess ||
+      dalloc(&m->kpart, (size_t)KSPLIT_MAX_ROWS * std::max(KSPLIT_MAX * c.hidden, KSPLIT_MAX * m->qkv_w) * 4) !=
+          hipSuccess ||
       dalloc(&m->lm_pv, (size_t)GEMV_LOGITS_MAX_M * lm_blocks * 4) != hipSuccess ||
       dalloc(&m->lm_pi, (size_t)GEMV_LOGITS_MAX_M * lm_blocks * 4) != hipSuccess)
     return bail(FS_ERR_OOM, "decode scratch allocation failed");
@@ -745,7 +764,7 @@ static fs_status enqueue_decode(fs_model* m, const int32_t* tokens, int B, float
     char* vc = (char*)m->vcache + (size_t)l * m->layer_stride * m->esz;
     auto attention = [&]() -> fs_status {
       AttnDecodeParams a{};
-      a.qkv = (const float*)m->qkv; a.kcache = kc; a.vcache = vc; a.kv_dt = m->dt;
+      a.qkv = m->qkv_src; a.qkv_np = m->qkv_np; a.kcache = kc; a.vcache = vc; a.kv_dt = m->dt;
       a.gq = L.q_norm; a.gk = L.k_norm; a.eps = c.rms_eps;
       a.cos_t = m->rope_cos; a.sin_t = m->rope_sin; a.positions = m->d_pos; a.slots = m->d_slot;
       a.part = m->part;
@@ -882,7 +901,7 @@ fs_status fs_kernel_bench(fs_model* m, const char* label, int32_t slot, int32_t 
       HIP_TRY(gemv(m->wdt, EPI_LOGITS, p, ls));
     } else if (is_attn) {
       AttnDecodeParams a{};
-      a.qkv = (const float*)m->qkv;
+      a.qkv = (const float*)m->qkv; a.qkv_np = 1;
       a.kcache = (char*)m->kcache + (size_t)l * m->layer_stride * m->esz;
       a.vcache = (char*)m->vcache + (size_t)l * m->layer_stride * m->esz;
       a.kv_dt = m->dt; a.gq = L.q_norm; a.gk = L.k_norm; a.eps = c.rms_eps;

@@ -88,9 +88,17 @@ template <typename KV> struct RawKV<KV, 16> {
 // dims (pairs (i, i + rot/2), angles from the table rows cs / sn of length
 // rot/2), times `mul`.  One wave: lane holds elements lane + 64i (returned
 // in y[i]); a rotated element also reads its partner from x.
+// x[e] summed over the np split-K partials of the projection (pst floats apart).
+__device__ __forceinline__ float ld_sum(const float* x, size_t pst, int np, int e) {
+  float r = x[e];
+  for (int q = 1; q < np; ++q) r += x[q * pst + e];
+  return r;
+}
+
 template <int D>
-__device__ __forceinline__ void norm_rope_wave(const float* x, const float* g, const float* cs, const float* sn,
-                                               int rot, float eps, float mul, int lane, float (&y)[D / 64]) {
+__device__ __forceinline__ void norm_rope_wave(const float* x, size_t pst, int np, const float* g, const float* cs,
+                                               const float* sn, int rot, float eps, float mul, int lane,
+                                               float (&y)[D / 64]) {
   constexpr int NE = D / 64;
   const int rh = rot >> 1;
   if constexpr (NE >= 2) {
@@ -100,7 +108,7 @@ __device__ __forceinline__ void norm_rope_wave(const float* x, const float* g, c
       float v[NE], gv[NE], c[H], sv[H];
 #pragma unroll
       for (int i = 0; i < NE; ++i) {
-        v[i] = x[lane + 64 * i];
+        v[i] = ld_sum(x, pst, np, lane + 64 * i);
         gv[i] = g[lane + 64 * i];
       }
 #pragma unroll
@@ -129,8 +137,8 @@ __device__ __forceinline__ void norm_rope_wave(const float* x, const float* g, c
     const int e = lane + 64 * i;
     const bool r = e < rot, lo = e < rh;
     const int pe = r ? (lo ? e + rh : e - rh) : e, fi = r ? (lo ? e : e - rh) : 0;
-    v[i] = x[e];
-    vp[i] = x[pe];
+    v[i] = ld_sum(x, pst, np, e);
+    vp[i] = ld_sum(x, pst, np, pe);
     gv[i] = g[e];
     gp[i] = g[pe];
     c[i] = r ? cs[fi] : 1.f;
@@ -260,6 +268,7 @@ __global__ __launch_bounds__(ONE ? 1024 : 256) void attn_decode_kernel(const Att
   const int qmul = p.gated ? 2 : 1;                      // q rows interleaved with gate rows
   const int W = (p.nq * qmul + 2 * p.nkv) * D;
   const float* row = p.qkv + (size_t)b * W;
+  const size_t pst = (size_t)p.B * W;                   // between split-K partials of the projection
   const size_t kvoff = (size_t)slot * p.slot_stride + (size_t)j * p.head_stride;
   KV* kb = reinterpret_cast<KV*>(p.kcache) + kvoff;
   KV* vb = reinterpret_cast<KV*>(p.vcache) + kvoff;
@@ -284,7 +293,7 @@ __global__ __launch_bounds__(ONE ? 1024 : 256) void attn_decode_kernel(const Att
   for (int r = wid; r < REP; r += NW) {
     const int h = j * REP + r;
     float y[D / 64];
-    norm_rope_wave<D>(row + (size_t)h * D * qmul, p.gq, cs_row, sn_row, p.rot, p.eps, qscale, lane, y);
+    norm_rope_wave<D>(row + (size_t)h * D * qmul, pst, p.qkv_np, p.gq, cs_row, sn_row, p.rot, p.eps, qscale, lane, y);
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) qs[r][lane + 64 * i] = y[i];
   }
@@ -294,8 +303,8 @@ __global__ __launch_bounds__(ONE ? 1024 : 256) void attn_decode_kernel(const Att
     const float* vr = kr + (size_t)p.nkv * D;
     float vv[D / 64], y[D / 64];
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) vv[i] = vr[lane + 64 * i];
-    norm_rope_wave<D>(kr, p.gk, cs_row, sn_row, p.rot, p.eps, 1.f, lane, y);
+    for (int i = 0; i < D / 64; ++i) vv[i] = ld_sum(vr, pst, p.qkv_np, lane + 64 * i);
+    norm_rope_wave<D>(kr, pst, p.qkv_np, p.gk, cs_row, sn_row, p.rot, p.eps, 1.f, lane, y);
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) {
       const int e = lane + 64 * i;
