@@ -183,11 +183,13 @@ def test_scorer_6_tokens(big):
         assert ref[g] >= kth - 2 * TOL["bf16"]
 
 
-@pytest.mark.parametrize("S", [1, 3, 5, 9, 130, 1100])
+@pytest.mark.parametrize("S", [1, 3, 5, 8, 9, 64, 65, 130, 1100])
 def test_prefill_lengths_both_paths(big, S):
-    # S <= 8 runs the GEMV path (1, 4 or 8 rows per workgroup), larger S the MFMA
-    # GEMM path (128-row tiles, ragged tails at 9 and 130; 256-row tiles with a
-    # 76-row tail at 1100)
+    # S <= 8 runs the GEMV path (1, 4 or 8 rows per workgroup); 9..64 the few-row
+    # MFMA GEMM, whose O and down projections split K over workgroups and leave
+    # partials for the next RMSNorm (the last layer's are added before the
+    # head); larger S the tiled MFMA GEMMs (128-row tiles with ragged tails at
+    # 65 and 130; 256-row tiles with a 76-row tail at 1100)
     shape, model = big
     toks = synth.tokens(500 + S, shape.vocab, (1, S))
     ref = oracle_for(shape).forward(toks[0])
@@ -223,6 +225,24 @@ def test_decode_bs1_teacher_forced(big):
     vo = orc.cache[0][0][1][:, 3, :]
     np.testing.assert_allclose(kk.float().cpu().numpy(), ko, atol=2e-2, rtol=1e-2)
     np.testing.assert_allclose(vv.float().cpu().numpy(), vo, atol=2e-2, rtol=1e-2)
+
+
+def test_decode_crosses_onepass_context(big):
+    # batch-1 steps at 127..130 keys: the attention switches from the one-pass
+    # form (up to 128 keys) to split-K chunks plus the merge launch (another
+    # captured graph) in the middle of the sequence
+    shape, model = big
+    prompt = synth.tokens(4242, shape.vocab, 126)
+    orc = fresh_oracle(shape)
+    ref = orc.prefill(0, prompt)
+    model.prefill(dev_tokens(prompt[None, :]), [5])
+    logits = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda")
+    for k in range(5):
+        tok = O.greedy_argmax_fast(ref)
+        pos = len(prompt) + k
+        model.decode_step(dev_tokens([tok]), [pos], [5], logits=logits)
+        ref = orc.decode_step(0, tok, pos)
+        check_logits(logits.cpu().numpy()[0], ref, TOL["bf16"], f"decode at {pos + 1} keys")
 
 
 def test_decode_bs1_free_running_then_uncached(big):
