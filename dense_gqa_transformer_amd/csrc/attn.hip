@@ -257,7 +257,8 @@ __global__ __launch_bounds__(ONE ? 1024 : 256) void attn_decode_kernel(const Att
 
   constexpr int NPRE = 2;                               // key rows per lane in flight
   const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches below
   const int grp = lane >> 4, li = lane & 15;
   const int pos = p.positions[b];
   const int slot = p.slots[b];
@@ -342,30 +343,40 @@ __global__ __launch_bounds__(ONE ? 1024 : 256) void attn_decode_kernel(const Att
   // row i is unpacked.  `base` (and so the trip count) is uniform across the
   // wave, so the 16-lane shuffles stay converged.
   static_assert(NPRE == 2, "two register slots");
-  auto step = [&](int i, RawKV<KV, DP>& sk, RawKV<KV, DP>& sv) -> bool {
-    const int base = c0 + wid * 4 + STEP * i;
-    if (base >= c1) return false;
+  // steps of this wave (uniform: the wave's first position is c0 + 4 wid)
+  const int wfirst = c0 + wid * 4;
+  const int nsteps = (wfirst < c1) ? (c1 - wfirst + STEP - 1) / STEP : 0;
+  auto step = [&](int i, RawKV<KV, DP>& sk, RawKV<KV, DP>& sv) {
     const int u = ufirst + STEP * i;
+    // The slot is always unpacked and always refilled (past the chunk's end
+    // the address is clamped to its last row), the new token's row (not in the
+    // cache yet) replaces it from LDS under a wave-uniform test, and the two
+    // slots run back to back with no exit between them: a load that some
+    // lanes or paths might skip, or registers some lanes might not read, make
+    // the compiler wait for the other slot's loads too, which takes away the
+    // overlap of the two slots.
     float k[DP], v[DP];
-    if (u == u_new) {
+    sk.get(k);
+    sv.get(v);
+    if (__ballot(u == u_new) != 0) {
+      const bool mine = (u == u_new);
 #pragma unroll
-      for (int e = 0; e < DP; ++e) { k[e] = knew[li * DP + e]; v[e] = vnew[li * DP + e]; }
-    } else {
-      sk.get(k);
-      sv.get(v);
+      for (int e = 0; e < DP; ++e) {
+        k[e] = mine ? knew[li * DP + e] : k[e];
+        v[e] = mine ? vnew[li * DP + e] : v[e];
+      }
     }
-    if (base + STEP * NPRE < c1) {
-      const int un = min(u + STEP * NPRE, c1 - 1);
-      sk.load(kb + (size_t)un * D + li * DP);
-      sv.load(vb + (size_t)un * D + li * DP);
-    }
+    const int un = min(u + STEP * NPRE, c1 - 1);
+    sk.load(kb + (size_t)un * D + li * DP);
+    sv.load(vb + (size_t)un * D + li * DP);
     fold(u, k, v);
-    return true;
   };
-  for (int i = 0;; i += 2) {
-    if (!step(i, pk[0], pv[0])) break;
-    if (!step(i + 1, pk[1], pv[1])) break;
+  int i = 0;
+  for (; i + 1 < nsteps; i += 2) {
+    step(i, pk[0], pv[0]);
+    step(i + 1, pk[1], pv[1]);
   }
+  if (i < nsteps) step(i, pk[0], pv[0]);
   st.template merge_xor<16>();
   st.template merge_xor<32>();
   if (lane < 16) {
