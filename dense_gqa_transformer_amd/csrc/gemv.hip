@@ -19,6 +19,7 @@ namespace fsk {
 
 static constexpr int GEMV_THREADS = 256;
 static constexpr int GEMV_WAVES = 4;
+static constexpr int GEMV_LOGITS_GROUPS = 8;   // row groups per wave for the lm_head
 
 // One lane's chunk of a weight row: CE consecutive elements.
 template <typename W> struct Raw;
@@ -80,72 +81,96 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
   // activations held in registers when they fit (always for one row)
   constexpr bool XREG = (MB * CPL * CE <= 64);
   const int K = p.K;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m0 = blockIdx.y * MB;
   const int mcount = min(MB, p.M - m0);
   const W* __restrict__ w = reinterpret_cast<const W*>(p.w);
   const int nchunk = K / CE;
   const int slots_total = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;   // weight rows to cover
-  const int rows_per_block = GEMV_WAVES * RPW * p.groups;
+  constexpr int GROUPS = (EPI == EPI_LOGITS) ? GEMV_LOGITS_GROUPS : 1;
+  const int rows_per_block = GEMV_WAVES * RPW * GROUPS;
 
+  // Weight loads are unconditional: past a row's end a lane re-reads the
+  // row's last chunk and past the last row a wave re-reads that row (both
+  // ignored below).  A load that some lanes skip makes the compiler wait for
+  // every earlier load at each use, which serialises the row groups.
   auto load_group = [&](int g, Raw<W> (&raw)[CPL][RPW]) {
     const int rbase = blockIdx.x * rows_per_block + (g * GEMV_WAVES + wid) * RPW;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
+      const int c = min(lane + 64 * j, nchunk - 1);
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         int f;
-        const int r = weight_row<EPI>(rbase + i, f);
-        if (c < nchunk && rbase + i < slots_total)
-          raw_load(w + (size_t)r * K + c * CE, raw[j][i]);
-        else
-          raw_zero(raw[j][i]);
+        const int r = weight_row<EPI>(min(rbase + i, slots_total - 1), f);
+        raw_load(w + (size_t)r * K + c * CE, raw[j][i]);
       }
     }
   };
   Raw<W> ra[CPL][RPW], rb[CPL][RPW];
-  load_group(0, ra);          // weights first: their latency covers the prologue
-
-  // ---- prologue: per-row RMSNorm scale from this wave's own slices
   float inv[MB];
   float xv[XREG ? MB : 1][XREG ? CPL : 1][CE];
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    const float* arow = p.a + (size_t)(m0 + min(m, mcount - 1)) * p.lda;
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
-      float v[CE];
-      if (c < nchunk) load_act<CE>(arow + c * CE, v);
-      else {
-#pragma unroll
-        for (int e = 0; e < CE; ++e) v[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < CE; ++e) ss = fmaf(v[e], v[e], ss);
-      if (XREG) {
-#pragma unroll
-        for (int e = 0; e < CE; ++e) xv[XREG ? m : 0][XREG ? j : 0][e] = v[e];
-      }
-    }
-    inv[m] = (p.gamma != nullptr) ? rsqrtf(wave_sum(ss) / (float)K + p.eps) : 1.f;
-  }
-  if (XREG && p.gamma != nullptr) {
+  if constexpr (XREG) {
+    // the activation rows and the norm weight are requested before the
+    // weights (the counter of outstanding loads is in order), so the RMSNorm
+    // runs while the weights are in flight
+    float gm[CPL][CE];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = lane + 64 * j;
-      float g[CE];
-      if (c < nchunk) load_act<CE>(p.gamma + c * CE, g);
-      else {
-#pragma unroll
-        for (int e = 0; e < CE; ++e) g[e] = 0.f;
-      }
+      const int cc = min(c, nchunk - 1);
 #pragma unroll
       for (int m = 0; m < MB; ++m)
+        load_act<CE>(p.a + (size_t)(m0 + min(m, mcount - 1)) * p.lda + cc * CE, xv[m][j]);
+      if (p.gamma != nullptr) load_act<CE>(p.gamma + cc * CE, gm[j]);
+    }
+    load_group(0, ra);
 #pragma unroll
-        for (int e = 0; e < CE; ++e) xv[XREG ? m : 0][XREG ? j : 0][e] *= inv[m] * g[e];
+    for (int j = 0; j < CPL; ++j)
+      if (lane + 64 * j >= nchunk) {      // past the row's end: zero activations
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+          for (int e = 0; e < CE; ++e) xv[m][j][e] = 0.f;
+      }
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j)
+#pragma unroll
+        for (int e = 0; e < CE; ++e) ss = fmaf(xv[m][j][e], xv[m][j][e], ss);
+      inv[m] = (p.gamma != nullptr) ? rsqrtf(wave_sum(ss) / (float)K + p.eps) : 1.f;
+    }
+    if (p.gamma != nullptr) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j)
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+          for (int e = 0; e < CE; ++e) xv[m][j][e] *= inv[m] * gm[j][e];
+    }
+  } else {
+    load_group(0, ra);          // weights first: their latency covers the prologue
+    // ---- prologue: per-row RMSNorm scale from this wave's own slices
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const float* arow = p.a + (size_t)(m0 + min(m, mcount - 1)) * p.lda;
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;
+        float v[CE];
+        if (c < nchunk) load_act<CE>(arow + c * CE, v);
+        else {
+#pragma unroll
+          for (int e = 0; e < CE; ++e) v[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < CE; ++e) ss = fmaf(v[e], v[e], ss);
+      }
+      inv[m] = (p.gamma != nullptr) ? rsqrtf(wave_sum(ss) / (float)K + p.eps) : 1.f;
     }
   }
 
@@ -240,13 +265,23 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
     }
   };
 
-  // ping-pong over row groups with statically indexed register buffers
-  for (int g = 0; g < p.groups; g += 2) {
-    if (g + 1 < p.groups) load_group(g + 1, rb);
-    compute(g, ra);
-    if (g + 1 >= p.groups) break;
-    if (g + 2 < p.groups) load_group(g + 2, ra);
-    compute(g + 1, rb);
+  // ping-pong over row groups with statically indexed register buffers: group
+  // g + 1 is in flight while group g is reduced (no load is conditional, and
+  // the last pair is peeled off the rolled loop)
+  if constexpr (GROUPS == 1) {
+    compute(0, ra);
+  } else {
+    static_assert(GROUPS % 2 == 0, "row groups come in pairs");
+#pragma unroll 1
+    for (int g = 0; g < GROUPS - 2; g += 2) {
+      load_group(g + 1, rb);
+      compute(g, ra);
+      load_group(g + 2, ra);
+      compute(g + 1, rb);
+    }
+    load_group(GROUPS - 1, rb);
+    compute(GROUPS - 2, ra);
+    compute(GROUPS - 1, rb);
   }
 
   if (EPI == EPI_LOGITS) {
@@ -322,7 +357,7 @@ int gemv_logits_blocks(int dt, int N, int K) {
   const bool q = (dt == DT_I8);
   const int cpl = cpl_for(K, q ? 16 : 8);
   const int rows_per_group = GEMV_WAVES * rpw_for(q, cpl);
-  const int groups = 8;
+  const int groups = GEMV_LOGITS_GROUPS;
   return (N + rows_per_group * groups - 1) / (rows_per_group * groups);
 }
 
@@ -331,8 +366,7 @@ static hipError_t launch_gemv(GemvParams p, hipStream_t s) {
   constexpr int RPW = rpw_for(Raw<W>::CE == 16, CPL);
   const int slots_total = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
   const int rows_per_group = GEMV_WAVES * RPW;
-  int groups = 1;
-  if (EPI == EPI_LOGITS) groups = 8;
+  const int groups = (EPI == EPI_LOGITS) ? GEMV_LOGITS_GROUPS : 1;
   const int gx = (slots_total + rows_per_group * groups - 1) / (rows_per_group * groups);
   p.groups = groups;
   const int gy = (p.M + MB - 1) / MB;
