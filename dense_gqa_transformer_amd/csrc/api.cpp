@@ -391,10 +391,12 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
     wb = m->wconv;
   }
   LAUNCH(m, "norm", s, norm_in(m, rows, L.attn_norm, xn_lo, s));
-  // decode (fp32 q/k/v): the few-row form splits K and the attention sums the
-  // partials as it loads q/k/v (not for the gated variant, whose gate rows are
-  // read from m->qkv afterwards)
-  const int qks = (qkv_f32 && !m->gated) ? ksplit_for(m->xn, c.hidden, wb, rows, m->qkv_w, c.hidden, xn_lo) : 1;
+  // decode (fp32 q/k/v): the few-row form splits K in two and the attention
+  // sums the partials as it loads q/k/v (not for the gated variant, whose gate
+  // rows are read from m->qkv afterwards)
+  const int qks = (qkv_f32 && !m->gated)
+                      ? std::min(2, ksplit_for(m->xn, c.hidden, wb, rows, m->qkv_w, c.hidden, xn_lo))
+                      : 1;
   m->qkv_src = (const float*)m->qkv;
   m->qkv_np = 1;
   if (qks > 1) {

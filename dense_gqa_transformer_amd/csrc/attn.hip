@@ -84,74 +84,96 @@ template <typename KV> struct RawKV<KV, 16> {
   __device__ __forceinline__ void get(float* o) const { a.get(o); b.get(o + 8); }
 };
 
-// RMSNorm over d with weight g, then rotate-half RoPE on the first `rot`
-// dims (pairs (i, i + rot/2), angles from the table rows cs / sn of length
-// rot/2), times `mul`.  One wave: lane holds elements lane + 64i (returned
-// in y[i]); a rotated element also reads its partner from x.
-// x[e] summed over the np split-K partials of the projection (pst floats apart).
-__device__ __forceinline__ float ld_sum(const float* x, size_t pst, int np, int e) {
-  float r = x[e];
-  for (int q = 1; q < np; ++q) r += x[q * pst + e];
-  return r;
+// x[e] of the np (1 or 2) split-K partials of the projection, pst floats
+// apart, as a pair to be summed once the loads are in (psum).  Both loads are
+// issued either way (with one partial the second re-reads x[e]), so the
+// number of loads does not depend on np.
+struct Part2 {
+  float a, b;
+};
+__device__ __forceinline__ Part2 ld_part(const float* x, size_t pst, int np, int e) {
+  return Part2{x[e], x[(np > 1 ? pst : 0) + e]};
 }
+__device__ __forceinline__ float psum(const Part2& p, int np) { return np > 1 ? p.a + p.b : p.a; }
+
+// RMSNorm over d (weight g) of one head's projection row x (summed over its
+// np split-K partials, pst floats apart), then rotate-half RoPE on the first
+// `rot` dims (element e < rot/2 pairs with e + rot/2; cos/sin rows of length
+// rot/2), times `mul`.  One wave: lane holds elements lane + 64i (returned in
+// y[i]).  Split in two so that a kernel can request every load of the step
+// (nr_fetch) before other loads, and compute (nr_finish) once they are in.
+template <int D>
+struct NormRopeIn {
+  static constexpr int NE = D / 64;
+  Part2 v[NE], vp[NE];
+  float gv[NE], gp[NE], c[NE], s[NE];
+};
 
 template <int D>
-__device__ __forceinline__ void norm_rope_wave(const float* x, size_t pst, int np, const float* g, const float* cs,
-                                               const float* sn, int rot, float eps, float mul, int lane,
-                                               float (&y)[D / 64]) {
+__device__ __forceinline__ void nr_fetch(const float* x, size_t pst, int np, const float* g, const float* cs,
+                                         const float* sn, int rot, int lane, NormRopeIn<D>& in) {
   constexpr int NE = D / 64;
   const int rh = rot >> 1;
   if constexpr (NE >= 2) {
     if (rot == D) {
       // full rotation: element i's partner is element i +- NE/2 of the same lane
-      constexpr int H = NE / 2;
-      float v[NE], gv[NE], c[H], sv[H];
 #pragma unroll
       for (int i = 0; i < NE; ++i) {
-        v[i] = ld_sum(x, pst, np, lane + 64 * i);
-        gv[i] = g[lane + 64 * i];
+        in.v[i] = ld_part(x, pst, np, lane + 64 * i);
+        in.gv[i] = g[lane + 64 * i];
       }
 #pragma unroll
-      for (int i = 0; i < H; ++i) {
-        c[i] = cs[lane + 64 * i];
-        sv[i] = sn[lane + 64 * i];
-      }
-      float ss = 0.f;
-#pragma unroll
-      for (int i = 0; i < NE; ++i) ss = fmaf(v[i], v[i], ss);
-      const float inv = rsqrtf(wave_sum(ss) / (float)D + eps);
-#pragma unroll
-      for (int i = 0; i < H; ++i) {
-        const float a = v[i] * inv * gv[i], b = v[i + H] * inv * gv[i + H];
-        y[i] = (a * c[i] - b * sv[i]) * mul;
-        y[i + H] = (b * c[i] + a * sv[i]) * mul;
+      for (int i = 0; i < NE / 2; ++i) {
+        in.c[i] = cs[lane + 64 * i];
+        in.s[i] = sn[lane + 64 * i];
       }
       return;
     }
   }
-  // every load first (one memory round trip): the element, its rotation
-  // partner, both weights and the angle
-  float v[NE], vp[NE], gv[NE], gp[NE], c[NE], sv[NE];
+  // every load is unconditional (a dim outside the rotation reads angle 0 and
+  // ignores it)
 #pragma unroll
   for (int i = 0; i < NE; ++i) {
     const int e = lane + 64 * i;
     const bool r = e < rot, lo = e < rh;
     const int pe = r ? (lo ? e + rh : e - rh) : e, fi = r ? (lo ? e : e - rh) : 0;
-    v[i] = ld_sum(x, pst, np, e);
-    vp[i] = ld_sum(x, pst, np, pe);
-    gv[i] = g[e];
-    gp[i] = g[pe];
-    c[i] = r ? cs[fi] : 1.f;
-    sv[i] = r ? (lo ? -sn[fi] : sn[fi]) : 0.f;
+    in.v[i] = ld_part(x, pst, np, e);
+    in.vp[i] = ld_part(x, pst, np, pe);
+    in.gv[i] = g[e];
+    in.gp[i] = g[pe];
+    const float cv = cs[fi], sv = sn[fi];
+    in.c[i] = r ? cv : 1.f;
+    in.s[i] = r ? (lo ? -sv : sv) : 0.f;
   }
+}
+
+template <int D>
+__device__ __forceinline__ void nr_finish(const NormRopeIn<D>& in, int np, int rot, float eps, float mul,
+                                          float (&y)[D / 64]) {
+  constexpr int NE = D / 64;
+  float v[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) v[i] = psum(in.v[i], np);
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < NE; ++i) ss = fmaf(v[i], v[i], ss);
   const float inv = rsqrtf(wave_sum(ss) / (float)D + eps);
+  if constexpr (NE >= 2) {
+    if (rot == D) {
+      constexpr int H = NE / 2;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float a = v[i] * inv * in.gv[i], b = v[i + H] * inv * in.gv[i + H];
+        y[i] = (a * in.c[i] - b * in.s[i]) * mul;
+        y[i + H] = (b * in.c[i] + a * in.s[i]) * mul;
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NE; ++i) {
-    const float a = v[i] * inv * gv[i], b = vp[i] * inv * gp[i];
-    y[i] = (a * c[i] + b * sv[i]) * mul;
+    const float a = v[i] * inv * in.gv[i], b = psum(in.vp[i], np) * inv * in.gp[i];
+    y[i] = (a * in.c[i] + b * in.s[i]) * mul;
   }
 }
 
@@ -276,9 +298,32 @@ __global__ __launch_bounds__(ONE ? 1024 : 256) void attn_decode_kernel(const Att
   const float qscale = p.scale * LOG2E;
   const bool has_new = (pos >= c0 && pos < c1);
 
-  // ---- this lane's first key/value rows go out before anything else; the
-  //      q/k projections and RoPE tables below are fetched in the same round
-  //      trip.  (Row `pos` is not written yet: it is taken from LDS below.)
+  // ---- every load of the prologue in one round trip, in this order: the q
+  //      heads of this wave and (the chunk holding pos, last wave) the new
+  //      token's k and v, then this lane's first key/value rows.  The loads
+  //      complete in order, so the q/k normalisation waits only for the first
+  //      group while the key/value rows are still in flight.  (Row `pos` is
+  //      not in the cache yet: it is taken from LDS below.)
+  const float* cs_row = p.cos_t + (size_t)pos * (p.rot >> 1);
+  const float* sn_row = p.sin_t + (size_t)pos * (p.rot >> 1);
+  constexpr int QPW = (REP + NW - 1) / NW;             // q heads per wave, at most
+  NormRopeIn<D> qin[QPW];
+#pragma unroll
+  for (int t = 0; t < QPW; ++t) {
+    const int r = wid + NW * t;
+    if (r < REP)
+      nr_fetch<D>(row + (size_t)(j * REP + r) * D * qmul, pst, p.qkv_np, p.gq, cs_row, sn_row, p.rot, lane, qin[t]);
+  }
+  const bool do_new = has_new && wid == NW - 1;
+  const float* kr = row + (size_t)p.nq * D * qmul + j * D;
+  const float* vr = kr + (size_t)p.nkv * D;
+  NormRopeIn<D> kin;
+  Part2 vv[D / 64];
+  if (do_new) {
+    nr_fetch<D>(kr, pst, p.qkv_np, p.gk, cs_row, sn_row, p.rot, lane, kin);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) vv[i] = ld_part(vr, pst, p.qkv_np, lane + 64 * i);
+  }
   const int ufirst = c0 + wid * 4 + grp;
   RawKV<KV, DP> pk[NPRE], pv[NPRE];
 #pragma unroll
@@ -288,28 +333,25 @@ __global__ __launch_bounds__(ONE ? 1024 : 256) void attn_decode_kernel(const Att
     pv[i].load(vb + (size_t)u * D + li * DP);
   }
 
-  // ---- q heads of this group: RMSNorm over d, RoPE at pos, pre-scale
-  const float* cs_row = p.cos_t + (size_t)pos * (p.rot >> 1);
-  const float* sn_row = p.sin_t + (size_t)pos * (p.rot >> 1);
-  for (int r = wid; r < REP; r += NW) {
-    const int h = j * REP + r;
-    float y[D / 64];
-    norm_rope_wave<D>(row + (size_t)h * D * qmul, pst, p.qkv_np, p.gq, cs_row, sn_row, p.rot, p.eps, qscale, lane, y);
+  // ---- q heads: RMSNorm over d, RoPE at pos, pre-scale
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) qs[r][lane + 64 * i] = y[i];
+  for (int t = 0; t < QPW; ++t) {
+    const int r = wid + NW * t;
+    if (r < REP) {
+      float y[D / 64];
+      nr_finish<D>(qin[t], p.qkv_np, p.rot, p.eps, qscale, y);
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) qs[r][lane + 64 * i] = y[i];
+    }
   }
   // ---- the new token's k, v if it falls in this chunk: normalise, rotate, append
-  if (has_new && wid == NW - 1) {
-    const float* kr = row + (size_t)p.nq * D * qmul + j * D;
-    const float* vr = kr + (size_t)p.nkv * D;
-    float vv[D / 64], y[D / 64];
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) vv[i] = ld_sum(vr, pst, p.qkv_np, lane + 64 * i);
-    norm_rope_wave<D>(kr, pst, p.qkv_np, p.gk, cs_row, sn_row, p.rot, p.eps, 1.f, lane, y);
+  if (do_new) {
+    float y[D / 64];
+    nr_finish<D>(kin, p.qkv_np, p.rot, p.eps, 1.f, y);
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) {
       const int e = lane + 64 * i;
-      const KV kk = from_f32<KV>(y[i]), vk = from_f32<KV>(vv[i]);
+      const KV kk = from_f32<KV>(y[i]), vk = from_f32<KV>(psum(vv[i], p.qkv_np));
       kb[(size_t)pos * D + e] = kk;
       vb[(size_t)pos * D + e] = vk;
       knew[e] = to_f32(kk);

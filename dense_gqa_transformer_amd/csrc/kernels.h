@@ -152,7 +152,7 @@ hipError_t attn_prefill_fa(const AttnPrefillParams& p, hipStream_t s);
 // the query heads of its KV head; attn_combine merges them.
 struct AttnDecodeParams {
   const float* qkv;            // [qkv_np][B, (nq+2nkv)*d] fp32 (raw projections; qkv_np
-  int qkv_np;                  //   split-K partials, summed on load; 1 = the plain rows)
+  int qkv_np;                  //   (1 or 2) split-K partials, summed on load; 1 = the plain rows)
   void* kcache; void* vcache; int kv_dt;
   const float* gq; const float* gk; float eps;
   const float* cos_t; const float* sin_t;
