@@ -474,24 +474,27 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
   for (int e = 0; e < NE; ++e) o[e] = 0.f;
   for (int c0 = 0; c0 < nvalid; c0 += CB) {
     const int n = min(CB, nvalid - c0);
-    // lane c < n holds chunk c0 + c's max and sum; every lane holds its output slice of each chunk
-    const float mc = (lane < n) ? pr[(size_t)(c0 + lane) * ST + D] : -INFINITY;
-    const float lc = (lane < n) ? pr[(size_t)(c0 + lane) * ST + D + 1] : 0.f;
+    // lane c < n holds chunk c0 + c's max and sum; every lane holds its output
+    // slice of each chunk.  The loads are unconditional (chunks past the
+    // last re-read it and get weight 0), so they all go out together.
+    const float* pl = pr + (size_t)(c0 + min(lane, n - 1)) * ST;
+    const float mraw = pl[D], lraw = pl[D + 1];
     float ov[CB][NE];
 #pragma unroll
     for (int i = 0; i < CB; ++i)
 #pragma unroll
-      for (int e = 0; e < NE; ++e) ov[i][e] = (i < n) ? pr[(size_t)(c0 + i) * ST + lane + 64 * e] : 0.f;
+      for (int e = 0; e < NE; ++e) ov[i][e] = pr[(size_t)(c0 + min(i, n - 1)) * ST + lane + 64 * e];
+    const float mc = (lane < n) ? mraw : -INFINITY;
     const float mb = wave_max(mc);
     const float mn = fmaxf(M, mb);
     const float corr = (M == -INFINITY) ? 0.f : exp2f(M - mn);
     const float wl = (lane < n) ? exp2f(mc - mn) : 0.f;
-    L = L * corr + wave_sum(lc * wl);
+    L = L * corr + wave_sum((lane < n) ? lraw * wl : 0.f);
 #pragma unroll
     for (int e = 0; e < NE; ++e) o[e] *= corr;
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
-      const float wi = __shfl(wl, i);
+      const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
 #pragma unroll
       for (int e = 0; e < NE; ++e) o[e] = fmaf(wi, ov[i][e], o[e]);
     }
