@@ -109,6 +109,19 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
     }
   };
   Raw<W> ra[CPL][RPW], rb[CPL][RPW];
+  // RESID: the residual values this wave adds to are requested first (each
+  // output element belongs to one wave), so the epilogue needs no further
+  // round trip
+  float old[EPI == EPI_RESID ? RPW : 1][MB];
+  if constexpr (EPI == EPI_RESID) {
+    static_assert(GROUPS == 1, "one row group per wave");
+    const int rb0 = blockIdx.x * rows_per_block + wid * RPW;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+        old[i][m] = p.out[(size_t)(m0 + min(m, mcount - 1)) * p.ldo + min(rb0 + i, slots_total - 1)];
+  }
   float inv[MB];
   float xv[XREG ? MB : 1][XREG ? CPL : 1][CE];
   if constexpr (XREG) {
@@ -251,7 +264,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
           if (EPI == EPI_STORE) {
             p.out[o] = acc[i][m];
           } else if (EPI == EPI_RESID) {
-            p.out[o] += acc[i][m];
+            p.out[o] = old[EPI == EPI_RESID ? i : 0][m] + acc[i][m];
           } else if (EPI == EPI_SWIGLU) {
             // slot rows come in (gate, up) pairs: i even = gate, i + 1 = up
             if ((i & 1) == 0) p.out[o] = silu(acc[i][m]) * acc[(i + 1) % RPW][m];
