@@ -734,7 +734,7 @@ struct AttnSplit {
 };
 static AttnSplit attn_split(const fs_model* m, int B, int maxn, bool pow2, int mode) {
   const fs_config& c = m->cfg;
-  const bool can1 = attn_decode_onepass_ok(c.n_heads, c.n_kv_heads, c.head_dim);
+  const bool can1 = attn_decode_onepass_ok(c.n_heads, c.n_kv_heads, c.head_dim) && !m->gated;
   const bool one = can1 && (mode == 2 || (mode == 0 && maxn <= ONEPASS_MAX_CTX &&
                                           (long long)B * c.n_kv_heads <= ONEPASS_MAX_GROUPS));
   if (one) return {0, 1, true};
@@ -776,12 +776,12 @@ static fs_status enqueue_decode(fs_model* m, const int32_t* tokens, int B, float
       a.scale = 1.0f / std::sqrt((float)c.head_dim);
       a.rot = m->rot; a.gated = m->gated;
       LAUNCH(m, "attn", s, attn_decode(a, s));
+      // the gated variant's output gate is applied by the merge (the one-pass
+      // form is not used for it)
       if (!sp.onepass)
         LAUNCH(m, "combine", s, attn_combine(m->part, m->d_pos, B, c.n_heads, c.head_dim, sp.chunk, sp.nchunks,
-                                             m->attn, skinny ? DT_F32 : DT_BF16, s));
-      if (m->gated)
-        LAUNCH(m, "attn_gate", s, attn_gate(m->attn, skinny ? DT_F32 : DT_BF16, m->qkv, DT_F32, B, c.n_heads,
-                                       c.head_dim, m->qkv_w, s));
+                                             m->attn, skinny ? DT_F32 : DT_BF16, s,
+                                             m->gated ? (const float*)m->qkv : nullptr, m->qkv_w));
       return FS_OK;
     };
     st = skinny ? block_skinny(m, L, B, attention, s) : block_gemm(m, L, B, true, attention, s);

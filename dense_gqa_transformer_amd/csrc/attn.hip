@@ -464,9 +464,16 @@ __global__ __launch_bounds__(ONE ? 1024 : 256) void attn_decode_kernel(const Att
 template <typename TO, int D>
 __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ part,
                                                           const int32_t* __restrict__ positions, int nq,
-                                                          int chunk, int nchunks, TO* __restrict__ out) {
+                                                          int chunk, int nchunks, TO* __restrict__ out,
+                                                          const float* __restrict__ gate, int ldg) {
   constexpr int ST = D + 2, NE = D / 64, CB = 32;
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  // gated variant: this head's output gate (requested first, applied at the store)
+  float gv[NE];
+  if (gate != nullptr) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) gv[e] = gate[(size_t)b * ldg + (size_t)(2 * h + 1) * D + lane + 64 * e];
+  }
   const float* pr = part + ((size_t)b * nq + h) * nchunks * ST;
   const int nvalid = (positions[b] + chunk) / chunk;
   float M = -INFINITY, L = 0.f, o[NE];
@@ -503,25 +510,29 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
   const float invL = 1.f / L;
   TO* orow = out + ((size_t)b * nq + h) * D;
 #pragma unroll
-  for (int e = 0; e < NE; ++e) orow[lane + 64 * e] = from_f32<TO>(o[e] * invL);
+  for (int e = 0; e < NE; ++e) {
+    float y = o[e] * invL;
+    if (gate != nullptr) y = y / (1.f + __expf(-gv[e]));
+    orow[lane + 64 * e] = from_f32<TO>(y);
+  }
 }
 
 hipError_t attn_combine(const float* part, const int32_t* positions, int B, int nq, int d, int chunk,
-                        int nchunks, void* out, int o_dt, hipStream_t s) {
+                        int nchunks, void* out, int o_dt, hipStream_t s, const float* gate, int ldg) {
   if (B <= 0) return hipSuccess;
   const dim3 grid(nq, B);
   if (d == 128 && o_dt == DT_BF16)
-    attn_combine_kernel<bf16, 128><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (bf16*)out);
+    attn_combine_kernel<bf16, 128><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (bf16*)out, gate, ldg);
   else if (d == 128)
-    attn_combine_kernel<float, 128><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (float*)out);
+    attn_combine_kernel<float, 128><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (float*)out, gate, ldg);
   else if (d == 256 && o_dt == DT_BF16)
-    attn_combine_kernel<bf16, 256><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (bf16*)out);
+    attn_combine_kernel<bf16, 256><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (bf16*)out, gate, ldg);
   else if (d == 256)
-    attn_combine_kernel<float, 256><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (float*)out);
+    attn_combine_kernel<float, 256><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (float*)out, gate, ldg);
   else if (d == 64 && o_dt == DT_BF16)
-    attn_combine_kernel<bf16, 64><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (bf16*)out);
+    attn_combine_kernel<bf16, 64><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (bf16*)out, gate, ldg);
   else if (d == 64)
-    attn_combine_kernel<float, 64><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (float*)out);
+    attn_combine_kernel<float, 64><<<grid, 64, 0, s>>>(part, positions, nq, chunk, nchunks, (float*)out, gate, ldg);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -174,8 +174,11 @@ hipError_t attn_decode(const AttnDecodeParams& p, hipStream_t s);
 constexpr int ATTN_ONEPASS_MAX_REP_D = 256;
 bool attn_decode_onepass_ok(int nq, int nkv, int d);
 // out[b, h*d + e] from the chunk partials of sequence b (chunks 0..positions[b]/chunk).
+// gate (optional, fp32 rows of width ldg, the gated variant's q projection with
+// per-head interleaved [q | gate]): out[b, h*d + e] *= sigmoid(gate[b*ldg + (2h+1)*d + e]).
 hipError_t attn_combine(const float* part, const int32_t* positions, int B, int nq, int d, int chunk,
-                        int nchunks, void* out, int o_dt, hipStream_t s);
+                        int nchunks, void* out, int o_dt, hipStream_t s, const float* gate = nullptr,
+                        int ldg = 0);
 
 // ---------------------------------------------------------------- argmax
 // out[b] = greedy ID of row b of logits [B, V] (row stride ldl).
