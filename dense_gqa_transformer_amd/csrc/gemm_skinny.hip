@@ -25,7 +25,7 @@ namespace {
 
 constexpr int SK_WAVES = 4;
 
-template <int EPI, int NT, int MT>
+template <int EPI, int NT, int MT, bool PIPE>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16* __restrict__ A, int lda,
                                                           const bf16* __restrict__ A_lo,
                                                           const bf16* __restrict__ B, int ldb,
@@ -63,32 +63,66 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16* __restrict
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[t][i][e] = 0.f;
 
-#pragma unroll 2
-  for (int k = 0; k < kw; k += 64) {
-    bf16x8 bv[NT][4], av[MT][4], alv[MT][4];
+  // One 64-wide K chunk's fragments.  PIPE (launches of a few hundred
+  // workgroups, where each one's latency is the cost): two buffers ping-pong,
+  // chunk c + 1 requested before chunk c's products in a loop body without
+  // branches (the tail of one or two chunks is peeled), so that the
+  // compiler's in-order load counting lets the two chunks overlap.  Otherwise
+  // one buffer, fewer registers and more workgroups per CU.
+  struct Frag {
+    bf16x8 b[NT][4], a[MT][4], al[MT][4];
+  };
+  auto load = [&](int k, Frag& f) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) bv[t][s] = *reinterpret_cast<const bf16x8*>(bp[t] + k + 8 * s);
+      for (int s = 0; s < 4; ++s) f.b[t][s] = *reinterpret_cast<const bf16x8*>(bp[t] + k + 8 * s);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) av[i][s] = *reinterpret_cast<const bf16x8*>(ap[i] + k + 8 * s);
+      for (int s = 0; s < 4; ++s) f.a[i][s] = *reinterpret_cast<const bf16x8*>(ap[i] + k + 8 * s);
     if (lo) {
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) alv[i][s] = *reinterpret_cast<const bf16x8*>(alp[i] + k + 8 * s);
+        for (int s = 0; s < 4; ++s) f.al[i][s] = *reinterpret_cast<const bf16x8*>(alp[i] + k + 8 * s);
     }
+  };
+  auto mma = [&](const Frag& f) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-          acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[t][s], av[i][s], acc[t][i], 0, 0, 0);
-          if (lo) acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[t][s], alv[i][s], acc[t][i], 0, 0, 0);
+          acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[t][s], f.a[i][s], acc[t][i], 0, 0, 0);
+          if (lo) acc[t][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[t][s], f.al[i][s], acc[t][i], 0, 0, 0);
         }
+  };
+  const int nk = kw / 64;                      // >= 1 (K % (256 * splits) == 0)
+  if constexpr (PIPE) {
+    Frag fa, fb;
+    load(0, fa);
+    int c = 0;
+    for (; c + 2 < nk; c += 2) {
+      load(64 * (c + 1), fb);
+      mma(fa);
+      load(64 * (c + 2), fa);
+      mma(fb);
+    }
+    if (c + 1 < nk) {
+      load(64 * (c + 1), fb);
+      mma(fa);
+      mma(fb);
+    } else {
+      mma(fa);
+    }
+  } else {
+    for (int c = 0; c < nk; ++c) {
+      Frag f;
+      load(64 * c, f);
+      mma(f);
+    }
   }
 
   // ---- the four K quarters meet in LDS: red[w][m * RS + n]
@@ -143,10 +177,14 @@ template <int EPI, int NT>
 hipError_t launch_nt(const bf16* a, int lda, const bf16* alo, const bf16* b, int ldb, void* out, int ldc, int M,
                      int N, int K, const float* cs, int ksplit, hipStream_t s) {
   const dim3 grid((N + 32 * NT - 1) / (32 * NT), ksplit);
-  if (M <= 32)
-    gemm_skinny_kernel<EPI, NT, 1><<<grid, 256, 0, s>>>(a, lda, alo, b, ldb, out, ldc, M, N, K, cs);
-  else
-    gemm_skinny_kernel<EPI, NT, 2><<<grid, 256, 0, s>>>(a, lda, alo, b, ldb, out, ldc, M, N, K, cs);
+  const bool pipe = (long long)grid.x * grid.y <= 512;
+  if (M <= 32) {
+    if (pipe) gemm_skinny_kernel<EPI, NT, 1, true><<<grid, 256, 0, s>>>(a, lda, alo, b, ldb, out, ldc, M, N, K, cs);
+    else gemm_skinny_kernel<EPI, NT, 1, false><<<grid, 256, 0, s>>>(a, lda, alo, b, ldb, out, ldc, M, N, K, cs);
+  } else {
+    if (pipe) gemm_skinny_kernel<EPI, NT, 2, true><<<grid, 256, 0, s>>>(a, lda, alo, b, ldb, out, ldc, M, N, K, cs);
+    else gemm_skinny_kernel<EPI, NT, 2, false><<<grid, 256, 0, s>>>(a, lda, alo, b, ldb, out, ldc, M, N, K, cs);
+  }
   return hipGetLastError();
 }
 
