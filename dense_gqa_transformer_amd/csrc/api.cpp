@@ -718,14 +718,14 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
 // How the decode attention covers the context (longest sequence maxn keys).
 // Short contexts at small batch take the one-pass kernel: one 16-wave
 // workgroup per (sequence, KV head) and no merge launch (one CU streams the
-// head's whole context at ~60 GB/s, so this pays only below ~180 keys).
+// head's whole context at ~60 GB/s, so this pays only below ~110 keys).
 // Otherwise split-K chunks of at least min_chunk positions, doubled (up to
 // 256) while a sequence would need more than 32 chunks (the merge reads up to
 // 32 partials in one round trip and loops beyond) or the launch would exceed
 // 1024 workgroups; with pow2 the chunk count is rounded up to a power of two
 // (chunks past a sequence's end exit at once) so one captured graph serves
 // many consecutive positions.
-constexpr int ONEPASS_MAX_CTX = 128;
+constexpr int ONEPASS_MAX_CTX = 96;
 constexpr int SPLIT_MAX_CHUNKS = 32;
 constexpr int ONEPASS_MAX_GROUPS = 64;      // B * n_kv_heads
 struct AttnSplit {

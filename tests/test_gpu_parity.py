@@ -228,11 +228,11 @@ def test_decode_bs1_teacher_forced(big):
 
 
 def test_decode_crosses_onepass_context(big):
-    # batch-1 steps at 127..130 keys: the attention switches from the one-pass
-    # form (up to 128 keys) to split-K chunks plus the merge launch (another
+    # batch-1 steps at 95..99 keys: the attention switches from the one-pass
+    # form (up to 96 keys) to split-K chunks plus the merge launch (another
     # captured graph) in the middle of the sequence
     shape, model = big
-    prompt = synth.tokens(4242, shape.vocab, 126)
+    prompt = synth.tokens(4242, shape.vocab, 94)
     orc = fresh_oracle(shape)
     ref = orc.prefill(0, prompt)
     model.prefill(dev_tokens(prompt[None, :]), [5])
