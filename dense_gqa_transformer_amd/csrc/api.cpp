@@ -122,7 +122,7 @@ struct fs_model {
   void* hbuf = nullptr;
   // decode scratch
   int32_t* d_pos = nullptr;
-  int32_t* d_slot = nullptr;
+  int32_t* d_slot = nullptr;      // = d_pos + max_seqs (one allocation, staged by one copy)
   float* part = nullptr;
   int max_chunks = 0;
   // split-K partials of the few-row O / down projections, [KSPLIT_MAX][64][hidden];
@@ -174,7 +174,7 @@ struct fs_model {
     hipFree(wblob); hipFree(nblob); hipFree(sblob); hipFree(wconv); hipFree(kcache); hipFree(vcache);
     hipFree(rope_cos); hipFree(rope_sin);
     hipFree(x); hipFree(xn); hipFree(qkv); hipFree(qr); hipFree(attn); hipFree(hbuf);
-    hipFree(d_pos); hipFree(d_slot); hipFree(part); hipFree(kpart);
+    hipFree(d_pos); hipFree(part); hipFree(kpart);
     hipFree(lm_pv); hipFree(lm_pi); hipFree(logits_tmp); hipFree(sample_scr);
     for (int i = 0; i < STAGE_RING; ++i)
       if (stage_ev[i]) hipEventDestroy(stage_ev[i]);
@@ -231,16 +231,21 @@ fs_status ensure_rows(fs_model* m, long long rows, hipStream_t s) {
   return FS_OK;
 }
 
-// Copies two host int arrays [n] to d_pos / d_slot through the pinned ring.
+// Copies two host int arrays [n] to d_pos / d_slot through the pinned ring:
+// the ring slot mirrors the device layout [positions | slots] (max_seqs each),
+// so with positions both go in one copy.
 fs_status stage_ints(fs_model* m, const int32_t* a, const int32_t* b, int n, hipStream_t s) {
   const int i = m->stage_next;
+  const int ms = m->cfg.max_seqs;
   m->stage_next = (i + 1) % STAGE_RING;
   if (m->stage_used[i]) HIP_TRY(hipEventSynchronize(m->stage_ev[i]));
-  int32_t* buf = m->stage + (size_t)i * 2 * m->cfg.max_seqs;
+  int32_t* buf = m->stage + (size_t)i * 2 * ms;
   if (a) std::memcpy(buf, a, sizeof(int32_t) * n);
-  std::memcpy(buf + m->cfg.max_seqs, b, sizeof(int32_t) * n);
-  if (a) HIP_TRY(hipMemcpyAsync(m->d_pos, buf, sizeof(int32_t) * n, hipMemcpyHostToDevice, s));
-  HIP_TRY(hipMemcpyAsync(m->d_slot, buf + m->cfg.max_seqs, sizeof(int32_t) * n, hipMemcpyHostToDevice, s));
+  std::memcpy(buf + ms, b, sizeof(int32_t) * n);
+  if (a)
+    HIP_TRY(hipMemcpyAsync(m->d_pos, buf, sizeof(int32_t) * (ms + n), hipMemcpyHostToDevice, s));
+  else
+    HIP_TRY(hipMemcpyAsync(m->d_slot, buf + ms, sizeof(int32_t) * n, hipMemcpyHostToDevice, s));
   HIP_TRY(hipEventRecord(m->stage_ev[i], s));
   m->stage_used[i] = true;
   return FS_OK;
@@ -613,14 +618,14 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   // decode scratch
   m->max_chunks = (c.max_ctx + 31) / 32;
   const int lm_blocks = gemv_logits_blocks(m->wdt, c.vocab, c.hidden);
-  if (dalloc(&m->d_pos, (size_t)c.max_seqs * 4) != hipSuccess ||
-      dalloc(&m->d_slot, (size_t)c.max_seqs * 4) != hipSuccess ||
+  if (dalloc(&m->d_pos, (size_t)2 * c.max_seqs * 4) != hipSuccess ||
       dalloc(&m->part, (size_t)c.max_seqs * c.n_heads * m->max_chunks * (c.head_dim + 2) * 4) != hipSuccess ||
       dalloc(&m->kpart, (size_t)KSPLIT_MAX_ROWS * std::max(KSPLIT_MAX * c.hidden, KSPLIT_MAX * m->qkv_w) * 4) !=
           hipSuccess ||
       dalloc(&m->lm_pv, (size_t)GEMV_LOGITS_MAX_M * lm_blocks * 4) != hipSuccess ||
       dalloc(&m->lm_pi, (size_t)GEMV_LOGITS_MAX_M * lm_blocks * 4) != hipSuccess)
     return bail(FS_ERR_OOM, "decode scratch allocation failed");
+  m->d_slot = m->d_pos + c.max_seqs;
   if (hipHostMalloc((void**)&m->stage, sizeof(int32_t) * 2 * c.max_seqs * STAGE_RING, hipHostMallocDefault) !=
       hipSuccess)
     return bail(FS_ERR_OOM, "pinned staging allocation failed");
