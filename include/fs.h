@@ -111,7 +111,13 @@ typedef struct fs_model fs_model;
  * the weights into library-owned device memory (fused QKV, paired gate/up),
  * so the caller may free its tensors on return.  Allocates the KV cache
  * (max_seqs * max_ctx positions per layer) and the RoPE tables.  All slots
- * start empty.  *out receives the handle (NULL on error). */
+ * start empty.  *out receives the handle (NULL on error).
+ * Environment read here, for measurement and tests (results agree to
+ * rounding either way): FS_DECODE_GRAPHS=0 launches decode steps one kernel
+ * at a time instead of replaying captured graphs; FS_DECODE_ATTN=split or
+ * =onepass forces one form of the decode attention (split-K chunks plus a
+ * merge launch, or one workgroup per sequence and KV head) where it exists;
+ * FS_DECODE_MIN_CHUNK=32|64|128|256 sets the shortest split-K chunk. */
 fs_status fs_model_create(const fs_config *cfg, const fs_weights *w,
                           void *stream, fs_model **out);
 
