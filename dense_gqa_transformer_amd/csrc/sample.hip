@@ -30,6 +30,7 @@ namespace fsk {
 namespace {
 
 constexpr int NT = 256;      // threads per block
+constexpr int PER = 8;       // IDs per thread requested together (a block's slice in one round trip)
 constexpr int NB1 = 4096;    // bins, levels 1 and 2 (12 bits each)
 constexpr int NB3 = 256;     // bins, level 3 (8 bits)
 
@@ -181,10 +182,14 @@ __global__ __launch_bounds__(NT) void sample_pass_kernel(const SampleParams p) {
     pre = (b1 << 12) | (uint32_t)b;
     pshift = 8;
   } else if (MODE == 3) {
-    int b;
-    uint32_t r;
-    select_desc<uint32_t>(sc->c3, NB3, sc->kr2, &b, &r);
-    kcut = (sc->kb1 << 20) | (sc->kb2 << 8) | (uint32_t)b;
+    if (p.top_k > 0) {
+      int b;
+      uint32_t r;
+      select_desc<uint32_t>(sc->c3, NB3, sc->kr2, &b, &r);
+      kcut = (sc->kb1 << 20) | (sc->kb2 << 8) | (uint32_t)b;
+    } else {
+      kcut = 0u;                              // no top-k: every finite key is kept
+    }
     if (store) sc->kcut = kcut;
   } else if (MODE == 4) {
     const float z = hist_total<float>(sc->m1, NB1);
@@ -221,9 +226,17 @@ __global__ __launch_bounds__(NT) void sample_pass_kernel(const SampleParams p) {
   __syncthreads();
   uint32_t lmax = 0u, lcnt = 0u;
   float lsum = 0.f;
-  for (int i = i0 + threadIdx.x; i < i1; i += NT) {
-    const float v = x[i];
-    if (!finite(v)) continue;
+  for (int base = i0; base < i1; base += NT * PER) {
+    // the thread's IDs of this stretch, all requested before any is used
+    // (past the slice the last ID is re-read and skipped)
+    float vals[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) vals[j] = x[min(base + (int)threadIdx.x + j * NT, i1 - 1)];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+    const int i = base + (int)threadIdx.x + j * NT;
+    const float v = vals[j];
+    if (i >= i1 || !finite(v)) continue;
     const uint32_t key = fkey(v);
     if (MODE == 0) {
       atomicAdd(&hc[key >> 20], 1u);
@@ -240,6 +253,7 @@ __global__ __launch_bounds__(NT) void sample_pass_kernel(const SampleParams p) {
       } else if (key >= cut) {
         lsum += e;
       }
+    }
     }
   }
   if (MODE == 0) {
@@ -304,13 +318,25 @@ __global__ __launch_bounds__(NT) void sample_final_kernel(const SampleParams p) 
   const float* x = p.logits + (size_t)row * p.ld;
   const float xmax = keyf(sc->maxkey);
   const int i0 = sblk * p.slice, i1 = min(i0 + p.slice, p.V);
-  // each thread takes a contiguous run of IDs
+  // each thread takes a contiguous run of IDs (requested together while the
+  // run fits PER; the clamped re-reads past the run are skipped)
   const int per = (p.slice + NT - 1) / NT;
   const int a0 = i0 + threadIdx.x * per, a1 = min(a0 + per, i1);
   float mine = 0.f;
-  for (int i = a0; i < a1; ++i) {
-    const float v = x[i];
-    if (finite(v) && fkey(v) >= cut) mine += __builtin_amdgcn_exp2f((v - xmax) * p.sc);
+  if (per <= PER) {
+    float vals[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) vals[j] = x[min(a0 + j, max(a1 - 1, i0))];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const float v = vals[j];
+      if (a0 + j < a1 && finite(v) && fkey(v) >= cut) mine += __builtin_amdgcn_exp2f((v - xmax) * p.sc);
+    }
+  } else {
+    for (int i = a0; i < a1; ++i) {
+      const float v = x[i];
+      if (finite(v) && fkey(v) >= cut) mine += __builtin_amdgcn_exp2f((v - xmax) * p.sc);
+    }
   }
   __shared__ float runs[NT];
   __shared__ int swho;
@@ -353,8 +379,10 @@ hipError_t sample_rows(const SampleParams& p, hipStream_t s) {
   const dim3 grid(p.G, p.B);
   sample_zero_kernel<<<p.B, NT, 0, s>>>(p.scr);
   sample_pass_kernel<0><<<grid, NT, 0, s>>>(p);
-  sample_pass_kernel<1><<<grid, NT, 0, s>>>(p);
-  sample_pass_kernel<2><<<grid, NT, 0, s>>>(p);
+  if (p.top_k > 0) {                              // the top-k cut's two upper radix levels
+    sample_pass_kernel<1><<<grid, NT, 0, s>>>(p);
+    sample_pass_kernel<2><<<grid, NT, 0, s>>>(p);
+  }
   sample_pass_kernel<3><<<grid, NT, 0, s>>>(p);   // m1: Z_k, needed by the draw too
   if (p.top_p < 1.f) {
     sample_pass_kernel<4><<<grid, NT, 0, s>>>(p);
