@@ -78,37 +78,48 @@ __device__ T block_inclusive(T v, T* before, T* total) {
 // >= target, and target minus what lies above.  When rounding leaves the
 // total short of target, the lowest non-empty bin.  Called by all NT threads;
 // every thread gets the result.
-template <typename T>
-__device__ void select_desc(const T* h, int nb, T target, int* out_bin, T* out_rem) {
+template <typename T, int NB>
+__device__ void select_desc(const T* h, T target, int* out_bin, T* out_rem) {
+  static_assert(NB % NT == 0, "whole bins per thread");
+  constexpr int W = NB / NT;                  // bins per thread (16 or 1)
   __shared__ int sbin;
   __shared__ T srem;
   const int t = threadIdx.x;
-  const int w = nb / NT;                      // bins per thread (16 or 1)
-  const int hi = nb - t * w;                  // thread t owns bins [hi - w, hi), read downward
+  const int hi = NB - t * W;                  // thread t owns bins [hi - W, hi), read downward
+  T hv[W];                                    // all of them requested at once, kept for the walk
+#pragma unroll
+  for (int i = 0; i < W; ++i) hv[i] = h[hi - 1 - i];
   T s = 0;
-  for (int i = 1; i <= w; ++i) s += h[hi - i];
+#pragma unroll
+  for (int i = 0; i < W; ++i) s += hv[i];
   if (t == 0) sbin = -1;
   __syncthreads();
   T above, total;
   const T upto = block_inclusive<T>(s, &above, &total);
   if (above < target && upto >= target) {     // exactly one thread's interval holds target
+    // descending walk: the first non-empty bin that brings the mass to target
+    // (or, failing that, the last non-empty bin seen)
     T a = above, last_a = above;
     int last = -1;
-    for (int i = 1; i <= w; ++i) {
-      const T v = h[hi - i];
-      if (v > 0) {
-        last = hi - i;
-        last_a = a;
-        if (a + v >= target) break;
+    bool done = false;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      if (!done) {
+        const T v = hv[i];
+        if (v > 0) {
+          last = hi - 1 - i;
+          last_a = a;
+          done = (a + v >= target);
+        }
+        a += v;
       }
-      a += v;
     }
     if (last >= 0) { sbin = last; srem = target - last_a; }
   }
   __syncthreads();
   if (sbin < 0 && t == 0) {                   // total fell short: lowest non-empty bin
     int b = 0;
-    for (int i = 0; i < nb; ++i) if (h[i] > 0) { b = i; break; }
+    for (int i = 0; i < NB; ++i) if (h[i] > 0) { b = i; break; }
     sbin = b;
     srem = h[b];
   }
@@ -119,11 +130,15 @@ __device__ void select_desc(const T* h, int nb, T target, int* out_bin, T* out_r
 }
 
 // Sum of a histogram in a fixed order (identical in every block)
-template <typename T>
-__device__ T hist_total(const T* h, int nb) {
-  const int w = nb / NT;
+template <typename T, int NB>
+__device__ T hist_total(const T* h) {
+  constexpr int W = NB / NT;
+  T hv[W];
+#pragma unroll
+  for (int i = 0; i < W; ++i) hv[i] = h[threadIdx.x * W + i];
   T s = 0;
-  for (int i = 0; i < w; ++i) s += h[threadIdx.x * w + i];
+#pragma unroll
+  for (int i = 0; i < W; ++i) s += hv[i];
   T before, total;
   block_inclusive<T>(s, &before, &total);
   return total;
@@ -169,7 +184,7 @@ __global__ __launch_bounds__(NT) void sample_pass_kernel(const SampleParams p) {
     const uint32_t k = (p.top_k <= 0 || (uint32_t)p.top_k > nf) ? nf : (uint32_t)p.top_k;
     int b;
     uint32_t r;
-    select_desc<uint32_t>(sc->c1, NB1, k, &b, &r);
+    select_desc<uint32_t, NB1>(sc->c1, k, &b, &r);
     if (store) { sc->kb1 = (uint32_t)b; sc->kr1 = r; }
     pre = (uint32_t)b;
     pshift = 20;
@@ -177,7 +192,7 @@ __global__ __launch_bounds__(NT) void sample_pass_kernel(const SampleParams p) {
     int b;
     uint32_t r;
     const uint32_t b1 = sc->kb1;
-    select_desc<uint32_t>(sc->c2, NB1, sc->kr1, &b, &r);
+    select_desc<uint32_t, NB1>(sc->c2, sc->kr1, &b, &r);
     if (store) { sc->kb2 = (uint32_t)b; sc->kr2 = r; }
     pre = (b1 << 12) | (uint32_t)b;
     pshift = 8;
@@ -185,17 +200,17 @@ __global__ __launch_bounds__(NT) void sample_pass_kernel(const SampleParams p) {
     if (p.top_k > 0) {
       int b;
       uint32_t r;
-      select_desc<uint32_t>(sc->c3, NB3, sc->kr2, &b, &r);
+      select_desc<uint32_t, NB3>(sc->c3, sc->kr2, &b, &r);
       kcut = (sc->kb1 << 20) | (sc->kb2 << 8) | (uint32_t)b;
     } else {
       kcut = 0u;                              // no top-k: every finite key is kept
     }
     if (store) sc->kcut = kcut;
   } else if (MODE == 4) {
-    const float z = hist_total<float>(sc->m1, NB1);
+    const float z = hist_total<float, NB1>(sc->m1);
     int b;
     float r;
-    select_desc<float>(sc->m1, NB1, p.top_p * z, &b, &r);
+    select_desc<float, NB1>(sc->m1, p.top_p * z, &b, &r);
     if (store) { sc->z = z; sc->pb1 = (uint32_t)b; sc->pr1 = r; }
     pre = (uint32_t)b;
     pshift = 20;
@@ -203,7 +218,7 @@ __global__ __launch_bounds__(NT) void sample_pass_kernel(const SampleParams p) {
     int b;
     float r;
     const uint32_t b1 = sc->pb1;
-    select_desc<float>(sc->m2, NB1, sc->pr1, &b, &r);
+    select_desc<float, NB1>(sc->m2, sc->pr1, &b, &r);
     if (store) { sc->pb2 = (uint32_t)b; sc->pr2 = r; }
     pre = (b1 << 12) | (uint32_t)b;
     pshift = 8;
@@ -211,7 +226,7 @@ __global__ __launch_bounds__(NT) void sample_pass_kernel(const SampleParams p) {
     if (p.top_p < 1.f) {
       int b;
       float r;
-      select_desc<float>(sc->m3, NB3, sc->pr2, &b, &r);
+      select_desc<float, NB3>(sc->m3, sc->pr2, &b, &r);
       cut = (sc->pb1 << 20) | (sc->pb2 << 8) | (uint32_t)b;
     } else {
       cut = sc->kcut;
