@@ -146,11 +146,13 @@ __device__ T hist_total(const T* h) {
 
 }  // namespace
 
+// Clears the row scratch: blockIdx.y = row, blockIdx.x = one of ZB pieces.
+constexpr int ZB = 16;
 __global__ __launch_bounds__(NT) void sample_zero_kernel(SampleRowScratch* scr) {
-  SampleRowScratch* sc = scr + blockIdx.x;
+  SampleRowScratch* sc = scr + blockIdx.y;
   uint32_t* p = reinterpret_cast<uint32_t*>(sc);
   const int n = (int)(sizeof(SampleRowScratch) / 4);
-  for (int i = threadIdx.x; i < n; i += NT) p[i] = 0u;
+  for (int i = blockIdx.x * NT + threadIdx.x; i < n; i += ZB * NT) p[i] = 0u;
 }
 
 // mode 0: level-1 count histogram (+ max key, finite count)
@@ -164,9 +166,15 @@ template <int MODE>
 __global__ __launch_bounds__(NT) void sample_pass_kernel(const SampleParams p) {
   const int row = blockIdx.y;
   SampleRowScratch* sc = p.scr + row;
-  if (MODE > 0 && sc->nfinite == 0) return;
   const float* x = p.logits + (size_t)row * p.ld;
   const int i0 = blockIdx.x * p.slice, i1 = min(i0 + p.slice, p.V);
+  // the first stretch of this block's logits is requested before anything
+  // else: it does not depend on the selection below, which then runs while
+  // the values are in flight (past the slice the last ID is re-read and skipped)
+  float vals0[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) vals0[j] = x[min(i0 + (int)threadIdx.x + j * NT, i1 - 1)];
+  if (MODE > 0 && sc->nfinite == 0) return;
   constexpr bool MASS = MODE >= 3 && MODE <= 5;
   constexpr int NB = (MODE == 2 || MODE == 5) ? NB3 : NB1;
   __shared__ uint32_t hc[NB1];
@@ -243,10 +251,14 @@ __global__ __launch_bounds__(NT) void sample_pass_kernel(const SampleParams p) {
   float lsum = 0.f;
   for (int base = i0; base < i1; base += NT * PER) {
     // the thread's IDs of this stretch, all requested before any is used
-    // (past the slice the last ID is re-read and skipped)
     float vals[PER];
+    if (base == i0) {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) vals[j] = x[min(base + (int)threadIdx.x + j * NT, i1 - 1)];
+      for (int j = 0; j < PER; ++j) vals[j] = vals0[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) vals[j] = x[min(base + (int)threadIdx.x + j * NT, i1 - 1)];
+    }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
     const int i = base + (int)threadIdx.x + j * NT;
@@ -293,8 +305,41 @@ __global__ __launch_bounds__(NT) void sample_pass_kernel(const SampleParams p) {
   }
 }
 
-// One workgroup per row: walk the block sums to the block holding u * Z, then
-// that block's token IDs in order to the token.
+// The interval walk shared by both levels of the draw: given this thread's
+// mass v (threads in increasing token-ID order) and the target, the thread
+// whose cumulative interval first exceeds target (the last thread with mass
+// when rounding never lets it).  Returns that thread's index and the mass
+// before it through *before; every thread gets the result.
+__device__ int walk_to(float v, float target, float* before) {
+  __shared__ int swho;
+  __shared__ float sbefore;
+  __shared__ int slast;
+  if (threadIdx.x == 0) { swho = -1; slast = -1; }
+  __syncthreads();
+  float prev, total;
+  const float inc = block_inclusive<float>(v, &prev, &total);
+  if (v > 0.f) {
+    if (prev <= target && inc > target) { swho = threadIdx.x; sbefore = prev; }
+    atomicMax(&slast, (int)threadIdx.x);
+  }
+  __syncthreads();
+  int who = swho;
+  float bef = sbefore;
+  if (who < 0) {                              // rounding: the last thread with mass
+    who = max(slast, 0);
+    __syncthreads();
+    if ((int)threadIdx.x == who) sbefore = prev;
+    __syncthreads();
+    bef = sbefore;
+  }
+  __syncthreads();
+  *before = bef;
+  return who;
+}
+
+// One workgroup per row: the block of token IDs holding u * Z (a scan over
+// the block sums), then the thread run holding it within that block (a scan
+// over the threads' run sums), then that run's IDs in order.
 __global__ __launch_bounds__(NT) void sample_final_kernel(const SampleParams p) {
   const int row = blockIdx.x;
   SampleRowScratch* sc = p.scr + row;
@@ -302,37 +347,18 @@ __global__ __launch_bounds__(NT) void sample_final_kernel(const SampleParams p) 
     if (threadIdx.x == 0) p.out[row] = -1;
     return;
   }
+  static_assert(SAMPLE_MAX_BLOCKS <= NT, "one block sum per thread");
   const uint32_t cut = sc->cut;
-  __shared__ float bs[SAMPLE_MAX_BLOCKS];
-  __shared__ int sblk;
-  __shared__ float sbefore, starget;
-  if (threadIdx.x < p.G) bs[threadIdx.x] = sc->bsum[threadIdx.x];   // all loads at once
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float tot = 0.f;
-    for (int g = 0; g < p.G; ++g) tot += bs[g];
-    const float target = p.u[row] * tot;
-    // first block whose cumulative mass exceeds target; if rounding never
-    // lets it, the last non-empty block
-    float acc = 0.f, before = 0.f;
-    int blk = 0;
-    for (int g = 0; g < p.G; ++g) {
-      const float sg = bs[g];
-      if (sg > 0.f) {
-        blk = g;
-        before = acc;
-        if (acc + sg > target) break;
-      }
-      acc += sg;
-    }
-    sblk = blk;
-    sbefore = before;
-    starget = target;
-  }
-  __syncthreads();
+  const float bsv = ((int)threadIdx.x < p.G) ? sc->bsum[threadIdx.x] : 0.f;
+  float bprev, btot;
+  block_inclusive<float>(bsv, &bprev, &btot);
+  const float target = p.u[row] * btot;
+  float before;
+  const int blk = walk_to(bsv, target, &before);
+
   const float* x = p.logits + (size_t)row * p.ld;
   const float xmax = keyf(sc->maxkey);
-  const int i0 = sblk * p.slice, i1 = min(i0 + p.slice, p.V);
+  const int i0 = blk * p.slice, i1 = min(i0 + p.slice, p.V);
   // each thread takes a contiguous run of IDs (requested together while the
   // run fits PER; the clamped re-reads past the run are skipped)
   const int per = (p.slice + NT - 1) / NT;
@@ -353,36 +379,19 @@ __global__ __launch_bounds__(NT) void sample_final_kernel(const SampleParams p) 
       if (finite(v) && fkey(v) >= cut) mine += __builtin_amdgcn_exp2f((v - xmax) * p.sc);
     }
   }
-  __shared__ float runs[NT];
-  __shared__ int swho;
-  __shared__ float sacc;
-  runs[threadIdx.x] = mine;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float acc = sbefore, before = sbefore;
-    int who = 0;
-    for (int t = 0; t < NT; ++t) {
-      if (runs[t] > 0.f) {
-        who = t;
-        before = acc;
-        if (acc + runs[t] > starget) break;
-      }
-      acc += runs[t];
-    }
-    swho = who;
-    sacc = before;
-  }
-  __syncthreads();
-  if ((int)threadIdx.x == swho) {
+  float rbefore;
+  const int who = walk_to(mine, target - before, &rbefore);
+  if ((int)threadIdx.x == who) {
     // the chosen run, walked by the thread that summed it (its IDs are cached)
+    const float t = target - before;
     int pick = -1;
-    float acc = sacc;
+    float acc = rbefore;
     for (int i = a0; i < a1; ++i) {
       const float v = x[i];
       if (!(finite(v) && fkey(v) >= cut)) continue;
       pick = i;
       acc += __builtin_amdgcn_exp2f((v - xmax) * p.sc);
-      if (acc > starget) break;
+      if (acc > t) break;
     }
     p.out[row] = pick;
   }
@@ -392,7 +401,7 @@ hipError_t sample_rows(const SampleParams& p, hipStream_t s) {
   if (p.B <= 0) return hipSuccess;
   if (p.G <= 0 || p.G > SAMPLE_MAX_BLOCKS) return hipErrorInvalidValue;
   const dim3 grid(p.G, p.B);
-  sample_zero_kernel<<<p.B, NT, 0, s>>>(p.scr);
+  sample_zero_kernel<<<dim3(ZB, p.B), NT, 0, s>>>(p.scr);
   sample_pass_kernel<0><<<grid, NT, 0, s>>>(p);
   if (p.top_k > 0) {                              // the top-k cut's two upper radix levels
     sample_pass_kernel<1><<<grid, NT, 0, s>>>(p);
