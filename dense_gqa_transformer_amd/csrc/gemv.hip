@@ -360,23 +360,30 @@ static int cpl_for(int K, int ce) {
   return -1;
 }
 
-// rows per wave: short rows (one chunk per lane) four at a time, longer ones
-// two, which keeps the decode projections at 128-384 workgroups
-static constexpr int rpw_for(bool quant, int cpl) {
-  return quant ? (cpl <= 1 ? 4 : 2) : (cpl <= 2 ? 4 : 2);
+// Rows per wave.  The decode projections run fastest at a few hundred
+// workgroups with a few KB of weights per wave (measured per class): SwiGLU
+// takes rows in (gate, up) pairs; one-row calls with at least 2048 output
+// rows (QKV) and SwiGLU two bf16 / fp32 rows or four int8 rows per wave;
+// smaller one-row calls (O, down) one row; the lm_head one bf16 / fp32 row or
+// four int8 rows per wave over its 8 groups; several activation rows two
+// (int8: four for one-chunk rows).
+static constexpr int logits_rpw(bool quant) { return quant ? 4 : 1; }
+static int rpw_for(int epi, bool quant, int M, int cpl, int slots) {
+  if (epi == EPI_LOGITS) return logits_rpw(quant);
+  if (M > 1) return quant ? (cpl <= 1 ? 4 : 2) : 2;
+  if (epi == EPI_SWIGLU || slots >= 2048) return quant ? 4 : 2;
+  return 1;
 }
 
 int gemv_logits_blocks(int dt, int N, int K) {
-  const bool q = (dt == DT_I8);
-  const int cpl = cpl_for(K, q ? 16 : 8);
-  const int rows_per_group = GEMV_WAVES * rpw_for(q, cpl);
+  (void)K;
+  const int rows_per_group = GEMV_WAVES * logits_rpw(dt == DT_I8);
   const int groups = GEMV_LOGITS_GROUPS;
   return (N + rows_per_group * groups - 1) / (rows_per_group * groups);
 }
 
-template <typename W, int EPI, int MB, int CPL>
-static hipError_t launch_gemv(GemvParams p, hipStream_t s) {
-  constexpr int RPW = rpw_for(Raw<W>::CE == 16, CPL);
+template <typename W, int EPI, int MB, int CPL, int RPW>
+static hipError_t launch_rpw(GemvParams p, hipStream_t s) {
   const int slots_total = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
   const int rows_per_group = GEMV_WAVES * RPW;
   const int groups = (EPI == EPI_LOGITS) ? GEMV_LOGITS_GROUPS : 1;
@@ -385,6 +392,26 @@ static hipError_t launch_gemv(GemvParams p, hipStream_t s) {
   const int gy = (p.M + MB - 1) / MB;
   gemv_kernel<W, EPI, MB, CPL, RPW><<<dim3(gx, gy), GEMV_THREADS, 0, s>>>(p);
   return hipGetLastError();
+}
+
+template <typename W, int EPI, int MB, int CPL>
+static hipError_t launch_gemv(GemvParams p, hipStream_t s) {
+  constexpr bool QUANT = Raw<W>::CE == 16;
+  const int slots = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
+  const int r = rpw_for(EPI, QUANT, p.M, CPL, slots);
+  // the instantiations each kind of call can reach
+  if constexpr (EPI == EPI_LOGITS) {
+    return launch_rpw<W, EPI, MB, CPL, logits_rpw(QUANT)>(p, s);
+  } else {
+    if constexpr (MB == 1 && EPI != EPI_SWIGLU) {
+      if (r == 1) return launch_rpw<W, EPI, MB, CPL, 1>(p, s);
+    }
+    if constexpr (QUANT) {
+      if (r == 4) return launch_rpw<W, EPI, MB, CPL, 4>(p, s);
+    }
+    if (r == 2) return launch_rpw<W, EPI, MB, CPL, 2>(p, s);
+    return hipErrorInvalidValue;
+  }
 }
 
 template <typename W, int EPI, int MB>
