@@ -19,7 +19,7 @@ namespace fsk {
 
 static constexpr int GEMV_THREADS = 256;
 static constexpr int GEMV_WAVES = 4;
-static constexpr int GEMV_LOGITS_GROUPS = 8;   // row groups per wave for the lm_head
+static constexpr int GEMV_LOGITS_GROUPS = 4;   // row groups per wave for the lm_head (measured: 2, 8, 16 slower)
 
 // One lane's chunk of a weight row: CE consecutive elements.
 template <typename W> struct Raw;
@@ -365,7 +365,7 @@ static int cpl_for(int K, int ce) {
 // takes rows in (gate, up) pairs; one-row calls with at least 2048 output
 // rows (QKV) and SwiGLU two bf16 / fp32 rows or four int8 rows per wave;
 // smaller one-row calls (O, down) one row; the lm_head one bf16 / fp32 row or
-// four int8 rows per wave over its 8 groups; several activation rows two
+// four int8 rows per wave over its row groups; several activation rows two
 // (int8: four for one-chunk rows).
 static constexpr int logits_rpw(bool quant) { return quant ? 4 : 1; }
 static int rpw_for(int epi, bool quant, int M, int cpl, int slots) {
