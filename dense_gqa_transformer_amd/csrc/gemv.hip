@@ -320,18 +320,29 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
 
 // Final step of the LOGITS epilogue: one workgroup per row reduces the
 // per-block (value, index) bests to the greedy ID.
-__global__ __launch_bounds__(256) void argmax_partials_kernel(const float* __restrict__ pv,
-                                                              const int32_t* __restrict__ pi, int nblocks,
-                                                              int32_t* __restrict__ next) {
-  __shared__ float sv[4];
-  __shared__ int si[4];
+__global__ __launch_bounds__(1024) void argmax_partials_kernel(const float* __restrict__ pv,
+                                                               const int32_t* __restrict__ pi, int nblocks,
+                                                               int32_t* __restrict__ next) {
+  constexpr int NTH = 1024, PER = 16;       // a thread's partials of a stretch, requested together
+  __shared__ float sv[NTH / 64];
+  __shared__ int si[NTH / 64];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const float* rv = pv + (size_t)m * nblocks;
+  const int32_t* ri = pi + (size_t)m * nblocks;
   float bv = 0.f;
   int bi = -1;
-  for (int b = tid; b < nblocks; b += 256) {
-    const float v = pv[(size_t)m * nblocks + b];
-    const int i = pi[(size_t)m * nblocks + b];
-    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  for (int base = 0; base < nblocks; base += NTH * PER) {
+    float v[PER];
+    int ix[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = min(base + tid + j * NTH, nblocks - 1);   // past the end: re-read, skipped
+      v[j] = rv[c];
+      ix[j] = ri[c];
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (base + tid + j * NTH < nblocks && better(v[j], ix[j], bv, bi)) { bv = v[j]; bi = ix[j]; }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -342,7 +353,7 @@ __global__ __launch_bounds__(256) void argmax_partials_kernel(const float* __res
   if (lane == 0) { sv[wid] = bv; si[wid] = bi; }
   __syncthreads();
   if (tid == 0) {
-    for (int ww = 1; ww < 4; ++ww)
+    for (int ww = 1; ww < NTH / 64; ++ww)
       if (better(sv[ww], si[ww], bv, bi)) { bv = sv[ww]; bi = si[ww]; }
     next[m] = bi;
   }
@@ -443,7 +454,7 @@ static hipError_t dispatch_mb(GemvParams p, hipStream_t s) {
 hipError_t argmax_partials(const float* pv, const int32_t* pi, int nblocks, int M, int32_t* next,
                            hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  argmax_partials_kernel<<<M, 256, 0, s>>>(pv, pi, nblocks, next);
+  argmax_partials_kernel<<<M, 1024, 0, s>>>(pv, pi, nblocks, next);
   return hipGetLastError();
 }
 
