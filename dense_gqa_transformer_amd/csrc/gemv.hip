@@ -5,9 +5,13 @@
 // with 16-byte loads, lane l covering the 8-element chunks l, l+64, l+128, ...
 // of every row, so the 64 lanes of a wave together span the whole reduction
 // length: the RMSNorm of the activation row (fused prologue) is one wave sum,
-// with no LDS staging or workgroup barrier.  Weight loads are issued before
-// anything else and the next row group is fetched while the current one is
-// reduced.  The cross-lane dot-product sum is a wave64 shuffle tree.
+// with no LDS staging or workgroup barrier.  Loads complete in order and the
+// compiler waits for every load before the one a use needs, so the order of
+// requests is the design: the one-row path requests the residual values it
+// will add to, then the activation row and norm weight, then the weights (the
+// norm runs while the weights are in flight); every load is unconditional
+// (clamped addresses); the lm_head's next row group is in flight while the
+// current one is reduced.  Cross-lane sums run on DPP row operations.
 // Epilogues: plain store, residual add, SwiGLU on paired gate/up rows, and
 // lm_head logits with a per-workgroup argmax (reduced by argmax_partials).
 // Int8 weights (one scale per row) stream 16 codes per lane per load; each
