@@ -138,7 +138,8 @@ struct fs_model {
   float* logits_tmp = nullptr;    // [max_seqs, V] when the caller passes none
   SampleRowScratch* sample_scr = nullptr;   // [max_seqs], on the first fs_sample
   int32_t* gen_tok = nullptr;     // device int32 [1]: the token fs_generate feeds back
-  int32_t* gen_host = nullptr;    // pinned int32 [1]: its host copy
+  int32_t* gen_host = nullptr;    // pinned int32 [2]: host copies of two consecutive tokens
+  hipEvent_t gen_ev[2] = {};      // their copies' completion
   // pinned staging of per-call host arrays
   int32_t* stage = nullptr;       // [STAGE_RING][2 * max_seqs]
   hipEvent_t stage_ev[STAGE_RING] = {};
@@ -180,6 +181,8 @@ struct fs_model {
       if (stage_ev[i]) hipEventDestroy(stage_ev[i]);
     if (stage) hipHostFree(stage);
     if (gen_host) hipHostFree(gen_host);
+    for (auto e : gen_ev)
+      if (e) hipEventDestroy(e);
     hipFree(gen_tok);
   }
 };
@@ -1066,35 +1069,57 @@ fs_status fs_generate(fs_model* m, const int32_t* prompt, int32_t S, int32_t slo
   if (m->gen_tok == nullptr && dalloc(&m->gen_tok, sizeof(int32_t)) != hipSuccess)
     return fail(FS_ERR_OOM, "token buffer allocation failed");
   if (m->gen_host == nullptr &&
-      hipHostMalloc((void**)&m->gen_host, sizeof(int32_t), hipHostMallocDefault) != hipSuccess)
+      hipHostMalloc((void**)&m->gen_host, 2 * sizeof(int32_t), hipHostMallocDefault) != hipSuccess)
     return fail(FS_ERR_OOM, "pinned token buffer allocation failed");
+  for (auto& e : m->gen_ev)
+    if (e == nullptr) HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   float* lg = m->logits_tmp;
   if ((st = fs_prefill(m, prompt, 1, S, &slot, lg, stream)) != FS_OK) return st;
+  // Token i's read-back is requested before the decode step that forwards it,
+  // so the host checks token i while that step runs on the device (no idle
+  // gap per token).  Whether the step may follow is known before the token
+  // is read (budget and context); when token i then stops the loop (an EOS ID
+  // or no finite logit) the step already issued is discarded: the slot length
+  // goes back to S + i and the stream is drained before returning.
+  auto done = [&](fs_status r) {
+    const hipError_t e = hipStreamSynchronize(s);
+    if (r == FS_OK && e != hipSuccess) return fail(FS_ERR_HIP, std::string("HIP error: ") + hipGetErrorString(e));
+    return r;
+  };
   for (int i = 0;; ++i) {
     // select token i (greedy after a decode step comes fused with the lm_head)
     if (sampled) {
-      if ((st = fs_sample(m, lg, 1, c.vocab, g->sampling, g->uniforms + i, m->gen_tok, stream)) != FS_OK) return st;
+      if ((st = fs_sample(m, lg, 1, c.vocab, g->sampling, g->uniforms + i, m->gen_tok, stream)) != FS_OK)
+        return done(st);
     } else if (i == 0) {
       HIP_TRY(argmax_rows(lg, 1, c.vocab, c.vocab, m->gen_tok, s));
     }
-    HIP_TRY(hipMemcpyAsync(m->gen_host, m->gen_tok, sizeof(int32_t), hipMemcpyDeviceToHost, s));
-    HIP_TRY(hipStreamSynchronize(s));
-    const int32_t tok = *m->gen_host;
-    if (tok < 0) return fail(FS_ERR_UNSUPPORTED, "no finite logit at step " + std::to_string(i));
+    int32_t* host_tok = m->gen_host + (i & 1);
+    HIP_TRY(hipMemcpyAsync(host_tok, m->gen_tok, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipEventRecord(m->gen_ev[i & 1], s));
+    const int32_t pos = S + i;
+    const bool forward = (i + 1 < g->max_new_tokens) && (pos < c.max_ctx);   // unless token i stops the loop
+    if (forward && (st = fs_decode_step(m, m->gen_tok, &pos, &slot, 1, sampled ? lg : nullptr,
+                                        sampled ? nullptr : m->gen_tok, stream)) != FS_OK)
+      return done(st);
+    HIP_TRY(hipEventSynchronize(m->gen_ev[i & 1]));
+    const int32_t tok = *host_tok;
+    if (tok < 0) {
+      if (forward) m->slot_len[slot] = pos;
+      done(FS_OK);
+      return fail(FS_ERR_UNSUPPORTED, "no finite logit at step " + std::to_string(i));
+    }
     bool eos = false;
     for (int e = 0; e < g->n_eos; ++e) eos = eos || g->eos_ids[e] == tok;
     if (eos) {
+      if (forward) m->slot_len[slot] = pos;
       if (g->include_stop_id) out_ids[(*n_out)++] = tok;
       *stop_reason = FS_STOP_EOS;
-      return FS_OK;
+      return done(FS_OK);
     }
     out_ids[(*n_out)++] = tok;
-    if (*n_out == g->max_new_tokens) { *stop_reason = FS_STOP_BUDGET; return FS_OK; }
-    const int32_t pos = S + i;
-    if (pos >= c.max_ctx) { *stop_reason = FS_STOP_CONTEXT; return FS_OK; }
-    if ((st = fs_decode_step(m, m->gen_tok, &pos, &slot, 1, sampled ? lg : nullptr,
-                             sampled ? nullptr : m->gen_tok, stream)) != FS_OK)
-      return st;
+    if (*n_out == g->max_new_tokens) { *stop_reason = FS_STOP_BUDGET; return done(FS_OK); }
+    if (pos >= c.max_ctx) { *stop_reason = FS_STOP_CONTEXT; return done(FS_OK); }
   }
 }
 
