@@ -227,7 +227,9 @@ typedef struct {
  * token's own position S+i is >= max_ctx it cannot be forwarded and the loop
  * stops with the token kept (FS_STOP_CONTEXT); else one decode step (graph
  * replay) forwards it.  The host reads each 4-byte token back to check the
- * stop rules.  Synchronous.
+ * stop rules while the step forwarding it already runs; a step issued for a
+ * token that then stops the loop is discarded (the slot length counts only
+ * the forwarded tokens: S plus the IDs fed back).  Synchronous.
  * Errors: INVALID_ARG (NULL pointer, S <= 0, bad slot, max_new_tokens < 0,
  * n_eos < 0, bad sampling parameters); CAPACITY (S > max_ctx); UNSUPPORTED
  * (a step's logits hold no finite value: the loop stops, *n_out and
