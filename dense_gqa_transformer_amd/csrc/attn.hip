@@ -102,6 +102,11 @@ __device__ __forceinline__ float psum(const Part2& p, int np) { return np > 1 ? 
 // rot/2), times `mul`.  One wave: lane holds elements lane + 64i (returned in
 // y[i]).  Split in two so that a kernel can request every load of the step
 // (nr_fetch) before other loads, and compute (nr_finish) once they are in.
+// A full rotation of two elements per lane has a path of its own (the partner
+// is the lane's other element, so half the loads); wider rows take the general
+// path for every rotation width: with a second path there the compiler merges
+// the two paths' stores into one store at a path-dependent index, which puts
+// the struct in scratch memory.
 template <int D>
 struct NormRopeIn {
   static constexpr int NE = D / 64;
@@ -114,7 +119,7 @@ __device__ __forceinline__ void nr_fetch(const float* x, size_t pst, int np, con
                                          const float* sn, int rot, int lane, NormRopeIn<D>& in) {
   constexpr int NE = D / 64;
   const int rh = rot >> 1;
-  if constexpr (NE >= 2) {
+  if constexpr (NE == 2) {
     if (rot == D) {
       // full rotation: element i's partner is element i +- NE/2 of the same lane
 #pragma unroll
@@ -158,7 +163,7 @@ __device__ __forceinline__ void nr_finish(const NormRopeIn<D>& in, int np, int r
 #pragma unroll
   for (int i = 0; i < NE; ++i) ss = fmaf(v[i], v[i], ss);
   const float inv = rsqrtf(wave_sum(ss) / (float)D + eps);
-  if constexpr (NE >= 2) {
+  if constexpr (NE == 2) {
     if (rot == D) {
       constexpr int H = NE / 2;
 #pragma unroll
