@@ -153,6 +153,8 @@ struct fs_model {
   int attn_mode = 0;
   // shortest split-K chunk (positions per workgroup)
   int min_chunk = 32;
+  // prefill: q/k norm + RoPE + K/V write in the QKV GEMM's epilogue where it applies
+  bool fuse_rope = true;
   // measurement hook: per-launch event pairs, labelled by step
   bool timing = false;
   std::vector<TimedLaunch> timed;
@@ -384,7 +386,7 @@ fs_status block_skinny(fs_model* m, const LayerW& L, int rows, Attn&& attention,
 // qkv_f32: the QKV projection is stored fp32 (decode attention) or bf16 (prefill).
 template <class Attn>
 fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&& attention,
-                     hipStream_t s) {
+                     hipStream_t s, const RopeKvParams* rope = nullptr, bool* rope_done = nullptr) {
   const fs_config& c = m->cfg;
   // The attention input keeps ~16 significant bits (bf16 value + bf16 remainder):
   // rounding it to bf16 alone moves the logits by about as much as the whole
@@ -412,6 +414,15 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
                                     m->qkv_w, c.hidden, s, xn_lo, L.sqkv, qks));
     m->qkv_src = m->kpart;
     m->qkv_np = qks;
+  } else if (rope != nullptr && m->fuse_rope && !qkv_f32 &&
+             gemm_dma_ok(GEPI_QKV_ROPE, m->xn, c.hidden, wb, c.hidden, nullptr, 0, rows, m->qkv_w, c.hidden,
+                         xn_lo) &&
+             gemm_dma_rope_ok(*rope, rows, m->qkv_w)) {
+    // prefill on the large GEMM: the per-head norm, RoPE and K/V write run in
+    // its epilogue (rope_done tells the attention step to skip rope_kv)
+    LAUNCH(m, "qkv", s, gemm_dma(GEPI_QKV_ROPE, m->xn, c.hidden, wb, c.hidden, nullptr, 0, rows, m->qkv_w,
+                                 c.hidden, s, xn_lo, L.sqkv, rope));
+    if (rope_done != nullptr) *rope_done = true;
   } else {
     LAUNCH(m, "qkv", s, gemm_bf16(qkv_f32 ? GEPI_STORE_F32 : GEPI_STORE_BF16, m->xn, c.hidden, wb, c.hidden,
                                   m->qkv, m->qkv_w, rows, m->qkv_w, c.hidden, s, xn_lo, L.sqkv));
@@ -640,6 +651,8 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
     const char* am = std::getenv("FS_DECODE_ATTN");
     if (am != nullptr && std::strcmp(am, "split") == 0) m->attn_mode = 1;
     if (am != nullptr && std::strcmp(am, "onepass") == 0) m->attn_mode = 2;
+    const char* fr = std::getenv("FS_PREFILL_FUSE_ROPE");
+    if (fr != nullptr && fr[0] == '0') m->fuse_rope = false;
     const char* mc = std::getenv("FS_DECODE_MIN_CHUNK");
     if (mc != nullptr) {
       const int v = std::atoi(mc);
@@ -687,32 +700,34 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
     const LayerW& L = m->layers[l];
     char* kc = (char*)m->kcache + (size_t)l * m->layer_stride * m->esz;
     char* vc = (char*)m->vcache + (size_t)l * m->layer_stride * m->esz;
+    AttnPrefillParams a{};
+    a.q = m->qr; a.q_dt = act_dt; a.kcache = kc; a.vcache = vc; a.kv_dt = m->dt;
+    a.out = m->attn; a.o_dt = act_dt; a.slots = m->d_slot;
+    a.B = B; a.S = S; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim;
+    a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
+    a.scale = 1.0f / std::sqrt((float)c.head_dim);
+    // the head_dim-128 kernel takes q pre-multiplied by scale * log2(e)
+    const bool fa = !skinny && attn_prefill_fa_ok(a);
+    a.q_prescale = fa ? a.scale * 1.4426950408889634f : 1.0f;
+    RopeKvParams r{};
+    r.qscale = a.q_prescale;
+    r.rot = m->rot; r.gated = m->gated;
+    r.qkv = m->qkv; r.in_dt = act_dt; r.qout = m->qr; r.q_dt = act_dt;
+    r.kcache = kc; r.vcache = vc; r.kv_dt = m->dt;
+    r.gq = L.q_norm; r.gk = L.k_norm; r.eps = c.rms_eps;
+    r.cos_t = m->rope_cos; r.sin_t = m->rope_sin; r.slots = m->d_slot;
+    r.T = (int)T; r.S_per = S; r.nq = c.n_heads; r.nkv = c.n_kv_heads; r.d = c.head_dim;
+    r.slot_stride = m->slot_stride; r.head_stride = m->head_stride;
+    bool rope_done = false;       // set when the QKV GEMM's epilogue did rope_kv's work
     auto attention = [&]() -> fs_status {
-      AttnPrefillParams a{};
-      a.q = m->qr; a.q_dt = act_dt; a.kcache = kc; a.vcache = vc; a.kv_dt = m->dt;
-      a.out = m->attn; a.o_dt = act_dt; a.slots = m->d_slot;
-      a.B = B; a.S = S; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim;
-      a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
-      a.scale = 1.0f / std::sqrt((float)c.head_dim);
-      // the head_dim-128 kernel takes q pre-multiplied by scale * log2(e)
-      const bool fa = !skinny && attn_prefill_fa_ok(a);
-      a.q_prescale = fa ? a.scale * 1.4426950408889634f : 1.0f;
-      RopeKvParams r{};
-      r.qscale = a.q_prescale;
-      r.rot = m->rot; r.gated = m->gated;
-      r.qkv = m->qkv; r.in_dt = act_dt; r.qout = m->qr; r.q_dt = act_dt;
-      r.kcache = kc; r.vcache = vc; r.kv_dt = m->dt;
-      r.gq = L.q_norm; r.gk = L.k_norm; r.eps = c.rms_eps;
-      r.cos_t = m->rope_cos; r.sin_t = m->rope_sin; r.slots = m->d_slot;
-      r.T = (int)T; r.S_per = S; r.nq = c.n_heads; r.nkv = c.n_kv_heads; r.d = c.head_dim;
-      r.slot_stride = m->slot_stride; r.head_stride = m->head_stride;
-      LAUNCH(m, "rope_kv", s, rope_kv(r, s));
+      if (!rope_done) LAUNCH(m, "rope_kv", s, rope_kv(r, s));
       LAUNCH(m, "attn", s, skinny ? attn_prefill_vec(a, s) : fa ? attn_prefill_fa(a, s) : attn_prefill(a, s));
       if (m->gated)
         LAUNCH(m, "attn_gate", s, attn_gate(m->attn, act_dt, m->qkv, act_dt, (int)T, c.n_heads, c.head_dim, m->qkv_w, s));
       return FS_OK;
     };
-    st = skinny ? block_skinny(m, L, (int)T, attention, s) : block_gemm(m, L, (int)T, false, attention, s);
+    st = skinny ? block_skinny(m, L, (int)T, attention, s)
+                : block_gemm(m, L, (int)T, false, attention, s, &r, &rope_done);
     if (st != FS_OK) return st;
   }
   if ((st = flush_partials(m, (int)T, s)) != FS_OK) return st;

@@ -72,11 +72,85 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 
 }  // namespace
 
+// QKV epilogue of a prefill: the tile's 256 tokens x 256 columns (two heads of
+// 128, all q, all k or all v: the section boundaries fall on tile boundaries)
+// are staged as bf16 in the eight wave regions, exactly as the plain bf16
+// store would write them; then per (token, head) the q/k heads get the
+// per-head RMSNorm and rotate-half RoPE over all 128 dims (q also the
+// attention's pre-scale) and go to the q buffer or the K cache, and v goes to
+// the V cache as it is.  The arithmetic is the standalone norm/RoPE pass's,
+// step for step, on the same bf16 inputs, so the results are the same bits.
+// Eight lanes per (token, head): lane `sub` holds dims [8 sub, 8 sub + 8) and
+// their partners [64 + 8 sub, ...), which sit in the next wave's region.
+__device__ __forceinline__ void qkv_rope_epilogue(const RopeKvParams& p, int m0, int n0, int M, int tid) {
+  constexpr int D = 128;
+  __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
+  lds_barrier();
+  const int hsec = n0 / D;                         // first of the tile's two heads in q|k|v order
+  const bool is_q = hsec < p.nq, is_k = !is_q && hsec < p.nq + p.nkv;
+  const int sub = tid & 7;
+  const float* g = is_q ? p.gq : p.gk;
+  float g0[8], g1[8];
+  load8(g + 8 * sub, g0);
+  load8(g + 64 + 8 * sub, g1);
+#pragma unroll 2
+  for (int it = 0; it < 8; ++it) {
+    const int item = it * 512 + tid;
+    const int hd = (item >> 3) & 1, row = item >> 4;
+    const int mr = row & 127;
+    const char* R0 = wave_region((row >> 7) * 4 + 2 * hd);
+    const int off = mr * 128 + ((sub ^ (mr & 7)) << 4);
+    float x0[8], x1[8];
+    load8(reinterpret_cast<const bf16*>(R0 + off), x0);
+    load8(reinterpret_cast<const bf16*>(R0 + 16384 + off), x1);     // the next wave's region
+    const int t = min(m0 + row, M - 1);
+    const int b = t / p.S_per, pos = t % p.S_per;
+    const int hh = hsec + hd;
+    if (is_q || is_k) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(x0[e], x0[e], fmaf(x1[e], x1[e], ss));
+      ss = group_sum<8>(ss);
+      const float inv = rsqrtf(__fadd_rn(ss / (float)D, p.eps));
+      float cs[8], sn[8];
+      load8(p.cos_t + (size_t)pos * (D / 2) + 8 * sub, cs);
+      load8(p.sin_t + (size_t)pos * (D / 2) + 8 * sub, sn);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float a = x0[e] * inv * g0[e], c = x1[e] * inv * g1[e];
+        const float y0 = fmaf(a, cs[e], -(c * sn[e])), y1 = fmaf(c, cs[e], a * sn[e]);
+        x0[e] = is_q ? y0 * p.qscale : y0;
+        x1[e] = is_q ? y1 * p.qscale : y1;
+      }
+    }
+    if (m0 + row >= M) continue;
+    bf16* dst;
+    if (is_q) {
+      dst = reinterpret_cast<bf16*>(p.qout) + (size_t)t * p.nq * D + (size_t)hh * D;
+    } else {
+      const int j = is_k ? hh - p.nq : hh - p.nq - p.nkv;
+      const size_t o = (size_t)p.slots[b] * p.slot_stride + (size_t)j * p.head_stride + (size_t)pos * D;
+      dst = reinterpret_cast<bf16*>(is_k ? p.kcache : p.vcache) + o;
+    }
+    u32x4 u0, u1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u0[i] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x0[2 * i]) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x0[2 * i + 1]) << 16);
+      u1[i] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x1[2 * i]) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x1[2 * i + 1]) << 16);
+    }
+    *reinterpret_cast<u32x4*>(dst + 8 * sub) = u0;
+    *reinterpret_cast<u32x4*>(dst + 64 + 8 * sub) = u1;
+  }
+}
+
 template <int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ A_lo,
                   const bf16* __restrict__ B, int ldb, void* __restrict__ out, int ldc,
-                  int M, int N, int K, int tiles_n, int nblocks, const float* __restrict__ colscale) {
+                  int M, int N, int K, int tiles_n, int nblocks, const float* __restrict__ colscale,
+                  const RopeKvParams rp) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid >> 2, wn = wid & 3;
@@ -214,7 +288,7 @@ void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict
       }
   }
 
-  if (EPI == GEPI_STORE_BF16) {
+  if (EPI == GEPI_STORE_BF16 || EPI == GEPI_QKV_ROPE) {
     // 128 rows x 128 B; chunk c of row m at slot c ^ (m & 7)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -229,6 +303,10 @@ void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict
           const int c = j * 4 + g;
           *reinterpret_cast<bf16x4*>(R + m * 128 + ((c ^ (m & 7)) << 4) + hl * 8) = v;
         }
+    }
+    if constexpr (EPI == GEPI_QKV_ROPE) {
+      qkv_rope_epilogue(rp, m0, n0, M, tid);
+      return;
     }
     bf16* o = reinterpret_cast<bf16*>(out);
     const int c = lane & 7;
@@ -321,9 +399,21 @@ bool gemm_dma_ok(int epi, const void* A, int lda, const void* B, int ldb, const 
   return M >= 1024 && tiles >= 256;
 }
 
+bool gemm_dma_rope_ok(const RopeKvParams& r, int M, int N) {
+  return r.d == 128 && r.rot == 128 && !r.gated && r.nq % 2 == 0 && r.nkv % 2 == 0 && r.T == M &&
+         r.S_per > 0 && M % r.S_per == 0 && N == (r.nq + 2 * r.nkv) * 128 && r.in_dt == DT_BF16 &&
+         r.q_dt == DT_BF16 && r.kv_dt == DT_BF16;
+}
+
 hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc,
-                    int M, int N, int K, hipStream_t s, const void* A_lo, const float* colscale) {
+                    int M, int N, int K, hipStream_t s, const void* A_lo, const float* colscale,
+                    const RopeKvParams* rope) {
   if (colscale != nullptr && ((uintptr_t)colscale & 15)) return hipErrorInvalidValue;
+  RopeKvParams rp{};
+  if (epi == GEPI_QKV_ROPE) {
+    if (rope == nullptr || !gemm_dma_rope_ok(*rope, M, N)) return hipErrorInvalidValue;
+    rp = *rope;
+  }
   const int tn = (N + TILE - 1) / TILE, tm = (M + TILE - 1) / TILE;
   const int nb = tn * tm;
   const bf16* a = (const bf16*)A;
@@ -331,16 +421,19 @@ hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, voi
   const bf16* al = (const bf16*)A_lo;
   switch (epi) {
     case GEPI_STORE_BF16:
-      gemm_dma_kernel<GEPI_STORE_BF16><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
+      gemm_dma_kernel<GEPI_STORE_BF16><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale, rp);
       break;
     case GEPI_RESID_F32:
-      gemm_dma_kernel<GEPI_RESID_F32><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
+      gemm_dma_kernel<GEPI_RESID_F32><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale, rp);
       break;
     case GEPI_SWIGLU_BF16:
-      gemm_dma_kernel<GEPI_SWIGLU_BF16><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
+      gemm_dma_kernel<GEPI_SWIGLU_BF16><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale, rp);
       break;
     case GEPI_STORE_F32:
-      gemm_dma_kernel<GEPI_STORE_F32><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale);
+      gemm_dma_kernel<GEPI_STORE_F32><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale, rp);
+      break;
+    case GEPI_QKV_ROPE:
+      gemm_dma_kernel<GEPI_QKV_ROPE><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale, rp);
       break;
     default:
       return hipErrorInvalidValue;

@@ -70,7 +70,7 @@ hipError_t argmax_partials(const float* pv, const int32_t* pi, int nblocks, int 
 
 // ---------------------------------------------------------------- MFMA GEMM (bf16)
 enum GemmEpi { GEPI_STORE_BF16 = 0, GEPI_RESID_F32 = 1, GEPI_SWIGLU_BF16 = 2, GEPI_STORE_F32 = 3,
-               GEPI_PART_F32 = 4 };
+               GEPI_PART_F32 = 4, GEPI_QKV_ROPE = 5 };
 // C[M, N] = A[M, K] . B[N, K]^T; A, B bf16 row-major with K contiguous (lda, ldb);
 // fp32 accumulation.  STORE_*: out[m*ldc + n] = C; RESID_F32: out[m*ldc + n] += C;
 // SWIGLU_BF16: B is packed gate/up (blocks of 32+32 rows, N = 2*ffn) and
@@ -84,10 +84,18 @@ hipError_t gemm_bf16(int epi, const void* A, int lda, const void* B, int ldb, vo
                      const float* colscale = nullptr);
 // The large-problem kernel behind gemm_bf16 (256x256 tiles, operands streamed
 // into LDS by DMA): gemm_dma_ok says whether it applies to a call.
+// QKV_ROPE (only here): C is a prefill's fused q|k|v projection and never
+// stored as such; the epilogue applies rope_kv's per-head q/k RMSNorm + RoPE
+// (head_dim 128, full rotation, no output gate, bf16 q and KV) and writes q'
+// and the K/V cache rows as rope_kv would (same bits); gemm_dma_rope_ok says
+// whether a rope_kv call qualifies (M = its T, N = its packed width).
 bool gemm_dma_ok(int epi, const void* A, int lda, const void* B, int ldb, const void* out, int ldc,
                  int M, int N, int K, const void* A_lo);
+struct RopeKvParams;
+bool gemm_dma_rope_ok(const RopeKvParams& r, int M, int N);
 hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc,
-                    int M, int N, int K, hipStream_t s, const void* A_lo, const float* colscale);
+                    int M, int N, int K, hipStream_t s, const void* A_lo, const float* colscale,
+                    const RopeKvParams* rope = nullptr);
 // The few-rows kernel behind gemm_bf16 (M <= 64, K % 256 == 0, N % 32 == 0):
 // one weight slab per workgroup, K split over its waves, each weight read once.
 // PART_F32 (only here): K is also split over ksplit workgroups per slab

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const RopeKvParams p) {
   for (int e = 0; e < 8; ++e) ss = fmaf(x0[e], x0[e], fmaf(x1[e], x1[e], ss));
   ss = group_sum<LPH>(ss);
   if (!live) return;
-  const float inv = rsqrtf(ss / (float)D + p.eps);
+  const float inv = rsqrtf(__fadd_rn(ss / (float)D, p.eps));
   const float* g = is_q ? p.gq : p.gk;
   float g0[8], g1[8];
   load8(g + oA, g0);
@@ -83,9 +83,11 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const RopeKvParams p) {
     load8(p.sin_t + (size_t)pos * RH + 8 * sub, sn);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+      // explicit fused multiply-adds: the QKV GEMM's fused epilogue computes the
+      // same expressions and must round the same way
       const float a = x0[e] * inv * g0[e], c = x1[e] * inv * g1[e];
-      y0[e] = a * cs[e] - c * sn[e];
-      y1[e] = c * cs[e] + a * sn[e];
+      y0[e] = fmaf(a, cs[e], -(c * sn[e]));
+      y1[e] = fmaf(c, cs[e], a * sn[e]);
     }
   } else {
 #pragma unroll

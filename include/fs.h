@@ -117,7 +117,9 @@ typedef struct fs_model fs_model;
  * at a time instead of replaying captured graphs; FS_DECODE_ATTN=split or
  * =onepass forces one form of the decode attention (split-K chunks plus a
  * merge launch, or one workgroup per sequence and KV head) where it exists;
- * FS_DECODE_MIN_CHUNK=32|64|128|256 sets the shortest split-K chunk. */
+ * FS_DECODE_MIN_CHUNK=32|64|128|256 sets the shortest split-K chunk;
+ * FS_PREFILL_FUSE_ROPE=0 keeps the per-head q/k norm + RoPE + K/V write of a
+ * large prefill in a pass of its own instead of the QKV GEMM's epilogue. */
 fs_status fs_model_create(const fs_config *cfg, const fs_weights *w,
                           void *stream, fs_model **out);
 
@@ -251,7 +253,9 @@ fs_status fs_kv_read(const fs_model *m, int32_t layer, int32_t slot, int32_t kv_
  * records and starts recording: every kernel this model launches is then
  * bracketed by a pair of HIP events on the call's stream, labelled with the
  * step it implements ("embed", "norm", "qkv", "rope_kv", "attn", "combine",
- * "attn_gate", "wconv", "o_proj", "gate_up", "down", "head", "argmax"), and decode steps run
+ * "attn_gate", "wconv", "o_proj", "gate_up", "down", "head", "argmax"; a
+ * prefill whose QKV GEMM does the q/k norm + RoPE + K/V write in its epilogue
+ * has no "rope_kv" launches), and decode steps run
  * without graph replay.  fs_timing(m, 0) stops recording (records are kept
  * until the next fs_timing call).  Errors: INVALID_ARG for a NULL model. */
 fs_status fs_timing(fs_model *m, int32_t enable);

@@ -315,6 +315,39 @@ def test_prefill_4x4096_sampled():
         check_logits(lg4[0], orc.forward(toks[0]), TOL["bf16"], "4x4096 row 0 vs oracle")
 
 
+def test_prefill_fused_rope_epilogue_matches_separate_pass(monkeypatch):
+    # On the large GEMM the per-head q/k norm + RoPE + K/V write run in the QKV
+    # GEMM's epilogue; it must give the same bits as the GEMM storing q|k|v and
+    # the separate rope_kv pass.  2 x 2048 tokens (16 x 16 tiles of 256): the
+    # logits and the K/V of both sequences in four layers, with the timing hook
+    # confirming which path ran.
+    shape = synth.QWEN3_0P6B
+    toks = synth.tokens(2055, shape.vocab, (2, 2048))
+    res = {}
+    for mode in ("0", "1"):
+        monkeypatch.setenv("FS_PREFILL_FUSE_ROPE", mode)
+        model = make_model(shape, max_seqs=2, max_ctx=2048)
+        _flush(f"2 x 2048 prefill, fused norm/RoPE epilogue {mode}")
+        model.timing(True)
+        lg = model.prefill(dev_tokens(toks), [0, 1]).cpu().numpy()
+        torch.cuda.synchronize()
+        n_rope = model.timing_read("rope_kv")[1]
+        model.timing(False)
+        assert n_rope == (0 if mode == "1" else shape.n_layers), (mode, n_rope)
+        assert np.all(np.isfinite(lg))
+        kv = []
+        for layer in (0, 1, 14, 27):
+            for slot in (0, 1):
+                for j in (0, 3, 7):
+                    kk, vv = model.kv_read(layer, slot, j, 0, 2048)
+                    kv.append((kk.cpu(), vv.cpu()))
+        res[mode] = (lg, kv)
+        model.close()
+    np.testing.assert_array_equal(res["0"][0], res["1"][0])
+    for (k0, v0), (k1, v1) in zip(res["0"][1], res["1"][1]):
+        assert torch.equal(k0, k1) and torch.equal(v0, v1)
+
+
 # ------------------------------------------------------------------ 64-way ragged decode
 def test_decode_bs64_ragged():
     shape = synth.QWEN3_0P6B
