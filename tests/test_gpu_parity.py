@@ -315,21 +315,23 @@ def test_prefill_4x4096_sampled():
         check_logits(lg4[0], orc.forward(toks[0]), TOL["bf16"], "4x4096 row 0 vs oracle")
 
 
-def test_prefill_fused_rope_epilogue_matches_separate_pass(monkeypatch):
+@pytest.mark.parametrize("B,S", [(2, 2048), (3, 1400)])
+def test_prefill_fused_rope_epilogue_matches_separate_pass(monkeypatch, B, S):
     # On the large GEMM the per-head q/k norm + RoPE + K/V write run in the QKV
     # GEMM's epilogue; it must give the same bits as the GEMM storing q|k|v and
-    # the separate rope_kv pass.  2 x 2048 tokens (16 x 16 tiles of 256): the
-    # logits and the K/V of both sequences in four layers, with the timing hook
+    # the separate rope_kv pass.  2 x 2048 tokens (16 x 16 tiles of 256) and
+    # 3 x 1400 (a ragged last row tile, sequences starting inside tiles): the
+    # logits and the K/V of every sequence in four layers, with the timing hook
     # confirming which path ran.
     shape = synth.QWEN3_0P6B
-    toks = synth.tokens(2055, shape.vocab, (2, 2048))
+    toks = synth.tokens(2055 + S, shape.vocab, (B, S))
     res = {}
     for mode in ("0", "1"):
         monkeypatch.setenv("FS_PREFILL_FUSE_ROPE", mode)
-        model = make_model(shape, max_seqs=2, max_ctx=2048)
-        _flush(f"2 x 2048 prefill, fused norm/RoPE epilogue {mode}")
+        model = make_model(shape, max_seqs=B, max_ctx=S)
+        _flush(f"{B} x {S} prefill, fused norm/RoPE epilogue {mode}")
         model.timing(True)
-        lg = model.prefill(dev_tokens(toks), [0, 1]).cpu().numpy()
+        lg = model.prefill(dev_tokens(toks), list(range(B))).cpu().numpy()
         torch.cuda.synchronize()
         n_rope = model.timing_read("rope_kv")[1]
         model.timing(False)
@@ -337,9 +339,9 @@ def test_prefill_fused_rope_epilogue_matches_separate_pass(monkeypatch):
         assert np.all(np.isfinite(lg))
         kv = []
         for layer in (0, 1, 14, 27):
-            for slot in (0, 1):
+            for slot in range(B):
                 for j in (0, 3, 7):
-                    kk, vv = model.kv_read(layer, slot, j, 0, 2048)
+                    kk, vv = model.kv_read(layer, slot, j, 0, S)
                     kv.append((kk.cpu(), vv.cpu()))
         res[mode] = (lg, kv)
         model.close()
