@@ -315,21 +315,22 @@ def test_prefill_4x4096_sampled():
         check_logits(lg4[0], orc.forward(toks[0]), TOL["bf16"], "4x4096 row 0 vs oracle")
 
 
-@pytest.mark.parametrize("B,S", [(2, 2048), (3, 1400)])
-def test_prefill_fused_rope_epilogue_matches_separate_pass(monkeypatch, B, S):
+@pytest.mark.parametrize("which,B,S", [("bf16", 2, 2048), ("bf16", 3, 1400), ("int8", 2, 2048)])
+def test_prefill_fused_rope_epilogue_matches_separate_pass(monkeypatch, which, B, S):
     # On the large GEMM the per-head q/k norm + RoPE + K/V write run in the QKV
     # GEMM's epilogue; it must give the same bits as the GEMM storing q|k|v and
     # the separate rope_kv pass.  2 x 2048 tokens (16 x 16 tiles of 256) and
     # 3 x 1400 (a ragged last row tile, sequences starting inside tiles): the
     # logits and the K/V of every sequence in four layers, with the timing hook
-    # confirming which path ran.
-    shape = synth.QWEN3_0P6B
+    # confirming which path ran; int8 weights take the per-column scales
+    # before the epilogue.
+    shape = synth.QWEN3_0P6B if which == "bf16" else synth.QWEN3_0P6B_I8
     toks = synth.tokens(2055 + S, shape.vocab, (B, S))
     res = {}
     for mode in ("0", "1"):
         monkeypatch.setenv("FS_PREFILL_FUSE_ROPE", mode)
         model = make_model(shape, max_seqs=B, max_ctx=S)
-        _flush(f"{B} x {S} prefill, fused norm/RoPE epilogue {mode}")
+        _flush(f"{which} {B} x {S} prefill, fused norm/RoPE epilogue {mode}")
         model.timing(True)
         lg = model.prefill(dev_tokens(toks), list(range(B))).cpu().numpy()
         torch.cuda.synchronize()
