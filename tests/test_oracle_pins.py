@@ -290,3 +290,89 @@ def test_zero_output_projection_keeps_embedding():
     dump = {}
     O.Oracle(shape, w).forward([9, 10], dump=dump)
     np.testing.assert_array_equal(dump["final"], w["embed"][[9, 10]].astype(np.float64))
+
+
+# ---------------------------------------------------------------- attention scale (1/sqrt(head_dim))
+# "Coming back to Failed Star", Second sitting: 16 query heads of width 128
+# give 2048, not H, so head_dim is not hidden / n_heads and the two candidate
+# scales differ.  Both brute-force shapes above have head_dim = hidden /
+# n_heads; these cases do not.
+def test_attention_scale_closed_form():
+    d = 16
+    q = np.zeros((1, 1, d))
+    q[0, 0, 0] = 4.0                   # score against k0: 4 / sqrt(16) = 1
+    k = np.zeros((2, 1, d))
+    k[0, 0, 0] = 1.0                   # k1 = 0: score 0
+    v = np.zeros((2, 1, d))
+    v[0, 0, 1] = 1.0
+    v[1, 0, 2] = 1.0
+    out = O.gqa_attention(q, k, v, np.array([1]))
+    w0 = math.e / (math.e + 1.0)
+    np.testing.assert_allclose(out[0, 0, 1:3], [w0, 1.0 - w0], rtol=1e-14)
+
+
+def _wide_head_shape():
+    # hidden 32, 4 query heads of width 16 (q width 64 = 2 x hidden, as the
+    # 0.6B shape's 2048 = 2 x 1024), 2 KV heads
+    return synth.small_shape(hidden=32, n_heads=4, n_kv_heads=2, head_dim=16, ffn=48, vocab=64)
+
+
+def test_brute_force_head_dim_not_hidden_over_heads():
+    shape = _wide_head_shape()
+    assert shape.head_dim != shape.hidden // shape.n_heads
+    w = synth.make_weights(shape, 16)
+    ids = [5, 61, 0, 5, 33, 12]
+    want = np.array(brute_forward(shape, w, ids, all_rows=True))
+    got = O.Oracle(shape, w).forward(ids, all_rows=True)
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+
+
+def test_wrong_attention_scale_is_caught(monkeypatch):
+    # A planted mistake in the oracle (scores scaled by 1/sqrt(hidden/n_heads)
+    # instead of 1/sqrt(head_dim)) must fail the brute-force comparison.
+    shape = _wide_head_shape()
+    w = synth.make_weights(shape, 16)
+    ids = [5, 61, 0, 5, 33, 12]
+    want = np.array(brute_forward(shape, w, ids, all_rows=True))
+    right = O.gqa_attention
+    wrong = math.sqrt(shape.head_dim) / math.sqrt(shape.hidden / shape.n_heads)
+    monkeypatch.setattr(O, "gqa_attention", lambda q, k, v, pos: right(q * wrong, k, v, pos))
+    got = O.Oracle(shape, w).forward(ids, all_rows=True)
+    assert np.max(np.abs(got - want)) > 1e-6
+
+
+# ---------------------------------------------------------------- top2_gap (decides where argmax must match)
+def test_top2_gap_closed_forms():
+    nan, inf = float("nan"), float("inf")
+    cases = [
+        ([1.0, 3.0, 2.0], 1.0),
+        ([3.0, 1.0, 3.0], 0.0),                 # exact tie: no gap
+        ([-3.0, -1.0, -2.5], 1.5),              # all negative
+        ([nan, 2.0, inf, 1.0], 1.0),            # +inf and NaN are not finite: excluded
+        ([-inf, 0.25, nan, -0.5], 0.75),
+        ([nan, 5.0, -inf], inf),                # one finite value: nothing to tie with
+        ([nan, nan], inf),
+        ([7.0], inf),
+    ]
+    for row, want in cases:
+        got = O.top2_gap(np.array(row, dtype=np.float32))
+        assert got == want, (row, got, want)
+
+
+def test_top2_gap_matches_enumeration():
+    rng = np.random.default_rng(17)
+    for trial in range(50):
+        row = rng.standard_normal(40).astype(np.float32)
+        if trial % 3 == 0:
+            row[rng.integers(40)] = row.max()           # planted tie at the top
+        if trial % 4 == 1:
+            row[rng.integers(40, size=3)] = np.nan
+        if trial % 5 == 2:
+            row[rng.integers(40)] = np.inf
+        fin = [float(v) for v in row if math.isfinite(float(v))]
+        best = max(fin)
+        rest = list(fin)
+        rest.remove(best)                                # one copy only: a tie leaves the same value
+        want = best - max(rest)
+        assert O.top2_gap(row) == pytest.approx(want, abs=0.0)
+        assert O.greedy_argmax_fast(row) == O.greedy_argmax(row)
