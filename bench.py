@@ -16,7 +16,8 @@ Also reported:
   prefill      -- prefill tok/s and the MFMA roofline of its dominant kernel;
   traffic      -- (in each roofline) HBM bytes per launch from the committed
                   counter summary, while the kernel sources are unchanged;
-  cpu_baseline -- the CPU oracle on a bounded sample of the same decode workload.
+  cpu_baseline -- the float32 CPU oracle on a bounded sample of the same workload
+                  (a 512-token prefill and decode steps), on the host's cores.
 
 Prints one JSON line.  Inputs are seeded synthetic weights and tokens
 (random-init, no checkpoint).
@@ -88,26 +89,51 @@ def prefill_flops(shape, B, S):
 
 
 # --------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(wl, w, steps):
-    """The CPU oracle on a bounded sample: prefill (untimed), then `steps` decode steps."""
+def cpu_baseline(wl, w, steps, prefill_tokens=512):
+    """The CPU oracle in float32 (the precision of the pages' own CPU path) on a
+    bounded sample of the same workload: one `prefill_tokens`-token prefill of
+    the prompt (timed), then `steps` greedy decode steps (timed).  BLAS threads =
+    the CPUs this process may run on; the CPU model and BLAS library are reported."""
     import numpy as np
     from oracle import oracle as O
+    threads = len(os.sched_getaffinity(0))
+    blas, cores = "unknown", threads
+    limiter = None
     try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=threads, user_api="blas")
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            cores = int(info[0].get("num_threads", threads))
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')} ({info[0].get('architecture')})"
     except Exception:
-        cores = 1
-    orc = O.Oracle(wl.shape, w)
-    prompt = wl.prompts[0]
+        pass
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    orc = O.Oracle(wl.shape, w, dtype=np.float32)
+    prompt = wl.prompts[0][:prefill_tokens]
+    t0 = time.perf_counter()
     logits = orc.prefill(0, prompt)
+    pdt = time.perf_counter() - t0
     t0 = time.perf_counter()
     for k in range(steps):
         tok = O.greedy_argmax_fast(logits)
         logits = orc.decode_step(0, tok, len(prompt) + k)
     dt = time.perf_counter() - t0
-    return {"value": round(steps / dt, 3), "unit": "tok/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{steps} greedy bs1 decode steps from position {len(prompt)} of the same "
-                      f"512-token prompt (float64 NumPy oracle; prefill untimed)"}
+    if limiter is not None:
+        limiter.restore_original_limits()
+    return {"value": round(steps / dt, 3), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"{steps} greedy bs1 decode steps from position {len(prompt)} after a {len(prompt)}-token "
+                      f"prefill of the same prompt (float32 NumPy oracle)",
+            "dtype": "float32", "cpu_model": cpu_model, "blas": blas,
+            "prefill_tok_s": round(len(prompt) / pdt, 2), "prefill_tokens": len(prompt)}
 
 
 def measured_traffic(key):

@@ -137,6 +137,10 @@ struct fs_model {
   int32_t* lm_pi = nullptr;
   float* logits_tmp = nullptr;    // [max_seqs, V] when the caller passes none
   SampleRowScratch* sample_scr = nullptr;   // [max_seqs], on the first fs_sample
+  // out-of-range token report: pinned host words {flag, id, row} the embedding
+  // kernel writes through their device mapping (tokerr_dev)
+  int32_t* tokerr = nullptr;
+  int32_t* tokerr_dev = nullptr;
   int32_t* gen_tok = nullptr;     // device int32 [1]: the token fs_generate feeds back
   int32_t* gen_host = nullptr;    // pinned int32 [2]: host copies of two consecutive tokens
   hipEvent_t gen_ev[2] = {};      // their copies' completion
@@ -183,6 +187,7 @@ struct fs_model {
       if (stage_ev[i]) hipEventDestroy(stage_ev[i]);
     if (stage) hipHostFree(stage);
     if (gen_host) hipHostFree(gen_host);
+    if (tokerr) hipHostFree(tokerr);
     for (auto e : gen_ev)
       if (e) hipEventDestroy(e);
     hipFree(gen_tok);
@@ -269,6 +274,17 @@ fs_status check_slots(const fs_model* m, const int32_t* slots, int B) {
 }
 
 int cpl_ok(int K) { return K % 8 == 0 && K <= 4096; }
+
+// A token ID outside [0, vocab) seen by an earlier call's embedding kernel
+// (that sequence's rows were made NaN): reported once, then cleared.
+fs_status check_token_error(fs_model* m) {
+  volatile int32_t* f = m->tokerr;
+  if (f == nullptr || f[0] == 0) return FS_OK;
+  const int id = f[1], row = f[2];
+  f[0] = 0;
+  return fail(FS_ERR_INVALID_ARG, "token ID " + std::to_string(id) + " (row " + std::to_string(row) +
+                                      " of an earlier call) is outside [0, vocab); that sequence's logits are NaN");
+}
 
 // Final RMSNorm of `rows` rows of x at stride ldx, tied head E . h, and
 // optionally the greedy IDs.  logits may be null only when `next` is set.
@@ -382,15 +398,20 @@ fs_status block_skinny(fs_model* m, const LayerW& L, int rows, Attn&& attention,
   return FS_OK;
 }
 
-// One transformer block over `rows` rows in the GEMM (MFMA, bf16) form.
-// qkv_f32: the QKV projection is stored fp32 (decode attention) or bf16 (prefill).
+// One transformer block over `rows` rows in the GEMM (MFMA, bf16) form.  The
+// Q/K/V projection is kept in fp32 up to the per-head norm and RoPE (stored
+// fp32, or normalised in the large GEMM's epilogue); qkv_f32 marks the decode
+// form, whose attention loads the raw fp32 projection itself.
 template <class Attn>
 fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&& attention,
                      hipStream_t s, const RopeKvParams* rope = nullptr, bool* rope_done = nullptr) {
   const fs_config& c = m->cfg;
-  // The attention input keeps ~16 significant bits (bf16 value + bf16 remainder):
-  // rounding it to bf16 alone moves the logits by about as much as the whole
-  // error budget, while the MLP input tolerates plain bf16.
+  // Both normalised inputs (attention and MLP) keep ~16 significant bits as a
+  // bf16 value plus a bf16 remainder (a second MFMA pass over the same weight
+  // tiles): with plain bf16 operands at every GEMM input and a 4096-token
+  // context the last-token logits reach the whole 2e-2 error budget; the two
+  // norm outputs are the largest of those rounding points that the bf16 KV
+  // cache does not fix.
   void* xn_lo = (char*)m->xn + (size_t)rows * c.hidden * 2;
   // int8 weights: each matrix's codes are widened to bf16 (exact) into wconv
   // just before its GEMM, and the row scales are applied per output column
@@ -424,8 +445,8 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
                                  c.hidden, s, xn_lo, L.sqkv, rope));
     if (rope_done != nullptr) *rope_done = true;
   } else {
-    LAUNCH(m, "qkv", s, gemm_bf16(qkv_f32 ? GEPI_STORE_F32 : GEPI_STORE_BF16, m->xn, c.hidden, wb, c.hidden,
-                                  m->qkv, m->qkv_w, rows, m->qkv_w, c.hidden, s, xn_lo, L.sqkv));
+    LAUNCH(m, "qkv", s, gemm_bf16(GEPI_STORE_F32, m->xn, c.hidden, wb, c.hidden, m->qkv, m->qkv_w, rows,
+                                  m->qkv_w, c.hidden, s, xn_lo, L.sqkv));
   }
   fs_status st = attention();
   if (st != FS_OK) return st;
@@ -440,9 +461,9 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
     LAUNCH(m, "wconv", s, codes_to_bf16((const int8_t*)L.wgu, (size_t)2 * c.ffn * c.hidden, m->wconv, s));
     wb = m->wconv;
   }
-  LAUNCH(m, "norm", s, norm_in(m, rows, L.mlp_norm, nullptr, s));
+  LAUNCH(m, "norm", s, norm_in(m, rows, L.mlp_norm, xn_lo, s));
   LAUNCH(m, "gate_up", s, gemm_bf16(GEPI_SWIGLU_BF16, m->xn, c.hidden, wb, c.hidden, m->hbuf, c.ffn, rows,
-                                    2 * c.ffn, c.hidden, s, nullptr, L.sgu));
+                                    2 * c.ffn, c.hidden, s, xn_lo, L.sgu));
   wb = L.wdown;
   if (q8) {
     LAUNCH(m, "wconv", s, codes_to_bf16((const int8_t*)L.wdown, (size_t)c.hidden * c.ffn, m->wconv, s));
@@ -643,6 +664,11 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   if (hipHostMalloc((void**)&m->stage, sizeof(int32_t) * 2 * c.max_seqs * STAGE_RING, hipHostMallocDefault) !=
       hipSuccess)
     return bail(FS_ERR_OOM, "pinned staging allocation failed");
+  if (hipHostMalloc((void**)&m->tokerr, 4 * sizeof(int32_t), hipHostMallocMapped | hipHostMallocCoherent) !=
+      hipSuccess)
+    return bail(FS_ERR_OOM, "pinned token-report allocation failed");
+  std::memset(m->tokerr, 0, 4 * sizeof(int32_t));
+  chk(hipHostGetDevicePointer((void**)&m->tokerr_dev, m->tokerr, 0));
   for (int i = 0; i < STAGE_RING; ++i) chk(hipEventCreateWithFlags(&m->stage_ev[i], hipEventDisableTiming));
   chk(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
   {
@@ -686,13 +712,15 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
   if (S > c.max_ctx) return fail(FS_ERR_CAPACITY, "prompt longer than max_ctx");
   fs_status st = check_slots(m, slots, B);
   if (st != FS_OK) return st;
+  if ((st = check_token_error(m)) != FS_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   const long long T = (long long)B * S;
   if (T > (1LL << 31) / std::max(m->qkv_w, c.ffn)) return fail(FS_ERR_UNSUPPORTED, "B*S too large");
   if ((st = ensure_rows(m, T, s)) != FS_OK) return st;
   if ((st = stage_ints(m, nullptr, slots, B, s)) != FS_OK) return st;
   if (m->timing) LAUNCH(m, "gate", s, spin_wait(TIMING_GATE_US, s));
-  LAUNCH(m, "embed", s, embed(m->embed, m->wdt, tokens, (int)T, c.hidden, c.vocab, m->x, s, m->embed_scale));
+  LAUNCH(m, "embed", s, embed(m->embed, m->wdt, tokens, (int)T, c.hidden, c.vocab, m->x, s, m->embed_scale,
+                              m->tokerr_dev));
   const bool skinny = (m->dt == DT_F32) || T <= SKINNY_MAX_ROWS;
   const int act_dt = skinny ? DT_F32 : DT_BF16;
   m->pend_np = 0;
@@ -712,7 +740,7 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
     RopeKvParams r{};
     r.qscale = a.q_prescale;
     r.rot = m->rot; r.gated = m->gated;
-    r.qkv = m->qkv; r.in_dt = act_dt; r.qout = m->qr; r.q_dt = act_dt;
+    r.qkv = m->qkv; r.in_dt = DT_F32; r.qout = m->qr; r.q_dt = act_dt;
     r.kcache = kc; r.vcache = vc; r.kv_dt = m->dt;
     r.gq = L.q_norm; r.gk = L.k_norm; r.eps = c.rms_eps;
     r.cos_t = m->rope_cos; r.sin_t = m->rope_sin; r.slots = m->d_slot;
@@ -723,7 +751,7 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
       if (!rope_done) LAUNCH(m, "rope_kv", s, rope_kv(r, s));
       LAUNCH(m, "attn", s, skinny ? attn_prefill_vec(a, s) : fa ? attn_prefill_fa(a, s) : attn_prefill(a, s));
       if (m->gated)
-        LAUNCH(m, "attn_gate", s, attn_gate(m->attn, act_dt, m->qkv, act_dt, (int)T, c.n_heads, c.head_dim, m->qkv_w, s));
+        LAUNCH(m, "attn_gate", s, attn_gate(m->attn, act_dt, m->qkv, DT_F32, (int)T, c.n_heads, c.head_dim, m->qkv_w, s));
       return FS_OK;
     };
     st = skinny ? block_skinny(m, L, (int)T, attention, s)
@@ -779,7 +807,8 @@ static fs_status enqueue_decode(fs_model* m, const int32_t* tokens, int B, float
                                 const AttnSplit& sp, hipStream_t s) {
   const fs_config& c = m->cfg;
   if (m->timing) LAUNCH(m, "gate", s, spin_wait(TIMING_GATE_US, s));
-  LAUNCH(m, "embed", s, embed(m->embed, m->wdt, tokens, B, c.hidden, c.vocab, m->x, s, m->embed_scale));
+  LAUNCH(m, "embed", s, embed(m->embed, m->wdt, tokens, B, c.hidden, c.vocab, m->x, s, m->embed_scale,
+                              m->tokerr_dev));
   const bool skinny = (m->dt == DT_F32) || B <= SKINNY_MAX_ROWS;
   fs_status st = FS_OK;
   m->pend_np = 0;
@@ -824,6 +853,7 @@ fs_status fs_decode_step(fs_model* m, const int32_t* tokens, const int32_t* posi
   if (B <= 0 || B > c.max_seqs) return fail(FS_ERR_INVALID_ARG, "B out of range");
   fs_status st = check_slots(m, slots, B);
   if (st != FS_OK) return st;
+  if ((st = check_token_error(m)) != FS_OK) return st;
   int maxn = 0;
   for (int i = 0; i < B; ++i) {
     if (positions[i] != m->slot_len[slots[i]])
@@ -1074,6 +1104,10 @@ fs_status fs_generate(fs_model* m, const int32_t* prompt, int32_t S, int32_t slo
   const bool sampled = g->sampling != nullptr && g->sampling->temperature != 0.f;
   if (g->max_new_tokens > 0 && out_ids == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL out_ids");
   if (sampled && g->uniforms == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL uniforms");
+  {
+    const fs_status te = check_token_error(m);
+    if (te != FS_OK) return te;
+  }
   if (g->max_new_tokens == 0) {                 // zero budget: no forward pass at all
     *stop_reason = FS_STOP_BUDGET;
     return FS_OK;
@@ -1122,6 +1156,7 @@ fs_status fs_generate(fs_model* m, const int32_t* prompt, int32_t S, int32_t slo
     if (tok < 0) {
       if (forward) m->slot_len[slot] = pos;
       done(FS_OK);
+      if ((st = check_token_error(m)) != FS_OK) return st;      // a prompt token out of range
       return fail(FS_ERR_UNSUPPORTED, "no finite logit at step " + std::to_string(i));
     }
     bool eos = false;

@@ -55,6 +55,10 @@ __shared__ __attribute__((aligned(1024))) bf16 g_stage4[STAGE];
 template <int S> __device__ __forceinline__ bf16* stage_buf() {
   return S == 0 ? g_stage0 : S == 1 ? g_stage1 : S == 2 ? g_stage2 : S == 3 ? g_stage3 : g_stage4;
 }
+// stage buffer w (0..3) as raw bytes
+__device__ __forceinline__ char* stage_bytes(int w) {
+  return reinterpret_cast<char*>(w == 0 ? g_stage0 : w == 1 ? g_stage1 : w == 2 ? g_stage2 : g_stage3);
+}
 // 16 KB of LDS for wave w's epilogue: half (w & 1) of stage buffer w >> 1
 __device__ __forceinline__ char* wave_region(int w) {
   char* b = reinterpret_cast<char*>((w >> 1) == 0 ? g_stage0 : (w >> 1) == 1 ? g_stage1 : (w >> 1) == 2 ? g_stage2 : g_stage3);
@@ -72,20 +76,24 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 
 }  // namespace
 
-// QKV epilogue of a prefill: the tile's 256 tokens x 256 columns (two heads of
-// 128, all q, all k or all v: the section boundaries fall on tile boundaries)
-// are staged as bf16 in the eight wave regions, exactly as the plain bf16
-// store would write them; then per (token, head) the q/k heads get the
-// per-head RMSNorm and rotate-half RoPE over all 128 dims (q also the
-// attention's pre-scale) and go to the q buffer or the K cache, and v goes to
-// the V cache as it is.  The arithmetic is the standalone norm/RoPE pass's,
-// step for step, on the same bf16 inputs, so the results are the same bits.
-// Eight lanes per (token, head): lane `sub` holds dims [8 sub, 8 sub + 8) and
-// their partners [64 + 8 sub, ...), which sit in the next wave's region.
-__device__ __forceinline__ void qkv_rope_epilogue(const RopeKvParams& p, int m0, int n0, int M, int tid) {
+// QKV epilogue of a prefill: the tile's 256 tokens x 256 columns are two
+// heads of 128 (all q, all k or all v: the section boundaries fall on tile
+// boundaries).  The fp32 products are staged in LDS 128 tokens at a time (the
+// four waves of one token half each write their 128 x 64 block, 32 KB, into
+// one stage buffer); then per (token, head) the q/k heads get the per-head
+// RMSNorm and rotate-half RoPE over all 128 dims (q also the attention's
+// pre-scale) and go to the q buffer or the K cache, and v goes to the V cache
+// as it is.  The arithmetic is the standalone norm/RoPE pass's, step for step,
+// on the same fp32 inputs, so the results are the same bits.  Eight lanes per
+// (token, head): lane `sub` holds dims [8 sub, 8 sub + 8) (block of wave
+// 2 head) and their partners [64 + 8 sub, ...) (block of wave 2 head + 1).
+// Row m of a staged block is 64 floats in 16 chunks of 16 B, chunk c at slot
+// c ^ (m & 15).
+__device__ __forceinline__ void qkv_rope_epilogue(const RopeKvParams& p, const f32x16 (&acc)[2][4], int m0,
+                                                  int n0, int M, int tid) {
   constexpr int D = 128;
-  __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
-  lds_barrier();
+  const int lane = tid & 63, wid = tid >> 6, wm = wid >> 2, wn = wid & 3;
+  const int lrow = lane & 31, hl = lane >> 5;
   const int hsec = n0 / D;                         // first of the tile's two heads in q|k|v order
   const bool is_q = hsec < p.nq, is_k = !is_q && hsec < p.nq + p.nkv;
   const int sub = tid & 7;
@@ -93,55 +101,82 @@ __device__ __forceinline__ void qkv_rope_epilogue(const RopeKvParams& p, int m0,
   float g0[8], g1[8];
   load8(g + 8 * sub, g0);
   load8(g + 64 + 8 * sub, g1);
-#pragma unroll 2
-  for (int it = 0; it < 8; ++it) {
-    const int item = it * 512 + tid;
-    const int hd = (item >> 3) & 1, row = item >> 4;
-    const int mr = row & 127;
-    const char* R0 = wave_region((row >> 7) * 4 + 2 * hd);
-    const int off = mr * 128 + ((sub ^ (mr & 7)) << 4);
-    float x0[8], x1[8];
-    load8(reinterpret_cast<const bf16*>(R0 + off), x0);
-    load8(reinterpret_cast<const bf16*>(R0 + 16384 + off), x1);     // the next wave's region
-    const int t = min(m0 + row, M - 1);
-    const int b = t / p.S_per, pos = t % p.S_per;
-    const int hh = hsec + hd;
-    if (is_q || is_k) {
-      float ss = 0.f;
+#pragma unroll 1
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+      char* R = stage_bytes(wn);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(x0[e], x0[e], fmaf(x1[e], x1[e], ss));
-      ss = group_sum<8>(ss);
-      const float inv = rsqrtf(__fadd_rn(ss / (float)D, p.eps));
-      float cs[8], sn[8];
-      load8(p.cos_t + (size_t)pos * (D / 2) + 8 * sub, cs);
-      load8(p.sin_t + (size_t)pos * (D / 2) + 8 * sub, sn);
+      for (int i = 0; i < 4; ++i) {
+        const int m = i * 32 + lrow;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float a = x0[e] * inv * g0[e], c = x1[e] * inv * g1[e];
-        const float y0 = fmaf(a, cs[e], -(c * sn[e])), y1 = fmaf(c, cs[e], a * sn[e]);
-        x0[e] = is_q ? y0 * p.qscale : y0;
-        x1[e] = is_q ? y1 * p.qscale : y1;
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * gq + e];
+            const int cc = j * 8 + 2 * gq + hl;
+            *reinterpret_cast<f32x4*>(R + m * 256 + ((cc ^ (m & 15)) << 4)) = v;
+          }
       }
     }
-    if (m0 + row >= M) continue;
-    bf16* dst;
-    if (is_q) {
-      dst = reinterpret_cast<bf16*>(p.qout) + (size_t)t * p.nq * D + (size_t)hh * D;
-    } else {
-      const int j = is_k ? hh - p.nq : hh - p.nq - p.nkv;
-      const size_t o = (size_t)p.slots[b] * p.slot_stride + (size_t)j * p.head_stride + (size_t)pos * D;
-      dst = reinterpret_cast<bf16*>(is_k ? p.kcache : p.vcache) + o;
-    }
-    u32x4 u0, u1;
+    lds_barrier();
+#pragma unroll 2
+    for (int it = 0; it < 4; ++it) {
+      const int item = it * 512 + tid;
+      const int hd = (item >> 3) & 1, mr = item >> 4;      // head of the tile, row of the half
+      const int row = half * 128 + mr;
+      const char* RA = stage_bytes(2 * hd) + mr * 256;
+      const char* RB = stage_bytes(2 * hd + 1) + mr * 256;
+      float x0[8], x1[8];
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(RA + (((2 * sub) ^ (mr & 15)) << 4));
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(RA + (((2 * sub + 1) ^ (mr & 15)) << 4));
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(RB + (((2 * sub) ^ (mr & 15)) << 4));
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(RB + (((2 * sub + 1) ^ (mr & 15)) << 4));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u0[i] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x0[2 * i]) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x0[2 * i + 1]) << 16);
-      u1[i] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x1[2 * i]) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x1[2 * i + 1]) << 16);
+      for (int e = 0; e < 4; ++e) { x0[e] = a0[e]; x0[4 + e] = a1[e]; x1[e] = b0[e]; x1[4 + e] = b1[e]; }
+      const int t = min(m0 + row, M - 1);
+      const int b = t / p.S_per, pos = t % p.S_per;
+      const int hh = hsec + hd;
+      if (is_q || is_k) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(x0[e], x0[e], fmaf(x1[e], x1[e], ss));
+        ss = group_sum<8>(ss);
+        const float inv = rsqrtf(__fadd_rn(ss / (float)D, p.eps));
+        float cs[8], sn[8];
+        load8(p.cos_t + (size_t)pos * (D / 2) + 8 * sub, cs);
+        load8(p.sin_t + (size_t)pos * (D / 2) + 8 * sub, sn);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a = x0[e] * inv * g0[e], c = x1[e] * inv * g1[e];
+          const float y0 = fmaf(a, cs[e], -(c * sn[e])), y1 = fmaf(c, cs[e], a * sn[e]);
+          x0[e] = is_q ? y0 * p.qscale : y0;
+          x1[e] = is_q ? y1 * p.qscale : y1;
+        }
+      }
+      if (m0 + row < M) {
+        bf16* dst;
+        if (is_q) {
+          dst = reinterpret_cast<bf16*>(p.qout) + (size_t)t * p.nq * D + (size_t)hh * D;
+        } else {
+          const int j = is_k ? hh - p.nq : hh - p.nq - p.nkv;
+          const size_t o = (size_t)p.slots[b] * p.slot_stride + (size_t)j * p.head_stride + (size_t)pos * D;
+          dst = reinterpret_cast<bf16*>(is_k ? p.kcache : p.vcache) + o;
+        }
+        u32x4 u0, u1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u0[i] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x0[2 * i]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x0[2 * i + 1]) << 16);
+          u1[i] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x1[2 * i]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x1[2 * i + 1]) << 16);
+        }
+        *reinterpret_cast<u32x4*>(dst + 8 * sub) = u0;
+        *reinterpret_cast<u32x4*>(dst + 64 + 8 * sub) = u1;
+      }
     }
-    *reinterpret_cast<u32x4*>(dst + 8 * sub) = u0;
-    *reinterpret_cast<u32x4*>(dst + 64 + 8 * sub) = u1;
+    lds_barrier();                                 // the next half reuses the buffers
   }
 }
 
@@ -288,7 +323,11 @@ void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict
       }
   }
 
-  if (EPI == GEPI_STORE_BF16 || EPI == GEPI_QKV_ROPE) {
+  if constexpr (EPI == GEPI_QKV_ROPE) {
+    qkv_rope_epilogue(rp, acc, m0, n0, M, tid);
+    return;
+  }
+  if (EPI == GEPI_STORE_BF16) {
     // 128 rows x 128 B; chunk c of row m at slot c ^ (m & 7)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -303,10 +342,6 @@ void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict
           const int c = j * 4 + g;
           *reinterpret_cast<bf16x4*>(R + m * 128 + ((c ^ (m & 7)) << 4) + hl * 8) = v;
         }
-    }
-    if constexpr (EPI == GEPI_QKV_ROPE) {
-      qkv_rope_epilogue(rp, m0, n0, M, tid);
-      return;
     }
     bf16* o = reinterpret_cast<bf16*>(out);
     const int c = lane & 7;
@@ -401,7 +436,7 @@ bool gemm_dma_ok(int epi, const void* A, int lda, const void* B, int ldb, const 
 
 bool gemm_dma_rope_ok(const RopeKvParams& r, int M, int N) {
   return r.d == 128 && r.rot == 128 && !r.gated && r.nq % 2 == 0 && r.nkv % 2 == 0 && r.T == M &&
-         r.S_per > 0 && M % r.S_per == 0 && N == (r.nq + 2 * r.nkv) * 128 && r.in_dt == DT_BF16 &&
+         r.S_per > 0 && M % r.S_per == 0 && N == (r.nq + 2 * r.nkv) * 128 && r.in_dt == DT_F32 &&
          r.q_dt == DT_BF16 && r.kv_dt == DT_BF16;
 }
 

@@ -11,10 +11,11 @@ enum Dt { DT_F32 = 0, DT_BF16 = 1, DT_I8 = 2 };
 inline size_t dt_size(int dt) { return dt == DT_BF16 ? 2 : dt == DT_I8 ? 1 : 4; }
 
 // ---------------------------------------------------------------- small ops
-// x[t, :] = E[tok[t], :] widened to fp32 (ids clamped to [0, V)); DT_I8 rows
-// are multiplied by their scale (escale[id]).
+// x[t, :] = E[tok[t], :] widened to fp32; DT_I8 rows are multiplied by their
+// scale (escale[id]).  An id outside [0, V) gives a NaN row and, when bad is
+// set, bad[1] = id, bad[2] = t, then bad[0] = 1.
 hipError_t embed(const void* E, int dt, const int32_t* tok, int T, int H, int V,
-                 float* x, hipStream_t s, const float* escale = nullptr);
+                 float* x, hipStream_t s, const float* escale = nullptr, int32_t* bad = nullptr);
 // Per-row symmetric int8: scale[r] = max|src[r,:]| / 127, codes = rint(src / scale)
 // (fp32 quotients, ties to even; zero row -> scale 0).  cols % 8 == 0.
 hipError_t quantize_rows(const void* src, int dt, int rows, int cols, int8_t* codes, float* scales,
@@ -86,9 +87,10 @@ hipError_t gemm_bf16(int epi, const void* A, int lda, const void* B, int ldb, vo
 // into LDS by DMA): gemm_dma_ok says whether it applies to a call.
 // QKV_ROPE (only here): C is a prefill's fused q|k|v projection and never
 // stored as such; the epilogue applies rope_kv's per-head q/k RMSNorm + RoPE
-// (head_dim 128, full rotation, no output gate, bf16 q and KV) and writes q'
-// and the K/V cache rows as rope_kv would (same bits); gemm_dma_rope_ok says
-// whether a rope_kv call qualifies (M = its T, N = its packed width).
+// (head_dim 128, full rotation, no output gate, fp32 input, bf16 q and KV) to
+// the fp32 products and writes q' and the K/V cache rows as rope_kv would from
+// the stored fp32 projection (same bits); gemm_dma_rope_ok says whether a
+// rope_kv call qualifies (M = its T, N = its packed width).
 bool gemm_dma_ok(int epi, const void* A, int lda, const void* B, int ldb, const void* out, int ldc,
                  int M, int N, int K, const void* A_lo);
 struct RopeKvParams;

@@ -20,12 +20,31 @@ __device__ __forceinline__ float block_sum256(float v, float* sh) {
 // ------------------------------------------------------------------ embedding
 // Token embedding gather ("Coming back to Failed Star", Second sitting:
 // ids[S] -> embedding[S,H]); the residual stream is kept in fp32.
+// A token ID outside [0, V) is not clamped to a plausible row: its residual
+// row is filled with NaN (the sequence's logits become NaN, its greedy ID -1)
+// and the call is recorded in bad[0..2] = {1, id, row} for the host.
+__device__ __forceinline__ bool bad_token(int id, int V, int t, int H, float* __restrict__ x,
+                                          int32_t* __restrict__ bad) {
+  if (id >= 0 && id < V) return false;
+  float* dst = x + (size_t)t * H;
+  const float qnan = __int_as_float(0x7fc00000);
+  for (int k = threadIdx.x; k < H; k += 256) dst[k] = qnan;
+  if (threadIdx.x == 0 && bad != nullptr) {
+    bad[1] = id;
+    bad[2] = t;
+    __threadfence_system();
+    bad[0] = 1;
+  }
+  return true;
+}
+
 template <typename W>
 __global__ __launch_bounds__(256) void embed_kernel(const W* __restrict__ E, const int32_t* __restrict__ tok,
-                                                    int H, int V, float* __restrict__ x) {
+                                                    int H, int V, float* __restrict__ x,
+                                                    int32_t* __restrict__ bad) {
   const int t = blockIdx.x;
-  int id = tok[t];
-  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+  const int id = tok[t];
+  if (bad_token(id, V, t, H, x, bad)) return;
   const W* row = E + (size_t)id * H;
   float* dst = x + (size_t)t * H;
   for (int k = threadIdx.x * 8; k < H; k += 256 * 8) {
@@ -40,10 +59,10 @@ __global__ __launch_bounds__(256) void embed_kernel(const W* __restrict__ E, con
 __global__ __launch_bounds__(256) void embed_i8_kernel(const int8_t* __restrict__ E,
                                                        const float* __restrict__ escale,
                                                        const int32_t* __restrict__ tok, int H, int V,
-                                                       float* __restrict__ x) {
+                                                       float* __restrict__ x, int32_t* __restrict__ bad) {
   const int t = blockIdx.x;
-  int id = tok[t];
-  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+  const int id = tok[t];
+  if (bad_token(id, V, t, H, x, bad)) return;
   const int8_t* row = E + (size_t)id * H;
   const float sc = escale[id];
   float* dst = x + (size_t)t * H;
@@ -58,15 +77,15 @@ __global__ __launch_bounds__(256) void embed_i8_kernel(const int8_t* __restrict_
 }
 
 hipError_t embed(const void* E, int dt, const int32_t* tok, int T, int H, int V, float* x, hipStream_t s,
-                 const float* escale) {
+                 const float* escale, int32_t* bad) {
   if (T <= 0) return hipSuccess;
   if (dt == DT_I8) {
     if (escale == nullptr || H % 8 != 0) return hipErrorInvalidValue;
-    embed_i8_kernel<<<T, 256, 0, s>>>((const int8_t*)E, escale, tok, H, V, x);
+    embed_i8_kernel<<<T, 256, 0, s>>>((const int8_t*)E, escale, tok, H, V, x, bad);
   } else if (dt == DT_BF16) {
-    embed_kernel<bf16><<<T, 256, 0, s>>>((const bf16*)E, tok, H, V, x);
+    embed_kernel<bf16><<<T, 256, 0, s>>>((const bf16*)E, tok, H, V, x, bad);
   } else {
-    embed_kernel<float><<<T, 256, 0, s>>>((const float*)E, tok, H, V, x);
+    embed_kernel<float><<<T, 256, 0, s>>>((const float*)E, tok, H, V, x, bad);
   }
   return hipGetLastError();
 }

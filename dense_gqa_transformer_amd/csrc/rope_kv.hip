@@ -136,6 +136,7 @@ hipError_t rope_kv(const RopeKvParams& p, hipStream_t s) {
   if (p.kv_dt == DT_BF16) {
     if (p.in_dt == DT_BF16 && p.q_dt == DT_BF16) return launch_rope<bf16, bf16, bf16>(p, s);
     if (p.in_dt == DT_F32 && p.q_dt == DT_F32) return launch_rope<float, float, bf16>(p, s);
+    if (p.in_dt == DT_F32 && p.q_dt == DT_BF16) return launch_rope<float, bf16, bf16>(p, s);
   } else if (p.in_dt == DT_F32 && p.q_dt == DT_F32) {
     return launch_rope<float, float, float>(p, s);
   }

@@ -133,8 +133,13 @@ void fs_model_destroy(fs_model *m);
  *           of each row ("Coming back to Failed Star", First sitting, item 4).
  * Positions are 0..S-1 (no implicit BOS).  After the call slot length = S.
  * Errors: INVALID_ARG for NULL pointers, B <= 0 or > max_seqs, S <= 0 (empty
- * input), bad or duplicate slots; CAPACITY for S > max_ctx.  Token IDs out
- * of range are clamped on the device (not detected). */
+ * input), bad or duplicate slots; CAPACITY for S > max_ctx.
+ * Token IDs are device data, checked on the device: an ID outside [0, vocab)
+ * turns its sequence's residual row NaN (that row's logits are NaN, its greedy
+ * ID -1, and the slot's cache holds NaN) and is recorded in pinned host memory;
+ * the next fs_prefill, fs_decode_step or fs_generate on the model (or the same
+ * fs_generate, which is synchronous) returns INVALID_ARG naming the ID and
+ * enqueues nothing.  The record is cleared once reported. */
 fs_status fs_prefill(fs_model *m, const int32_t *tokens, int32_t B, int32_t S,
                      const int32_t *slots, float *logits, void *stream);
 
@@ -148,7 +153,9 @@ fs_status fs_prefill(fs_model *m, const int32_t *tokens, int32_t B, int32_t S,
  * Appends K/V at positions[i] and attends over 0..positions[i]; afterwards
  * the slot length is positions[i]+1.
  * Errors: INVALID_ARG (NULL tokens, B out of range, bad/duplicate slot,
- * position != slot length, both outputs NULL); CAPACITY if positions[i] >= max_ctx. */
+ * position != slot length, both outputs NULL, or an out-of-range token ID
+ * recorded by an earlier call, see fs_prefill); CAPACITY if positions[i] >= max_ctx.
+ * An out-of-range ID in `tokens` makes that row's logits NaN and its `next` -1. */
 fs_status fs_decode_step(fs_model *m, const int32_t *tokens, const int32_t *positions,
                          const int32_t *slots, int32_t B, float *logits, int32_t *next,
                          void *stream);

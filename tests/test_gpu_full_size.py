@@ -1,0 +1,187 @@
+"""GPU parity at the full sizes of the timed workloads, against the oracle.
+
+The oracle runs in float32 here (the precision of the pages' own CPU path,
+"Failed Star (fs)", Status; it agrees with the float64 form to ~1e-5 relative,
+tests/test_oracle_pins.py::test_cached_equals_uncached), since a 4096-token
+pass of the 28-layer model in float64 would take minutes.  Each case runs
+the launch configuration the benchmark times:
+
+* 4 x 4096 prefill of the 0.6B shape in one fs_prefill (the 256 x 256 DMA-fed
+  GEMMs with the norm/RoPE/KV epilogue, the flash attention over 4096 keys):
+  one row's last-token logits and its late K/V rows against the oracle;
+* the same prefill on a 2-layer model of the 0.6B widths: all four rows;
+* the 64-sequence ragged decode (contexts 256..4096): the longest and the
+  median row teacher-forced for four steps at B = 64 (the 256-position split
+  of the long rows and its merge), on a 4-layer model of the 0.6B widths;
+* a batch-1 decode step at context 768 (the last step of the bs1 workload)
+  on the 28-layer model, against the oracle's uncached 768-token pass.
+
+Tolerances: 2e-2 max-abs on every logit, greedy IDs exact where the oracle's
+top-2 gap exceeds 1e-2 ("Milestones", M5: the CPU remains the correctness
+oracle; M4: cached and uncached passes agree).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import oracle as O
+from tests.gpu_common import TOL, check_argmax, check_logits, dev_tokens, make_model, need_gpu, weights
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+def _orc32(shape):
+    return O.Oracle(shape, weights(shape), dtype=np.float32)
+
+
+def _widths(n_layers):
+    return dataclasses.replace(synth.QWEN3_0P6B, n_layers=n_layers)
+
+
+def test_prefill_4x4096_row_vs_oracle():
+    shape = synth.QWEN3_0P6B
+    wl = synth.workload("prefill_0p6b_4x4096")
+    toks = np.stack(wl.prompts)
+    model = make_model(shape, max_seqs=4, max_ctx=4096)
+    try:
+        _flush("gpu prefill 4 x 4096, 28 layers")
+        lg = model.prefill(dev_tokens(toks), [0, 1, 2, 3]).cpu().numpy()
+        row = 2
+        late = {}
+        for layer in (0, 13, 27):
+            for j in (0, 7):
+                kk, vv = model.kv_read(layer, row, j, 4032, 64)
+                late[(layer, j)] = (kk.float().cpu().numpy(), vv.float().cpu().numpy())
+    finally:
+        model.close()
+    _flush("oracle (float32) 4096-token prefill of row 2")
+    orc = _orc32(shape)
+    ref = orc.prefill(0, toks[row])
+    err = check_logits(lg[row], ref, TOL["bf16"], "4x4096 row 2 logits")
+    check_argmax(int(np.argmax(lg[row])), ref, "4x4096 row 2 argmax")
+    _flush(f"4x4096 row 2 max-abs logit error {err:.3e}")
+    for (layer, j), (kk, vv) in late.items():
+        np.testing.assert_allclose(kk, orc.cache[0][layer][0][4032:, j], atol=3e-2, rtol=2e-2,
+                                   err_msg=f"K layer {layer} head {j} positions 4032..4095")
+        np.testing.assert_allclose(vv, orc.cache[0][layer][1][4032:, j], atol=3e-2, rtol=2e-2,
+                                   err_msg=f"V layer {layer} head {j} positions 4032..4095")
+
+
+def test_prefill_4x4096_all_rows_two_layers():
+    shape = _widths(2)
+    toks = synth.tokens(1044, shape.vocab, (4, 4096))
+    model = make_model(shape, max_seqs=4, max_ctx=4096)
+    try:
+        _flush("gpu prefill 4 x 4096, 2 layers of the 0.6B widths")
+        lg = model.prefill(dev_tokens(toks), [0, 1, 2, 3]).cpu().numpy()
+    finally:
+        model.close()
+    orc = _orc32(shape)
+    for b in range(4):
+        _flush(f"oracle row {b}")
+        ref = orc.forward(toks[b])
+        err = check_logits(lg[b], ref, TOL["bf16"], f"2-layer 4x4096 row {b}")
+        _flush(f"2-layer 4x4096 row {b} max-abs logit error {err:.3e}")
+        check_argmax(int(np.argmax(lg[b])), ref, f"2-layer 4x4096 row {b} argmax")
+
+
+def test_decode_bs64_long_and_median_rows_vs_oracle():
+    wl = synth.workload("decode_0p6b_bs64")
+    shape = _widths(4)
+    B = wl.batch
+    lens = np.array([len(p) for p in wl.prompts])
+    order = np.argsort(lens)
+    watch = [int(order[-1]), int(order[B // 2])]          # the longest and the median context
+    model = make_model(shape, max_seqs=B, max_ctx=int(lens.max()) + 8)
+    from dense_gqa_transformer_amd.model import argmax
+    try:
+        nxt = torch.empty((B,), dtype=torch.int32, device="cuda")
+        _flush(f"gpu prefill of 64 sequences (4 layers); watching rows {watch} of {lens[watch].tolist()} tokens")
+        for i, p in enumerate(wl.prompts):
+            argmax(model.prefill(dev_tokens(p[None, :]), [i]), out=nxt[i:i + 1])
+        orcs, refs = {}, {}
+        for i in watch:
+            _flush(f"oracle prefill of row {i} ({lens[i]} tokens)")
+            orcs[i] = _orc32(shape)
+            refs[i] = orcs[i].prefill(0, wl.prompts[i])
+        logits = torch.empty((B, shape.vocab), dtype=torch.float32, device="cuda")
+        for k in range(4):
+            host_next = nxt.cpu().numpy().copy()
+            for i in watch:
+                host_next[i] = O.greedy_argmax_fast(refs[i])
+            model.decode_step(dev_tokens(host_next), [int(n) + k for n in lens], list(range(B)),
+                              logits=logits, next_ids=nxt)
+            lg = logits.cpu().numpy()
+            ids = nxt.cpu().numpy()
+            for i in watch:
+                refs[i] = orcs[i].decode_step(0, int(host_next[i]), int(lens[i]) + k)
+                err = check_logits(lg[i], refs[i], TOL["bf16"], f"bs64 row {i} ({lens[i] + k + 1} keys) step {k}")
+                check_argmax(ids[i], refs[i], f"bs64 row {i} step {k}")
+                _flush(f"bs64 row {i} step {k}: max-abs {err:.3e}")
+    finally:
+        model.close()
+
+
+def test_decode_bs1_at_context_768_vs_uncached_oracle():
+    shape = synth.QWEN3_0P6B
+    wl = synth.workload("decode_0p6b_bs1")
+    toks = np.concatenate([wl.prompts[0], synth.tokens(1031, shape.vocab, 256)]).astype(np.int32)
+    assert toks.size == 768
+    model = make_model(shape, max_seqs=1, max_ctx=768)
+    try:
+        model.prefill(dev_tokens(toks[None, :767]), [0])
+        logits = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda")
+        nxt = torch.empty((1,), dtype=torch.int32, device="cuda")
+        # graph-replayed step at position 767 (the last position of the workload)
+        model.decode_step(dev_tokens(toks[767:768]), [767], [0], logits=logits, next_ids=nxt)
+        got, gid = logits.cpu().numpy()[0], int(nxt.cpu()[0])
+    finally:
+        model.close()
+    _flush("oracle (float32) uncached 768-token pass")
+    ref = _orc32(shape).forward(toks)
+    err = check_logits(got, ref, TOL["bf16"], "bs1 decode at context 768")
+    check_argmax(gid, ref, "bs1 decode at context 768 argmax")
+    _flush(f"bs1 context 768 max-abs logit error {err:.3e}")
+
+
+def test_out_of_range_token_reported():
+    from dense_gqa_transformer_amd import native
+    shape = synth.TINY
+    model = make_model(shape, max_seqs=3, max_ctx=32)
+    try:
+        toks = synth.tokens(1200, shape.vocab, (2, 6))
+        toks[1, 3] = shape.vocab                           # one ID past the vocabulary
+        lg = model.prefill(dev_tokens(toks), [0, 1]).cpu().numpy()
+        ref = O.Oracle(shape, weights(shape)).forward(toks[0])
+        check_logits(lg[0], ref, TOL["f32"], "the other sequence of the batch")
+        assert np.all(np.isnan(lg[1])), "the sequence with the bad ID must not give plausible logits"
+        out = torch.empty((1,), dtype=torch.int32, device="cuda")
+        with pytest.raises(native.FsError) as e:            # reported by the next call
+            model.decode_step(dev_tokens([1]), [6], [0], next_ids=out)
+        assert e.value.status == native.FS_ERR_INVALID_ARG and str(shape.vocab) in str(e.value)
+        assert model.slot_length(0) == 6                   # nothing was enqueued
+        model.decode_step(dev_tokens([1]), [6], [0], next_ids=out)     # reported once, then cleared
+        assert 0 <= int(out.cpu()[0]) < shape.vocab
+        # a negative ID in a decode step: that row's greedy ID is -1
+        model.prefill(dev_tokens(toks[:1]), [2])
+        out2 = torch.empty((2,), dtype=torch.int32, device="cuda")
+        model.decode_step(dev_tokens([-5, 7]), [7, 6], [0, 2], next_ids=out2)
+        ids = out2.cpu().numpy()
+        assert ids[0] == -1 and 0 <= ids[1] < shape.vocab
+        with pytest.raises(native.FsError) as e:
+            model.prefill(dev_tokens(toks[:1]), [1])
+        assert e.value.status == native.FS_ERR_INVALID_ARG and "-5" in str(e.value)
+    finally:
+        model.close()

@@ -9,13 +9,17 @@ random-init weights, uniform-random tokens) is checked against the oracle on
 a batched prefill of two prompts (the MFMA GEMM and attention paths for bf16,
 more than 64 rows), a one-token prompt, teacher-forced decode at batch 2 (GEMV)
 and a decode step at batch 12 (the few-row MFMA GEMM for bf16).  Tolerances
-as elsewhere: 1e-4 (fp32), 2e-2 (bf16) on every logit, except that the bf16
-bound scales with the spread of the logits for the hidden-4096 model: its
-logits spread twice as wide as the 0.6B shape's (std 1.31 against 0.64), and
-rounding the oracle's activations on the CPU at the points where the GPU
-path rounds them to bf16 moves its logits by 3.3e-2 max-abs, the error the GPU
-shows.
+as elsewhere: 1e-4 (fp32) and 2e-2 (bf16) on every logit, the bf16 bound
+being the one set for the 0.6B shape's hidden width of 1024.  Its scaling to
+wider models follows from the weight distribution, not from measured error:
+a logit is E[v] . h with E ~ N(0, 0.02^2) and h the final RMSNorm output
+(unit RMS times norm weights of mean 1), so logits spread with standard
+deviation 0.02 * sqrt(hidden); rounding the activations to bf16 perturbs h by
+a relative amount that does not depend on the width, so the logit error grows
+with that spread, and the bound is 2e-2 * sqrt(hidden / 1024) for hidden
+above 1024 (4e-2 at hidden 4096).
 """
+import math
 import numpy as np
 import pytest
 import torch
@@ -38,8 +42,11 @@ def _shape(nq, nkv, d, dtype, rope_dim=0, hidden=512, ffn=768):
                             vocab=2048, dtype=dtype, rope_dim=rope_dim)
 
 
-# bf16 tolerance factor of the cases whose logit spread exceeds the 0.6B shape's
-TOL_SCALE = {"wide_h4096_bf16": 2.0}
+
+def bf16_tol(shape):
+    """The 0.6B shape's 2e-2 bound scaled by the logit spread, sqrt(hidden / 1024)."""
+    return TOL["bf16"] * max(1.0, math.sqrt(shape.hidden / 1024.0))
+
 
 CASES = {
     "mha_d64_bf16": _shape(4, 4, 64, synth.BF16, hidden=256),      # ratio 1, odd group: one head per workgroup
@@ -58,7 +65,7 @@ CASES = {
 @pytest.mark.parametrize("name", list(CASES))
 def test_shape_parity(name):
     shape = CASES[name]
-    tol = TOL["f32"] if shape.dtype == synth.F32 else TOL["bf16"] * TOL_SCALE.get(name, 1.0)
+    tol = TOL["f32"] if shape.dtype == synth.F32 else bf16_tol(shape)
     seed = 700 + list(CASES).index(name)
     S = 96
     prompts = synth.tokens(seed, shape.vocab, (2, S))
