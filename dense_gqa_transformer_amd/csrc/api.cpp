@@ -1057,33 +1057,76 @@ fs_status fs_quantize_rows_i8(const void* src, int32_t dtype, int32_t rows, int3
   return FS_OK;
 }
 
-fs_status fs_sample(fs_model* m, const float* logits, int32_t B, int32_t V, const fs_sampling* sp,
-                    const float* u, int32_t* out, void* stream) {
-  g_err.clear();
-  if (m == nullptr || logits == nullptr || sp == nullptr || out == nullptr)
-    return fail(FS_ERR_INVALID_ARG, "NULL argument");
-  if (B <= 0 || B > m->cfg.max_seqs) return fail(FS_ERR_INVALID_ARG, "B out of range");
+}  // extern "C"
+
+namespace {
+
+// Checks the sampling arguments shared by fs_sample and fs_sample_noalloc and
+// fills the kernel parameters (scratch left to the caller).  *greedy is set
+// for temperature 0, which needs no scratch.
+fs_status sample_setup(const float* logits, int32_t B, int32_t V, const fs_sampling* sp, const float* u,
+                       int32_t* out, int32_t max_rows, SampleParams* p, bool* greedy) {
+  if (logits == nullptr || sp == nullptr || out == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+  if (B <= 0 || B > max_rows) return fail(FS_ERR_INVALID_ARG, "B out of range");
   if (V <= 0) return fail(FS_ERR_INVALID_ARG, "V must be positive");
   const float T = sp->temperature;
   if (!(T >= 0.f) || !std::isfinite(T)) return fail(FS_ERR_INVALID_ARG, "temperature must be finite and >= 0");
   if (sp->top_k < 0) return fail(FS_ERR_INVALID_ARG, "top_k must be >= 0");
   if (!(sp->top_p > 0.f && sp->top_p <= 1.f)) return fail(FS_ERR_INVALID_ARG, "top_p must be in (0, 1]");
+  *greedy = (T == 0.f);
+  if (*greedy) return FS_OK;
+  if (u == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL u");
+  *p = SampleParams{};
+  p->logits = logits; p->ld = V; p->B = B; p->V = V;
+  p->G = std::min(SAMPLE_MAX_BLOCKS, std::max(1, (V + 2047) / 2048));
+  p->slice = (V + p->G - 1) / p->G;
+  p->sc = 1.4426950408889634f / T;
+  p->top_k = sp->top_k; p->top_p = sp->top_p;
+  p->u = u; p->out = out;
+  return FS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fs_status fs_sample(fs_model* m, const float* logits, int32_t B, int32_t V, const fs_sampling* sp,
+                    const float* u, int32_t* out, void* stream) {
+  g_err.clear();
+  if (m == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+  SampleParams p{};
+  bool greedy = false;
+  fs_status st = sample_setup(logits, B, V, sp, u, out, m->cfg.max_seqs, &p, &greedy);
+  if (st != FS_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (T == 0.f) {
+  if (greedy) {
     HIP_TRY(argmax_rows(logits, B, V, V, out, s));
     return FS_OK;
   }
-  if (u == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL u");
   if (m->sample_scr == nullptr &&
       dalloc(&m->sample_scr, (size_t)m->cfg.max_seqs * sizeof(SampleRowScratch)) != hipSuccess)
     return fail(FS_ERR_OOM, "sampling scratch allocation failed");
+  p.scr = m->sample_scr;
+  HIP_TRY(sample_rows(p, s));
+  return FS_OK;
+}
+
+fs_status fs_sample_noalloc(const float* logits, int32_t B, int32_t V, const fs_sampling* sp, const float* u,
+                            int32_t* out, void* stream) {
+  g_err.clear();
+  if (B > SAMPLE_STATIC_MAX_ROWS)
+    return fail(FS_ERR_CAPACITY, "B = " + std::to_string(B) + " exceeds the static sampling scratch of " +
+                                     std::to_string(SAMPLE_STATIC_MAX_ROWS) + " rows");
   SampleParams p{};
-  p.logits = logits; p.ld = V; p.B = B; p.V = V;
-  p.G = std::min(SAMPLE_MAX_BLOCKS, std::max(1, (V + 2047) / 2048));
-  p.slice = (V + p.G - 1) / p.G;
-  p.sc = 1.4426950408889634f / T;
-  p.top_k = sp->top_k; p.top_p = sp->top_p;
-  p.u = u; p.out = out; p.scr = m->sample_scr;
+  bool greedy = false;
+  fs_status st = sample_setup(logits, B, V, sp, u, out, SAMPLE_STATIC_MAX_ROWS, &p, &greedy);
+  if (st != FS_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (greedy) {
+    HIP_TRY(argmax_rows(logits, B, V, V, out, s));
+    return FS_OK;
+  }
+  HIP_TRY(sample_static_scratch(&p.scr));
   HIP_TRY(sample_rows(p, s));
   return FS_OK;
 }

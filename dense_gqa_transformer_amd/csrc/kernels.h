@@ -218,7 +218,12 @@ struct SampleParams {
   SampleRowScratch* scr;               // device [B]
 };
 // temperature -> top-k -> top-p -> renormalise -> draw for B rows; -1 for a row
-// without a finite logit.
+// without a finite logit.  Clears p.scr rows 0..B-1 itself (a fill kernel).
 hipError_t sample_rows(const SampleParams& p, hipStream_t s);
+// Device address, on the current device, of the library's static row scratch
+// (SAMPLE_STATIC_MAX_ROWS rows, one copy per device, never freed); looked up
+// with hipGetSymbolAddress on the first call per device.  Allocates nothing.
+constexpr int SAMPLE_STATIC_MAX_ROWS = 64;
+hipError_t sample_static_scratch(SampleRowScratch** out);
 
 }  // namespace fsk

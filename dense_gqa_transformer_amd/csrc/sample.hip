@@ -22,6 +22,8 @@
 // block 0 stores it in the row scratch), then builds the next histogram, so
 // no separate selection step runs between launches and no pass repeats an
 // earlier selection.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -395,6 +397,36 @@ __global__ __launch_bounds__(NT) void sample_final_kernel(const SampleParams p) 
     }
     p.out[row] = pick;
   }
+}
+
+// ------------------------------------------------------------------ static scratch
+// Row scratch for callers that cannot allocate: one copy per device, held
+// until the process ends.  Host code never passes this name to a kernel (on
+// the host it only stands in for the symbol); it passes the device address
+// hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) SampleRowScratch scratch[SAMPLE_STATIC_MAX_ROWS];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+SampleRowScratch* g_scratch_ptr[MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t sample_static_scratch(SampleRowScratch** out) {
+  *out = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<SampleRowScratch*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t sample_rows(const SampleParams& p, hipStream_t s) {

@@ -204,3 +204,21 @@ def argmax(logits: torch.Tensor, out: Optional[torch.Tensor] = None,
         out = torch.empty((B,), dtype=torch.int32, device=logits.device)
     check(lib.fs_argmax(_ptr(logits), B, V, _ptr(out), _stream_ptr(stream)))
     return out
+
+
+def sample_noalloc(logits: torch.Tensor, temperature: float, top_k: int = 0, top_p: float = 1.0,
+                   u: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """fs_sample_noalloc: Model.sample without a model, on the library's static
+    scratch (rows up to FS_SAMPLE_NOALLOC_MAX_ROWS; the library allocates nothing)."""
+    lib = native.load()
+    assert logits.dtype == torch.float32 and logits.is_contiguous() and logits.dim() == 2
+    B, V = logits.shape
+    if out is None:
+        out = torch.empty((B,), dtype=torch.int32, device=logits.device)
+    if u is not None:
+        assert u.dtype == torch.float32 and u.is_contiguous() and u.numel() >= B
+    sp = native.FsSampling(float(temperature), int(top_k), float(top_p))
+    check(lib.fs_sample_noalloc(_ptr(logits), B, V, ctypes.byref(sp), _ptr(u) if u is not None else None,
+                                _ptr(out), _stream_ptr(stream)))
+    return out

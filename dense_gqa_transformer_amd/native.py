@@ -99,6 +99,8 @@ def load() -> ctypes.CDLL:
     lib.fs_quantize_rows_i8.restype = ctypes.c_int
     lib.fs_sample.argtypes = [P, P, i32, i32, ctypes.POINTER(FsSampling), P, P, P]
     lib.fs_sample.restype = ctypes.c_int
+    lib.fs_sample_noalloc.argtypes = [P, i32, i32, ctypes.POINTER(FsSampling), P, P, P]
+    lib.fs_sample_noalloc.restype = ctypes.c_int
     lib.fs_generate.argtypes = [P, P, i32, i32, ctypes.POINTER(FsGeneration), ctypes.POINTER(i32),
                                 ctypes.POINTER(i32), ctypes.POINTER(i32), P]
     lib.fs_generate.restype = ctypes.c_int

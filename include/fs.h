@@ -204,6 +204,23 @@ typedef struct {
 fs_status fs_sample(fs_model *m, const float *logits, int32_t B, int32_t V,
                     const fs_sampling *sampling, const float *u, int32_t *out, void *stream);
 
+/* fs_sample for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, rule and results as fs_sample, without a model handle; the
+ * per-row histograms live in a static device array of the library
+ * (FS_SAMPLE_NOALLOC_MAX_ROWS rows, about 68 KB each; one copy per GPU, held
+ * until the process ends), whose address is looked up once per device on the
+ * first call there.  Allocates nothing; each call clears the rows it uses.
+ * Every call on one GPU shares that array: calls that overlap on a GPU (on
+ * different streams, or from different threads) race and must be serialised
+ * by the caller.
+ * Errors: CAPACITY for B > FS_SAMPLE_NOALLOC_MAX_ROWS; otherwise as fs_sample
+ * (INVALID_ARG for NULL pointers, B <= 0, V <= 0 or bad sampling
+ * parameters; HIP). */
+#define FS_SAMPLE_NOALLOC_MAX_ROWS 64
+fs_status fs_sample_noalloc(const float *logits, int32_t B, int32_t V, const fs_sampling *sampling,
+                            const float *u, int32_t *out, void *stream);
+
 /* Why fs_generate stopped. */
 typedef enum {
     FS_STOP_NONE = 0,

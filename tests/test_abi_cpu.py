@@ -13,7 +13,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == {"fs_model_create", "fs_model_destroy", "fs_prefill", "fs_decode_step",
                           "fs_argmax", "fs_slot_length", "fs_kv_read", "fs_last_error",
                           "fs_timing", "fs_timing_read", "fs_kernel_bench", "fs_sample", "fs_generate",
-                          "fs_quantize_rows_i8"}
+                          "fs_quantize_rows_i8", "fs_sample_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -32,6 +32,13 @@ def test_argument_errors_without_device():
     assert lib.fs_timing(None, 1) == native.FS_ERR_INVALID_ARG
     sp = native.FsSampling(1.0, 0, 1.0)
     assert lib.fs_sample(None, fake, 1, 10, ctypes.byref(sp), fake, fake, None) == native.FS_ERR_INVALID_ARG
+    ns = lib.fs_sample_noalloc
+    assert ns(None, 1, 10, ctypes.byref(sp), fake, fake, None) == native.FS_ERR_INVALID_ARG
+    assert ns(fake, 0, 10, ctypes.byref(sp), fake, fake, None) == native.FS_ERR_INVALID_ARG
+    assert ns(fake, 65, 10, ctypes.byref(sp), fake, fake, None) == native.FS_ERR_CAPACITY
+    assert "static" in native.last_error()
+    assert ns(fake, 2, 10, ctypes.byref(native.FsSampling(1.0, 0, 1.5)), fake, fake, None) == native.FS_ERR_INVALID_ARG
+    assert ns(fake, 2, 10, ctypes.byref(sp), None, fake, None) == native.FS_ERR_INVALID_ARG
     g = native.FsGeneration(4, None, 0, 0, None, None)
     n, why = ctypes.c_int32(), ctypes.c_int32()
     out = (ctypes.c_int32 * 4)()
