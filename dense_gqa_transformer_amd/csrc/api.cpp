@@ -137,6 +137,13 @@ struct fs_model {
   int32_t* lm_pi = nullptr;
   float* logits_tmp = nullptr;    // [max_seqs, V] when the caller passes none
   SampleRowScratch* sample_scr = nullptr;   // [max_seqs], on the first fs_sample
+  // persistent batch-1 decode step (one launch per step) where the shape allows
+  bool use_persist = false;
+  void* pex = nullptr;            // its exchange records
+  uint32_t pstep = 0;             // steps launched (the records' tag)
+  int32_t* pabort = nullptr;      // pinned host word the kernel sets when a wait times out
+  int32_t* pabort_dev = nullptr;
+  long long* ptrace = nullptr;    // clock stamps of the last persistent step (FS_DECODE_TRACE=1)
   // out-of-range token report: pinned host words {flag, id, row} the embedding
   // kernel writes through their device mapping (tokerr_dev)
   int32_t* tokerr = nullptr;
@@ -188,6 +195,9 @@ struct fs_model {
     if (stage) hipHostFree(stage);
     if (gen_host) hipHostFree(gen_host);
     if (tokerr) hipHostFree(tokerr);
+    if (pabort) hipHostFree(pabort);
+    hipFree(ptrace);
+    hipFree(pex);
     for (auto e : gen_ev)
       if (e) hipEventDestroy(e);
     hipFree(gen_tok);
@@ -684,6 +694,31 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
       const int v = std::atoi(mc);
       if (v == 32 || v == 64 || v == 128 || v == 256) m->min_chunk = v;
     }
+    // the persistent decode step (opt-in: measured slower than the graph of
+    // per-product kernels) needs the 0.6B shape, bf16 weights and all 256 CUs
+    // for its 256 resident workgroups
+    const char* pe = std::getenv("FS_DECODE_PERSIST");
+    int cus = 0;
+    chk(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device));
+    m->use_persist = (pe != nullptr && pe[0] == '1') && cus == 256 &&
+                     decode_persist_ok(c.n_layers, c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, m->dt,
+                                       m->wdt, m->gated, m->rot);
+    if (m->use_persist) {
+      if (dalloc(&m->pex, decode_persist_exchange_bytes()) != hipSuccess)
+        return bail(FS_ERR_OOM, "decode exchange allocation failed");
+      chk(hipMemsetAsync(m->pex, 0, decode_persist_exchange_bytes(), s));
+      if (hipHostMalloc((void**)&m->pabort, 4 * sizeof(int32_t), hipHostMallocMapped | hipHostMallocCoherent) !=
+          hipSuccess)
+        return bail(FS_ERR_OOM, "pinned abort-word allocation failed");
+      std::memset(m->pabort, 0, 4 * sizeof(int32_t));
+      chk(hipHostGetDevicePointer((void**)&m->pabort_dev, m->pabort, 0));
+      const char* tr = std::getenv("FS_DECODE_TRACE");
+      if (tr != nullptr && tr[0] == '1') {
+        if (dalloc(&m->ptrace, 1024 * sizeof(long long)) != hipSuccess)
+          return bail(FS_ERR_OOM, "trace allocation failed");
+        chk(hipMemsetAsync(m->ptrace, 0, 1024 * sizeof(long long), s));
+      }
+    }
   }
   chk(hipStreamSynchronize(s));
   if (e != hipSuccess) return bail(FS_ERR_HIP, std::string("model setup failed: ") + hipGetErrorString(e));
@@ -864,6 +899,41 @@ fs_status fs_decode_step(fs_model* m, const int32_t* tokens, const int32_t* posi
     maxn = std::max(maxn, positions[i] + 1);
   }
   hipStream_t s = (hipStream_t)stream;
+  if (m->pabort != nullptr && ((volatile int32_t*)m->pabort)[0] != 0) {
+    // a persistent step gave up waiting (workgroups not all resident?): report
+    // it once and run later steps on the multi-kernel path
+    ((volatile int32_t*)m->pabort)[0] = 0;
+    m->use_persist = false;
+    return fail(FS_ERR_HIP, "an earlier decode step timed out waiting between workgroups (its logits are "
+                            "invalid); later steps use the multi-kernel path");
+  }
+  if (B == 1 && m->use_persist && maxn <= decode_persist_max_ctx()) {
+    const fs_config& cc = m->cfg;
+    const LayerW& L0 = m->layers[0];
+    DecodePersistParams p{};
+    p.wqkv0 = L0.wqkv; p.wo0 = L0.wo; p.wgu0 = L0.wgu; p.wdown0 = L0.wdown;
+    p.wstride = cc.n_layers > 1 ? ((const char*)m->layers[1].wqkv - (const char*)L0.wqkv) / 2 : 0;
+    p.attn_norm0 = L0.attn_norm; p.mlp_norm0 = L0.mlp_norm; p.q_norm0 = L0.q_norm; p.k_norm0 = L0.k_norm;
+    p.nstride = cc.n_layers > 1 ? m->layers[1].attn_norm - L0.attn_norm : 0;
+    p.embed = m->embed; p.final_norm = m->final_norm;
+    p.V = cc.vocab; p.n_layers = cc.n_layers;
+    p.eps = cc.rms_eps; p.qscale = 1.0f / std::sqrt((float)cc.head_dim) * 1.4426950408889634f;
+    p.kcache = m->kcache; p.vcache = m->vcache;
+    p.layer_stride = m->layer_stride; p.slot_stride = m->slot_stride; p.head_stride = m->head_stride;
+    p.cos_t = m->rope_cos; p.sin_t = m->rope_sin;
+    p.tokens = tokens; p.pos = positions[0]; p.slot = slots[0]; p.chunk = (positions[0] + 1 + 31) / 32;
+    p.logits = logits; p.next = next;
+    p.ex = m->pex;
+    m->pstep = (m->pstep + 1) & 0xFFFFFFu;
+    if (m->pstep == 0) m->pstep = 1;
+    p.step_tag = m->pstep << 8;
+    p.abort_host = m->pabort_dev;
+    p.tokerr = m->tokerr_dev;
+    p.trace = m->ptrace;
+    LAUNCH(m, "decode_step", s, decode_persist(p, s));
+    m->slot_len[slots[0]] = positions[0] + 1;
+    return FS_OK;
+  }
   if ((st = ensure_rows(m, B, s)) != FS_OK) return st;
   if (B > GEMV_LOGITS_MAX_M && logits == nullptr && (st = ensure_logits_tmp(m)) != FS_OK) return st;
   if ((st = stage_ints(m, positions, slots, B, s)) != FS_OK) return st;
@@ -1002,6 +1072,15 @@ fs_status fs_kernel_bench(fs_model* m, const char* label, int32_t slot, int32_t 
   hipGraphDestroy(g);
   if (e != hipSuccess) return fail(FS_ERR_HIP, std::string("kernel bench failed: ") + hipGetErrorString(e));
   *avg_us = (double)ms * 1e3 / ((double)reps * per_pass);
+  return FS_OK;
+}
+
+fs_status fs_decode_trace(fs_model* m, int64_t* out, int32_t n) {
+  g_err.clear();
+  if (m == nullptr || out == nullptr || n <= 0 || n > 1024) return fail(FS_ERR_INVALID_ARG, "bad argument");
+  if (m->ptrace == nullptr) return fail(FS_ERR_UNSUPPORTED, "no trace (set FS_DECODE_TRACE=1 before creating the model)");
+  HIP_TRY(hipDeviceSynchronize());
+  HIP_TRY(hipMemcpy(out, m->ptrace, (size_t)n * sizeof(long long), hipMemcpyDeviceToHost));
   return FS_OK;
 }
 

@@ -190,6 +190,43 @@ hipError_t attn_combine(const float* part, const int32_t* positions, int B, int 
                         int nchunks, void* out, int o_dt, hipStream_t s, const float* gate = nullptr,
                         int ldg = 0);
 
+// ---------------------------------------------------------------- persistent batch-1 decode step
+// One launch of 256 workgroups (one per CU, all resident) runs a whole decode
+// step of one sequence: embedding, every layer, final norm, tied head, logits
+// and/or the greedy ID.  The 0.6B shape only (decode_persist_ok); contexts up
+// to decode_persist_max_ctx() keys.  Workgroups hand activations to each other
+// through `ex` (decode_persist_exchange_bytes(), zeroed once at allocation),
+// records tagged with step_tag (distinct per step, nonzero, low 8 bits 0).  A
+// wait that exceeds its bound sets *abort_host (host-mapped) and the ex abort
+// word; after that the exchange buffer must be cleared before another launch.
+struct DecodePersistParams {
+  const void *wqkv0, *wo0, *wgu0, *wdown0;   // layer 0's matrices (bf16, packed as the model stores them)
+  long long wstride;                          // elements from one layer's matrices to the next
+  const float *attn_norm0, *mlp_norm0, *q_norm0, *k_norm0;
+  long long nstride;                          // floats from one layer's norm vectors to the next
+  const void* embed;                          // [V, H] bf16, also the head
+  const float* final_norm;
+  int V, n_layers;
+  float eps, qscale;                          // rms eps; 1/sqrt(head_dim) * log2(e)
+  void *kcache, *vcache;                      // bf16 [layer][slot][kv head][pos][d]
+  long long layer_stride, slot_stride, head_stride;
+  const float *cos_t, *sin_t;                 // [max_ctx][d/2]
+  const int32_t* tokens;                      // device [1]
+  int pos, slot, chunk;                       // chunk = keys per workgroup = ceil((pos + 1) / 32)
+  float* logits;                              // device [V] or null
+  int32_t* next;                              // device [1] or null
+  void* ex;
+  unsigned step_tag;
+  int32_t* abort_host;                        // host-mapped word
+  int32_t* tokerr;                            // host-mapped {flag, id, row} or null
+  long long* trace;                           // device [1024] clock stamps of workgroup 0, or null
+};
+bool decode_persist_ok(int n_layers, int hidden, int n_heads, int n_kv_heads, int head_dim, int ffn, int dt,
+                       int wdt, int gated, int rot);
+int decode_persist_max_ctx();
+size_t decode_persist_exchange_bytes();
+hipError_t decode_persist(const DecodePersistParams& p, hipStream_t s);
+
 // ---------------------------------------------------------------- argmax
 // out[b] = greedy ID of row b of logits [B, V] (row stride ldl).
 hipError_t argmax_rows(const float* logits, int B, int V, int ldl, int32_t* out, hipStream_t s);

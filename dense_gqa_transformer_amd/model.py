@@ -133,6 +133,12 @@ class Model:
                                         _stream_ptr(stream)))
         return us.value
 
+    def decode_trace(self, n: int = 1024):
+        """Clock stamps (100 MHz) of the last persistent decode step (FS_DECODE_TRACE=1)."""
+        buf = (ctypes.c_int64 * n)()
+        check(self._lib.fs_decode_trace(self._h, buf, n))
+        return np.array(buf[:], dtype=np.int64)
+
     def sample(self, logits: torch.Tensor, temperature: float, top_k: int = 0, top_p: float = 1.0,
                u: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:

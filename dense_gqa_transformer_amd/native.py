@@ -115,6 +115,8 @@ def load() -> ctypes.CDLL:
     lib.fs_timing_read.restype = ctypes.c_int
     lib.fs_kernel_bench.argtypes = [P, ctypes.c_char_p, i32, i32, i32, ctypes.POINTER(ctypes.c_double), P]
     lib.fs_kernel_bench.restype = ctypes.c_int
+    lib.fs_decode_trace.argtypes = [P, ctypes.POINTER(ctypes.c_int64), i32]
+    lib.fs_decode_trace.restype = ctypes.c_int
     lib.fs_last_error.argtypes = []
     lib.fs_last_error.restype = ctypes.c_char_p
     _lib = lib

@@ -119,7 +119,11 @@ typedef struct fs_model fs_model;
  * merge launch, or one workgroup per sequence and KV head) where it exists;
  * FS_DECODE_MIN_CHUNK=32|64|128|256 sets the shortest split-K chunk;
  * FS_PREFILL_FUSE_ROPE=0 keeps the per-head q/k norm + RoPE + K/V write of a
- * large prefill in a pass of its own instead of the QKV GEMM's epilogue. */
+ * large prefill in a pass of its own instead of the QKV GEMM's epilogue;
+ * FS_DECODE_PERSIST=1 runs batch-1 decode steps of the 0.6B shape as one
+ * persistent launch (all 256 CUs resident, workgroups exchanging activations
+ * in memory; measured slower than the default, see fs_decode_trace);
+ * FS_DECODE_TRACE=1 (with it) records the clock stamps fs_decode_trace reads. */
 fs_status fs_model_create(const fs_config *cfg, const fs_weights *w,
                           void *stream, fs_model **out);
 
@@ -308,6 +312,17 @@ fs_status fs_timing_read(fs_model *m, const char *label, double *total_ms, int64
  * form), HIP. */
 fs_status fs_kernel_bench(fs_model *m, const char *label, int32_t slot, int32_t position,
                           int32_t reps, double *avg_us, void *stream);
+
+/* Measurement hook of the persistent batch-1 decode step (the one-launch
+ * step the 0.6B shape takes at batch 1): with FS_DECODE_TRACE=1 set when the
+ * model is created, each such step records the GPU's 100 MHz real-time clock
+ * at fixed points of workgroup 0 into a 1024-entry device buffer (entry 0:
+ * start; 8l+1..8l+6: layer l's waits done in the control wave, 8l+7: polls
+ * its first wait took; 512+8l..: the compute wave's phase boundaries; 511,
+ * 1023: the end); fs_decode_trace
+ * copies the first n entries of the last step's record to host `out`
+ * (synchronous).  Errors: INVALID_ARG, UNSUPPORTED (no trace buffer). */
+fs_status fs_decode_trace(fs_model *m, int64_t *out, int32_t n);
 
 /* Message of the last error on this thread ("" if none); valid until the
  * next fs_* call on this thread. */
