@@ -161,9 +161,13 @@ class Oracle:
     widened exactly to float32, so no rounding happens on this side.
     """
 
-    def __init__(self, shape, weights: dict, dtype=np.float64):
+    def __init__(self, shape, weights: dict, dtype=np.float64, quantize_norm_outputs=None):
         self.shape = shape
         self.dtype = np.dtype(dtype)
+        # optional rule applied to every RMSNorm output that feeds a projection
+        # (Q/K/V, gate/up, the head): the fp8 option's activation quantization
+        # (oracle/fp8.py); None leaves them exact
+        self.qn = quantize_norm_outputs
         c = lambda a: np.asarray(a, dtype=self.dtype)
         self.embed = c(weights["embed"])
         self.final_norm = c(weights["final_norm"])
@@ -181,6 +185,8 @@ class Oracle:
         s = x.shape[0]
         # attention half
         xn = rms_norm(x, w["attn_norm"], sh.rms_eps)
+        if self.qn is not None:
+            xn = np.asarray(self.qn(xn), dtype=self.dtype)
         qp = linear(xn, w["wq"])
         gate = None
         if getattr(sh, "attn_gate", False):
@@ -212,6 +218,8 @@ class Oracle:
             dump[f"layer{li}.x_mid"] = x
         # FFN half
         xn = rms_norm(x, w["mlp_norm"], sh.rms_eps)
+        if self.qn is not None:
+            xn = np.asarray(self.qn(xn), dtype=self.dtype)
         hmid = silu(linear(xn, w["w_gate"])) * linear(xn, w["w_up"])
         x = x + linear(hmid, w["w_down"])
         if dump is not None:
@@ -221,6 +229,8 @@ class Oracle:
     def _head(self, x_last: np.ndarray) -> np.ndarray:
         """Final RMSNorm of the last row(s), then the tied head E . h."""
         hn = rms_norm(x_last, self.final_norm, self.shape.rms_eps)
+        if self.qn is not None:
+            hn = np.asarray(self.qn(hn), dtype=self.dtype)
         return hn @ self.embed.T
 
     # ---------------------------------------------------------------- uncached
