@@ -14,20 +14,26 @@ module is the oracle of the library's fp8 option, whose reading is:
   fp8 operand.)
 * Rounding: a real value goes to the nearest representable value, a tie to
   the one with an even mantissa field; magnitudes beyond 448 saturate to 448.
+* Scales are powers of two, one per row: for a row with largest magnitude
+  a > 0, ``t = a / 448`` (correctly rounded float32) and ``s = 2^e`` with e the
+  smallest integer such that ``2^e >= t``; a zero row has scale 0 and codes 0.
+  Then ``code = e4m3(x / s)`` (the division is exact), and ``code * s`` is
+  exact in float32 and in bfloat16, so a code times its scale is the value
+  the products use, and a matrix unit that takes a power-of-two scale per
+  row (the gfx950 fp8 products take an 8-bit exponent per 32 operands) applies
+  it without rounding.  A float format loses nothing to the power-of-two
+  choice: only the window of representable magnitudes moves, by less than 2x.
 * Weights: every matrix of the pass (wq, wk, wv, wo, w_gate, w_up, w_down
   and the tied embedding / head) is stored as codes with one scale per output
-  row: ``s_n = max_k |W[n, k]| / 448`` (correctly rounded float32) and
-  ``code = e4m3(W[n, k] / s_n)`` (the float32 quotient, correctly rounded,
-  then rounded to e4m3 as above); a zero row has scale 0 and codes 0.  The
-  model computes with ``code * s_n`` exactly.  Norm weights stay in the
-  model's dtype.
+  row (row n of the ``[out, in]`` matrix).  Norm weights stay in the model's
+  dtype.
 * Activations: the outputs of the RMSNorms, which feed the Q/K/V projection,
-  the gate/up projection and the tied head, are quantized per row the same
-  way (``s_r = max |row| / 448``, ``q = e4m3(row / s_r)``) and the projection
-  takes ``q * s_r``; so each product ``sum_k q_k c_k`` is a sum of products of
-  two e4m3 values, which the fp8 matrix instructions compute exactly.  The
-  inputs of the output and down projections (the attention output and the
-  SwiGLU output) are not quantized: those products are weight-only.
+  the gate/up projection and the tied head, are quantized per row by the same
+  rule (the float32 row values) and the projection takes ``q * s``; so each
+  product ``sum_k q_k c_k`` is a sum of products of two e4m3 values, which the
+  fp8 matrix instructions compute exactly.  The inputs of the output and down
+  projections (the attention output and the SwiGLU output) are not quantized:
+  those products are weight-only.
 
 The fp8 forward pass is the oracle's, on ``dequantized_weights`` and with
 ``quantize_act_rows`` applied to the norm outputs
@@ -95,9 +101,20 @@ def e4m3_code(v: np.ndarray) -> np.ndarray:
     return (idx | np.where(np.signbit(v) & (v != 0), 0x80, 0)).astype(np.uint8)
 
 
+def pow2_scale(amax: np.ndarray) -> np.ndarray:
+    """Per-row scales 2^e, e the smallest integer with 2^e >= fl32(amax / 448);
+    0 where amax is 0 (float32)."""
+    amax = np.asarray(amax, dtype=np.float32)
+    t = (amax / np.float32(FP8_MAX)).astype(np.float32)           # correctly rounded float32
+    m, e = np.frexp(t.astype(np.float64))                          # t = m * 2^e, m in [0.5, 1)
+    e = np.where(m == 0.5, e - 1, e)                               # t itself a power of two
+    s = np.ldexp(np.float64(1.0), e).astype(np.float32)
+    return np.where(amax > 0, s, np.float32(0)).astype(np.float32)
+
+
 def quantize_rows(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Per-row e4m3 codes (as their float64 values) and float32 scales of a
-    ``[rows, cols]`` float32-representable matrix (the weight rule)."""
+    """Per-row e4m3 codes (as their float64 values) and power-of-two float32
+    scales of a ``[rows, cols]`` float32-representable matrix."""
     w = np.asarray(w)
     if w.ndim != 2:
         raise ValueError("quantize_rows takes a matrix")
@@ -105,12 +122,11 @@ def quantize_rows(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     if not np.array_equal(x.astype(w.dtype), w):
         raise ValueError("values are not float32-representable")
     amax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
-    scale = (amax / np.float32(FP8_MAX)).astype(np.float32)        # correctly rounded float32
+    scale = pow2_scale(amax)
     vals = np.zeros(x.shape, dtype=np.float64)
     nz = scale > 0
     if np.any(nz):
-        r = (x[nz] / scale[nz, None]).astype(np.float32)            # correctly rounded float32
-        vals[nz] = e4m3_round(r)
+        vals[nz] = e4m3_round(x[nz].astype(np.float64) / scale[nz, None])   # exact quotient
     return vals, scale
 
 
@@ -121,8 +137,7 @@ def dequantize_rows(vals: np.ndarray, scale: np.ndarray) -> np.ndarray:
 
 def quantize_act_rows(x: np.ndarray) -> np.ndarray:
     """The activation rule applied to each row of x (last axis): the row's
-    e4m3 codes times its scale, ``s = max|row| / 448`` and ``q = e4m3(row / s)``,
-    with the scale and the quotient rounded to float32 as for weights."""
+    e4m3 codes times its power-of-two scale, on the row's float32 values."""
     x = np.asarray(x, dtype=np.float64)
     flat = x.reshape(-1, x.shape[-1]).astype(np.float32)          # the rows as float32 values
     vals, scale = quantize_rows(flat)

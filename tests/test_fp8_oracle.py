@@ -93,23 +93,31 @@ def test_weight_rows_on_the_grid_are_lossless():
     assert np.array_equal(F.dequantize_rows(vals, scale), w.astype(np.float64))
 
 
+def test_power_of_two_scales():
+    # the smallest 2^e with 2^e >= fl32(amax / 448)
+    amax = np.array([448.0, 449.0, 447.0, 224.0, 0.5, 1e-30, 0.0, 3.0e5], dtype=np.float32)
+    s = F.pow2_scale(amax)
+    assert s.tolist()[:7] == [1.0, 2.0, 1.0, 0.5, 2.0 ** -9, 2.0 ** -108, 0.0]
+    assert s[7] == 1024.0                            # 3e5 / 448 = 669.6 -> 2^10
+    for a, sc in zip(amax[:6].tolist() + [3.0e5], s[:6].tolist() + [1024.0]):
+        t = float(np.float32(np.float32(a) / np.float32(448)))
+        assert sc >= t and sc / 2 < t
+
+
 def test_weight_rule_per_row_and_zero_rows():
     w = np.array([[448.0, 1.0, -3.0], [0.5, -0.3, 0.1], [0.0, 0.0, 0.0]], dtype=np.float32)
     vals, scale = F.quantize_rows(w)
     assert scale[0] == 1.0 and scale[2] == 0.0 and not vals[2].any()
     assert vals[0].tolist() == [448.0, 1.0, -3.0]
-    # row 1: s = 0.5 / 448; 0.5 -> 448, -0.3 / s = -268.8 -> -256, 0.1 / s = 89.6 -> 88
-    assert scale[1] == np.float32(0.5) / np.float32(448)
-    assert vals[1].tolist() == [448.0, -256.0, 88.0]
+    # row 1: s = 2^-9 (>= 0.5/448 = 2^-9.8); 0.5 -> 256, -0.3 / s = -153.6 -> -160, 0.1 / s = 51.2 -> 52
+    assert scale[1] == 2.0 ** -9
+    assert vals[1].tolist() == [256.0, -160.0, 52.0]
 
 
 def test_activation_rule():
     rng = np.random.default_rng(24)
     x = rng.standard_normal((5, 64))
     q = F.quantize_act_rows(x)
-    # each row's largest magnitude survives exactly (it maps to 448 and back)
-    i = np.argmax(np.abs(x), axis=1)
-    np.testing.assert_allclose(np.abs(q[np.arange(5), i]), np.abs(x[np.arange(5), i]), rtol=2e-7)
     # relative error of every element at most half a mantissa step (plus the
     # float32 rounding of the row), idempotent, sign-symmetric, power-of-two-equivariant
     big = np.abs(x) >= np.max(np.abs(x), axis=1, keepdims=True) * 2 ** -6
