@@ -38,8 +38,13 @@ fs_status fail(fs_status st, const std::string& msg) {
   } while (0)
 
 // Up to this many rows per call the projections run as GEMV (weights streamed
-// once, fp32 activations); above it as MFMA GEMM on bf16 activations.
+// once, fp32 activations); above it as MFMA GEMM on bf16 activations.  With
+// fp8 weights the GEMV quantizes its activation rows in registers, up to 4.
 constexpr int SKINNY_MAX_ROWS = 8;
+constexpr int SKINNY_MAX_ROWS_F8 = 4;
+// fp8 weights: from this many rows a prefill's Q/K/V and gate/up products run
+// on the fp8 matrix instructions (gemm_f8); below it on widened weights
+constexpr int F8_GEMM_MIN_ROWS = 512;
 // Few-row (<= 64) O and down projections split K over up to 12 workgroups per
 // 32-column slab (N = hidden gives only hidden / 32 slabs otherwise).
 constexpr int KSPLIT_MAX = 12;
@@ -96,7 +101,7 @@ struct fs_model {
   int qpw = 0;          // rows of the q (+ gate) projection
   int rot = 0;          // rotated dims per head
   int gated = 0;        // attention output gate carried by the q projection
-  int wdt = 0;          // storage of the matrices: dt, or DT_I8 (codes + row scales)
+  int wdt = 0;          // storage of the matrices: dt, or DT_I8 / DT_F8 (codes + row scales)
   // weights
   void* wblob = nullptr;
   float* nblob = nullptr;
@@ -116,6 +121,7 @@ struct fs_model {
   long long scratch_rows = 0;
   float* x = nullptr;
   void* xn = nullptr;
+  float* ascale = nullptr;        // fp8 option: row scales of the quantized norm outputs
   void* qkv = nullptr;
   void* qr = nullptr;
   void* attn = nullptr;
@@ -166,6 +172,7 @@ struct fs_model {
   int min_chunk = 32;
   // prefill: q/k norm + RoPE + K/V write in the QKV GEMM's epilogue where it applies
   bool fuse_rope = true;
+  bool f8_mfma = true;            // fp8 weights: prefill Q/K/V and gate/up on fp8 matrix instructions
   // measurement hook: per-launch event pairs, labelled by step
   bool timing = false;
   std::vector<TimedLaunch> timed;
@@ -187,7 +194,7 @@ struct fs_model {
     for (auto e : ev_free) hipEventDestroy(e);
     hipFree(wblob); hipFree(nblob); hipFree(sblob); hipFree(wconv); hipFree(kcache); hipFree(vcache);
     hipFree(rope_cos); hipFree(rope_sin);
-    hipFree(x); hipFree(xn); hipFree(qkv); hipFree(qr); hipFree(attn); hipFree(hbuf);
+    hipFree(x); hipFree(xn); hipFree(qkv); hipFree(qr); hipFree(attn); hipFree(hbuf); hipFree(ascale);
     hipFree(d_pos); hipFree(part); hipFree(kpart);
     hipFree(lm_pv); hipFree(lm_pi); hipFree(logits_tmp); hipFree(sample_scr);
     for (int i = 0; i < STAGE_RING; ++i)
@@ -205,6 +212,8 @@ struct fs_model {
 };
 
 namespace {
+
+int skinny_rows(const fs_model* m) { return m->wdt == DT_F8 ? SKINNY_MAX_ROWS_F8 : SKINNY_MAX_ROWS; }
 
 hipEvent_t take_event(fs_model* m) {
   if (!m->ev_free.empty()) {
@@ -238,14 +247,17 @@ fs_status ensure_rows(fs_model* m, long long rows, hipStream_t s) {
   HIP_TRY(hipStreamSynchronize(s));
   m->drop_graphs();   // captured graphs point at the old buffers
   hipFree(m->x); hipFree(m->xn); hipFree(m->qkv); hipFree(m->qr); hipFree(m->attn); hipFree(m->hbuf);
+  hipFree(m->ascale);
   m->x = nullptr; m->xn = m->qkv = m->qr = m->attn = m->hbuf = nullptr;
+  m->ascale = nullptr;
   m->scratch_rows = 0;
   const fs_config& c = m->cfg;
   const size_t R = (size_t)rows;
   // fp32-sized buffers so either activation dtype fits
   if (dalloc(&m->x, R * c.hidden * 4) != hipSuccess || dalloc(&m->xn, R * c.hidden * 4) != hipSuccess ||
       dalloc(&m->qkv, R * m->qkv_w * 4) != hipSuccess || dalloc(&m->qr, R * m->qw * 4) != hipSuccess ||
-      dalloc(&m->attn, R * m->qw * 4) != hipSuccess || dalloc(&m->hbuf, R * c.ffn * 4) != hipSuccess)
+      dalloc(&m->attn, R * m->qw * 4) != hipSuccess || dalloc(&m->hbuf, R * c.ffn * 4) != hipSuccess ||
+      dalloc(&m->ascale, R * 4) != hipSuccess)
     return fail(FS_ERR_OOM, "activation scratch allocation failed");
   m->scratch_rows = rows;
   return FS_OK;
@@ -308,6 +320,7 @@ fs_status head(fs_model* m, const float* xrows, int rows, int ldx, float* logits
     p.gamma = m->final_norm; p.eps = c.rms_eps;
     p.logits = logits; p.ldo = c.vocab;
     p.part_val = m->lm_pv; p.part_idx = m->lm_pi;
+    p.aquant = (m->wdt == DT_F8);
     LAUNCH(m, "head", s, gemv(m->wdt, EPI_LOGITS, p, s));
     if (next)
       LAUNCH(m, "argmax", s, argmax_partials(m->lm_pv, m->lm_pi, gemv_logits_blocks(m->wdt, c.vocab, c.hidden),
@@ -319,6 +332,17 @@ fs_status head(fs_model* m, const float* xrows, int rows, int ldx, float* logits
     LAUNCH(m, "norm", s, rmsnorm(xrows, rows, c.hidden, ldx, m->final_norm, c.rms_eps, m->xn, DT_BF16, c.hidden, s));
     LAUNCH(m, "head", s, gemm_bf16(GEPI_STORE_F32, m->xn, c.hidden, m->embed, c.hidden, lg, c.vocab, rows,
                                    c.vocab, c.hidden, s));
+  } else if (m->wdt == DT_F8) {
+    // fp8 head: GEMV over groups of up to 4 rows (each quantized in registers)
+    for (int r0 = 0; r0 < rows; r0 += 4) {
+      GemvParams p{};
+      p.w = m->embed; p.wscale = m->embed_scale; p.N = c.vocab; p.K = c.hidden;
+      p.a = xrows + (size_t)r0 * ldx; p.lda = ldx; p.M = std::min(4, rows - r0);
+      p.gamma = m->final_norm; p.eps = c.rms_eps;
+      p.out = lg + (size_t)r0 * c.vocab; p.ldo = c.vocab;
+      p.aquant = 1;
+      LAUNCH(m, "head", s, gemv(m->wdt, EPI_STORE, p, s));
+    }
   } else {
     // fp32 and int8 heads: GEMV over row groups (int8 codes stream once per 4 rows)
     GemvParams p{};
@@ -363,15 +387,38 @@ hipError_t resid_proj(fs_model* m, const void* A, int lda, const void* W, int ro
   return gemm_skinny(GEPI_PART_F32, A, lda, W, K, m->kpart, c.hidden, rows, c.hidden, K, s, nullptr, cs, ks);
 }
 
-// RMSNorm of x into xn (bf16, optional remainder), first adding pending partials.
-hipError_t norm_in(fs_model* m, int rows, const float* gamma, void* lo, hipStream_t s) {
+// RMSNorm of x into xn (bf16, optional remainder), first adding pending
+// partials.  fp8 weights: xn holds the quantized rows, as exact bf16 values of
+// code * power-of-two scale (codes = false) or as the e4m3 codes themselves
+// with the scales in m->ascale (codes = true), and no remainder.
+hipError_t norm_in(fs_model* m, int rows, const float* gamma, void* lo, hipStream_t s, bool codes = false) {
   const fs_config& c = m->cfg;
+  float* qs = (m->wdt == DT_F8) ? m->ascale : nullptr;
+  if (qs != nullptr) lo = nullptr;
+  const int odt = (qs != nullptr && codes) ? DT_F8 : DT_BF16;
   if (m->pend_np == 0)
-    return rmsnorm(m->x, rows, c.hidden, c.hidden, gamma, c.rms_eps, m->xn, DT_BF16, c.hidden, s, lo);
+    return rmsnorm(m->x, rows, c.hidden, c.hidden, gamma, c.rms_eps, m->xn, odt, c.hidden, s, lo, qs);
   const int np = m->pend_np;
   m->pend_np = 0;
-  return rmsnorm_add(m->x, m->kpart, np, rows, c.hidden, c.hidden, gamma, c.rms_eps, m->xn, DT_BF16, c.hidden, s,
-                     lo);
+  return rmsnorm_add(m->x, m->kpart, np, rows, c.hidden, c.hidden, gamma, c.rms_eps, m->xn, odt, c.hidden, s,
+                     lo, qs);
+}
+
+// A GEMV over p.M rows; with fp8 weights the quantizing form (the
+// RMSNorm-fused inputs) holds at most 4 rows, so larger calls run in groups
+// of 4 rows (each streaming the weights once).
+hipError_t gemv_rows(fs_model* m, int epi, GemvParams p, hipStream_t s) {
+  if (!p.aquant || p.M <= 4) return gemv(m->wdt, epi, p, s);
+  const int M = p.M;
+  for (int r0 = 0; r0 < M; r0 += 4) {
+    GemvParams q = p;
+    q.a = p.a + (size_t)r0 * p.lda;
+    q.out = p.out + (size_t)r0 * p.ldo;
+    q.M = std::min(4, M - r0);
+    const hipError_t e = gemv(m->wdt, epi, q, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // One transformer block over `rows` activation rows in the skinny (GEMV) form.
@@ -385,7 +432,8 @@ fs_status block_skinny(fs_model* m, const LayerW& L, int rows, Attn&& attention,
   p.w = L.wqkv; p.wscale = L.sqkv; p.N = m->qkv_w; p.K = c.hidden;
   p.a = m->x; p.lda = c.hidden; p.M = rows; p.gamma = L.attn_norm;
   p.out = (float*)m->qkv; p.ldo = m->qkv_w;
-  LAUNCH(m, "qkv", s, gemv(m->wdt, EPI_STORE, p, s));
+  p.aquant = (m->wdt == DT_F8);
+  LAUNCH(m, "qkv", s, gemv_rows(m, EPI_STORE, p, s));
   m->qkv_src = (const float*)m->qkv;
   m->qkv_np = 1;
   fs_status st = attention();
@@ -394,16 +442,19 @@ fs_status block_skinny(fs_model* m, const LayerW& L, int rows, Attn&& attention,
   p.w = L.wo; p.wscale = L.so; p.N = c.hidden; p.K = m->qw;
   p.a = (const float*)m->attn; p.lda = m->qw; p.gamma = nullptr;
   p.out = m->x; p.ldo = c.hidden;
+  p.aquant = 0;
   LAUNCH(m, "o_proj", s, gemv(m->wdt, EPI_RESID, p, s));
   // RMSNorm + gate/up + SwiGLU
   p.w = L.wgu; p.wscale = L.sgu; p.N = c.ffn; p.K = c.hidden;
   p.a = m->x; p.lda = c.hidden; p.gamma = L.mlp_norm;
   p.out = (float*)m->hbuf; p.ldo = c.ffn;
-  LAUNCH(m, "gate_up", s, gemv(m->wdt, EPI_SWIGLU, p, s));
+  p.aquant = (m->wdt == DT_F8);
+  LAUNCH(m, "gate_up", s, gemv_rows(m, EPI_SWIGLU, p, s));
   // down projection + residual
   p.w = L.wdown; p.wscale = L.sdown; p.N = c.hidden; p.K = c.ffn;
   p.a = (const float*)m->hbuf; p.lda = c.ffn; p.gamma = nullptr;
   p.out = m->x; p.ldo = c.hidden;
+  p.aquant = 0;
   LAUNCH(m, "down", s, gemv(m->wdt, EPI_RESID, p, s));
   return FS_OK;
 }
@@ -422,13 +473,48 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
   // context the last-token logits reach the whole 2e-2 error budget; the two
   // norm outputs are the largest of those rounding points that the bf16 KV
   // cache does not fix.
-  void* xn_lo = (char*)m->xn + (size_t)rows * c.hidden * 2;
-  // int8 weights: each matrix's codes are widened to bf16 (exact) into wconv
-  // just before its GEMM, and the row scales are applied per output column
-  const bool q8 = (m->wdt == DT_I8);
+  void* xn_lo = (m->wdt == DT_F8) ? nullptr : (char*)m->xn + (size_t)rows * c.hidden * 2;
+  // int8 / fp8 weights: each matrix's codes are widened to bf16 (exact) into
+  // wconv just before its GEMM, and the row scales are applied per output column
+  const bool q8 = (m->wdt == DT_I8 || m->wdt == DT_F8);
+  auto widen = [&](const void* codes, size_t n) -> hipError_t {
+    return m->wdt == DT_F8 ? f8codes_to_bf16((const uint8_t*)codes, n, m->wconv, s)
+                           : codes_to_bf16((const int8_t*)codes, n, m->wconv, s);
+  };
+  // fp8 weights at prefill sizes: the Q/K/V and gate/up products take the
+  // quantized norm outputs as e4m3 codes on the fp8 matrix instructions
+  // (gemm_f8); the output and down projections stay weight-only (widened)
+  const bool f8mm = m->wdt == DT_F8 && m->f8_mfma && !qkv_f32 && rows >= F8_GEMM_MIN_ROWS &&
+                    gemm_f8_ok(GEPI_STORE_F32, m->xn, c.hidden, L.wqkv, c.hidden, m->qkv, m->qkv_w, rows, m->qkv_w,
+                               c.hidden) &&
+                    gemm_f8_ok(GEPI_SWIGLU_BF16, m->xn, c.hidden, L.wgu, c.hidden, m->hbuf, c.ffn, rows, 2 * c.ffn,
+                               c.hidden);
+  if (f8mm) {
+    LAUNCH(m, "norm", s, norm_in(m, rows, L.attn_norm, nullptr, s, true));
+    m->qkv_src = (const float*)m->qkv;
+    m->qkv_np = 1;
+    if (rope != nullptr && m->fuse_rope && gemm_dma_rope_ok(*rope, rows, m->qkv_w)) {
+      LAUNCH(m, "qkv", s, gemm_f8(GEPI_QKV_ROPE, m->xn, c.hidden, L.wqkv, c.hidden, nullptr, 0, rows, m->qkv_w,
+                                  c.hidden, s, m->ascale, L.sqkv, rope));
+      if (rope_done != nullptr) *rope_done = true;
+    } else {
+      LAUNCH(m, "qkv", s, gemm_f8(GEPI_STORE_F32, m->xn, c.hidden, L.wqkv, c.hidden, m->qkv, m->qkv_w, rows,
+                                  m->qkv_w, c.hidden, s, m->ascale, L.sqkv));
+    }
+    fs_status st = attention();
+    if (st != FS_OK) return st;
+    LAUNCH(m, "wconv", s, widen(L.wo, (size_t)c.hidden * m->qw));
+    LAUNCH(m, "o_proj", s, resid_proj(m, m->attn, m->qw, m->wconv, rows, m->qw, L.so, s));
+    LAUNCH(m, "norm", s, norm_in(m, rows, L.mlp_norm, nullptr, s, true));
+    LAUNCH(m, "gate_up", s, gemm_f8(GEPI_SWIGLU_BF16, m->xn, c.hidden, L.wgu, c.hidden, m->hbuf, c.ffn, rows,
+                                    2 * c.ffn, c.hidden, s, m->ascale, L.sgu));
+    LAUNCH(m, "wconv", s, widen(L.wdown, (size_t)c.hidden * c.ffn));
+    LAUNCH(m, "down", s, resid_proj(m, m->hbuf, c.ffn, m->wconv, rows, c.ffn, L.sdown, s));
+    return FS_OK;
+  }
   const void* wb = L.wqkv;
   if (q8) {
-    LAUNCH(m, "wconv", s, codes_to_bf16((const int8_t*)L.wqkv, (size_t)m->qkv_w * c.hidden, m->wconv, s));
+    LAUNCH(m, "wconv", s, widen(L.wqkv, (size_t)m->qkv_w * c.hidden));
     wb = m->wconv;
   }
   LAUNCH(m, "norm", s, norm_in(m, rows, L.attn_norm, xn_lo, s));
@@ -462,13 +548,13 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
   if (st != FS_OK) return st;
   wb = L.wo;
   if (q8) {
-    LAUNCH(m, "wconv", s, codes_to_bf16((const int8_t*)L.wo, (size_t)c.hidden * m->qw, m->wconv, s));
+    LAUNCH(m, "wconv", s, widen(L.wo, (size_t)c.hidden * m->qw));
     wb = m->wconv;
   }
   LAUNCH(m, "o_proj", s, resid_proj(m, m->attn, m->qw, wb, rows, m->qw, L.so, s));
   wb = L.wgu;
   if (q8) {
-    LAUNCH(m, "wconv", s, codes_to_bf16((const int8_t*)L.wgu, (size_t)2 * c.ffn * c.hidden, m->wconv, s));
+    LAUNCH(m, "wconv", s, widen(L.wgu, (size_t)2 * c.ffn * c.hidden));
     wb = m->wconv;
   }
   LAUNCH(m, "norm", s, norm_in(m, rows, L.mlp_norm, xn_lo, s));
@@ -476,7 +562,7 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
                                     2 * c.ffn, c.hidden, s, xn_lo, L.sgu));
   wb = L.wdown;
   if (q8) {
-    LAUNCH(m, "wconv", s, codes_to_bf16((const int8_t*)L.wdown, (size_t)c.hidden * c.ffn, m->wconv, s));
+    LAUNCH(m, "wconv", s, widen(L.wdown, (size_t)c.hidden * c.ffn));
     wb = m->wconv;
   }
   LAUNCH(m, "down", s, resid_proj(m, m->hbuf, c.ffn, wb, rows, c.ffn, L.sdown, s));
@@ -520,7 +606,8 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   if (c.rope_dim < 0 || c.rope_dim > c.head_dim || c.rope_dim % 16 != 0)
     return fail(FS_ERR_UNSUPPORTED, "rope_dim must be 0 or a multiple of 16 up to head_dim");
   if (c.attn_gate != 0 && c.attn_gate != 1) return fail(FS_ERR_INVALID_ARG, "attn_gate must be 0 or 1");
-  if (c.weight_format != FS_WEIGHTS_DTYPE && c.weight_format != FS_WEIGHTS_I8_ROW)
+  if (c.weight_format != FS_WEIGHTS_DTYPE && c.weight_format != FS_WEIGHTS_I8_ROW &&
+      c.weight_format != FS_WEIGHTS_F8_ROW)
     return fail(FS_ERR_UNSUPPORTED, "unknown weight_format");
   if (c.hidden % 64 != 0 || c.ffn % 64 != 0)
     return fail(FS_ERR_UNSUPPORTED, "hidden and ffn must be multiples of 64");
@@ -529,7 +616,8 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return fail(FS_ERR_INVALID_ARG, "bad rms_eps or rope_theta");
   if (w->embed == nullptr || w->final_norm == nullptr || (c.n_layers > 0 && w->layers == nullptr))
     return fail(FS_ERR_INVALID_ARG, "NULL weight pointer");
-  const bool q8 = (c.weight_format == FS_WEIGHTS_I8_ROW);
+  const bool q8 = (c.weight_format == FS_WEIGHTS_I8_ROW || c.weight_format == FS_WEIGHTS_F8_ROW);
+  const bool f8w = (c.weight_format == FS_WEIGHTS_F8_ROW);
   for (int l = 0; l < c.n_layers; ++l) {
     const fs_layer_weights& L = w->layers[l];
     const void* ps[] = {L.attn_norm, L.wq, L.wk, L.wv, L.q_norm, L.k_norm, L.wo, L.mlp_norm, L.w_gate, L.w_up, L.w_down};
@@ -539,9 +627,9 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
     const void* mats[] = {L.wq, L.wk, L.wv, L.wo, L.w_down};
     for (const void* p : mats)
       if (q8 && ((uintptr_t)p & 15))
-        return fail(FS_ERR_INVALID_ARG, "int8 weights need 16-byte aligned matrices (layer " + std::to_string(l) + ")");
+        return fail(FS_ERR_INVALID_ARG, "8-bit weights need 16-byte aligned matrices (layer " + std::to_string(l) + ")");
   }
-  if (q8 && ((uintptr_t)w->embed & 15)) return fail(FS_ERR_INVALID_ARG, "int8 weights need a 16-byte aligned embed");
+  if (q8 && ((uintptr_t)w->embed & 15)) return fail(FS_ERR_INVALID_ARG, "8-bit weights need a 16-byte aligned embed");
   hipStream_t s = (hipStream_t)stream;
   int device = 0;
   HIP_TRY(hipGetDevice(&device));
@@ -556,7 +644,7 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   m->gated = c.attn_gate;
   m->qpw = m->qw * (m->gated ? 2 : 1);          // q (+ gate) projection rows
   m->qkv_w = m->qpw + 2 * m->kvw;
-  m->wdt = q8 ? DT_I8 : m->dt;
+  m->wdt = f8w ? DT_F8 : q8 ? DT_I8 : m->dt;
   const size_t H = c.hidden, I = c.ffn, V = c.vocab, es = m->esz, wes = dt_size(m->wdt);
   const size_t per_layer = ((size_t)m->qkv_w * H + H * m->qw + 2 * I * H + H * I) * wes;
   const size_t wbytes = V * H * wes + per_layer * c.n_layers;
@@ -593,7 +681,8 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
       return;
     }
     if (*scale == nullptr) *scale = sp;     // the matrix's run of scales starts here
-    chk(quantize_rows(src, m->dt, rows, cols, (int8_t*)dst, sp, s));
+    if (f8w) chk(quantize_rows_f8(src, m->dt, rows, cols, (uint8_t*)dst, sp, s));
+    else chk(quantize_rows(src, m->dt, rows, cols, (int8_t*)dst, sp, s));
     sp += rows;
   };
   auto close_run = [&](float* start) {
@@ -689,6 +778,8 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
     if (am != nullptr && std::strcmp(am, "onepass") == 0) m->attn_mode = 2;
     const char* fr = std::getenv("FS_PREFILL_FUSE_ROPE");
     if (fr != nullptr && fr[0] == '0') m->fuse_rope = false;
+    const char* f8 = std::getenv("FS_PREFILL_F8_MFMA");
+    if (f8 != nullptr && f8[0] == '0') m->f8_mfma = false;
     const char* mc = std::getenv("FS_DECODE_MIN_CHUNK");
     if (mc != nullptr) {
       const int v = std::atoi(mc);
@@ -756,7 +847,7 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
   if (m->timing) LAUNCH(m, "gate", s, spin_wait(TIMING_GATE_US, s));
   LAUNCH(m, "embed", s, embed(m->embed, m->wdt, tokens, (int)T, c.hidden, c.vocab, m->x, s, m->embed_scale,
                               m->tokerr_dev));
-  const bool skinny = (m->dt == DT_F32) || T <= SKINNY_MAX_ROWS;
+  const bool skinny = (m->dt == DT_F32) || T <= skinny_rows(m);
   const int act_dt = skinny ? DT_F32 : DT_BF16;
   m->pend_np = 0;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -844,7 +935,7 @@ static fs_status enqueue_decode(fs_model* m, const int32_t* tokens, int B, float
   if (m->timing) LAUNCH(m, "gate", s, spin_wait(TIMING_GATE_US, s));
   LAUNCH(m, "embed", s, embed(m->embed, m->wdt, tokens, B, c.hidden, c.vocab, m->x, s, m->embed_scale,
                               m->tokerr_dev));
-  const bool skinny = (m->dt == DT_F32) || B <= SKINNY_MAX_ROWS;
+  const bool skinny = (m->dt == DT_F32) || B <= skinny_rows(m);
   fs_status st = FS_OK;
   m->pend_np = 0;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -1007,6 +1098,7 @@ fs_status fs_kernel_bench(fs_model* m, const char* label, int32_t slot, int32_t 
     if (std::strcmp(label, "qkv") == 0) {
       p.w = L.wqkv; p.wscale = L.sqkv; p.N = m->qkv_w; p.K = c.hidden; p.a = m->x; p.lda = c.hidden; p.gamma = L.attn_norm;
       p.out = (float*)m->qkv; p.ldo = m->qkv_w;
+      p.aquant = (m->wdt == DT_F8);
       HIP_TRY(gemv(m->wdt, EPI_STORE, p, ls));
     } else if (std::strcmp(label, "o_proj") == 0) {
       p.w = L.wo; p.wscale = L.so; p.N = c.hidden; p.K = m->qw; p.a = (const float*)m->attn; p.lda = m->qw;
@@ -1015,6 +1107,7 @@ fs_status fs_kernel_bench(fs_model* m, const char* label, int32_t slot, int32_t 
     } else if (std::strcmp(label, "gate_up") == 0) {
       p.w = L.wgu; p.wscale = L.sgu; p.N = c.ffn; p.K = c.hidden; p.a = m->x; p.lda = c.hidden; p.gamma = L.mlp_norm;
       p.out = (float*)m->hbuf; p.ldo = c.ffn;
+      p.aquant = (m->wdt == DT_F8);
       HIP_TRY(gemv(m->wdt, EPI_SWIGLU, p, ls));
     } else if (std::strcmp(label, "down") == 0) {
       p.w = L.wdown; p.wscale = L.sdown; p.N = c.hidden; p.K = c.ffn; p.a = (const float*)m->hbuf; p.lda = c.ffn;
@@ -1023,6 +1116,7 @@ fs_status fs_kernel_bench(fs_model* m, const char* label, int32_t slot, int32_t 
     } else if (std::strcmp(label, "head") == 0) {
       p.w = m->embed; p.wscale = m->embed_scale; p.N = c.vocab; p.K = c.hidden; p.a = m->x; p.lda = c.hidden; p.gamma = m->final_norm;
       p.ldo = c.vocab; p.part_val = m->lm_pv; p.part_idx = m->lm_pi;
+      p.aquant = (m->wdt == DT_F8);
       HIP_TRY(gemv(m->wdt, EPI_LOGITS, p, ls));
     } else if (is_attn) {
       AttnDecodeParams a{};
@@ -1168,6 +1262,32 @@ fs_status sample_setup(const float* logits, int32_t B, int32_t V, const fs_sampl
 }  // namespace
 
 extern "C" {
+
+fs_status fs_quantize_rows_f8(const void* src, int32_t dtype, int32_t rows, int32_t cols, uint8_t* codes,
+                              float* scales, void* stream) {
+  g_err.clear();
+  if (src == nullptr || codes == nullptr || scales == nullptr) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+  if (dtype != FS_F32 && dtype != FS_BF16) return fail(FS_ERR_UNSUPPORTED, "unknown dtype");
+  if (rows <= 0 || cols <= 0 || cols % 8 != 0) return fail(FS_ERR_INVALID_ARG, "rows, cols must be > 0, cols % 8 == 0");
+  if (((uintptr_t)src & 15) || ((uintptr_t)codes & 7) || ((uintptr_t)scales & 3))
+    return fail(FS_ERR_INVALID_ARG, "misaligned src (16 B), codes (8 B) or scales (4 B)");
+  HIP_TRY(quantize_rows_f8(src, dtype, rows, cols, codes, scales, (hipStream_t)stream));
+  return FS_OK;
+}
+
+fs_status fs_gemm_f8(const uint8_t* a_codes, const float* a_scales, const uint8_t* w_codes, const float* w_scales,
+                     int32_t M, int32_t N, int32_t K, float* out, void* stream) {
+  g_err.clear();
+  if (a_codes == nullptr || a_scales == nullptr || w_codes == nullptr || w_scales == nullptr || out == nullptr)
+    return fail(FS_ERR_INVALID_ARG, "NULL argument");
+  if (M <= 0 || N <= 0 || K <= 0 || K % 64 != 0 || N % 8 != 0)
+    return fail(FS_ERR_INVALID_ARG, "M, N, K must be > 0, K % 64 == 0, N % 8 == 0");
+  if (((uintptr_t)a_codes & 15) || ((uintptr_t)w_codes & 15) || ((uintptr_t)out & 15) || ((uintptr_t)w_scales & 15) ||
+      ((uintptr_t)a_scales & 3))
+    return fail(FS_ERR_INVALID_ARG, "misaligned codes, out or w_scales (16 B) or a_scales (4 B)");
+  HIP_TRY(gemm_f8(GEPI_STORE_F32, a_codes, K, w_codes, K, out, N, M, N, K, (hipStream_t)stream, a_scales, w_scales));
+  return FS_OK;
+}
 
 fs_status fs_sample(fs_model* m, const float* logits, int32_t B, int32_t V, const fs_sampling* sp,
                     const float* u, int32_t* out, void* stream) {

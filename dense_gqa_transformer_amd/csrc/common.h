@@ -131,3 +131,39 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   if (i < 0) return false;
   return v > bv || (v == bv && i < bi);
 }
+
+// ---------------------------------------------------------------- fp8 (e4m3)
+// 1 sign, 4 exponent (bias 7), 3 mantissa bits, no infinities, largest 448:
+// the operand format of the gfx950 fp8 matrix instructions.
+// Nearest e4m3 code of x (ties to an even mantissa, magnitudes past 448
+// saturate, a zero result is code 0 whatever the sign); x finite.
+__device__ __forceinline__ uint32_t f8_encode(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.f);
+  if (a < 0.015625f) {                               // below 2^-6: steps of 2^-9 (8 -> the smallest normal)
+    const uint32_t m = (uint32_t)(int)rintf(a * 512.f);
+    return m ? (sign | m) : 0u;
+  }
+  const uint32_t u = __float_as_uint(a);
+  int e = (int)((u >> 23) & 0xFF) - 127;            // -6 .. 8
+  uint32_t keep = (u >> 20) & 7u;
+  const uint32_t rest = u & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++keep;
+  if (keep == 8u) { keep = 0u; ++e; }
+  return sign | ((uint32_t)(e + 7) << 3) | keep;
+}
+// value of an e4m3 code (exact in fp32)
+__device__ __forceinline__ float f8_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -v : v;
+}
+// Row scale of the fp8 rule: the smallest power of two >= fl(amax / 448), 0 for amax 0.
+__device__ __forceinline__ float f8_row_scale(float amax) {
+  if (!(amax > 0.f)) return 0.f;
+  const float t = amax / 448.f;
+  const uint32_t u = __float_as_uint(t);
+  const uint32_t ex = (u >> 23) & 0xFF, man = u & 0x7FFFFF;
+  if (ex != 0) return man == 0 ? t : __uint_as_float((ex + 1u) << 23);
+  return man == 1u ? ldexpf(1.f, -149) : ldexpf(1.f, 32 - __builtin_clz(man - 1u) - 149);   // t subnormal
+}

@@ -35,150 +35,9 @@
 // registers r..r+3.  The epilogue writes those quads into LDS (reused once the
 // K loop has drained) with an XOR-swizzled row layout and streams whole rows
 // back to HBM in 16-B chunks.
-#include "common.h"
-#include "kernels.h"
+#include "gemm_dma_common.h"
 
 namespace fsk {
-
-namespace {
-
-constexpr int DK = 32;                  // K per stage
-constexpr int TILE = 256;               // output tile edge
-constexpr int STAGE = 2 * TILE * DK;    // bf16 elements per stage: A rows then B rows (32 KB)
-
-__shared__ __attribute__((aligned(1024))) bf16 g_stage0[STAGE];
-__shared__ __attribute__((aligned(1024))) bf16 g_stage1[STAGE];
-__shared__ __attribute__((aligned(1024))) bf16 g_stage2[STAGE];
-__shared__ __attribute__((aligned(1024))) bf16 g_stage3[STAGE];
-__shared__ __attribute__((aligned(1024))) bf16 g_stage4[STAGE];
-
-template <int S> __device__ __forceinline__ bf16* stage_buf() {
-  return S == 0 ? g_stage0 : S == 1 ? g_stage1 : S == 2 ? g_stage2 : S == 3 ? g_stage3 : g_stage4;
-}
-// stage buffer w (0..3) as raw bytes
-__device__ __forceinline__ char* stage_bytes(int w) {
-  return reinterpret_cast<char*>(w == 0 ? g_stage0 : w == 1 ? g_stage1 : w == 2 ? g_stage2 : g_stage3);
-}
-// 16 KB of LDS for wave w's epilogue: half (w & 1) of stage buffer w >> 1
-__device__ __forceinline__ char* wave_region(int w) {
-  char* b = reinterpret_cast<char*>((w >> 1) == 0 ? g_stage0 : (w >> 1) == 1 ? g_stage1 : (w >> 1) == 2 ? g_stage2 : g_stage3);
-  return b + (w & 1) * 16384;
-}
-
-template <int V> struct Ic { static constexpr int value = V; };
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt low bits [3:0], high bits [15:14];
-// expcnt [6:4]; lgkmcnt [11:8]).
-constexpr int WAIT_VM12_LGKM0 = 0x7C;               // vmcnt(12) lgkmcnt(0)
-constexpr int WAIT_VM0_LGKM0 = 0x70;                // vmcnt(0) lgkmcnt(0)
-
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-}  // namespace
-
-// QKV epilogue of a prefill: the tile's 256 tokens x 256 columns are two
-// heads of 128 (all q, all k or all v: the section boundaries fall on tile
-// boundaries).  The fp32 products are staged in LDS 128 tokens at a time (the
-// four waves of one token half each write their 128 x 64 block, 32 KB, into
-// one stage buffer); then per (token, head) the q/k heads get the per-head
-// RMSNorm and rotate-half RoPE over all 128 dims (q also the attention's
-// pre-scale) and go to the q buffer or the K cache, and v goes to the V cache
-// as it is.  The arithmetic is the standalone norm/RoPE pass's, step for step,
-// on the same fp32 inputs, so the results are the same bits.  Eight lanes per
-// (token, head): lane `sub` holds dims [8 sub, 8 sub + 8) (block of wave
-// 2 head) and their partners [64 + 8 sub, ...) (block of wave 2 head + 1).
-// Row m of a staged block is 64 floats in 16 chunks of 16 B, chunk c at slot
-// c ^ (m & 15).
-__device__ __forceinline__ void qkv_rope_epilogue(const RopeKvParams& p, const f32x16 (&acc)[2][4], int m0,
-                                                  int n0, int M, int tid) {
-  constexpr int D = 128;
-  const int lane = tid & 63, wid = tid >> 6, wm = wid >> 2, wn = wid & 3;
-  const int lrow = lane & 31, hl = lane >> 5;
-  const int hsec = n0 / D;                         // first of the tile's two heads in q|k|v order
-  const bool is_q = hsec < p.nq, is_k = !is_q && hsec < p.nq + p.nkv;
-  const int sub = tid & 7;
-  const float* g = is_q ? p.gq : p.gk;
-  float g0[8], g1[8];
-  load8(g + 8 * sub, g0);
-  load8(g + 64 + 8 * sub, g1);
-#pragma unroll 1
-  for (int half = 0; half < 2; ++half) {
-    if (wm == half) {
-      char* R = stage_bytes(wn);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = i * 32 + lrow;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            f32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * gq + e];
-            const int cc = j * 8 + 2 * gq + hl;
-            *reinterpret_cast<f32x4*>(R + m * 256 + ((cc ^ (m & 15)) << 4)) = v;
-          }
-      }
-    }
-    lds_barrier();
-#pragma unroll 2
-    for (int it = 0; it < 4; ++it) {
-      const int item = it * 512 + tid;
-      const int hd = (item >> 3) & 1, mr = item >> 4;      // head of the tile, row of the half
-      const int row = half * 128 + mr;
-      const char* RA = stage_bytes(2 * hd) + mr * 256;
-      const char* RB = stage_bytes(2 * hd + 1) + mr * 256;
-      float x0[8], x1[8];
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(RA + (((2 * sub) ^ (mr & 15)) << 4));
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(RA + (((2 * sub + 1) ^ (mr & 15)) << 4));
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(RB + (((2 * sub) ^ (mr & 15)) << 4));
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(RB + (((2 * sub + 1) ^ (mr & 15)) << 4));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { x0[e] = a0[e]; x0[4 + e] = a1[e]; x1[e] = b0[e]; x1[4 + e] = b1[e]; }
-      const int t = min(m0 + row, M - 1);
-      const int b = t / p.S_per, pos = t % p.S_per;
-      const int hh = hsec + hd;
-      if (is_q || is_k) {
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf(x0[e], x0[e], fmaf(x1[e], x1[e], ss));
-        ss = group_sum<8>(ss);
-        const float inv = rsqrtf(__fadd_rn(ss / (float)D, p.eps));
-        float cs[8], sn[8];
-        load8(p.cos_t + (size_t)pos * (D / 2) + 8 * sub, cs);
-        load8(p.sin_t + (size_t)pos * (D / 2) + 8 * sub, sn);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float a = x0[e] * inv * g0[e], c = x1[e] * inv * g1[e];
-          const float y0 = fmaf(a, cs[e], -(c * sn[e])), y1 = fmaf(c, cs[e], a * sn[e]);
-          x0[e] = is_q ? y0 * p.qscale : y0;
-          x1[e] = is_q ? y1 * p.qscale : y1;
-        }
-      }
-      if (m0 + row < M) {
-        bf16* dst;
-        if (is_q) {
-          dst = reinterpret_cast<bf16*>(p.qout) + (size_t)t * p.nq * D + (size_t)hh * D;
-        } else {
-          const int j = is_k ? hh - p.nq : hh - p.nq - p.nkv;
-          const size_t o = (size_t)p.slots[b] * p.slot_stride + (size_t)j * p.head_stride + (size_t)pos * D;
-          dst = reinterpret_cast<bf16*>(is_k ? p.kcache : p.vcache) + o;
-        }
-        u32x4 u0, u1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u0[i] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x0[2 * i]) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x0[2 * i + 1]) << 16);
-          u1[i] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x1[2 * i]) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x1[2 * i + 1]) << 16);
-        }
-        *reinterpret_cast<u32x4*>(dst + 8 * sub) = u0;
-        *reinterpret_cast<u32x4*>(dst + 64 + 8 * sub) = u1;
-      }
-    }
-    lds_barrier();                                 // the next half reuses the buffers
-  }
-}
 
 template <int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -304,120 +163,7 @@ void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict
   // its own 16 KB of LDS and writes whole rows.
   __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
   lds_barrier();
-  char* R = wave_region(wid);
-  const int hl = lane >> 5;
-  const int mrow0 = m0 + wm * 128;
-  const int ncol0 = n0 + wn * 64;
-  if (colscale != nullptr) {
-    // per-column scale; columns past N (clamped reads) are never stored
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = min(ncol0 + 32 * j + 8 * g + 4 * hl, N - 4);
-        const f32x4 sc = *reinterpret_cast<const f32x4*>(colscale + n);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[j][i][4 * g + e] *= sc[e];
-      }
-  }
-
-  if constexpr (EPI == GEPI_QKV_ROPE) {
-    qkv_rope_epilogue(rp, acc, m0, n0, M, tid);
-    return;
-  }
-  if (EPI == GEPI_STORE_BF16) {
-    // 128 rows x 128 B; chunk c of row m at slot c ^ (m & 7)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = i * 32 + lrow;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[j][i][4 * g + e];
-          const int c = j * 4 + g;
-          *reinterpret_cast<bf16x4*>(R + m * 128 + ((c ^ (m & 7)) << 4) + hl * 8) = v;
-        }
-    }
-    bf16* o = reinterpret_cast<bf16*>(out);
-    const int c = lane & 7;
-#pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
-      const int m = it * 8 + (lane >> 3);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(R + m * 128 + ((c ^ (m & 7)) << 4));
-      const int gm = mrow0 + m, gn = ncol0 + c * 8;
-      if (gm < M && gn < N) *reinterpret_cast<u32x4*>(o + (size_t)gm * ldc + gn) = v;
-    }
-  } else if (EPI == GEPI_SWIGLU_BF16) {
-    // the wave's 64 packed columns are one [32 gate | 32 up] pair -> 32 outputs;
-    // 128 rows x 64 B, chunk c of row m at slot c ^ (m & 3)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = i * 32 + lrow;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)(silu(acc[0][i][4 * g + e]) * acc[1][i][4 * g + e]);
-        *reinterpret_cast<bf16x4*>(R + m * 64 + ((g ^ (m & 3)) << 4) + hl * 8) = v;
-      }
-    }
-    bf16* o = reinterpret_cast<bf16*>(out);
-    const int c = lane & 3;
-    const int f0 = ncol0 / 2, nf = N / 2;
-#pragma unroll 4
-    for (int it = 0; it < 8; ++it) {
-      const int m = it * 16 + (lane >> 2);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(R + m * 64 + ((c ^ (m & 3)) << 4));
-      const int gm = mrow0 + m, f = f0 + c * 8;
-      if (gm < M && f < nf) *reinterpret_cast<u32x4*>(o + (size_t)gm * ldc + f) = v;
-    }
-  } else {
-    // fp32: two passes of 64 rows x 256 B; chunk cc of row m at slot cc ^ (m & 15)
-    float* o = reinterpret_cast<float*>(out);
-    const int c = lane & 15;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = 2 * h + ii;
-        const int m = ii * 32 + lrow;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * g + e];
-            const int cc = j * 8 + 2 * g + hl;
-            *reinterpret_cast<f32x4*>(R + m * 256 + ((cc ^ (m & 15)) << 4)) = v;
-          }
-      }
-      const int gn = ncol0 + c * 4, gnc = min(gn, N - 4);
-      for (int it0 = 0; it0 < 16; it0 += 4) {
-        f32x4 old[4];
-        if (EPI == GEPI_RESID_F32) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int gmc = min(mrow0 + h * 64 + (it0 + u) * 4 + (lane >> 4), M - 1);
-            old[u] = *reinterpret_cast<const f32x4*>(o + (size_t)gmc * ldc + gnc);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int m = (it0 + u) * 4 + (lane >> 4);
-          f32x4 v = *reinterpret_cast<const f32x4*>(R + m * 256 + ((c ^ (m & 15)) << 4));
-          const int gm = mrow0 + h * 64 + m;
-          if (EPI == GEPI_RESID_F32) v += old[u];
-          if (gm < M && gn < N) *reinterpret_cast<f32x4*>(o + (size_t)gm * ldc + gn) = v;
-        }
-      }
-    }
-  }
+  dma_epilogue<EPI>(acc, tid, m0, n0, M, N, out, ldc, colscale, nullptr, rp);
 }
 
 // Usable when K is a multiple of 128, rows are 16-B aligned and the problem

@@ -5,10 +5,11 @@
 
 namespace fsk {
 
-// DT_I8: signed 8-bit codes with one fp32 scale per row (weights only)
-enum Dt { DT_F32 = 0, DT_BF16 = 1, DT_I8 = 2 };
+// DT_I8: signed 8-bit codes with one fp32 scale per row (weights only);
+// DT_F8: e4m3 codes with one power-of-two fp32 scale per row
+enum Dt { DT_F32 = 0, DT_BF16 = 1, DT_I8 = 2, DT_F8 = 3 };
 
-inline size_t dt_size(int dt) { return dt == DT_BF16 ? 2 : dt == DT_I8 ? 1 : 4; }
+inline size_t dt_size(int dt) { return dt == DT_BF16 ? 2 : (dt == DT_I8 || dt == DT_F8) ? 1 : 4; }
 
 // ---------------------------------------------------------------- small ops
 // x[t, :] = E[tok[t], :] widened to fp32; DT_I8 rows are multiplied by their
@@ -22,17 +23,26 @@ hipError_t quantize_rows(const void* src, int dt, int rows, int cols, int8_t* co
                          hipStream_t s);
 // dst[i] = bf16(codes[i]) (exact: |code| <= 127); n % 16 == 0.
 hipError_t codes_to_bf16(const int8_t* codes, size_t n, void* dst, hipStream_t s);
+// Per-row fp8: scale[r] = the smallest power of two >= fl32(max|src[r,:]| / 448),
+// codes = nearest e4m3 of src / scale (ties to even); zero row -> scale 0.  cols % 8 == 0.
+hipError_t quantize_rows_f8(const void* src, int dt, int rows, int cols, uint8_t* codes, float* scales,
+                            hipStream_t s);
+// dst[i] = bf16(value of e4m3 code i) (exact); n % 16 == 0.
+hipError_t f8codes_to_bf16(const uint8_t* codes, size_t n, void* dst, hipStream_t s);
 // out[t, :] = x[t*ldx, :] / sqrt(mean(x^2) + eps) * g; out of out_dt at row stride ldo.
 // lo (bf16 only, optional): the rounding remainder, y - out, also as bf16.
+// qs (optional): the fp8 activation rule instead -- qs[t] = the row's
+// power-of-two scale and out = its e4m3 codes (out_dt DT_F8) or the exact
+// bf16 values code * scale (DT_BF16).
 hipError_t rmsnorm(const float* x, int T, int H, int ldx, const float* g, float eps,
-                   void* out, int out_dt, int ldo, hipStream_t s, void* lo = nullptr);
+                   void* out, int out_dt, int ldo, hipStream_t s, void* lo = nullptr, float* qs = nullptr);
 // The same after adding np (<= RMSNORM_MAX_PARTS) split-K partials to the residual rows:
 // x[t, :] += parts[0][t, :] + ... + parts[np-1][t, :] (in that order; parts is
 // [np][T][H] dense), written back to x, then normalised into out as above.
 // out may be null (the additions only).
 constexpr int RMSNORM_MAX_PARTS = 16;
 hipError_t rmsnorm_add(float* x, const float* parts, int np, int T, int H, int ldx, const float* g, float eps,
-                       void* out, int out_dt, int ldo, hipStream_t s, void* lo = nullptr);
+                       void* out, int out_dt, int ldo, hipStream_t s, void* lo = nullptr, float* qs = nullptr);
 // dst[i] = float(src[i])
 hipError_t convert_f32(const void* src, int dt, float* dst, size_t n, hipStream_t s);
 // A one-wave kernel that waits about `us` microseconds of device wall clock.
@@ -61,8 +71,11 @@ struct GemvParams {
   float* part_val;     // [M * gemv_logits_blocks] per-block best values
   int32_t* part_idx;   // [M * gemv_logits_blocks] per-block best indices
   int groups;          // set by the launcher
+  int aquant;          // DT_F8 with gamma, M <= 4: quantize each normalised activation row to fp8
 };
 hipError_t gemv(int dt, int epi, GemvParams p, hipStream_t s);
+// The DT_F8 part of gemv (its own translation unit).
+hipError_t gemv_f8(int epi, GemvParams p, hipStream_t s);
 // Number of workgroups (and per-row partials) the LOGITS epilogue uses.
 int gemv_logits_blocks(int dt, int N, int K);
 // next[m] = best of the nblocks (value, index) partials of row m.
@@ -98,6 +111,19 @@ bool gemm_dma_rope_ok(const RopeKvParams& r, int M, int N);
 hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc,
                     int M, int N, int K, hipStream_t s, const void* A_lo, const float* colscale,
                     const RopeKvParams* rope = nullptr);
+// fp8 (e4m3) form of gemm_dma for the fp8 weight option: A [M, K] and B
+// [N, K] are e4m3 codes, K contiguous (lda, ldb in bytes, multiples of 16; K a
+// multiple of 64), C = diag(rowscale) . (A . B^T) . diag(colscale) in fp32
+// (either scale may be null), then the store form epi as for gemm_dma
+// (STORE_F32, SWIGLU_BF16 or QKV_ROPE: the quantized-input products).  Any
+// M, N >= 1 (tiles past the edges compute on clamped rows and store nothing);
+// the caller decides when the 256x256 tiling pays.
+bool gemm_f8_ok(int epi, const void* A, int lda, const void* B, int ldb, const void* out, int ldc, int M, int N,
+                int K);
+hipError_t gemm_f8(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc, int M, int N,
+                   int K, hipStream_t s, const float* rowscale, const float* colscale,
+                   const RopeKvParams* rope = nullptr);
+
 // The few-rows kernel behind gemm_bf16 (M <= 64, K % 256 == 0, N % 32 == 0):
 // one weight slab per workgroup, K split over its waves, each weight read once.
 // PART_F32 (only here): K is also split over ksplit workgroups per slab

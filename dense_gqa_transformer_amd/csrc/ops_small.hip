@@ -76,10 +76,34 @@ __global__ __launch_bounds__(256) void embed_i8_kernel(const int8_t* __restrict_
   }
 }
 
+// fp8 rows: e4m3 code * the row's power-of-two scale (exact in fp32)
+__global__ __launch_bounds__(256) void embed_f8_kernel(const uint8_t* __restrict__ E,
+                                                       const float* __restrict__ escale,
+                                                       const int32_t* __restrict__ tok, int H, int V,
+                                                       float* __restrict__ x, int32_t* __restrict__ bad) {
+  const int t = blockIdx.x;
+  const int id = tok[t];
+  if (bad_token(id, V, t, H, x, bad)) return;
+  const uint8_t* row = E + (size_t)id * H;
+  const float sc = escale[id];
+  float* dst = x + (size_t)t * H;
+  for (int k = threadIdx.x * 8; k < H; k += 256 * 8) {
+    const uint2 w = *reinterpret_cast<const uint2*>(row + k);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = f8_decode(((e < 4 ? w.x : w.y) >> (8 * (e & 3))) & 0xFFu) * sc;
+    *reinterpret_cast<float4*>(dst + k) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(dst + k + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
 hipError_t embed(const void* E, int dt, const int32_t* tok, int T, int H, int V, float* x, hipStream_t s,
                  const float* escale, int32_t* bad) {
   if (T <= 0) return hipSuccess;
-  if (dt == DT_I8) {
+  if (dt == DT_F8) {
+    if (escale == nullptr || H % 8 != 0) return hipErrorInvalidValue;
+    embed_f8_kernel<<<T, 256, 0, s>>>((const uint8_t*)E, escale, tok, H, V, x, bad);
+  } else if (dt == DT_I8) {
     if (escale == nullptr || H % 8 != 0) return hipErrorInvalidValue;
     embed_i8_kernel<<<T, 256, 0, s>>>((const int8_t*)E, escale, tok, H, V, x, bad);
   } else if (dt == DT_BF16) {
@@ -143,6 +167,79 @@ hipError_t quantize_rows(const void* src, int dt, int rows, int cols, int8_t* co
   return hipGetLastError();
 }
 
+// Per-row fp8 (e4m3) codes with a power-of-two scale, one wave per row: the
+// row's largest magnitude (wave max), s = the smallest power of two >=
+// fl32(amax / 448), code = nearest e4m3 of x / s (exact quotient).
+template <typename W>
+__global__ __launch_bounds__(256) void quantize_rows_f8_kernel(const W* __restrict__ src, int rows, int cols,
+                                                               uint8_t* __restrict__ codes,
+                                                               float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const W* row = src + (size_t)r * cols;
+  float amax = 0.f;
+  for (int k = lane * 8; k < cols; k += 64 * 8) {
+    float v[8];
+    load8(row + k, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  }
+  amax = wave_max(amax);
+  const float sc = f8_row_scale(amax);
+  if (lane == 0) scales[r] = sc;
+  uint8_t* out = codes + (size_t)r * cols;
+  for (int k = lane * 8; k < cols; k += 64 * 8) {
+    float v[8];
+    load8(row + k, v);
+    uint32_t w[2] = {0u, 0u};
+    if (sc > 0.f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e >> 2] |= f8_encode(v[e] / sc) << (8 * (e & 3));
+    }
+    *reinterpret_cast<uint2*>(out + k) = make_uint2(w[0], w[1]);
+  }
+}
+
+hipError_t quantize_rows_f8(const void* src, int dt, int rows, int cols, uint8_t* codes, float* scales,
+                            hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (cols <= 0 || cols % 8 != 0) return hipErrorInvalidValue;
+  const int blocks = (rows + 3) / 4;
+  if (dt == DT_BF16)
+    quantize_rows_f8_kernel<bf16><<<blocks, 256, 0, s>>>((const bf16*)src, rows, cols, codes, scales);
+  else if (dt == DT_F32)
+    quantize_rows_f8_kernel<float><<<blocks, 256, 0, s>>>((const float*)src, rows, cols, codes, scales);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// fp8 codes as bf16 operands of the MFMA GEMM (every e4m3 value is a bf16 value).
+__global__ __launch_bounds__(256) void f8codes_to_bf16_kernel(const uint8_t* __restrict__ codes, size_t n16,
+                                                              bf16* __restrict__ dst) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(codes + i * 16);
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = (bf16)f8_decode((w[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+      b[e] = (bf16)f8_decode((w[2 + (e >> 2)] >> (8 * (e & 3))) & 0xFFu);
+    }
+    *reinterpret_cast<bf16x8*>(dst + i * 16) = a;
+    *reinterpret_cast<bf16x8*>(dst + i * 16 + 8) = b;
+  }
+}
+
+hipError_t f8codes_to_bf16(const uint8_t* codes, size_t n, void* dst, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (n % 16 != 0) return hipErrorInvalidValue;
+  const size_t n16 = n / 16;
+  const size_t blocks = std::min<size_t>((n16 + 255) / 256, 4096);
+  f8codes_to_bf16_kernel<<<(unsigned)blocks, 256, 0, s>>>(codes, n16, (bf16*)dst);
+  return hipGetLastError();
+}
+
 // Codes as bf16 operands of the MFMA GEMM (integers up to 127 are exact).
 __global__ __launch_bounds__(256) void codes_to_bf16_kernel(const int8_t* __restrict__ codes, size_t n16,
                                                             bf16* __restrict__ dst) {
@@ -195,10 +292,30 @@ __device__ __forceinline__ void norm_store(const f32x4& v, float inv, const floa
   }
 }
 
-template <typename O, int MAXJ>
+// The fp8 form of the output (the activation rule of the fp8 weight option):
+// the normalised row y (fp32), its scale s = the smallest power of two >=
+// fl32(max|y| / 448) and codes e4m3(y / s); written as the codes (uint8) or as
+// the bf16 values code * s (exact), with s per row in qs.
+template <typename O>
+__device__ __forceinline__ void quant_store(const float* y, float sc, int c, O* o) {
+  if constexpr (sizeof(O) == 1) {
+    uint32_t w = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w |= (sc > 0.f ? f8_encode(y[e] / sc) : 0u) << (8 * e);
+    *reinterpret_cast<uint32_t*>(o + 4 * c) = w;
+  } else {
+    bf16x4 q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[e] = (bf16)(sc > 0.f ? f8_decode(f8_encode(y[e] / sc)) * sc : 0.f);
+    *reinterpret_cast<bf16x4*>(o + 4 * c) = q;
+  }
+}
+
+template <typename O, int MAXJ, bool QUANT>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int T, int H, int ldx,
                                                       const float* __restrict__ g, float eps,
-                                                      O* __restrict__ out, O* __restrict__ lo, int ldo) {
+                                                      O* __restrict__ out, O* __restrict__ lo, int ldo,
+                                                      float* __restrict__ qs) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= T) return;
@@ -215,6 +332,28 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
   const float inv = rsqrtf(wave_sum(ss) / (float)H + eps);
   O* o = out + (size_t)r * ldo;
+  if constexpr (QUANT) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nc) {
+        const f32x4 gg = *reinterpret_cast<const f32x4*>(g + 4 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[j][e] = v[j][e] * inv * gg[e]; amax = fmaxf(amax, fabsf(v[j][e])); }
+      }
+    }
+    const float sc = f8_row_scale(wave_max(amax));
+    if (lane == 0) qs[r] = sc;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int c = lane + 64 * j;
+      if (c >= nc) break;
+      const float y[4] = {v[j][0], v[j][1], v[j][2], v[j][3]};
+      quant_store<O>(y, sc, c, o);
+    }
+    return;
+  }
   O* ol = (lo != nullptr) ? lo + (size_t)r * ldo : nullptr;
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
@@ -229,13 +368,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 // together, the partials are added in order 0..np-1 (so the result does not
 // depend on launch timing) and the row is written back before it is
 // normalised (out == nullptr: the additions only).
-template <typename O>
+template <typename O, bool QUANT>
 __global__ __launch_bounds__(256) void rmsnorm_add_kernel(float* __restrict__ x, int T, int H, int ldx,
                                                           const float* __restrict__ g, float eps,
                                                           O* __restrict__ out, O* __restrict__ lo, int ldo,
-                                                          const float* __restrict__ parts, int np) {
+                                                          const float* __restrict__ parts, int np,
+                                                          float* __restrict__ qs) {
   constexpr int MAXC = 4;                          // H <= 4096
-  __shared__ float red[4];
+  __shared__ float red[4], redm[4];
   const int r = blockIdx.x, tid = threadIdx.x;
   float* row = x + (size_t)r * ldx;
   const int nc = H >> 2;
@@ -268,6 +408,32 @@ __global__ __launch_bounds__(256) void rmsnorm_add_kernel(float* __restrict__ x,
   __syncthreads();
   const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
   O* o = out + (size_t)r * ldo;
+  if constexpr (QUANT) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int c = tid + 256 * j;
+      if (c < nc) {
+        const f32x4 gg = *reinterpret_cast<const f32x4*>(g + 4 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[j][e] = v[j][e] * inv * gg[e]; amax = fmaxf(amax, fabsf(v[j][e])); }
+      }
+    }
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) redm[tid >> 6] = amax;
+    __syncthreads();
+    const float sc = f8_row_scale(fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3])));
+    if (tid == 0) qs[r] = sc;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int c = tid + 256 * j;
+      if (c < nc) {
+        const float y[4] = {v[j][0], v[j][1], v[j][2], v[j][3]};
+        quant_store<O>(y, sc, c, o);
+      }
+    }
+    return;
+  }
   O* ol = (lo != nullptr) ? lo + (size_t)r * ldo : nullptr;
 #pragma unroll
   for (int j = 0; j < MAXC; ++j) {
@@ -277,28 +443,44 @@ __global__ __launch_bounds__(256) void rmsnorm_add_kernel(float* __restrict__ x,
 }
 
 hipError_t rmsnorm(const float* x, int T, int H, int ldx, const float* g, float eps, void* out,
-                   int out_dt, int ldo, hipStream_t s, void* lo) {
+                   int out_dt, int ldo, hipStream_t s, void* lo, float* qs) {
   if (T <= 0) return hipSuccess;
   if (out == nullptr || H % 4 != 0 || H > 4096 || ldx % 4 != 0 || ldo % 4 != 0) return hipErrorInvalidValue;
   const int blocks = (T + 3) / 4;
-  if (out_dt == DT_BF16)
-    rmsnorm_kernel<bf16, 16><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, (bf16*)lo, ldo);
+  if (qs != nullptr) {                                 // fp8 activation rule
+    if (lo != nullptr || g == nullptr) return hipErrorInvalidValue;
+    if (out_dt == DT_BF16)
+      rmsnorm_kernel<bf16, 16, true><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, nullptr, ldo, qs);
+    else if (out_dt == DT_F8)
+      rmsnorm_kernel<uint8_t, 16, true><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (uint8_t*)out, nullptr, ldo, qs);
+    else
+      return hipErrorInvalidValue;
+  } else if (out_dt == DT_BF16)
+    rmsnorm_kernel<bf16, 16, false><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, (bf16*)lo, ldo, nullptr);
   else if (lo == nullptr)
-    rmsnorm_kernel<float, 16><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (float*)out, nullptr, ldo);
+    rmsnorm_kernel<float, 16, false><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (float*)out, nullptr, ldo, nullptr);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t rmsnorm_add(float* x, const float* parts, int np, int T, int H, int ldx, const float* g, float eps,
-                       void* out, int out_dt, int ldo, hipStream_t s, void* lo) {
+                       void* out, int out_dt, int ldo, hipStream_t s, void* lo, float* qs) {
   if (T <= 0) return hipSuccess;
   if (np <= 0 || np > RMSNORM_MAX_PARTS || parts == nullptr) return hipErrorInvalidValue;
   if (H % 4 != 0 || H > 4096 || ldx % 4 != 0 || ldo % 4 != 0) return hipErrorInvalidValue;
-  if (out_dt == DT_BF16)
-    rmsnorm_add_kernel<bf16><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, (bf16*)lo, ldo, parts, np);
+  if (qs != nullptr) {                                 // fp8 activation rule
+    if (lo != nullptr || g == nullptr || out == nullptr) return hipErrorInvalidValue;
+    if (out_dt == DT_BF16)
+      rmsnorm_add_kernel<bf16, true><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, nullptr, ldo, parts, np, qs);
+    else if (out_dt == DT_F8)
+      rmsnorm_add_kernel<uint8_t, true><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (uint8_t*)out, nullptr, ldo, parts, np, qs);
+    else
+      return hipErrorInvalidValue;
+  } else if (out_dt == DT_BF16)
+    rmsnorm_add_kernel<bf16, false><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, (bf16*)lo, ldo, parts, np, nullptr);
   else if (lo == nullptr)
-    rmsnorm_add_kernel<float><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (float*)out, nullptr, ldo, parts, np);
+    rmsnorm_add_kernel<float, false><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (float*)out, nullptr, ldo, parts, np, nullptr);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

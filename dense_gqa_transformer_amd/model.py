@@ -41,7 +41,9 @@ class Model:
     arrays or tensors, ``[out, in]`` row-major.  The values are copied into
     library-owned memory; for bf16 models they must be bf16-representable.
     ``shape.weight_format == "i8_row"`` has the library store the matrices as
-    int8 codes with one scale per output row (quantized at creation).
+    int8 codes with one scale per output row (quantized at creation);
+    ``"f8_row"`` as e4m3 codes with a power-of-two scale per row, the norm
+    outputs that feed Q/K/V, gate/up and the head quantized likewise.
     """
 
     def __init__(self, shape, weights: dict, max_seqs: int, max_ctx: int,
@@ -56,8 +58,8 @@ class Model:
                             shape.head_dim, shape.ffn, shape.vocab, float(shape.rms_eps),
                             float(shape.rope_theta), self.dtype, int(max_seqs), int(max_ctx),
                             int(getattr(shape, "rope_dim", 0)), int(bool(getattr(shape, "attn_gate", False))),
-                            native.FS_WEIGHTS_I8_ROW if getattr(shape, "weight_format", "dtype") == "i8_row"
-                            else native.FS_WEIGHTS_DTYPE)
+                            {"i8_row": native.FS_WEIGHTS_I8_ROW, "f8_row": native.FS_WEIGHTS_F8_ROW}.get(
+                                getattr(shape, "weight_format", "dtype"), native.FS_WEIGHTS_DTYPE))
         with torch.cuda.device(self.device):
             keep = []
 
@@ -198,6 +200,39 @@ def quantize_rows_i8(src: torch.Tensor, stream: Optional[torch.cuda.Stream] = No
     dt = native.FS_BF16 if src.dtype == torch.bfloat16 else native.FS_F32
     check(lib.fs_quantize_rows_i8(_ptr(src), dt, rows, cols, _ptr(codes), _ptr(scales), _stream_ptr(stream)))
     return codes, scales
+
+
+def quantize_rows_f8(src: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
+    """Per-row e4m3 codes and power-of-two fp32 scales of a device matrix
+    [rows, cols] (fp32 or bf16), by the library's quantizer (fs_quantize_rows_f8)."""
+    lib = native.load()
+    assert src.dim() == 2 and src.is_contiguous() and src.dtype in (torch.float32, torch.bfloat16)
+    rows, cols = src.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=src.device)
+    scales = torch.empty((rows,), dtype=torch.float32, device=src.device)
+    dt = native.FS_BF16 if src.dtype == torch.bfloat16 else native.FS_F32
+    check(lib.fs_quantize_rows_f8(_ptr(src), dt, rows, cols, _ptr(codes), _ptr(scales), _stream_ptr(stream)))
+    return codes, scales
+
+
+def gemm_f8(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
+            out: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """fs_gemm_f8: out[m, n] = a_scales[m] * w_scales[n] * sum_k a[m, k] * w[n, k]
+    over e4m3 code matrices a [M, K], w [N, K] (uint8), fp32 out [M, N]."""
+    lib = native.load()
+    assert a_codes.dtype == torch.uint8 and w_codes.dtype == torch.uint8
+    assert a_codes.dim() == 2 and w_codes.dim() == 2 and a_codes.shape[1] == w_codes.shape[1]
+    assert a_codes.is_contiguous() and w_codes.is_contiguous()
+    M, K = a_codes.shape
+    N = w_codes.shape[0]
+    assert a_scales.dtype == torch.float32 and a_scales.shape == (M,) and a_scales.is_contiguous()
+    assert w_scales.dtype == torch.float32 and w_scales.shape == (N,) and w_scales.is_contiguous()
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    assert out.dtype == torch.float32 and out.shape == (M, N) and out.is_contiguous()
+    check(lib.fs_gemm_f8(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), M, N, K, _ptr(out),
+                         _stream_ptr(stream)))
+    return out
 
 
 def argmax(logits: torch.Tensor, out: Optional[torch.Tensor] = None,

@@ -26,6 +26,7 @@ FS_F32 = 0
 FS_BF16 = 1
 FS_WEIGHTS_DTYPE = 0
 FS_WEIGHTS_I8_ROW = 1
+FS_WEIGHTS_F8_ROW = 2
 
 LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo",
                 "mlp_norm", "w_gate", "w_up", "w_down")
@@ -97,6 +98,10 @@ def load() -> ctypes.CDLL:
     lib.fs_argmax.restype = ctypes.c_int
     lib.fs_quantize_rows_i8.argtypes = [P, i32, i32, i32, P, P, P]
     lib.fs_quantize_rows_i8.restype = ctypes.c_int
+    lib.fs_quantize_rows_f8.argtypes = [P, i32, i32, i32, P, P, P]
+    lib.fs_quantize_rows_f8.restype = ctypes.c_int
+    lib.fs_gemm_f8.argtypes = [P, P, P, P, i32, i32, i32, P, P]
+    lib.fs_gemm_f8.restype = ctypes.c_int
     lib.fs_sample.argtypes = [P, P, i32, i32, ctypes.POINTER(FsSampling), P, P, P]
     lib.fs_sample.restype = ctypes.c_int
     lib.fs_sample_noalloc.argtypes = [P, i32, i32, ctypes.POINTER(FsSampling), P, P, P]

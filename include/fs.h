@@ -60,8 +60,18 @@ typedef enum { FS_F32 = 0, FS_BF16 = 1 } fs_dtype;
  *     fs_quantize_rows_i8 rule.  Products use code * scale exactly (the scale
  *     multiplies each row's fp32 dot product); the embedding lookup reads the
  *     same codes, so the head stays tied.  Norm weights, activations and the
- *     KV cache keep cfg.dtype. */
-typedef enum { FS_WEIGHTS_DTYPE = 0, FS_WEIGHTS_I8_ROW = 1 } fs_weight_format;
+ *     KV cache keep cfg.dtype.
+ *   FS_WEIGHTS_F8_ROW: 8-bit floating-point codes (e4m3: 1 sign, 4 exponent
+ *     bits with bias 7, 3 mantissa bits, largest 448; the gfx950 matrix
+ *     units' fp8 operand format) with one power-of-two fp32 scale per output
+ *     row, made by fs_model_create with the fs_quantize_rows_f8 rule; the
+ *     tied embedding / head likewise.  The RMSNorm outputs that feed the
+ *     Q/K/V projection, the gate/up projection and the head are quantized per
+ *     row by the same rule, so those products are sums of products of two fp8
+ *     values (the prefill computes the large ones on the fp8 matrix
+ *     instructions); the output and down projections are weight-only.
+ *     Requires cfg.dtype = FS_BF16 or FS_F32. */
+typedef enum { FS_WEIGHTS_DTYPE = 0, FS_WEIGHTS_I8_ROW = 1, FS_WEIGHTS_F8_ROW = 2 } fs_weight_format;
 
 /* Model shape and KV capacity.
  *   n_heads % n_kv_heads == 0; query head h reads KV head h / (n_heads/n_kv_heads).
@@ -120,6 +130,9 @@ typedef struct fs_model fs_model;
  * FS_DECODE_MIN_CHUNK=32|64|128|256 sets the shortest split-K chunk;
  * FS_PREFILL_FUSE_ROPE=0 keeps the per-head q/k norm + RoPE + K/V write of a
  * large prefill in a pass of its own instead of the QKV GEMM's epilogue;
+ * FS_PREFILL_F8_MFMA=0 keeps an FS_WEIGHTS_F8_ROW model's prefill on widened
+ * (bf16) weights instead of the fp8 matrix instructions (the same values:
+ * code * scale is exact in bf16);
  * FS_DECODE_PERSIST=1 runs batch-1 decode steps of the 0.6B shape as one
  * persistent launch (all 256 CUs resident, workgroups exchanging activations
  * in memory; measured slower than the default, see fs_decode_trace);
@@ -182,6 +195,37 @@ fs_status fs_argmax(const float *logits, int32_t B, int32_t V, int32_t *out, voi
  * UNSUPPORTED for an unknown dtype. */
 fs_status fs_quantize_rows_i8(const void *src, int32_t dtype, int32_t rows, int32_t cols,
                               int8_t *codes, float *scales, void *stream);
+
+/* Per-row fp8 quantization (the FS_WEIGHTS_F8_ROW rule, also the rule of its
+ * activation rows).
+ *   src:    device [rows, cols] of dtype (fs_dtype), row-major.
+ *   codes:  device uint8 [rows, cols] (e4m3 codes); scales: device fp32 [rows].
+ * scale[r] = the smallest power of two >= fl32(max_k |src[r, k]| / 448)
+ * (fl32: the correctly rounded fp32 quotient), codes[r, k] = the e4m3 value
+ * nearest to src[r, k] / scale[r] (an exact quotient; ties to the even
+ * mantissa; magnitudes past 448 saturate); a row of zeros gets scale 0 and
+ * zero codes.  Errors: INVALID_ARG for NULL pointers, rows or cols <= 0,
+ * cols % 8 != 0, misaligned pointers (src 16 B, codes 8 B, scales 4 B);
+ * UNSUPPORTED for an unknown dtype. */
+fs_status fs_quantize_rows_f8(const void *src, int32_t dtype, int32_t rows, int32_t cols,
+                              uint8_t *codes, float *scales, void *stream);
+
+/* Product of two e4m3 code matrices with one power-of-two scale per row: the
+ * arithmetic of the FS_WEIGHTS_F8_ROW model's Q/K/V and gate/up products at
+ * prefill sizes, where both the weights and the quantized norm outputs are
+ * codes ("Milestones", M7: the low-bit path measured against the baseline).
+ *   a_codes: device uint8 [M, K], a_scales: device fp32 [M];
+ *   w_codes: device uint8 [N, K], w_scales: device fp32 [N] (both as
+ *            fs_quantize_rows_f8 writes them; K contiguous);
+ *   out:     device fp32 [M, N], row-major:
+ *            out[m, n] = a_scales[m] * w_scales[n] * sum_k e4m3(a[m, k]) * e4m3(w[n, k]).
+ * Each product of two codes is exact; the sum is accumulated in fp32.  Runs
+ * the model's fp8 matrix-instruction kernel (256x256 tiles) whatever M.  A NaN
+ * code (0x7f, 0xff) makes its row / column NaN.  Asynchronous on stream.
+ * Errors: INVALID_ARG for NULL pointers, M, N or K <= 0, K % 64 != 0,
+ * N % 8 != 0, misaligned pointers (codes, out and w_scales 16 B, a_scales 4 B). */
+fs_status fs_gemm_f8(const uint8_t *a_codes, const float *a_scales, const uint8_t *w_codes,
+                     const float *w_scales, int32_t M, int32_t N, int32_t K, float *out, void *stream);
 
 /* Parameters of the sampling chain temperature -> top-k -> top-p ->
  * renormalise -> draw ("Coming back to Failed Star", section "Next": the

@@ -13,7 +13,8 @@ module is the oracle of the library's fp8 option, whose reading is:
   positive 2^-9.  (This is the layout the gfx950 matrix cores take as their
   fp8 operand.)
 * Rounding: a real value goes to the nearest representable value, a tie to
-  the one with an even mantissa field; magnitudes beyond 448 saturate to 448.
+  the one with an even mantissa field; magnitudes beyond 448 saturate to 448;
+  a result of zero is stored as code 0 (the positive zero) whatever the sign.
 * Scales are powers of two, one per row: for a row with largest magnitude
   a > 0, ``t = a / 448`` (correctly rounded float32) and ``s = 2^e`` with e the
   smallest integer such that ``2^e >= t``; a zero row has scale 0 and codes 0.

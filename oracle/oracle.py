@@ -161,13 +161,17 @@ class Oracle:
     widened exactly to float32, so no rounding happens on this side.
     """
 
-    def __init__(self, shape, weights: dict, dtype=np.float64, quantize_norm_outputs=None):
+    def __init__(self, shape, weights: dict, dtype=np.float64, quantize_norm_outputs=None, kv_round=None):
         self.shape = shape
         self.dtype = np.dtype(dtype)
         # optional rule applied to every RMSNorm output that feeds a projection
         # (Q/K/V, gate/up, the head): the fp8 option's activation quantization
         # (oracle/fp8.py); None leaves them exact
         self.qn = quantize_norm_outputs
+        # optional rounding of K (normed, rotated) and V as they enter the
+        # cache, for a cache kept in a narrower type (a bf16 cache stores them
+        # rounded to bf16); None keeps them exact
+        self.kv_round = kv_round
         c = lambda a: np.asarray(a, dtype=self.dtype)
         self.embed = c(weights["embed"])
         self.final_norm = c(weights["final_norm"])
@@ -200,6 +204,9 @@ class Oracle:
         rot = getattr(sh, "rope_dim", 0) or sh.head_dim
         q = rope(rms_norm(q, w["q_norm"], sh.rms_eps), pos, sh.rope_theta, rot)
         k = rope(rms_norm(k, w["k_norm"], sh.rms_eps), pos, sh.rope_theta, rot)
+        if self.kv_round is not None:
+            k = np.asarray(self.kv_round(k), dtype=self.dtype)
+            v = np.asarray(self.kv_round(v), dtype=self.dtype)
         if k_past is not None and k_past.shape[0] > 0:
             k_all = np.concatenate([k_past, k], axis=0)
             v_all = np.concatenate([v_past, v], axis=0)

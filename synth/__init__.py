@@ -49,7 +49,7 @@ class ModelShape:
     dtype: str = BF16
     rope_dim: int = 0          # rotated dims per head (0: all of head_dim)
     attn_gate: bool = False    # q projection carries a per-head output gate
-    weight_format: str = "dtype"   # "dtype", or "i8_row": int8 codes + one scale per output row
+    weight_format: str = "dtype"   # "dtype", "i8_row" (int8 codes + a scale per row) or "f8_row" (e4m3)
 
     @property
     def q_width(self) -> int:
@@ -98,6 +98,9 @@ GATED_0P6B = ModelShape(n_layers=28, hidden=1024, n_heads=8, n_kv_heads=2, head_
 # Int8 weights (one scale per output row) on the tiny fp32 model and the 0.6B shape.
 TINY_I8 = dataclasses.replace(TINY, weight_format="i8_row")
 QWEN3_0P6B_I8 = dataclasses.replace(QWEN3_0P6B, weight_format="i8_row")
+# fp8 (e4m3) weights with power-of-two row scales, norm outputs quantized too.
+TINY_F8 = dataclasses.replace(TINY, weight_format="f8_row")
+QWEN3_0P6B_F8 = dataclasses.replace(QWEN3_0P6B, weight_format="f8_row")
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -173,6 +176,18 @@ def logit_rows(seed: int, rows: int, vocab: int, std: float = 0.64) -> np.ndarra
     random-init model produces."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return (rng.standard_normal((rows, vocab), dtype=np.float32) * np.float32(std)).astype(np.float32)
+
+
+def activation_rows(seed: int, rows: int, cols: int) -> np.ndarray:
+    """Synthetic fp32 rows shaped like normalised activations: N(0, 1) times a
+    per-row magnitude spread over 2^-4 .. 2^4, with one column in 64 scaled up
+    8x (the outlier channels a norm gain produces)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((rows, cols), dtype=np.float32)
+    mag = np.exp2(rng.uniform(-4.0, 4.0, size=(rows, 1))).astype(np.float32)
+    out_cols = rng.permutation(cols)[: max(1, cols // 64)]
+    x[:, out_cols] *= np.float32(8.0)
+    return (x * mag).astype(np.float32)
 
 
 @dataclasses.dataclass(frozen=True)

@@ -13,7 +13,8 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == {"fs_model_create", "fs_model_destroy", "fs_prefill", "fs_decode_step",
                           "fs_argmax", "fs_slot_length", "fs_kv_read", "fs_last_error",
                           "fs_timing", "fs_timing_read", "fs_kernel_bench", "fs_sample", "fs_generate",
-                          "fs_quantize_rows_i8", "fs_sample_noalloc", "fs_decode_trace"}
+                          "fs_quantize_rows_i8", "fs_sample_noalloc", "fs_decode_trace", "fs_quantize_rows_f8",
+                          "fs_gemm_f8"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -50,6 +51,12 @@ def test_argument_errors_without_device():
     assert q(fake, native.FS_BF16, 0, 64, fake, fake, None) == native.FS_ERR_INVALID_ARG
     assert q(fake, native.FS_BF16, 4, 60, fake, fake, None) == native.FS_ERR_INVALID_ARG
     assert q(ctypes.c_void_p(0x1008), native.FS_BF16, 4, 64, fake, fake, None) == native.FS_ERR_INVALID_ARG
+    gf = lib.fs_gemm_f8
+    assert gf(None, fake, fake, fake, 4, 8, 64, fake, None) == native.FS_ERR_INVALID_ARG
+    assert gf(fake, fake, fake, fake, 0, 8, 64, fake, None) == native.FS_ERR_INVALID_ARG
+    assert gf(fake, fake, fake, fake, 4, 8, 96, fake, None) == native.FS_ERR_INVALID_ARG      # K % 64
+    assert gf(fake, fake, fake, fake, 4, 12, 64, fake, None) == native.FS_ERR_INVALID_ARG     # N % 8
+    assert gf(ctypes.c_void_p(0x1008), fake, fake, fake, 4, 8, 64, fake, None) == native.FS_ERR_INVALID_ARG
 
 
 def _cfg(**kw):
@@ -69,7 +76,7 @@ def _cfg(**kw):
     (dict(hidden=8192), native.FS_ERR_UNSUPPORTED),
     (dict(max_ctx=0), native.FS_ERR_INVALID_ARG),
     (dict(vocab=0), native.FS_ERR_INVALID_ARG),
-    (dict(weight_format=2), native.FS_ERR_UNSUPPORTED),
+    (dict(weight_format=3), native.FS_ERR_UNSUPPORTED),
 ])
 def test_create_rejects_bad_config(kw, status):
     lib = native.load()
