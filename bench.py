@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12           # bytes/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15     # dense bf16 flop/s, MI355X
+MFMA_FP8_PEAK = 5.0e15      # dense fp8 flop/s, MI355X
 
 
 # --------------------------------------------------------------------------- algorithmic work
@@ -198,24 +199,27 @@ def gated_variant_bench(dev, Model):
             "prefill_1x1024_tok_s": round(1024 / pdt, 1)}
 
 
-def int8_weights_bench(dev, Model, shape, w, ref_model, prompt):
-    """The low-bit decision's measurements: the 0.6B shape with int8 weights
-    (one scale per output row, quantized by the library from the same bf16
-    weights) against the bf16 model -- speed (bs1 decode, 4 x 4096 prefill),
-    weight memory, and quality (logits of both models on one teacher-forced
-    token stream, the bf16 model choosing the tokens)."""
+def lowbit_weights_bench(dev, Model, shape, w, ref_model, prompt, fmt):
+    """The low-bit decision's measurements ("Milestones", M7) for one weight
+    format -- "i8_row" (int8 codes) or "f8_row" (e4m3 codes; norm outputs
+    quantized per row, Q/K/V and gate/up on fp8 matrix instructions at prefill
+    sizes) -- with one scale per output row, quantized by the library from the
+    same bf16 weights, against the bf16 model: speed (bs1 decode, 4 x 4096
+    prefill, per-kernel times), weight memory, and quality (logits of both
+    models on one teacher-forced token stream, the bf16 model choosing the
+    tokens)."""
     import dataclasses
 
     import numpy as np
     import torch
 
     import synth
-    qs = dataclasses.replace(shape, weight_format="i8_row")
+    qs = dataclasses.replace(shape, weight_format=fmt)
     qm = Model(qs, w, max_seqs=4, max_ctx=4096)
     H, L, I, V = shape.hidden, shape.n_layers, shape.ffn, shape.vocab
     rows_cols = [(shape.q_width + 2 * shape.kv_width, H), (H, shape.q_width), (2 * I, H), (H, I)]
     bf16_w = 2 * (V * H + L * sum(r * c for r, c in rows_cols))
-    int8_w = V * H + 4 * V + L * sum(r * c + 4 * r for r, c in rows_cols)
+    code_w = V * H + 4 * V + L * sum(r * c + 4 * r for r, c in rows_cols)
     P = len(prompt)
     tok = torch.from_numpy(prompt[None, :].astype(np.int32)).to(dev)
     nxt = torch.empty((1,), dtype=torch.int32, device=dev)
@@ -234,10 +238,10 @@ def int8_weights_bench(dev, Model, shape, w, ref_model, prompt):
     dt = (time.perf_counter() - t0) / steps
     ctx = P + (steps + 1) / 2.0
     other = L * (2 * H + 2 * shape.head_dim) * 2 + 2 * H * 2       # norm weights, embedding row
-    step_bytes = int8_w + other + L * 2 * shape.kv_width * 2 * ctx
+    step_bytes = code_w + other + L * 2 * shape.kv_width * 2 * ctx
     per_launch = {lab: qm.kernel_bench(lab, reps=20, slot=2, position=P + steps // 2)
                   for lab in ("qkv", "o_proj", "gate_up", "down", "head")}
-    # speed: 4 x 4096 prefill
+    # speed: 4 x 4096 prefill, and its GEMMs one by one
     pw = synth.workload("prefill_0p6b_4x4096")
     ptok = torch.from_numpy(np.stack(pw.prompts).astype(np.int32)).to(dev)
     plg = torch.empty((4, V), dtype=torch.float32, device=dev)
@@ -247,6 +251,24 @@ def int8_weights_bench(dev, Model, shape, w, ref_model, prompt):
     qm.prefill(ptok, [0, 1, 2, 3], logits=plg)
     torch.cuda.synchronize()
     pdt = time.perf_counter() - t0
+    qm.timing(True)
+    qm.prefill(ptok, [0, 1, 2, 3], logits=plg)
+    torch.cuda.synchronize()
+    gemms = {}
+    for lab in ("wconv", "norm", "qkv", "o_proj", "gate_up", "down"):
+        ms, n = qm.timing_read(lab)
+        if n:
+            gemms[lab] = round(ms, 3)
+    qm.timing(False)
+    fp8_mm = ("qkv", "gate_up") if fmt == "f8_row" else ()
+    frac = {}
+    for lab in ("qkv", "o_proj", "gate_up", "down"):
+        if lab in gemms:
+            peak = MFMA_FP8_PEAK if lab in fp8_mm else MFMA_BF16_PEAK
+            fl = L * prefill_label_flops(shape, lab, 4, 4096)
+            frac[lab] = {"tflop_s": round(fl / (gemms[lab] / 1e3) / 1e12, 1),
+                         "peak": "fp8 5.0 PFLOP/s" if lab in fp8_mm else "bf16 2.5 PFLOP/s",
+                         "frac": round(fl / (gemms[lab] / 1e3) / peak, 4)}
     # quality: one token stream through both models
     ql = qm.prefill(tok, [0])
     rl = ref_model.prefill(tok, [3])
@@ -265,18 +287,35 @@ def int8_weights_bench(dev, Model, shape, w, ref_model, prompt):
         ref_model.decode_step(t, [P + k], [3], logits=b)
         cur_q, cur_r = a.clone(), b.clone()
     qm.close()
-    return {"workload": "0.6B shape, int8 codes + one fp32 scale per output row for every matrix (tied "
-                        "embedding / head included), bf16 activations and KV; bs1 decode from the same "
-                        "512-token prompt; 4 x 4096 prefill",
-            "decode_tok_s": round(1.0 / dt, 1), "ms_per_step": round(dt * 1e3, 4),
-            "decode_hbm_frac_step": round(step_bytes / dt / HBM_PEAK, 4),
-            "decode_us_per_launch": {k: round(v, 3) for k, v in per_launch.items()},
-            "prefill_4x4096_tok_s": round(4 * 4096 / pdt, 1), "prefill_ms": round(pdt * 1e3, 2),
-            "weight_bytes": {"int8": int(int8_w), "bf16": int(bf16_w)},
-            "quality_vs_bf16": {"positions": n_q, "greedy_agree": agree,
-                                "max_abs_logit_diff": round(max(diffs), 4),
-                                "mean_max_abs_logit_diff": round(float(np.mean(diffs)), 4),
-                                "mean_rel_rms_logit_diff": round(float(np.mean(rel)), 5)}}
+    code = "int8" if fmt == "i8_row" else "e4m3"
+    res = {"workload": f"0.6B shape, {code} codes + one fp32 scale per output row for every matrix (tied "
+                       "embedding / head included), bf16 KV; bs1 decode from the same 512-token prompt; "
+                       "4 x 4096 prefill",
+           "decode_tok_s": round(1.0 / dt, 1), "ms_per_step": round(dt * 1e3, 4),
+           "decode_hbm_frac_step": round(step_bytes / dt / HBM_PEAK, 4),
+           "decode_us_per_launch": {k: round(v, 3) for k, v in per_launch.items()},
+           "prefill_4x4096_tok_s": round(4 * 4096 / pdt, 1), "prefill_ms": round(pdt * 1e3, 2),
+           "prefill_kernel_ms_per_pass": gemms, "prefill_gemm_mfma": frac,
+           "weight_bytes": {code: int(code_w), "bf16": int(bf16_w)},
+           "quality_vs_bf16": {"positions": n_q, "greedy_agree": agree,
+                               "max_abs_logit_diff": round(max(diffs), 4),
+                               "mean_max_abs_logit_diff": round(float(np.mean(diffs)), 4),
+                               "mean_rel_rms_logit_diff": round(float(np.mean(rel)), 5)}}
+    if fmt == "f8_row":
+        # the same prefill with the fp8 products on widened (bf16) weights instead
+        os.environ["FS_PREFILL_F8_MFMA"] = "0"
+        try:
+            wm = Model(qs, w, max_seqs=4, max_ctx=4096)
+        finally:
+            del os.environ["FS_PREFILL_F8_MFMA"]
+        wm.prefill(ptok, [0, 1, 2, 3], logits=plg)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        wm.prefill(ptok, [0, 1, 2, 3], logits=plg)
+        torch.cuda.synchronize()
+        res["prefill_4x4096_tok_s_widened_bf16"] = round(4 * 4096 / (time.perf_counter() - t0), 1)
+        wm.close()
+    return res
 
 
 def scorer_bench(dev, model, shape):
@@ -582,7 +621,8 @@ def main():
     out["batched_decode"] = batched_decode_bench(dev, Model, w, argmax)
     out["tiny"] = tiny_bench(dev, Model, argmax)
     out["gated_variant"] = gated_variant_bench(dev, Model)
-    out["int8_weights"] = int8_weights_bench(dev, Model, shape, w, model, prompt)
+    out["int8_weights"] = lowbit_weights_bench(dev, Model, shape, w, model, prompt, "i8_row")
+    out["fp8_weights"] = lowbit_weights_bench(dev, Model, shape, w, model, prompt, "f8_row")
 
     # seeded sampling of one lm_head row (temperature -> top-k -> top-p -> draw)
     srow = torch.from_numpy(synth.logit_rows(900, 1, shape.vocab)).to(dev)

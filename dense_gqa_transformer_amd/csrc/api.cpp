@@ -172,7 +172,8 @@ struct fs_model {
   int min_chunk = 32;
   // prefill: q/k norm + RoPE + K/V write in the QKV GEMM's epilogue where it applies
   bool fuse_rope = true;
-  bool f8_mfma = true;            // fp8 weights: prefill Q/K/V and gate/up on fp8 matrix instructions
+  bool f8_mfma = true;
+  int lo_mask = 3;                // bf16 remainder of the norm outputs: 1 attention input, 2 MLP input            // fp8 weights: prefill Q/K/V and gate/up on fp8 matrix instructions
   // measurement hook: per-launch event pairs, labelled by step
   bool timing = false;
   std::vector<TimedLaunch> timed;
@@ -473,7 +474,9 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
   // context the last-token logits reach the whole 2e-2 error budget; the two
   // norm outputs are the largest of those rounding points that the bf16 KV
   // cache does not fix.
-  void* xn_lo = (m->wdt == DT_F8) ? nullptr : (char*)m->xn + (size_t)rows * c.hidden * 2;
+  void* xn_lo_buf = (m->wdt == DT_F8) ? nullptr : (char*)m->xn + (size_t)rows * c.hidden * 2;
+  void* xn_lo = (m->lo_mask & 1) ? xn_lo_buf : nullptr;          // attention input
+  void* xn_lo_mlp = (m->lo_mask & 2) ? xn_lo_buf : nullptr;      // MLP input
   // int8 / fp8 weights: each matrix's codes are widened to bf16 (exact) into
   // wconv just before its GEMM, and the row scales are applied per output column
   const bool q8 = (m->wdt == DT_I8 || m->wdt == DT_F8);
@@ -557,9 +560,9 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
     LAUNCH(m, "wconv", s, widen(L.wgu, (size_t)2 * c.ffn * c.hidden));
     wb = m->wconv;
   }
-  LAUNCH(m, "norm", s, norm_in(m, rows, L.mlp_norm, xn_lo, s));
+  LAUNCH(m, "norm", s, norm_in(m, rows, L.mlp_norm, xn_lo_mlp, s));
   LAUNCH(m, "gate_up", s, gemm_bf16(GEPI_SWIGLU_BF16, m->xn, c.hidden, wb, c.hidden, m->hbuf, c.ffn, rows,
-                                    2 * c.ffn, c.hidden, s, xn_lo, L.sgu));
+                                    2 * c.ffn, c.hidden, s, xn_lo_mlp, L.sgu));
   wb = L.wdown;
   if (q8) {
     LAUNCH(m, "wconv", s, widen(L.wdown, (size_t)c.hidden * c.ffn));
@@ -778,6 +781,8 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
     if (am != nullptr && std::strcmp(am, "onepass") == 0) m->attn_mode = 2;
     const char* fr = std::getenv("FS_PREFILL_FUSE_ROPE");
     if (fr != nullptr && fr[0] == '0') m->fuse_rope = false;
+    const char* lm = std::getenv("FS_GEMM_NORM_REMAINDER");
+    if (lm != nullptr && lm[0] >= '0' && lm[0] <= '3' && lm[1] == 0) m->lo_mask = lm[0] - '0';
     const char* f8 = std::getenv("FS_PREFILL_F8_MFMA");
     if (f8 != nullptr && f8[0] == '0') m->f8_mfma = false;
     const char* mc = std::getenv("FS_DECODE_MIN_CHUNK");

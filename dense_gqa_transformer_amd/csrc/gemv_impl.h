@@ -19,8 +19,9 @@
 // per load; each row's dot product is multiplied by its scale before the
 // epilogue.  With fp8 weights the RMSNorm-fused inputs (Q/K/V, gate/up, head)
 // are quantized too, per activation row in the prologue: scale = the smallest
-// power of two >= max|row| / 448, values rounded to the nearest e4m3 code,
-// the row's scale applied with the weight's in the epilogue.
+// power of two >= max|row| / 448, values rounded to the nearest e4m3 code
+// (the hardware conversion, which rounds as the library's quantizer does:
+// ties to even), the row's scale applied with the weight's in the epilogue.
 #pragma once
 #include <type_traits>
 
@@ -55,9 +56,15 @@ __device__ __forceinline__ void raw_load(const f8* p, Raw<f8>& r) {
   r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 __device__ __forceinline__ void raw_zero(Raw<f8>& r) { r.v = u32x4{0, 0, 0, 0}; }
+// e4m3 codes to fp32 with the hardware conversion, two codes per instruction
+// (exact; the library's codes are never the NaN pattern)
 __device__ __forceinline__ void raw_f32(const Raw<f8>& r, float* o) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) o[i] = f8_decode((r.v[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+  for (int i = 0; i < 4; ++i) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.v[i], false);   // bytes 0, 1
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.v[i], true);    // bytes 2, 3
+    o[4 * i] = lo[0]; o[4 * i + 1] = lo[1]; o[4 * i + 2] = hi[0]; o[4 * i + 3] = hi[1];
+  }
 }
 __device__ __forceinline__ void raw_zero(Raw<int8_t>& r) { r.v = u32x4{0, 0, 0, 0}; }
 __device__ __forceinline__ void raw_zero(Raw<bf16>& r) { r.v = u32x4{0, 0, 0, 0}; }
@@ -201,10 +208,24 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(const GemvParams p) 
           for (int e = 0; e < CE; ++e) amax = fmaxf(amax, fabsf(xv[m][j][e]));
         const float sc = f8_row_scale(wave_max(amax));
         asc[m] = sc;
+        // x / sc: a power-of-two scale of at least 2^-126 has an exact fp32
+        // reciprocal; below it (rows of magnitude under ~2^-117) divide
+        const bool recip = sc >= 1.17549435e-38f;
+        const float isc = recip ? 1.f / sc : 0.f;
+        // round to e4m3 and back with the hardware conversions (round to
+        // nearest even; |x / sc| <= 448, so nothing saturates; a negative
+        // value that rounds to zero becomes -0, the same value)
 #pragma unroll
         for (int j = 0; j < CPL; ++j)
 #pragma unroll
-          for (int e = 0; e < CE; ++e) xv[m][j][e] = sc > 0.f ? f8_decode(f8_encode(xv[m][j][e] / sc)) : 0.f;
+          for (int e = 0; e < CE; e += 2) {
+            float q0 = recip ? xv[m][j][e] * isc : (sc > 0.f ? xv[m][j][e] / sc : 0.f);
+            float q1 = recip ? xv[m][j][e + 1] * isc : (sc > 0.f ? xv[m][j][e + 1] / sc : 0.f);
+            const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+            const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false);
+            xv[m][j][e] = d[0];
+            xv[m][j][e + 1] = d[1];
+          }
       }
     }
   } else {

@@ -130,6 +130,9 @@ typedef struct fs_model fs_model;
  * FS_DECODE_MIN_CHUNK=32|64|128|256 sets the shortest split-K chunk;
  * FS_PREFILL_FUSE_ROPE=0 keeps the per-head q/k norm + RoPE + K/V write of a
  * large prefill in a pass of its own instead of the QKV GEMM's epilogue;
+ * FS_GEMM_NORM_REMAINDER=0..3 selects which normalised inputs of the MFMA
+ * (bf16) block carry a bf16 remainder pass (1 attention input, 2 MLP input;
+ * default 3, both);
  * FS_PREFILL_F8_MFMA=0 keeps an FS_WEIGHTS_F8_ROW model's prefill on widened
  * (bf16) weights instead of the fp8 matrix instructions (the same values:
  * code * scale is exact in bf16);
