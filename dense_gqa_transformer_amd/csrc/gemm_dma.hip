@@ -163,7 +163,26 @@ void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict
   // its own 16 KB of LDS and writes whole rows.
   __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
   lds_barrier();
-  dma_epilogue<EPI>(acc, tid, m0, n0, M, N, out, ldc, colscale, nullptr, rp);
+  if constexpr (EPI == GEPI_QKV_ROPE) {
+    // (kept inline: through the shared epilogue the compiler spills here)
+    if (colscale != nullptr) {
+      const int hl = lane >> 5, ncol0 = n0 + wn * 64;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = min(ncol0 + 32 * j + 8 * g + 4 * hl, N - 4);
+          const f32x4 sc = *reinterpret_cast<const f32x4*>(colscale + n);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[j][i][4 * g + e] *= sc[e];
+        }
+    }
+    qkv_rope_epilogue(rp, acc, m0, n0, M, tid);
+  } else {
+    dma_epilogue<EPI, false>(acc, tid, m0, n0, M, N, out, ldc, colscale, nullptr, rp);
+  }
 }
 
 // Usable when K is a multiple of 128, rows are 16-B aligned and the problem

@@ -154,7 +154,7 @@ __device__ __forceinline__ void qkv_rope_epilogue(const RopeKvParams& p, const f
 // per-column (weight row) and per-row (activation row) scales, then the
 // store form EPI.  Columns / rows past N / M are computed on clamped reads and
 // never stored.
-template <int EPI>
+template <int EPI, bool ROWSCALE>
 __device__ __forceinline__ void dma_epilogue(f32x16 (&acc)[2][4], int tid, int m0, int n0, int M, int N,
                                              void* __restrict__ out, int ldc, const float* __restrict__ colscale,
                                              const float* __restrict__ rowscale, const RopeKvParams& rp) {
@@ -166,7 +166,7 @@ __device__ __forceinline__ void dma_epilogue(f32x16 (&acc)[2][4], int tid, int m
   const int hl = lane >> 5;
   const int mrow0 = m0 + wm * 128;
   const int ncol0 = n0 + wn * 64;
-  if (rowscale != nullptr) {
+  if constexpr (ROWSCALE) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float sa = rowscale[min(mrow0 + i * 32 + lrow, M - 1)];

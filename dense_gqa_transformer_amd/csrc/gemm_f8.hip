@@ -175,7 +175,7 @@ void gemm_f8_kernel(const uint8_t* __restrict__ A, int lda, const uint8_t* __res
 
   __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
   lds_barrier();
-  dma_epilogue<EPI>(acc, tid, m0, n0, M, N, out, ldc, colscale, rowscale, rp);
+  dma_epilogue<EPI, true>(acc, tid, m0, n0, M, N, out, ldc, colscale, rowscale, rp);
 }
 
 bool gemm_f8_ok(int epi, const void* A, int lda, const void* B, int ldb, const void* out, int ldc, int M, int N,

@@ -71,12 +71,16 @@ def test_shape_parity(name):
     prompts = synth.tokens(seed, shape.vocab, (2, S))
     print(f"shape case {name} seed {seed}", flush=True)
     m = make_model(shape, max_seqs=12, max_ctx=160)
+    errs = []
+
+    def check(got, ref, tol, what):
+        errs.append(check_logits(got, ref, tol, what))
     try:
         orcs = [O.Oracle(shape, weights(shape)) for _ in range(2)]
         lg = m.prefill(dev_tokens(prompts), [0, 1]).cpu().numpy()
         refs = [orcs[i].prefill(0, prompts[i]) for i in range(2)]
         for i in range(2):
-            check_logits(lg[i], refs[i], tol, f"{name} prefill row {i}")
+            check(lg[i], refs[i], tol, f"{name} prefill row {i}")
         # teacher-forced decode at batch 2
         out = torch.empty((2, shape.vocab), dtype=torch.float32, device="cuda")
         for k in range(4):
@@ -85,7 +89,7 @@ def test_shape_parity(name):
             got = out.cpu().numpy()
             refs = [orcs[i].decode_step(0, toks[i], S + k) for i in range(2)]
             for i in range(2):
-                check_logits(got[i], refs[i], tol, f"{name} decode {k} row {i}")
+                check(got[i], refs[i], tol, f"{name} decode {k} row {i}")
         # one-token prompts in ten more slots, then one step over all twelve
         singles = synth.tokens(seed + 50, shape.vocab, (10, 1))
         lg1 = m.prefill(dev_tokens(singles), list(range(2, 12))).cpu().numpy()
@@ -93,7 +97,7 @@ def test_shape_parity(name):
         for i in range(10):
             o = O.Oracle(shape, weights(shape))
             r = o.prefill(0, singles[i])
-            check_logits(lg1[i], r, tol, f"{name} one-token prompt {i}")
+            check(lg1[i], r, tol, f"{name} one-token prompt {i}")
             o1.append((o, O.greedy_argmax(r)))
         toks = [O.greedy_argmax(r) for r in refs] + [t for _, t in o1]
         pos = [S + 4, S + 4] + [1] * 10
@@ -101,8 +105,9 @@ def test_shape_parity(name):
         m.decode_step(dev_tokens(toks), pos, list(range(12)), logits=out12)
         got = out12.cpu().numpy()
         for i in range(2):
-            check_logits(got[i], orcs[i].decode_step(0, toks[i], S + 4), tol, f"{name} B=12 row {i}")
+            check(got[i], orcs[i].decode_step(0, toks[i], S + 4), tol, f"{name} B=12 row {i}")
         for i, (o, t) in enumerate(o1):
-            check_logits(got[2 + i], o.decode_step(0, t, 1), tol, f"{name} B=12 row {2 + i}")
+            check(got[2 + i], o.decode_step(0, t, 1), tol, f"{name} B=12 row {2 + i}")
+        print(f"shape case {name}: max-abs logit error {max(errs):.3e} (bound {tol:.1e})", flush=True)
     finally:
         m.close()
