@@ -61,6 +61,10 @@ struct LayerW {
   float *attn_norm, *q_norm, *k_norm, *mlp_norm;
   // int8 weights: one scale per weight row (null otherwise)
   float *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sdown = nullptr;
+  // bf16 models: an fp8 (e4m3, power-of-two row scale) copy of the Q/K/V and
+  // gate/up weights for the remainder pass of the large prefill GEMMs
+  uint8_t *w8qkv = nullptr, *w8gu = nullptr;
+  float *s8qkv = nullptr, *s8gu = nullptr;
 };
 
 struct DecodeKey {
@@ -107,6 +111,9 @@ struct fs_model {
   float* nblob = nullptr;
   float* sblob = nullptr;         // int8 row scales
   void* wconv = nullptr;          // bf16 copy of one layer matrix's codes (MFMA operand)
+  void* w8blob = nullptr;         // fp8 copies of the Q/K/V and gate/up weights (bf16 models)
+  float* s8blob = nullptr;        // their row scales
+  bool lo8 = false;               // remainder passes of the large GEMMs on fp8 operands
   void* embed = nullptr;
   float* embed_scale = nullptr;
   float* final_norm = nullptr;
@@ -194,6 +201,7 @@ struct fs_model {
     for (auto& t : timed) { hipEventDestroy(t.a); hipEventDestroy(t.b); }
     for (auto e : ev_free) hipEventDestroy(e);
     hipFree(wblob); hipFree(nblob); hipFree(sblob); hipFree(wconv); hipFree(kcache); hipFree(vcache);
+    hipFree(w8blob); hipFree(s8blob);
     hipFree(rope_cos); hipFree(rope_sin);
     hipFree(x); hipFree(xn); hipFree(qkv); hipFree(qr); hipFree(attn); hipFree(hbuf); hipFree(ascale);
     hipFree(d_pos); hipFree(part); hipFree(kpart);
@@ -392,17 +400,25 @@ hipError_t resid_proj(fs_model* m, const void* A, int lda, const void* W, int ro
 // partials.  fp8 weights: xn holds the quantized rows, as exact bf16 values of
 // code * power-of-two scale (codes = false) or as the e4m3 codes themselves
 // with the scales in m->ascale (codes = true), and no remainder.
-hipError_t norm_in(fs_model* m, int rows, const float* gamma, void* lo, hipStream_t s, bool codes = false) {
+hipError_t norm_in(fs_model* m, int rows, const float* gamma, void* lo, hipStream_t s, bool codes = false,
+                   bool lo8 = false) {
   const fs_config& c = m->cfg;
   float* qs = (m->wdt == DT_F8) ? m->ascale : nullptr;
   if (qs != nullptr) lo = nullptr;
   const int odt = (qs != nullptr && codes) ? DT_F8 : DT_BF16;
+  // lo8: the remainder as e4m3 codes (uint8 [rows, hidden] at lo) with its row
+  // scales in m->ascale
+  int lo_dt = DT_BF16;
+  if (lo8 && lo != nullptr && qs == nullptr) {
+    qs = m->ascale;
+    lo_dt = DT_F8;
+  }
   if (m->pend_np == 0)
-    return rmsnorm(m->x, rows, c.hidden, c.hidden, gamma, c.rms_eps, m->xn, odt, c.hidden, s, lo, qs);
+    return rmsnorm(m->x, rows, c.hidden, c.hidden, gamma, c.rms_eps, m->xn, odt, c.hidden, s, lo, qs, lo_dt);
   const int np = m->pend_np;
   m->pend_np = 0;
   return rmsnorm_add(m->x, m->kpart, np, rows, c.hidden, c.hidden, gamma, c.rms_eps, m->xn, odt, c.hidden, s,
-                     lo, qs);
+                     lo, qs, lo_dt);
 }
 
 // A GEMV over p.M rows; with fp8 weights the quantizing form (the
@@ -473,7 +489,10 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
   // tiles): with plain bf16 operands at every GEMM input and a 4096-token
   // context the last-token logits reach the whole 2e-2 error budget; the two
   // norm outputs are the largest of those rounding points that the bf16 KV
-  // cache does not fix.
+  // cache does not fix.  On the large GEMM (prefill) the remainder is stored
+  // as e4m3 codes with a row scale and multiplied by the fp8 copy of the
+  // weights (lo8): twice the K per stage of a bf16 pass, so half its cost, and
+  // the remainder (~2^-9 of the value) keeps ~2^-4 relative accuracy.
   void* xn_lo_buf = (m->wdt == DT_F8) ? nullptr : (char*)m->xn + (size_t)rows * c.hidden * 2;
   void* xn_lo = (m->lo_mask & 1) ? xn_lo_buf : nullptr;          // attention input
   void* xn_lo_mlp = (m->lo_mask & 2) ? xn_lo_buf : nullptr;      // MLP input
@@ -520,7 +539,10 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
     LAUNCH(m, "wconv", s, widen(L.wqkv, (size_t)m->qkv_w * c.hidden));
     wb = m->wconv;
   }
-  LAUNCH(m, "norm", s, norm_in(m, rows, L.attn_norm, xn_lo, s));
+  const bool lo8_qkv = !q8 && m->lo8 && xn_lo != nullptr && !qkv_f32 &&
+                       gemm_dma_ok(GEPI_STORE_F32, m->xn, c.hidden, L.wqkv, c.hidden, m->qkv, m->qkv_w, rows,
+                                   m->qkv_w, c.hidden, nullptr);
+  LAUNCH(m, "norm", s, norm_in(m, rows, L.attn_norm, xn_lo, s, false, lo8_qkv));
   // decode (fp32 q/k/v): the few-row form splits K in two and the attention
   // sums the partials as it loads q/k/v (not for the gated variant, whose gate
   // rows are read from m->qkv afterwards)
@@ -534,6 +556,16 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
                                     m->qkv_w, c.hidden, s, xn_lo, L.sqkv, qks));
     m->qkv_src = m->kpart;
     m->qkv_np = qks;
+  } else if (lo8_qkv) {
+    const Lo8Params l8{(const uint8_t*)xn_lo, m->ascale, L.w8qkv, L.s8qkv};
+    if (rope != nullptr && m->fuse_rope && gemm_dma_rope_ok(*rope, rows, m->qkv_w)) {
+      LAUNCH(m, "qkv", s, gemm_dma(GEPI_QKV_ROPE, m->xn, c.hidden, wb, c.hidden, nullptr, 0, rows, m->qkv_w,
+                                   c.hidden, s, nullptr, L.sqkv, rope, &l8));
+      if (rope_done != nullptr) *rope_done = true;
+    } else {
+      LAUNCH(m, "qkv", s, gemm_dma(GEPI_STORE_F32, m->xn, c.hidden, wb, c.hidden, m->qkv, m->qkv_w, rows,
+                                   m->qkv_w, c.hidden, s, nullptr, L.sqkv, nullptr, &l8));
+    }
   } else if (rope != nullptr && m->fuse_rope && !qkv_f32 &&
              gemm_dma_ok(GEPI_QKV_ROPE, m->xn, c.hidden, wb, c.hidden, nullptr, 0, rows, m->qkv_w, c.hidden,
                          xn_lo) &&
@@ -560,9 +592,18 @@ fs_status block_gemm(fs_model* m, const LayerW& L, int rows, bool qkv_f32, Attn&
     LAUNCH(m, "wconv", s, widen(L.wgu, (size_t)2 * c.ffn * c.hidden));
     wb = m->wconv;
   }
-  LAUNCH(m, "norm", s, norm_in(m, rows, L.mlp_norm, xn_lo_mlp, s));
-  LAUNCH(m, "gate_up", s, gemm_bf16(GEPI_SWIGLU_BF16, m->xn, c.hidden, wb, c.hidden, m->hbuf, c.ffn, rows,
-                                    2 * c.ffn, c.hidden, s, xn_lo_mlp, L.sgu));
+  const bool lo8_gu = !q8 && m->lo8 && xn_lo_mlp != nullptr &&
+                      gemm_dma_ok(GEPI_SWIGLU_BF16, m->xn, c.hidden, L.wgu, c.hidden, m->hbuf, c.ffn, rows,
+                                  2 * c.ffn, c.hidden, nullptr);
+  LAUNCH(m, "norm", s, norm_in(m, rows, L.mlp_norm, xn_lo_mlp, s, false, lo8_gu));
+  if (lo8_gu) {
+    const Lo8Params l8{(const uint8_t*)xn_lo_mlp, m->ascale, L.w8gu, L.s8gu};
+    LAUNCH(m, "gate_up", s, gemm_dma(GEPI_SWIGLU_BF16, m->xn, c.hidden, wb, c.hidden, m->hbuf, c.ffn, rows,
+                                     2 * c.ffn, c.hidden, s, nullptr, L.sgu, nullptr, &l8));
+  } else {
+    LAUNCH(m, "gate_up", s, gemm_bf16(GEPI_SWIGLU_BF16, m->xn, c.hidden, wb, c.hidden, m->hbuf, c.ffn, rows,
+                                      2 * c.ffn, c.hidden, s, xn_lo_mlp, L.sgu));
+  }
   wb = L.wdown;
   if (q8) {
     LAUNCH(m, "wconv", s, widen(L.wdown, (size_t)c.hidden * c.ffn));
@@ -729,6 +770,31 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
     chk(convert_f32(src.k_norm, m->dt, L.k_norm, c.head_dim, s));
   }
   if (e != hipSuccess) return bail(FS_ERR_HIP, std::string("weight repack failed: ") + hipGetErrorString(e));
+
+  // bf16 models: fp8 copies of the Q/K/V and gate/up weights, the operands of
+  // the large GEMMs' remainder pass (FS_GEMM_REMAINDER_F8=0 keeps that pass in bf16)
+  {
+    const char* r8 = std::getenv("FS_GEMM_REMAINDER_F8");
+    m->lo8 = m->dt == DT_BF16 && m->wdt == DT_BF16 && H % 64 == 0 && !(r8 != nullptr && r8[0] == '0');
+  }
+  if (m->lo8) {
+    const size_t b8 = ((size_t)m->qkv_w * H + 2 * I * H) * c.n_layers;
+    const size_t f8 = (rup(m->qkv_w) + rup(2 * I)) * c.n_layers;
+    if (dalloc(&m->w8blob, b8) != hipSuccess || dalloc(&m->s8blob, f8 * 4) != hipSuccess)
+      return bail(FS_ERR_OOM, "fp8 weight copy allocation failed");
+    uint8_t* bp = (uint8_t*)m->w8blob;
+    float* fp = m->s8blob;
+    for (int l = 0; l < c.n_layers; ++l) {
+      LayerW& L = m->layers[l];
+      L.w8qkv = bp; bp += (size_t)m->qkv_w * H;
+      L.s8qkv = fp; fp += rup(m->qkv_w);
+      L.w8gu = bp; bp += 2 * I * H;
+      L.s8gu = fp; fp += rup(2 * I);
+      chk(quantize_rows_f8(L.wqkv, DT_BF16, m->qkv_w, (int)H, L.w8qkv, L.s8qkv, s));
+      chk(quantize_rows_f8(L.wgu, DT_BF16, 2 * (int)I, (int)H, L.w8gu, L.s8gu, s));
+    }
+    if (e != hipSuccess) return bail(FS_ERR_HIP, std::string("fp8 weight copy failed: ") + hipGetErrorString(e));
+  }
 
   // KV cache
   m->head_stride = (long long)c.max_ctx * c.head_dim;

@@ -34,15 +34,20 @@ hipError_t f8codes_to_bf16(const uint8_t* codes, size_t n, void* dst, hipStream_
 // qs (optional): the fp8 activation rule instead -- qs[t] = the row's
 // power-of-two scale and out = its e4m3 codes (out_dt DT_F8) or the exact
 // bf16 values code * scale (DT_BF16).
+// lo_dt DT_F8 (with lo and qs): out = bf16(y) and the remainder y - out as e4m3
+// codes in lo (uint8, row stride ldo) with qs[t] = the remainder row's
+// power-of-two scale (the smallest >= max|remainder| / 448).
 hipError_t rmsnorm(const float* x, int T, int H, int ldx, const float* g, float eps,
-                   void* out, int out_dt, int ldo, hipStream_t s, void* lo = nullptr, float* qs = nullptr);
+                   void* out, int out_dt, int ldo, hipStream_t s, void* lo = nullptr, float* qs = nullptr,
+                   int lo_dt = DT_BF16);
 // The same after adding np (<= RMSNORM_MAX_PARTS) split-K partials to the residual rows:
 // x[t, :] += parts[0][t, :] + ... + parts[np-1][t, :] (in that order; parts is
 // [np][T][H] dense), written back to x, then normalised into out as above.
 // out may be null (the additions only).
 constexpr int RMSNORM_MAX_PARTS = 16;
 hipError_t rmsnorm_add(float* x, const float* parts, int np, int T, int H, int ldx, const float* g, float eps,
-                       void* out, int out_dt, int ldo, hipStream_t s, void* lo = nullptr, float* qs = nullptr);
+                       void* out, int out_dt, int ldo, hipStream_t s, void* lo = nullptr, float* qs = nullptr,
+                       int lo_dt = DT_BF16);
 // dst[i] = float(src[i])
 hipError_t convert_f32(const void* src, int dt, float* dst, size_t n, hipStream_t s);
 // A one-wave kernel that waits about `us` microseconds of device wall clock.
@@ -108,9 +113,19 @@ bool gemm_dma_ok(int epi, const void* A, int lda, const void* B, int ldb, const 
                  int M, int N, int K, const void* A_lo);
 struct RopeKvParams;
 bool gemm_dma_rope_ok(const RopeKvParams& r, int M, int N);
+// The remainder pass of gemm_dma on fp8 operands (instead of A_lo): a [M, K]
+// e4m3 codes of the activation remainder with power-of-two row scales as[M],
+// b [N, K] an fp8 copy of the weights with row scales bs[N]; the kernel adds
+// diag(as) . (a . b^T) . diag(bs) into the same fp32 tile.  K % 64 == 0,
+// 16-B aligned code rows.
+struct Lo8Params {
+  const uint8_t* a; const float* as;
+  const uint8_t* b; const float* bs;
+};
 hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, void* out, int ldc,
                     int M, int N, int K, hipStream_t s, const void* A_lo, const float* colscale,
-                    const RopeKvParams* rope = nullptr);
+                    const RopeKvParams* rope = nullptr,
+                    const Lo8Params* lo8 = nullptr);
 // fp8 (e4m3) form of gemm_dma for the fp8 weight option: A [M, K] and B
 // [N, K] are e4m3 codes, K contiguous (lda, ldb in bytes, multiples of 16; K a
 // multiple of 64), C = diag(rowscale) . (A . B^T) . diag(colscale) in fp32

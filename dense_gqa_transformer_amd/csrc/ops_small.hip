@@ -311,11 +311,43 @@ __device__ __forceinline__ void quant_store(const float* y, float sc, int c, O* 
   }
 }
 
-template <typename O, int MAXJ, bool QUANT>
+// bf16 value + fp8 remainder of a normalised row (the remainder form that an
+// fp8 second product pass takes): hi = bf16(y), codes = e4m3((y - hi) * isc)
+// with the hardware conversion (round to nearest even; |(y - hi) * isc| <= 448
+// by the choice of the row's scale 1 / isc).
+__device__ __forceinline__ void lo8_store(const float* y, float isc, int c, bf16* o, uint8_t* lo) {
+  bf16x4 hi;
+  float r[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hi[e] = (bf16)y[e];
+    r[e] = (y[e] - (float)hi[e]) * isc;
+  }
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], w, true);
+  *reinterpret_cast<bf16x4*>(o + 4 * c) = hi;
+  *reinterpret_cast<int*>(lo + 4 * c) = w;
+}
+__device__ __forceinline__ float lo8_amax(const float* y) {
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a = fmaxf(a, fabsf(y[e] - (float)(bf16)y[e]));
+  return a;
+}
+// 1 / scale when the scale has an exact fp32 reciprocal, else 0 (a remainder
+// below ~2^-117 of a row is dropped)
+__device__ __forceinline__ float lo8_inv(float sc) { return sc >= 1.17549435e-38f ? 1.f / sc : 0.f; }
+
+// MODE 0: plain (optional bf16 remainder in lo); 1: the fp8 activation rule
+// (codes or code * scale in out, scales in qs); 2: bf16 value in out, fp8
+// remainder codes in lo (uint8, row stride ldo), remainder scales in qs.
+template <typename O, int MAXJ, int MODE>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int T, int H, int ldx,
                                                       const float* __restrict__ g, float eps,
-                                                      O* __restrict__ out, O* __restrict__ lo, int ldo,
+                                                      O* __restrict__ out, void* __restrict__ lo_, int ldo,
                                                       float* __restrict__ qs) {
+  constexpr bool QUANT = (MODE == 1);
+  O* lo = reinterpret_cast<O*>(lo_);
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= T) return;
@@ -332,6 +364,32 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
   const float inv = rsqrtf(wave_sum(ss) / (float)H + eps);
   O* o = out + (size_t)r * ldo;
+  if constexpr (MODE == 2) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nc) {
+        const f32x4 gg = *reinterpret_cast<const f32x4*>(g + 4 * c);
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[j][e] = v[j][e] * inv * gg[e]; y[e] = v[j][e]; }
+        amax = fmaxf(amax, lo8_amax(y));
+      }
+    }
+    const float sc = f8_row_scale(wave_max(amax));
+    if (lane == 0) qs[r] = sc;
+    const float isc = lo8_inv(sc);
+    uint8_t* l8 = reinterpret_cast<uint8_t*>(lo_) + (size_t)r * ldo;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int c = lane + 64 * j;
+      if (c >= nc) break;
+      const float y[4] = {v[j][0], v[j][1], v[j][2], v[j][3]};
+      lo8_store(y, isc, c, reinterpret_cast<bf16*>(o), l8);
+    }
+    return;
+  }
   if constexpr (QUANT) {
     float amax = 0.f;
 #pragma unroll
@@ -368,12 +426,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 // together, the partials are added in order 0..np-1 (so the result does not
 // depend on launch timing) and the row is written back before it is
 // normalised (out == nullptr: the additions only).
-template <typename O, bool QUANT>
+template <typename O, int MODE>
 __global__ __launch_bounds__(256) void rmsnorm_add_kernel(float* __restrict__ x, int T, int H, int ldx,
                                                           const float* __restrict__ g, float eps,
-                                                          O* __restrict__ out, O* __restrict__ lo, int ldo,
+                                                          O* __restrict__ out, void* __restrict__ lo_, int ldo,
                                                           const float* __restrict__ parts, int np,
                                                           float* __restrict__ qs) {
+  constexpr bool QUANT = (MODE == 1);
+  O* lo = reinterpret_cast<O*>(lo_);
   constexpr int MAXC = 4;                          // H <= 4096
   __shared__ float red[4], redm[4];
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -408,6 +468,36 @@ __global__ __launch_bounds__(256) void rmsnorm_add_kernel(float* __restrict__ x,
   __syncthreads();
   const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
   O* o = out + (size_t)r * ldo;
+  if constexpr (MODE == 2) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int c = tid + 256 * j;
+      if (c < nc) {
+        const f32x4 gg = *reinterpret_cast<const f32x4*>(g + 4 * c);
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[j][e] = v[j][e] * inv * gg[e]; y[e] = v[j][e]; }
+        amax = fmaxf(amax, lo8_amax(y));
+      }
+    }
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) redm[tid >> 6] = amax;
+    __syncthreads();
+    const float sc = f8_row_scale(fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3])));
+    if (tid == 0) qs[r] = sc;
+    const float isc = lo8_inv(sc);
+    uint8_t* l8 = reinterpret_cast<uint8_t*>(lo_) + (size_t)r * ldo;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      const int c = tid + 256 * j;
+      if (c < nc) {
+        const float y[4] = {v[j][0], v[j][1], v[j][2], v[j][3]};
+        lo8_store(y, isc, c, reinterpret_cast<bf16*>(o), l8);
+      }
+    }
+    return;
+  }
   if constexpr (QUANT) {
     float amax = 0.f;
 #pragma unroll
@@ -443,44 +533,51 @@ __global__ __launch_bounds__(256) void rmsnorm_add_kernel(float* __restrict__ x,
 }
 
 hipError_t rmsnorm(const float* x, int T, int H, int ldx, const float* g, float eps, void* out,
-                   int out_dt, int ldo, hipStream_t s, void* lo, float* qs) {
+                   int out_dt, int ldo, hipStream_t s, void* lo, float* qs, int lo_dt) {
   if (T <= 0) return hipSuccess;
   if (out == nullptr || H % 4 != 0 || H > 4096 || ldx % 4 != 0 || ldo % 4 != 0) return hipErrorInvalidValue;
   const int blocks = (T + 3) / 4;
-  if (qs != nullptr) {                                 // fp8 activation rule
+  if (lo_dt == DT_F8) {                                // bf16 value + fp8 remainder
+    if (lo == nullptr || qs == nullptr || g == nullptr || out_dt != DT_BF16) return hipErrorInvalidValue;
+    rmsnorm_kernel<bf16, 16, 2><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, lo, ldo, qs);
+  } else if (qs != nullptr) {                          // fp8 activation rule
     if (lo != nullptr || g == nullptr) return hipErrorInvalidValue;
     if (out_dt == DT_BF16)
-      rmsnorm_kernel<bf16, 16, true><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, nullptr, ldo, qs);
+      rmsnorm_kernel<bf16, 16, 1><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, nullptr, ldo, qs);
     else if (out_dt == DT_F8)
-      rmsnorm_kernel<uint8_t, 16, true><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (uint8_t*)out, nullptr, ldo, qs);
+      rmsnorm_kernel<uint8_t, 16, 1><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (uint8_t*)out, nullptr, ldo, qs);
     else
       return hipErrorInvalidValue;
   } else if (out_dt == DT_BF16)
-    rmsnorm_kernel<bf16, 16, false><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, (bf16*)lo, ldo, nullptr);
+    rmsnorm_kernel<bf16, 16, 0><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, lo, ldo, nullptr);
   else if (lo == nullptr)
-    rmsnorm_kernel<float, 16, false><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (float*)out, nullptr, ldo, nullptr);
+    rmsnorm_kernel<float, 16, 0><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (float*)out, nullptr, ldo, nullptr);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t rmsnorm_add(float* x, const float* parts, int np, int T, int H, int ldx, const float* g, float eps,
-                       void* out, int out_dt, int ldo, hipStream_t s, void* lo, float* qs) {
+                       void* out, int out_dt, int ldo, hipStream_t s, void* lo, float* qs, int lo_dt) {
   if (T <= 0) return hipSuccess;
   if (np <= 0 || np > RMSNORM_MAX_PARTS || parts == nullptr) return hipErrorInvalidValue;
   if (H % 4 != 0 || H > 4096 || ldx % 4 != 0 || ldo % 4 != 0) return hipErrorInvalidValue;
-  if (qs != nullptr) {                                 // fp8 activation rule
+  if (lo_dt == DT_F8) {                                // bf16 value + fp8 remainder
+    if (lo == nullptr || qs == nullptr || g == nullptr || out == nullptr || out_dt != DT_BF16)
+      return hipErrorInvalidValue;
+    rmsnorm_add_kernel<bf16, 2><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, lo, ldo, parts, np, qs);
+  } else if (qs != nullptr) {                          // fp8 activation rule
     if (lo != nullptr || g == nullptr || out == nullptr) return hipErrorInvalidValue;
     if (out_dt == DT_BF16)
-      rmsnorm_add_kernel<bf16, true><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, nullptr, ldo, parts, np, qs);
+      rmsnorm_add_kernel<bf16, 1><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, nullptr, ldo, parts, np, qs);
     else if (out_dt == DT_F8)
-      rmsnorm_add_kernel<uint8_t, true><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (uint8_t*)out, nullptr, ldo, parts, np, qs);
+      rmsnorm_add_kernel<uint8_t, 1><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (uint8_t*)out, nullptr, ldo, parts, np, qs);
     else
       return hipErrorInvalidValue;
   } else if (out_dt == DT_BF16)
-    rmsnorm_add_kernel<bf16, false><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, (bf16*)lo, ldo, parts, np, nullptr);
+    rmsnorm_add_kernel<bf16, 0><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, lo, ldo, parts, np, nullptr);
   else if (lo == nullptr)
-    rmsnorm_add_kernel<float, false><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (float*)out, nullptr, ldo, parts, np, nullptr);
+    rmsnorm_add_kernel<float, 0><<<T, 256, 0, s>>>(x, T, H, ldx, g, eps, (float*)out, nullptr, ldo, parts, np, nullptr);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

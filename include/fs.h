@@ -119,7 +119,9 @@ typedef struct fs_model fs_model;
 
 /* Creates a model on the current device.  Synchronous: copies and repacks
  * the weights into library-owned device memory (fused QKV, paired gate/up),
- * so the caller may free its tensors on return.  Allocates the KV cache
+ * so the caller may free its tensors on return (a bf16 model also keeps an
+ * fp8 copy of its Q/K/V and gate/up matrices, half their bf16 bytes, for the
+ * remainder pass of large prefills).  Allocates the KV cache
  * (max_seqs * max_ctx positions per layer) and the RoPE tables.  All slots
  * start empty.  *out receives the handle (NULL on error).
  * Environment read here, for measurement and tests (results agree to
@@ -132,7 +134,9 @@ typedef struct fs_model fs_model;
  * large prefill in a pass of its own instead of the QKV GEMM's epilogue;
  * FS_GEMM_NORM_REMAINDER=0..3 selects which normalised inputs of the MFMA
  * (bf16) block carry a bf16 remainder pass (1 attention input, 2 MLP input;
- * default 3, both);
+ * default 3, both); FS_GEMM_REMAINDER_F8=0 keeps those passes in bf16 on the
+ * large prefill GEMM too (by default there they run on fp8 copies of the
+ * remainder and of the Q/K/V and gate/up weights, at half the cost);
  * FS_PREFILL_F8_MFMA=0 keeps an FS_WEIGHTS_F8_ROW model's prefill on widened
  * (bf16) weights instead of the fp8 matrix instructions (the same values:
  * code * scale is exact in bf16);
