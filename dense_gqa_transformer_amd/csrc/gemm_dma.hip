@@ -50,16 +50,13 @@ template <int EPI, bool LO8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ A_lo,
                   const bf16* __restrict__ B, int ldb, void* __restrict__ out, int ldc,
-                  int M, int N, int K, int tiles_n, int nblocks, const float* __restrict__ colscale,
+                  int M, int N, int K, int tiles_n, int nblocks, int gm, const float* __restrict__ colscale,
                   const RopeKvParams rp, const Lo8Params l8) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid >> 2, wn = wid & 3;
-  // XCD-aware renumbering: the hardware deals workgroups round-robin over the
-  // 8 XCDs; consecutive tiles (sharing A rows / B rows) go to one XCD's L2.
-  int bid = blockIdx.x;
-  if ((nblocks & 7) == 0) bid = (bid & 7) * (nblocks >> 3) + (bid >> 3);
-  const int n0 = (bid % tiles_n) * TILE, m0 = (bid / tiles_n) * TILE;
+  int m0, n0;
+  tile_origin(nblocks, tiles_n, gm, m0, n0);
 
   // DMA assignment: wave w, instruction j fills tile rows (2w + j)*16 + lane/4
   // (chunk slot lane % 4) of A and of B.  Rows past M / N re-read the last
@@ -328,7 +325,7 @@ void gemm_dma_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict
     }
     qkv_rope_epilogue(rp, acc, m0, n0, M, tid);
   } else {
-    dma_epilogue<EPI, false>(acc, tid, m0, n0, M, N, out, ldc, colscale, nullptr, rp);
+    dma_epilogue<EPI>(acc, tid, m0, n0, M, N, out, ldc, colscale, nullptr, rp);
   }
 }
 
@@ -370,19 +367,20 @@ hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, voi
   }
   const int tn = (N + TILE - 1) / TILE, tm = (M + TILE - 1) / TILE;
   const int nb = tn * tm;
+  const int gm = gemm_tile_group();
   const bf16* a = (const bf16*)A;
   const bf16* b = (const bf16*)B;
   const bf16* al = (const bf16*)A_lo;
   if (lo8 != nullptr) {
     switch (epi) {
       case GEPI_SWIGLU_BF16:
-        gemm_dma_kernel<GEPI_SWIGLU_BF16, true><<<nb, 512, 0, s>>>(a, lda, nullptr, b, ldb, out, ldc, M, N, K, tn, nb, colscale, rp, l8);
+        gemm_dma_kernel<GEPI_SWIGLU_BF16, true><<<nb, 512, 0, s>>>(a, lda, nullptr, b, ldb, out, ldc, M, N, K, tn, nb, gm, colscale, rp, l8);
         break;
       case GEPI_STORE_F32:
-        gemm_dma_kernel<GEPI_STORE_F32, true><<<nb, 512, 0, s>>>(a, lda, nullptr, b, ldb, out, ldc, M, N, K, tn, nb, colscale, rp, l8);
+        gemm_dma_kernel<GEPI_STORE_F32, true><<<nb, 512, 0, s>>>(a, lda, nullptr, b, ldb, out, ldc, M, N, K, tn, nb, gm, colscale, rp, l8);
         break;
       case GEPI_QKV_ROPE:
-        gemm_dma_kernel<GEPI_QKV_ROPE, true><<<nb, 512, 0, s>>>(a, lda, nullptr, b, ldb, out, ldc, M, N, K, tn, nb, colscale, rp, l8);
+        gemm_dma_kernel<GEPI_QKV_ROPE, true><<<nb, 512, 0, s>>>(a, lda, nullptr, b, ldb, out, ldc, M, N, K, tn, nb, gm, colscale, rp, l8);
         break;
       default:
         return hipErrorInvalidValue;
@@ -391,19 +389,19 @@ hipError_t gemm_dma(int epi, const void* A, int lda, const void* B, int ldb, voi
   }
   switch (epi) {
     case GEPI_STORE_BF16:
-      gemm_dma_kernel<GEPI_STORE_BF16, false><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale, rp, l8);
+      gemm_dma_kernel<GEPI_STORE_BF16, false><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, gm, colscale, rp, l8);
       break;
     case GEPI_RESID_F32:
-      gemm_dma_kernel<GEPI_RESID_F32, false><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale, rp, l8);
+      gemm_dma_kernel<GEPI_RESID_F32, false><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, gm, colscale, rp, l8);
       break;
     case GEPI_SWIGLU_BF16:
-      gemm_dma_kernel<GEPI_SWIGLU_BF16, false><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale, rp, l8);
+      gemm_dma_kernel<GEPI_SWIGLU_BF16, false><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, gm, colscale, rp, l8);
       break;
     case GEPI_STORE_F32:
-      gemm_dma_kernel<GEPI_STORE_F32, false><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale, rp, l8);
+      gemm_dma_kernel<GEPI_STORE_F32, false><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, gm, colscale, rp, l8);
       break;
     case GEPI_QKV_ROPE:
-      gemm_dma_kernel<GEPI_QKV_ROPE, false><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, colscale, rp, l8);
+      gemm_dma_kernel<GEPI_QKV_ROPE, false><<<nb, 512, 0, s>>>(a, lda, al, b, ldb, out, ldc, M, N, K, tn, nb, gm, colscale, rp, l8);
       break;
     default:
       return hipErrorInvalidValue;

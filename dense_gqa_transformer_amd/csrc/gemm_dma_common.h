@@ -7,6 +7,8 @@
 // whatever the operand type; a stage row is 64 B either way (32 bf16 or 64
 // fp8 values).
 #pragma once
+#include <cstdlib>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -44,6 +46,45 @@ constexpr int WAIT_VM12_LGKM0 = 0x7C;               // vmcnt(12) lgkmcnt(0)
 constexpr int WAIT_VM0_LGKM0 = 0x70;                // vmcnt(0) lgkmcnt(0)
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Output tile of this workgroup.  The hardware deals workgroups to the 8 XCDs
+// round robin; renumbering gives each XCD a contiguous range of tiles, whose
+// shared operand rows its L2 then serves.  Within the range the tiles go gm
+// tile rows at a time across the columns, so the 32 tiles an XCD runs at once
+// cover gm rows x 32/gm columns (each activation block read by 32/gm of them,
+// each weight block by gm) instead of one or two tile rows across all
+// columns.  gm <= 1, or a tile-row count that gm does not divide, keeps
+// row-major order.
+__device__ __forceinline__ void tile_origin(int nblocks, int tiles_n, int gm, int& m0, int& n0) {
+  int bid = blockIdx.x;
+  if ((nblocks & 7) == 0) bid = (bid & 7) * (nblocks >> 3) + (bid >> 3);
+  const int tiles_m = nblocks / tiles_n;
+  int mt, nt;
+  if (gm > 1 && tiles_m % gm == 0) {
+    const int per = gm * tiles_n;
+    const int g = bid / per, r = bid - g * per;
+    mt = g * gm + r % gm;
+    nt = r / gm;
+  } else {
+    mt = bid / tiles_n;
+    nt = bid % tiles_n;
+  }
+  m0 = mt * TILE;
+  n0 = nt * TILE;
+}
+
+// Tile-row group of the launches (FS_GEMM_TILE_GROUP, read once; default 2:
+// measured on the 4 x 4096 prefill, groups of 4 halve the fetched bytes of
+// the Q/K/V and gate/up GEMMs against row-major order but run no faster, and
+// groups of 2 run 2-8% faster than either).
+inline int gemm_tile_group() {
+  static const int g = [] {
+    const char* e = std::getenv("FS_GEMM_TILE_GROUP");
+    const int v = e != nullptr ? std::atoi(e) : 2;
+    return (v >= 0 && v <= 16) ? v : 2;
+  }();
+  return g;
+}
 
 
 // QKV epilogue of a prefill: the tile's 256 tokens x 256 columns are two
@@ -154,7 +195,7 @@ __device__ __forceinline__ void qkv_rope_epilogue(const RopeKvParams& p, const f
 // per-column (weight row) and per-row (activation row) scales, then the
 // store form EPI.  Columns / rows past N / M are computed on clamped reads and
 // never stored.
-template <int EPI, bool ROWSCALE>
+template <int EPI>
 __device__ __forceinline__ void dma_epilogue(f32x16 (&acc)[2][4], int tid, int m0, int n0, int M, int N,
                                              void* __restrict__ out, int ldc, const float* __restrict__ colscale,
                                              const float* __restrict__ rowscale, const RopeKvParams& rp) {
@@ -166,7 +207,7 @@ __device__ __forceinline__ void dma_epilogue(f32x16 (&acc)[2][4], int tid, int m
   const int hl = lane >> 5;
   const int mrow0 = m0 + wm * 128;
   const int ncol0 = n0 + wn * 64;
-  if constexpr (ROWSCALE) {
+  if (rowscale != nullptr) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float sa = rowscale[min(mrow0 + i * 32 + lrow, M - 1)];

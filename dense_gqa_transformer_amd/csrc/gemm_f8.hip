@@ -45,16 +45,14 @@ constexpr int KS8 = 64;                 // K (bytes) per stage
 template <int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_f8_kernel(const uint8_t* __restrict__ A, int lda, const uint8_t* __restrict__ B, int ldb,
-                    void* __restrict__ out, int ldc, int M, int N, int K, int tiles_n, int nblocks,
+                    void* __restrict__ out, int ldc, int M, int N, int K, int tiles_n, int nblocks, int gm,
                     const float* __restrict__ rowscale, const float* __restrict__ colscale,
                     const RopeKvParams rp) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid >> 2, wn = wid & 3;
-  // XCD-aware renumbering, as in the bf16 kernel
-  int bid = blockIdx.x;
-  if ((nblocks & 7) == 0) bid = (bid & 7) * (nblocks >> 3) + (bid >> 3);
-  const int n0 = (bid % tiles_n) * TILE, m0 = (bid / tiles_n) * TILE;
+  int m0, n0;
+  tile_origin(nblocks, tiles_n, gm, m0, n0);
 
   // DMA: wave w, instruction j fills tile rows (2w + j)*16 + lane/4, chunk
   // slot lane % 4 (holding logical chunk slot ^ ((row >> 2) & 3)).
@@ -175,7 +173,7 @@ void gemm_f8_kernel(const uint8_t* __restrict__ A, int lda, const uint8_t* __res
 
   __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
   lds_barrier();
-  dma_epilogue<EPI, true>(acc, tid, m0, n0, M, N, out, ldc, colscale, rowscale, rp);
+  dma_epilogue<EPI>(acc, tid, m0, n0, M, N, out, ldc, colscale, rowscale, rp);
 }
 
 bool gemm_f8_ok(int epi, const void* A, int lda, const void* B, int ldb, const void* out, int ldc, int M, int N,
@@ -199,17 +197,18 @@ hipError_t gemm_f8(int epi, const void* A, int lda, const void* B, int ldb, void
   }
   const int tn = (N + TILE - 1) / TILE, tm = (M + TILE - 1) / TILE;
   const int nb = tn * tm;
+  const int gm = gemm_tile_group();
   const uint8_t* a = (const uint8_t*)A;
   const uint8_t* b = (const uint8_t*)B;
   switch (epi) {
     case GEPI_SWIGLU_BF16:
-      gemm_f8_kernel<GEPI_SWIGLU_BF16><<<nb, 512, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, tn, nb, rowscale, colscale, rp);
+      gemm_f8_kernel<GEPI_SWIGLU_BF16><<<nb, 512, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, tn, nb, gm, rowscale, colscale, rp);
       break;
     case GEPI_STORE_F32:
-      gemm_f8_kernel<GEPI_STORE_F32><<<nb, 512, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, tn, nb, rowscale, colscale, rp);
+      gemm_f8_kernel<GEPI_STORE_F32><<<nb, 512, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, tn, nb, gm, rowscale, colscale, rp);
       break;
     case GEPI_QKV_ROPE:
-      gemm_f8_kernel<GEPI_QKV_ROPE><<<nb, 512, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, tn, nb, rowscale, colscale, rp);
+      gemm_f8_kernel<GEPI_QKV_ROPE><<<nb, 512, 0, s>>>(a, lda, b, ldb, out, ldc, M, N, K, tn, nb, gm, rowscale, colscale, rp);
       break;
     default:
       return hipErrorInvalidValue;
