@@ -18,6 +18,11 @@
 // (four distinct LDS objects, loop unrolled by four so each access names its
 // buffer statically); tile t+3 is requested once tile t has been multiplied,
 // and the wait for tile t+1 is an explicit vmcnt before the tile's barrier.
+// The copies are written as inline global_load_lds instructions: the
+// compiler's tracking of LDS written by DMA does not cover the transposing V
+// reads, and with the builtin it put a wait for every copy in flight (tiles
+// t+1 and t+2) in front of tile t's V reads.  Nothing else in the tile loop
+// touches global memory, so the explicit waits below are the only ones.
 // Both tiles keep the cache's row-major [key][d] layout;
 // the 16-B chunk c of key row k sits at chunk slot c ^ g(k) with
 // g(k) = ((k & 3) << 2) | ((k >> 2) & 3): any 16 consecutive rows see a
@@ -79,6 +84,16 @@ __device__ __forceinline__ void fbarrier() { asm volatile("s_barrier" ::: "memor
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4: lane l's 16
+// bytes land at lds + 16 l), written out so that the compiler does not track
+// it: its tracking of LDS written by DMA does not cover the transposing LDS
+// reads, before which it would otherwise wait for every copy in flight; the
+// kernel's own vmcnt waits and barriers order each tile's copies.
+__device__ __forceinline__ void dma16(const bf16* g, bf16* lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(la), "v"(g) : "memory", "m0");
+}
+
 __device__ __forceinline__ bf16x4 tr_read(const bf16* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
   return __builtin_bit_cast(bf16x4, v);
@@ -123,8 +138,8 @@ void attn_prefill_fa_kernel(const AttnPrefillParams p, const bf16* __restrict__ 
       const int R = R0 + drow;
       const int key = min(k0 + R, S - 1);
       const size_t go = (size_t)key * FD + (size_t)((dslot ^ fswz(R)) * 8);
-      __builtin_amdgcn_global_load_lds(kg + go, L + R0 * FD, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vg + go, L + FTILE + R0 * FD, 16, 0, 0);
+      dma16(kg + go, L + R0 * FD);
+      dma16(vg + go, L + FTILE + R0 * FD);
     }
   };
 
