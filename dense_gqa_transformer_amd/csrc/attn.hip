@@ -49,7 +49,10 @@ template <> __device__ __forceinline__ void loadn<float, 16>(const float* p, flo
 template <typename KV, int N> struct RawKV;
 template <> struct RawKV<bf16, 8> {
   u32x4 v;
-  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const u32x4*>(p); }
+  // K/V rows are read once per step: streaming (nontemporal) loads
+  __device__ __forceinline__ void load(const bf16* p) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
   __device__ __forceinline__ void get(float* o) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) { o[2 * i] = __uint_as_float(v[i] << 16); o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u); }
