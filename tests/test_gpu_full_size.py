@@ -9,7 +9,8 @@ the launch configuration the benchmark times:
 * 4 x 4096 prefill of the 0.6B shape in one fs_prefill (the 256 x 256 DMA-fed
   GEMMs with the norm/RoPE/KV epilogue, the flash attention over 4096 keys):
   one row's last-token logits and its late K/V rows against the oracle;
-* the same prefill on a 2-layer model of the 0.6B widths: all four rows;
+* the same prefill on a 2-layer model of the 0.6B widths: all four rows, and
+  two rows again with the GEMMs' remainder pass in bf16 instead of fp8;
 * the 64-sequence ragged decode (contexts 256..4096): the longest and the
   median row teacher-forced for four steps at B = 64 (the 256-position split
   of the long rows and its merge), on a 4-layer model of the 0.6B widths;
@@ -95,6 +96,27 @@ def test_prefill_4x4096_all_rows_two_layers():
         err = check_logits(lg[b], ref, TOL["bf16"], f"2-layer 4x4096 row {b}")
         _flush(f"2-layer 4x4096 row {b} max-abs logit error {err:.3e}")
         check_argmax(int(np.argmax(lg[b])), ref, f"2-layer 4x4096 row {b} argmax")
+
+
+def test_prefill_bf16_remainder_pass_two_layers(monkeypatch):
+    # the large GEMMs' remainder pass kept in bf16 (FS_GEMM_REMAINDER_F8=0,
+    # read when the model is created) instead of the default fp8 copy: same
+    # bound on two 4096-token rows of the 2-layer model
+    shape = _widths(2)
+    toks = synth.tokens(1044, shape.vocab, (4, 4096))[:2]
+    monkeypatch.setenv("FS_GEMM_REMAINDER_F8", "0")
+    model = make_model(shape, max_seqs=2, max_ctx=4096)
+    monkeypatch.delenv("FS_GEMM_REMAINDER_F8")
+    try:
+        _flush("gpu prefill 2 x 4096, 2 layers, bf16 remainder pass")
+        lg = model.prefill(dev_tokens(toks), [0, 1]).cpu().numpy()
+    finally:
+        model.close()
+    orc = _orc32(shape)
+    for b in range(2):
+        ref = orc.forward(toks[b])
+        err = check_logits(lg[b], ref, TOL["bf16"], f"2-layer bf16-remainder row {b}")
+        _flush(f"2-layer bf16-remainder row {b} max-abs logit error {err:.3e}")
 
 
 def test_decode_bs64_long_and_median_rows_vs_oracle():
