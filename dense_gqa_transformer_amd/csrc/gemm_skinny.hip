@@ -39,6 +39,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16* __restrict
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int r = lane & 31, h = lane >> 5;
   const int n0 = blockIdx.x * NS;
+  const int m0 = blockIdx.z * MS;             // activation rows of this workgroup (split blockIdx.z)
   const int ks = K / (int)gridDim.y;          // K range of this workgroup (split blockIdx.y)
   const int kw = ks / SK_WAVES, kb = blockIdx.y * ks + wid * kw;
 
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16* __restrict
   const bf16* alp[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    const size_t row = (size_t)min(32 * i + r, M - 1);
+    const size_t row = (size_t)min(m0 + 32 * i + r, M - 1);
     ap[i] = A + row * lda + kb + 32 * h;
     alp[i] = (A_lo != nullptr) ? A_lo + row * lda + kb + 32 * h : nullptr;
   }
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16* __restrict
       }
   __syncthreads();
 
-  const int rows = min(M, MS);
+  const int rows = min(M - m0, MS);
   if (EPI == GEPI_SWIGLU_BF16) {
     // the slab is one packed [32 gate | 32 up] block: 32 output features
     const int f0 = n0 / 2;
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16* __restrict
         g *= colscale[n0 + n];
         u *= colscale[n0 + 32 + n];
       }
-      reinterpret_cast<bf16*>(out)[(size_t)m * ldc + f0 + n] = (bf16)(silu(g) * u);
+      reinterpret_cast<bf16*>(out)[(size_t)(m0 + m) * ldc + f0 + n] = (bf16)(silu(g) * u);
     }
   } else {
     for (int idx = threadIdx.x; idx < rows * NS; idx += 256) {
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16* __restrict
 #pragma unroll
       for (int w = 0; w < SK_WAVES; ++w) v += red[w][m * RS + n];
       if (colscale != nullptr) v *= colscale[n0 + n];
-      const size_t o = (size_t)m * ldc + n0 + n;
+      const size_t o = (size_t)(m0 + m) * ldc + n0 + n;
       if (EPI == GEPI_STORE_BF16) reinterpret_cast<bf16*>(out)[o] = (bf16)v;
       else if (EPI == GEPI_STORE_F32) reinterpret_cast<float*>(out)[o] = v;
       else if (EPI == GEPI_PART_F32) reinterpret_cast<float*>(out)[(size_t)blockIdx.y * M * ldc + o] = v;
@@ -176,6 +177,16 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16* __restrict
 template <int EPI, int NT>
 hipError_t launch_nt(const bf16* a, int lda, const bf16* alo, const bf16* b, int ldb, void* out, int ldc, int M,
                      int N, int K, const float* cs, int ksplit, hipStream_t s) {
+  // SwiGLU with more than 32 rows: 32-row halves in separate workgroups (each
+  // streams the weight slab once more, in exchange for twice the workgroups:
+  // N / 64 slabs alone leave most CUs idle)
+  if (EPI == GEPI_SWIGLU_BF16 && M > 32 && ksplit == 1) {
+    const dim3 g2((N + 32 * NT - 1) / (32 * NT), 1, (M + 31) / 32);
+    const bool pipe2 = (long long)g2.x * g2.z <= 512;
+    if (pipe2) gemm_skinny_kernel<EPI, NT, 1, true><<<g2, 256, 0, s>>>(a, lda, alo, b, ldb, out, ldc, M, N, K, cs);
+    else gemm_skinny_kernel<EPI, NT, 1, false><<<g2, 256, 0, s>>>(a, lda, alo, b, ldb, out, ldc, M, N, K, cs);
+    return hipGetLastError();
+  }
   const dim3 grid((N + 32 * NT - 1) / (32 * NT), ksplit);
   const bool pipe = (long long)grid.x * grid.y <= 512;
   if (M <= 32) {
