@@ -113,6 +113,8 @@ struct fs_model {
   void* wconv = nullptr;          // bf16 copy of one layer matrix's codes (MFMA operand)
   void* w8blob = nullptr;         // fp8 copies of the Q/K/V and gate/up weights (bf16 models)
   float* s8blob = nullptr;        // their row scales
+  float* am_pv = nullptr;         // argmax block bests of many-row heads [max_seqs][ARGMAX_BLOCKS]
+  int32_t* am_pi = nullptr;
   bool lo8 = false;               // remainder passes of the large GEMMs on fp8 operands
   void* embed = nullptr;
   float* embed_scale = nullptr;
@@ -201,7 +203,7 @@ struct fs_model {
     for (auto& t : timed) { hipEventDestroy(t.a); hipEventDestroy(t.b); }
     for (auto e : ev_free) hipEventDestroy(e);
     hipFree(wblob); hipFree(nblob); hipFree(sblob); hipFree(wconv); hipFree(kcache); hipFree(vcache);
-    hipFree(w8blob); hipFree(s8blob);
+    hipFree(w8blob); hipFree(s8blob); hipFree(am_pv); hipFree(am_pi);
     hipFree(rope_cos); hipFree(rope_sin);
     hipFree(x); hipFree(xn); hipFree(qkv); hipFree(qr); hipFree(attn); hipFree(hbuf); hipFree(ascale);
     hipFree(d_pos); hipFree(part); hipFree(kpart);
@@ -361,7 +363,7 @@ fs_status head(fs_model* m, const float* xrows, int rows, int ldx, float* logits
     p.out = lg; p.ldo = c.vocab;
     LAUNCH(m, "head", s, gemv(m->wdt, EPI_STORE, p, s));
   }
-  if (next) LAUNCH(m, "argmax", s, argmax_rows(lg, rows, c.vocab, c.vocab, next, s));
+  if (next) LAUNCH(m, "argmax", s, argmax_rows_blocks(lg, rows, c.vocab, c.vocab, m->am_pv, m->am_pi, next, s));
   return FS_OK;
 }
 
@@ -826,6 +828,8 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
       dalloc(&m->kpart, (size_t)KSPLIT_MAX_ROWS * std::max(KSPLIT_MAX * c.hidden, KSPLIT_MAX * m->qkv_w) * 4) !=
           hipSuccess ||
       dalloc(&m->lm_pv, (size_t)GEMV_LOGITS_MAX_M * lm_blocks * 4) != hipSuccess ||
+      dalloc(&m->am_pv, (size_t)c.max_seqs * ARGMAX_BLOCKS * 4) != hipSuccess ||
+      dalloc(&m->am_pi, (size_t)c.max_seqs * ARGMAX_BLOCKS * 4) != hipSuccess ||
       dalloc(&m->lm_pi, (size_t)GEMV_LOGITS_MAX_M * lm_blocks * 4) != hipSuccess)
     return bail(FS_ERR_OOM, "decode scratch allocation failed");
   m->d_slot = m->d_pos + c.max_seqs;

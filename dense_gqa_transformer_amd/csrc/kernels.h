@@ -271,6 +271,11 @@ hipError_t decode_persist(const DecodePersistParams& p, hipStream_t s);
 // ---------------------------------------------------------------- argmax
 // out[b] = greedy ID of row b of logits [B, V] (row stride ldl).
 hipError_t argmax_rows(const float* logits, int B, int V, int ldl, int32_t* out, hipStream_t s);
+// argmax_rows in two levels for many rows: ARGMAX_BLOCKS blocks per row write
+// (value, index) bests to pv / pi ([B][ARGMAX_BLOCKS]), then argmax_partials.
+constexpr int ARGMAX_BLOCKS = 16;
+hipError_t argmax_rows_blocks(const float* logits, int B, int V, int ldl, float* pv, int32_t* pi, int32_t* out,
+                              hipStream_t s);
 
 // ---------------------------------------------------------------- sampling
 // Per-row scratch of the sampler (count and mass histograms of the three radix

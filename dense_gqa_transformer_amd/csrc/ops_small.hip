@@ -667,6 +667,60 @@ hipError_t argmax_rows(const float* logits, int B, int V, int ldl, int32_t* out,
   return hipGetLastError();
 }
 
+// The same rule in two levels for many rows: block k of row b reduces the
+// logits [k * per, (k + 1) * per) to its best (value, index) (index -1 if none
+// is finite), four loads per thread in flight; argmax_partials then reduces
+// each row's nb bests (the lowest index still wins an exact tie).
+__global__ __launch_bounds__(256) void argmax_blocks_kernel(const float* __restrict__ logits, int V, int ldl,
+                                                            int per, float* __restrict__ pv,
+                                                            int32_t* __restrict__ pi) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int blk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const float* row = logits + (size_t)b * ldl;
+  const int s0 = blk * per, s1 = min(V, s0 + per);
+  float bv = 0.f;
+  int bi = -1;
+  for (int base = s0; base < s1; base += 1024) {
+    float v[4];
+    int ix[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ix[u] = base + tid + 256 * u;
+      v[u] = row[min(ix[u], s1 - 1)];          // past the range: re-read, skipped
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (ix[u] < s1 && __builtin_isfinite(v[u]) && better(v[u], ix[u], bv, bi)) { bv = v[u]; bi = ix[u]; }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  const int lane = tid & 63, wid = tid >> 6;
+  if (lane == 0) { sv[wid] = bv; si[wid] = bi; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
+    pv[(size_t)b * gridDim.x + blk] = bv;
+    pi[(size_t)b * gridDim.x + blk] = bi;
+  }
+}
+
+hipError_t argmax_rows_blocks(const float* logits, int B, int V, int ldl, float* pv, int32_t* pi, int32_t* out,
+                              hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  if (V <= 0) return hipErrorInvalidValue;
+  const int per = (V + ARGMAX_BLOCKS - 1) / ARGMAX_BLOCKS;
+  argmax_blocks_kernel<<<dim3(ARGMAX_BLOCKS, B), 256, 0, s>>>(logits, V, ldl, per, pv, pi);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return argmax_partials(pv, pi, ARGMAX_BLOCKS, B, out, s);
+}
+
 // ---------------------------------------------------------------- attention output gate
 // a[t, h*d + e] *= sigmoid(qkv[t, 2h*d + d + e]): the gated-attention variant's
 // per-head output gate, read from the gate rows the q projection interleaves

@@ -383,6 +383,10 @@ def test_decode_bs64_ragged():
         positions = [lens[i] + k for i in range(B)]
         model.decode_step(toks, positions, slots, logits=logits, next_ids=nxt)
         lg = logits.cpu().numpy()
+        ids = nxt.cpu().numpy()
+        # every row's greedy ID is the rule applied to the logits it returned
+        for i in range(B):
+            assert int(ids[i]) == O.greedy_argmax_fast(lg[i]), f"bs64 row {i} step {k}: next ID"
         for i in watch:
             refs[i] = orcs[i].decode_step(0, int(host_next[i]), lens[i] + k)
             check_logits(lg[i], refs[i], TOL["bf16"], f"bs64 row {i} step {k}")
