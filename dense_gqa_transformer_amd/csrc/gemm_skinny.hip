@@ -219,7 +219,12 @@ hipError_t gemm_skinny(int epi, const void* A, int lda, const void* B, int ldb, 
   const float* cs = colscale;
   switch (epi) {
     case GEPI_STORE_BF16: return launch_nt<GEPI_STORE_BF16, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, cs, 1, s);
-    case GEPI_STORE_F32: return launch_nt<GEPI_STORE_F32, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, cs, 1, s);
+    case GEPI_STORE_F32:
+      // very wide outputs (the tied head): 64 weight rows per workgroup, so each
+      // streams 128 KB rather than 64 KB per launch share
+      if (N >= 65536 && N % 64 == 0)
+        return launch_nt<GEPI_STORE_F32, 2>(a, lda, al, b, ldb, out, ldc, M, N, K, cs, 1, s);
+      return launch_nt<GEPI_STORE_F32, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, cs, 1, s);
     case GEPI_RESID_F32: return launch_nt<GEPI_RESID_F32, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, cs, 1, s);
     case GEPI_PART_F32: return launch_nt<GEPI_PART_F32, 1>(a, lda, al, b, ldb, out, ldc, M, N, K, cs, ksplit, s);
     case GEPI_SWIGLU_BF16: return launch_nt<GEPI_SWIGLU_BF16, 2>(a, lda, al, b, ldb, out, ldc, M, N, K, cs, 1, s);
