@@ -138,7 +138,8 @@ typedef struct fs_model fs_model;
  * large prefill GEMM too (by default there they run on fp8 copies of the
  * remainder and of the Q/K/V and gate/up weights, at half the cost);
  * FS_GEMM_TILE_GROUP=0..16 sets how many 256-row tile rows the large GEMMs'
- * workgroups walk together across the columns (default 2; 0 or 1 row-major);
+ * workgroups walk together across the columns (default 2; 0 or 1 row-major;
+ * read once per process, at the first large GEMM, not per model);
  * FS_PREFILL_F8_MFMA=0 keeps an FS_WEIGHTS_F8_ROW model's prefill on widened
  * (bf16) weights instead of the fp8 matrix instructions (the same values:
  * code * scale is exact in bf16);
