@@ -604,6 +604,11 @@ def main():
                          "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s", "frac": round(pach / MFMA_BF16_PEAK, 4),
                          "traffic": measured_traffic("prefill." + pdom), "avg_launch_us": round(pavg * 1e6, 1)},
             "kernel_ms_per_pass": {k: round(v[0], 3) for k, v in pper.items()},
+            # per projection: algorithmic flops over its time in the pass (Q/K/V and gate/up
+            # also run the fp8 remainder pass and their fused epilogues inside that time)
+            "gemm_mfma_frac": {k: round(shape.n_layers * prefill_label_flops(shape, k, 4, 4096)
+                                        / (pper[k][0] / 1e3) / MFMA_BF16_PEAK, 4)
+                               for k in ("qkv", "o_proj", "gate_up", "down") if k in pper},
         }
 
     # the library's generation loop on the same prompt (greedy, one host check per token)
