@@ -46,6 +46,9 @@ fs_status fail(fs_status st, const std::string& msg) {
 constexpr int SKINNY_MAX_ROWS = 4;
 constexpr int SKINNY_MAX_ROWS_I8 = 8;
 constexpr int SKINNY_MAX_ROWS_F8 = 4;
+// prefill: up to this many tokens per sequence the attention runs on the
+// vector kernel whatever the projections use
+constexpr int ATTN_VEC_MAX_S = 32;
 // fp8 weights: from this many rows a prefill's Q/K/V and gate/up products run
 // on the fp8 matrix instructions (gemm_f8); below it on widened weights
 constexpr int F8_GEMM_MIN_ROWS = 512;
@@ -941,8 +944,11 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
     a.B = B; a.S = S; a.nq = c.n_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim;
     a.slot_stride = m->slot_stride; a.head_stride = m->head_stride;
     a.scale = 1.0f / std::sqrt((float)c.head_dim);
-    // the head_dim-128 kernel takes q pre-multiplied by scale * log2(e)
-    const bool fa = !skinny && attn_prefill_fa_ok(a);
+    // short prompts (up to ATTN_VEC_MAX_S tokens per sequence) keep the vector
+    // attention on the GEMM path too: the MFMA kernels' fixed cost dominates
+    // there; the head_dim-128 kernel takes q pre-multiplied by scale * log2(e)
+    const bool vec = skinny || S <= ATTN_VEC_MAX_S;
+    const bool fa = !vec && attn_prefill_fa_ok(a);
     a.q_prescale = fa ? a.scale * 1.4426950408889634f : 1.0f;
     RopeKvParams r{};
     r.qscale = a.q_prescale;
@@ -956,7 +962,7 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
     bool rope_done = false;       // set when the QKV GEMM's epilogue did rope_kv's work
     auto attention = [&]() -> fs_status {
       if (!rope_done) LAUNCH(m, "rope_kv", s, rope_kv(r, s));
-      LAUNCH(m, "attn", s, skinny ? attn_prefill_vec(a, s) : fa ? attn_prefill_fa(a, s) : attn_prefill(a, s));
+      LAUNCH(m, "attn", s, vec ? attn_prefill_vec(a, s) : fa ? attn_prefill_fa(a, s) : attn_prefill(a, s));
       if (m->gated)
         LAUNCH(m, "attn_gate", s, attn_gate(m->attn, act_dt, m->qkv, DT_F32, (int)T, c.n_heads, c.head_dim, m->qkv_w, s));
       return FS_OK;
