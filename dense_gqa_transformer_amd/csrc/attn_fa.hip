@@ -5,7 +5,8 @@
 // registers.
 //
 // Work split.  A workgroup takes 128 queries of the two query heads that share
-// one KV head: 8 waves, two per SIMD; wave w owns 32 queries (one 32-column
+// one KV head (workgroups ordered longest first across all heads and
+// sequences): 8 waves, two per SIMD; wave w owns 32 queries (one 32-column
 // block) of head 2y + w/4, so the two waves on a SIMD overlap one's
 // exponentials with the other's products.  Each wave reads 32 KB of K and V
 // fragments from LDS per 64-key tile for 32 MFMAs, which puts the tile loop
@@ -112,9 +113,9 @@ void attn_prefill_fa_kernel(const AttnPrefillParams p, const bf16* __restrict__ 
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int S = p.S;
-  const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;   // longest rows first
-  const int b = blockIdx.z;
-  const int h = blockIdx.y * 2 + wid / WPH;
+  int qt, hy, b;
+  longest_first(blockIdx.x, (S + 127) / 128, p.nq / 2, p.B, qt, hy, b);
+  const int h = hy * 2 + wid / WPH;
   const int j = h / (p.nq / p.nkv);
   const int q0 = qt * 128;
   const int wq0 = q0 + (wid % WPH) * 32;
@@ -324,7 +325,7 @@ bool attn_prefill_fa_ok(const AttnPrefillParams& p) {
 
 hipError_t attn_prefill_fa(const AttnPrefillParams& p, hipStream_t s) {
   if (std::fabs(p.q_prescale - p.scale * FLOG2E) > 1e-6f * p.scale * FLOG2E) return hipErrorInvalidValue;
-  const dim3 grid((p.S + 127) / 128, p.nq / 2, p.B);
+  const int grid = (p.S + 127) / 128 * (p.nq / 2) * p.B;
   attn_prefill_fa_kernel<<<grid, 512, 0, s>>>(p, (const bf16*)p.kcache, (const bf16*)p.vcache, (const bf16*)p.q,
                                                (bf16*)p.out);
   return hipGetLastError();

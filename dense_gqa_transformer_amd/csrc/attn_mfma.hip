@@ -50,9 +50,9 @@ __global__ __launch_bounds__(256 * HPW) void attn_prefill_mfma_kernel(const Attn
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int S = p.S;
-  const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;   // longest tiles first
-  const int b = blockIdx.z;
-  const int h = blockIdx.y * HPW + (wid >> 2);            // this wave's query head
+  int qt, hy, b;                                          // longest tiles first
+  longest_first(blockIdx.x, (S + BQ - 1) / BQ, p.nq / HPW, p.B, qt, hy, b);
+  const int h = hy * HPW + (wid >> 2);                    // this wave's query head
   const int j = h / (p.nq / p.nkv);
   const int q0 = qt * BQ;
   const int wq0 = q0 + (wid & 3) * 32;
@@ -226,13 +226,13 @@ static hipError_t launch_mfma(const AttnPrefillParams& p, hipStream_t s) {
   const int rep = p.nq / p.nkv;
   if constexpr (D <= 128) {
     if (rep % 2 == 0) {
-      const dim3 grid((p.S + 127) / 128, p.nq / 2, p.B);
+      const int grid = (p.S + 127) / 128 * (p.nq / 2) * p.B;
       attn_prefill_mfma_kernel<D, 2><<<grid, 512, 0, s>>>(p);
       return hipGetLastError();
     }
   }
   {
-    const dim3 grid((p.S + 127) / 128, p.nq, p.B);
+    const int grid = (p.S + 127) / 128 * p.nq * p.B;
     attn_prefill_mfma_kernel<D, 1><<<grid, 256, 0, s>>>(p);
   }
   return hipGetLastError();

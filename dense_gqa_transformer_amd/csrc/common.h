@@ -167,3 +167,15 @@ __device__ __forceinline__ float f8_row_scale(float amax) {
   if (ex != 0) return man == 0 ? t : __uint_as_float((ex + 1u) << 23);
   return man == 1u ? ldexpf(1.f, -149) : ldexpf(1.f, 32 - __builtin_clz(man - 1u) - 149);   // t subnormal
 }
+
+// Causal prefill attention grids: workgroup L of a 1-D grid of nqt * ny * nb
+// takes query tile qt of head group y of sequence b, in order of decreasing
+// work across all heads and sequences (query tile qt reads qt + 1 key tiles),
+// so that the longest tiles start first and the short ones fill the tail.
+__device__ __forceinline__ void longest_first(int L, int nqt, int ny, int nb, int& qt, int& y, int& b) {
+  const int per = ny * nb;
+  const int g = L / per, r = L - g * per;
+  qt = nqt - 1 - g;
+  y = r % ny;
+  b = r / ny;
+}
