@@ -47,6 +47,21 @@ constexpr int WAIT_VM0_LGKM0 = 0x70;                // vmcnt(0) lgkmcnt(0)
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4: lane l's 16
+// bytes land at lds + 16 l; lds is the same for the whole wave), written out so
+// that the compiler does not track it.  Its tracking of DMA-written LDS cannot
+// tell the ring's stage buffers apart and put a wait for every copy in flight
+// (vmcnt(0)) in front of fragment reads of other stages, once per unrolled
+// pass of the K loop.  The kernel's own vmcnt waits and barriers order every
+// stage's copies; the compiler's waits for its own loads stay correct, since
+// loads complete in order and untracked copies only make them wait longer.
+// (The fp8 GEMM keeps the builtin: there the written-out form cost registers
+// and measured slower.)
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(la), "v"(g) : "memory", "m0");
+}
+
 // Output tile of this workgroup.  The hardware deals workgroups to the 8 XCDs
 // round robin; renumbering gives each XCD a contiguous range of tiles, whose
 // shared operand rows its L2 then serves.  Within the range the tiles go gm
