@@ -278,7 +278,10 @@ __device__ __forceinline__ void dma_epilogue(f32x16 (&acc)[2][4], int tid, int m
     }
   } else if (EPI == GEPI_SWIGLU_BF16) {
     // the wave's 64 packed columns are one [32 gate | 32 up] pair -> 32 outputs;
-    // 128 rows x 64 B, chunk c of row m at slot c ^ (m & 3)
+    // 128 rows x 64 B, chunk c of row m at slot c ^ ((m >> 2) & 3): a row's 64 B
+    // fill one quarter of the banks (m & 3 picks it), so the 8 rows of a write
+    // that share a quarter spread over its 4 chunk slots (2 per slot, the
+    // minimum) instead of all landing on one
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = i * 32 + lrow;
@@ -287,7 +290,7 @@ __device__ __forceinline__ void dma_epilogue(f32x16 (&acc)[2][4], int tid, int m
         bf16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (bf16)(silu(acc[0][i][4 * g + e]) * acc[1][i][4 * g + e]);
-        *reinterpret_cast<bf16x4*>(R + m * 64 + ((g ^ (m & 3)) << 4) + hl * 8) = v;
+        *reinterpret_cast<bf16x4*>(R + m * 64 + ((g ^ ((m >> 2) & 3)) << 4) + hl * 8) = v;
       }
     }
     bf16* o = reinterpret_cast<bf16*>(out);
@@ -296,7 +299,7 @@ __device__ __forceinline__ void dma_epilogue(f32x16 (&acc)[2][4], int tid, int m
 #pragma unroll 4
     for (int it = 0; it < 8; ++it) {
       const int m = it * 16 + (lane >> 2);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(R + m * 64 + ((c ^ (m & 3)) << 4));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(R + m * 64 + ((c ^ ((m >> 2) & 3)) << 4));
       const int gm = mrow0 + m, f = f0 + c * 8;
       if (gm < M && f < nf) *reinterpret_cast<u32x4*>(o + (size_t)gm * ldc + f) = v;
     }
