@@ -72,6 +72,8 @@ struct LayerW {
   // gate/up weights for the remainder pass of the large prefill GEMMs
   uint8_t *w8qkv = nullptr, *w8gu = nullptr;
   float *s8qkv = nullptr, *s8gu = nullptr;
+  // bound on every base-2 attention score of the layer (from the q/k norm weights)
+  float qk_bound = 0.f;
 };
 
 struct DecodeKey {
@@ -782,6 +784,34 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
   }
   if (e != hipSuccess) return bail(FS_ERR_HIP, std::string("weight repack failed: ") + hipGetErrorString(e));
 
+  // Per layer, a bound on every attention score in base 2.  After the per-head
+  // RMSNorm a head row has length <= sqrt(d) (the eps only shortens it), the
+  // norm weight g scales each element by at most max|g|, and RoPE rotates
+  // pairs (length kept), so |q'| <= sqrt(d) max|g_q| and |k'| <= sqrt(d) max|g_k|;
+  // the score q'.k' / sqrt(d) in base 2 is at most log2(e) sqrt(d) max|g_q| max|g_k|.
+  // The factor 1.01 covers the bf16 rounding of q' and k' (2^-9 each) and the
+  // fp32 sums.  The prefill attention uses it as a fixed softmax shift.
+  {
+    const char* fx = std::getenv("FS_PREFILL_FIXED_SHIFT");
+    const bool fixed = !(fx != nullptr && fx[0] == '0');
+    std::vector<float> g(2 * (size_t)c.head_dim);
+    for (int l = 0; l < c.n_layers && fixed; ++l) {
+      LayerW& L = m->layers[l];
+      chk(hipMemcpyAsync(g.data(), L.q_norm, c.head_dim * 4, hipMemcpyDeviceToHost, s));
+      chk(hipMemcpyAsync(g.data() + c.head_dim, L.k_norm, c.head_dim * 4, hipMemcpyDeviceToHost, s));
+      chk(hipStreamSynchronize(s));
+      if (e != hipSuccess) break;
+      float gq = 0.f, gk = 0.f;
+      for (int i = 0; i < c.head_dim; ++i) {
+        gq = std::max(gq, std::fabs(g[i]));
+        gk = std::max(gk, std::fabs(g[c.head_dim + i]));
+      }
+      const double b = 1.4426950408889634 * std::sqrt((double)c.head_dim) * gq * gk * 1.01;
+      L.qk_bound = std::isfinite(b) ? (float)b : 0.f;
+    }
+    if (e != hipSuccess) return bail(FS_ERR_HIP, std::string("norm weight read failed: ") + hipGetErrorString(e));
+  }
+
   // bf16 models: fp8 copies of the Q/K/V and gate/up weights, the operands of
   // the large GEMMs' remainder pass (FS_GEMM_REMAINDER_F8=0 keeps that pass in bf16)
   {
@@ -950,6 +980,7 @@ fs_status fs_prefill(fs_model* m, const int32_t* tokens, int32_t B, int32_t S, c
     const bool vec = skinny || S <= ATTN_VEC_MAX_S;
     const bool fa = !vec && attn_prefill_fa_ok(a);
     a.q_prescale = fa ? a.scale * 1.4426950408889634f : 1.0f;
+    a.m_fixed = L.qk_bound <= ATTN_FIXED_SHIFT_MAX ? L.qk_bound : 0.f;
     RopeKvParams r{};
     r.qscale = a.q_prescale;
     r.rot = m->rot; r.gated = m->gated;

@@ -46,7 +46,11 @@
 // since the final division uses the matching sum.  q arrives pre-multiplied
 // by scale * log2(e) and every score accumulator starts at -m, so the MFMA
 // returns exponents ready for exp2; when m moves, the tile in hand is shifted
-// by the same amount.
+// by the same amount.  FIXED: the per-head q/k RMSNorm bounds every score of
+// the layer by a constant m (|q'| <= sqrt(d) max|g_q| whatever q was, the
+// same for k', and RoPE keeps lengths), so m is that bound from the start
+// and the tile max, its exchange and the rescale test are not needed; every
+// p = 2^(s - m) lies in [2^(-2m), 1], a normal number for m <= 63.
 #include "common.h"
 #include "kernels.h"
 
@@ -102,6 +106,7 @@ __device__ __forceinline__ bf16x4 tr_read(const bf16* p) {
 
 }  // namespace
 
+template <bool FIXED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_fa_kernel(const AttnPrefillParams p, const bf16* __restrict__ kcache,
                             const bf16* __restrict__ vcache, const bf16* __restrict__ qin,
@@ -161,7 +166,7 @@ void attn_prefill_fa_kernel(const AttnPrefillParams p, const bf16* __restrict__ 
   const int vh = (lane & 1) * 4;                               // element offset of the 8-byte half
   const int qme = min(wq0 + col, S - 1);                       // the lane's query (clamped)
 
-  float m_run = 0.f, l_run = 0.f;   // m_run is set from the first tile's max
+  float m_run = FIXED ? p.m_fixed : 0.f, l_run = 0.f;   // running max: set from the first tile's max
   f32x16 o[4];   // O^T blocks [d block]
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -196,6 +201,7 @@ void attn_prefill_fa_kernel(const AttnPrefillParams p, const bf16* __restrict__ 
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + (r >> 2) * 8 + (r & 3) > lim) sv[kb][r] = -INFINITY;
     }
+    if constexpr (FIXED) return 0.f;   // FIXED: masking only, done as a tile turns into probabilities
     // two independent max3 chains over the 32 scores
     float ma = fmax3(sv[0][0], sv[0][1], sv[0][2]), mb = fmax3(sv[1][0], sv[1][1], sv[1][2]);
 #pragma unroll
@@ -209,6 +215,7 @@ void attn_prefill_fa_kernel(const AttnPrefillParams p, const bf16* __restrict__ 
   // move m_run when the tile's max (relative to it) exceeds FLAZY, or always
   // for the first tile; the unexponentiated tile sv follows the move
   auto rescale = [&](float mt, f32x16* sv, bool first) {
+    if constexpr (FIXED) return;
     if (first || mt > FLAZY) {
       const float corr = __builtin_amdgcn_exp2f(-mt);
       l_run *= corr;
@@ -224,7 +231,8 @@ void attn_prefill_fa_kernel(const AttnPrefillParams p, const bf16* __restrict__ 
     }
   };
   // p = 2^(s - m), row sum, bf16 operands for the 16-key steps
-  auto probs = [&](f32x16* sv) {
+  auto probs = [&](f32x16* sv, int t) {
+    if constexpr (FIXED) mask_max(sv, t);
     float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -264,7 +272,7 @@ void attn_prefill_fa_kernel(const AttnPrefillParams p, const bf16* __restrict__ 
   __builtin_amdgcn_s_waitcnt(W2);             // tile 0 landed
   fbarrier();
   scores(Fc<0>{}, sc[0]);
-  rescale(mask_max(sc[0], 0), sc[0], true);
+  if constexpr (!FIXED) rescale(mask_max(sc[0], 0), sc[0], true);
   __builtin_amdgcn_s_waitcnt(W1);             // tile 1 landed
   fbarrier();
 
@@ -279,14 +287,14 @@ void attn_prefill_fa_kernel(const AttnPrefillParams p, const bf16* __restrict__ 
     f32x16* cur = sc[C & 1];
     f32x16* nxt = sc[(C + 1) & 1];
     scores(Fc<(C + 1) & 3>{}, nxt);
-    probs(cur);
+    probs(cur, t);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
     }
-    const float mt = mask_max(nxt, t + 1);
+    const float mt = FIXED ? 0.f : mask_max(nxt, t + 1);
     pv(Cc);
     rescale(mt, nxt, false);
     issue(Fc<(C + 3) & 3>{}, min(t + 3, ntile - 1));
@@ -326,8 +334,12 @@ bool attn_prefill_fa_ok(const AttnPrefillParams& p) {
 hipError_t attn_prefill_fa(const AttnPrefillParams& p, hipStream_t s) {
   if (std::fabs(p.q_prescale - p.scale * FLOG2E) > 1e-6f * p.scale * FLOG2E) return hipErrorInvalidValue;
   const int grid = (p.S + 127) / 128 * (p.nq / 2) * p.B;
-  attn_prefill_fa_kernel<<<grid, 512, 0, s>>>(p, (const bf16*)p.kcache, (const bf16*)p.vcache, (const bf16*)p.q,
-                                               (bf16*)p.out);
+  if (p.m_fixed > 0.f && p.m_fixed <= ATTN_FIXED_SHIFT_MAX)
+    attn_prefill_fa_kernel<true><<<grid, 512, 0, s>>>(p, (const bf16*)p.kcache, (const bf16*)p.vcache,
+                                                       (const bf16*)p.q, (bf16*)p.out);
+  else
+    attn_prefill_fa_kernel<false><<<grid, 512, 0, s>>>(p, (const bf16*)p.kcache, (const bf16*)p.vcache,
+                                                        (const bf16*)p.q, (bf16*)p.out);
   return hipGetLastError();
 }
 
