@@ -48,9 +48,10 @@
 // returns exponents ready for exp2; when m moves, the tile in hand is shifted
 // by the same amount.  FIXED: the per-head q/k RMSNorm bounds every score of
 // the layer by a constant m (|q'| <= sqrt(d) max|g_q| whatever q was, the
-// same for k', and RoPE keeps lengths), so m is that bound from the start
-// and the tile max, its exchange and the rescale test are not needed; every
-// p = 2^(s - m) lies in [2^(-2m), 1], a normal number for m <= 63.
+// same for k', and RoPE keeps lengths); with m <= 63 every p = 2^s lies in
+// [2^-63, 2^63], a normal fp32 and bf16 number, and the sums stay far from
+// overflow, so no shift is needed at all: the score accumulators start at 0
+// and the tile max, its exchange and the rescale test go away.
 #include "common.h"
 #include "kernels.h"
 
@@ -166,7 +167,7 @@ void attn_prefill_fa_kernel(const AttnPrefillParams p, const bf16* __restrict__ 
   const int vh = (lane & 1) * 4;                               // element offset of the 8-byte half
   const int qme = min(wq0 + col, S - 1);                       // the lane's query (clamped)
 
-  float m_run = FIXED ? p.m_fixed : 0.f, l_run = 0.f;   // running max: set from the first tile's max
+  float m_run = 0.f, l_run = 0.f;   // running max: set from the first tile's max (FIXED: stays 0)
   f32x16 o[4];   // O^T blocks [d block]
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -181,7 +182,7 @@ void attn_prefill_fa_kernel(const AttnPrefillParams p, const bf16* __restrict__ 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sd[kb][r] = -m_run;
+      for (int r = 0; r < 16; ++r) sd[kb][r] = FIXED ? 0.f : -m_run;
 #pragma unroll
     for (int ks = 0; ks < FD / 16; ++ks)
 #pragma unroll

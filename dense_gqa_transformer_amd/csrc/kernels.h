@@ -189,11 +189,11 @@ struct AttnPrefillParams {
   float q_prescale;            // factor already applied to q (attn_prefill_fa expects scale*log2(e))
   // attn_prefill_fa: > 0 bounds every base-2 score |q'.k'| * scale * log2(e) of
   // the layer (per-head q/k RMSNorm makes |q'| <= sqrt(d) max|g_q|, likewise k');
-  // the softmax then shifts by this constant instead of a running max.  0: running max.
+  // up to ATTN_FIXED_SHIFT_MAX the softmax needs no running max.  0: running max.
   float m_fixed;
 };
-// Largest fixed shift used: with |s| <= m every p = 2^(s - m) >= 2^(-2m) stays a
-// normal fp32 / bf16 number for m <= 63.
+// Largest score bound taken without a running max: with |s| <= 63 every
+// p = 2^s lies in [2^-63, 2^63], a normal fp32 / bf16 number, unshifted.
 constexpr float ATTN_FIXED_SHIFT_MAX = 63.f;
 hipError_t attn_prefill(const AttnPrefillParams& p, hipStream_t s);      // MFMA path when bf16
 hipError_t attn_prefill_vec(const AttnPrefillParams& p, hipStream_t s);  // vector path, any dtype
