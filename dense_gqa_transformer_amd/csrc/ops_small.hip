@@ -354,14 +354,21 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   const float* row = x + (size_t)r * ldx;
   const int nc = H >> 2;
   f32x4 v[MAXJ];
-  float ss = 0.f;
+  // MODE 2 with a short row (MAXJ <= 4): the norm weights are requested with
+  // the row, so they do not cost a second round trip after the sum
+  constexpr bool GPRE = (MODE == 2 && MAXJ <= 4);
+  f32x4 gp[GPRE ? MAXJ : 1];
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
     const int c = lane + 64 * j;
     v[j] = (c < nc) ? *reinterpret_cast<const f32x4*>(row + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (GPRE) gp[j] = (c < nc) ? *reinterpret_cast<const f32x4*>(g + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) ss = fmaf(v[j][e], v[j][e], ss);
-  }
   const float inv = rsqrtf(wave_sum(ss) / (float)H + eps);
   O* o = out + (size_t)r * ldo;
   if constexpr (MODE == 2) {
@@ -370,7 +377,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
     for (int j = 0; j < MAXJ; ++j) {
       const int c = lane + 64 * j;
       if (c < nc) {
-        const f32x4 gg = *reinterpret_cast<const f32x4*>(g + 4 * c);
+        f32x4 gg;
+        if constexpr (GPRE) gg = gp[j];
+        else gg = *reinterpret_cast<const f32x4*>(g + 4 * c);
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) { v[j][e] = v[j][e] * inv * gg[e]; y[e] = v[j][e]; }
@@ -537,20 +546,29 @@ hipError_t rmsnorm(const float* x, int T, int H, int ldx, const float* g, float 
   if (T <= 0) return hipSuccess;
   if (out == nullptr || H % 4 != 0 || H > 4096 || ldx % 4 != 0 || ldo % 4 != 0) return hipErrorInvalidValue;
   const int blocks = (T + 3) / 4;
+  // rows up to 1024 wide: four 16-byte chunks per lane, a quarter of the
+  // registers of the 4096-wide form and so four times the resident waves
+  const bool narrow = H <= 1024;
   if (lo_dt == DT_F8) {                                // bf16 value + fp8 remainder
     if (lo == nullptr || qs == nullptr || g == nullptr || out_dt != DT_BF16) return hipErrorInvalidValue;
-    rmsnorm_kernel<bf16, 16, 2><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, lo, ldo, qs);
+    if (narrow) rmsnorm_kernel<bf16, 4, 2><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, lo, ldo, qs);
+    else rmsnorm_kernel<bf16, 16, 2><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, lo, ldo, qs);
   } else if (qs != nullptr) {                          // fp8 activation rule
     if (lo != nullptr || g == nullptr) return hipErrorInvalidValue;
-    if (out_dt == DT_BF16)
+    if (out_dt == DT_BF16 && narrow)
+      rmsnorm_kernel<bf16, 4, 1><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, nullptr, ldo, qs);
+    else if (out_dt == DT_BF16)
       rmsnorm_kernel<bf16, 16, 1><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, nullptr, ldo, qs);
+    else if (out_dt == DT_F8 && narrow)
+      rmsnorm_kernel<uint8_t, 4, 1><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (uint8_t*)out, nullptr, ldo, qs);
     else if (out_dt == DT_F8)
       rmsnorm_kernel<uint8_t, 16, 1><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (uint8_t*)out, nullptr, ldo, qs);
     else
       return hipErrorInvalidValue;
-  } else if (out_dt == DT_BF16)
-    rmsnorm_kernel<bf16, 16, 0><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, lo, ldo, nullptr);
-  else if (lo == nullptr)
+  } else if (out_dt == DT_BF16) {
+    if (narrow) rmsnorm_kernel<bf16, 4, 0><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, lo, ldo, nullptr);
+    else rmsnorm_kernel<bf16, 16, 0><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (bf16*)out, lo, ldo, nullptr);
+  } else if (lo == nullptr)
     rmsnorm_kernel<float, 16, 0><<<blocks, 256, 0, s>>>(x, T, H, ldx, g, eps, (float*)out, nullptr, ldo, nullptr);
   else
     return hipErrorInvalidValue;
