@@ -146,7 +146,10 @@ typedef struct fs_model fs_model;
  * FS_DECODE_PERSIST=1 runs batch-1 decode steps of the 0.6B shape as one
  * persistent launch (all 256 CUs resident, workgroups exchanging activations
  * in memory; measured slower than the default, see fs_decode_trace);
- * FS_DECODE_TRACE=1 (with it) records the clock stamps fs_decode_trace reads. */
+ * FS_DECODE_TRACE=1 (with it) records the clock stamps fs_decode_trace reads;
+ * FS_PREFILL_FIXED_SHIFT=0 keeps the running-max softmax in the head_dim-128
+ * prefill attention (by default a layer whose q/k-norm score bound,
+ * log2(e) sqrt(d) max|g_q| max|g_k|, is at most 63 takes no softmax shift). */
 fs_status fs_model_create(const fs_config *cfg, const fs_weights *w,
                           void *stream, fs_model **out);
 
