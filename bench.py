@@ -564,6 +564,9 @@ def main():
                      "traffic": measured_traffic("decode." + dom), "avg_launch_us": round(avg_s * 1e6, 3),
                      "bytes_per_launch": int(bytes_launch)},
         "decode_us_per_launch": {k: round(v, 3) for k, v in per_launch.items()},
+        # the same graph-replayed chain with a kernel that does nothing: the
+        # dispatch cost each of the step's dependent launches pays
+        "decode_launch_floor_us": round(model.kernel_bench("empty", reps=20, slot=4, position=P + steps // 2), 3),
     }
 
     if not args.no_prefill:

@@ -1251,6 +1251,8 @@ fs_status fs_kernel_bench(fs_model* m, const char* label, int32_t slot, int32_t 
       HIP_TRY(attn_decode(a, ls));
     } else if (std::strcmp(label, "combine") == 0) {
       HIP_TRY(attn_combine(m->part, m->d_pos, 1, c.n_heads, c.head_dim, sp.chunk, sp.nchunks, m->attn, DT_F32, ls));
+    } else if (std::strcmp(label, "empty") == 0) {
+      HIP_TRY(empty_launch(256, ls));
     } else {
       return fail(FS_ERR_INVALID_ARG, std::string("unknown label ") + label);
     }

@@ -52,6 +52,8 @@ hipError_t rmsnorm_add(float* x, const float* parts, int np, int T, int H, int l
 hipError_t convert_f32(const void* src, int dt, float* dst, size_t n, hipStream_t s);
 // A one-wave kernel that waits about `us` microseconds of device wall clock.
 hipError_t spin_wait(int us, hipStream_t s);
+// `blocks` workgroups of 256 threads that do nothing (the launch floor)
+hipError_t empty_launch(int blocks, hipStream_t s);
 // Packs gate/up [I, H] into blocks of 32 gate rows followed by the matching 32 up rows.
 hipError_t pack_gate_up(const void* gate, const void* up, int dt, int I, int H, void* dst,
                         hipStream_t s);

@@ -630,6 +630,16 @@ hipError_t spin_wait(int us, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ launch floor
+// A kernel that does nothing: its launches measure the dispatch cost a chain
+// of dependent kernels pays per link.
+__global__ void empty_kernel() {}
+
+hipError_t empty_launch(int blocks, hipStream_t s) {
+  empty_kernel<<<blocks, 256, 0, s>>>();
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ gate/up packing
 template <typename W>
 __global__ void pack_gate_up_kernel(const W* __restrict__ gate, const W* __restrict__ up, int H,

@@ -352,7 +352,9 @@ fs_status fs_timing_read(fs_model *m, const char *label, double *total_ms, int64
 /* Measurement hook: average duration of one decode-shaped (batch 1) launch
  * of the kernel that implements `label` ("qkv", "attn", "attn_split",
  * "attn_onepass", "combine", "o_proj", "gate_up", "down" or "head"), as it
- * runs inside a decode step.  "attn" is the form of the decode attention a
+ * runs inside a decode step; "empty" launches a kernel of 256 workgroups that
+ * does nothing, in the same chain, so its figure is the per-launch floor the
+ * step's dependent kernels each pay.  "attn" is the form of the decode attention a
  * batch-1 step at this position takes (one pass over the whole context with
  * no merge launch for short contexts, split-K chunks plus the "combine"
  * merge otherwise); "attn_split" and "attn_onepass" force one form.  One launch per layer,
