@@ -568,6 +568,13 @@ def main():
         # dispatch cost each of the step's dependent launches pays
         "decode_launch_floor_us": round(model.kernel_bench("empty", reps=20, slot=4, position=P + steps // 2), 3),
     }
+    # the matrix unit on register operands only: the bf16 throughput the MFMA
+    # kernels could reach at best (for context beside the published peak)
+    mus = model.kernel_bench("mfma", reps=3, slot=4, position=P)
+    mflops = 2 * 32 * 32 * 16 * 4 * 2048 * 256 * 8
+    out["mfma_bf16_register_only"] = {"tflop_s": round(mflops / (mus * 1e-6) / 1e12, 1),
+                                      "frac_of_peak": round(mflops / (mus * 1e-6) / MFMA_BF16_PEAK, 4),
+                                      "us_per_launch": round(mus, 2)}
 
     if not args.no_prefill:
         pw = synth.workload("prefill_0p6b_4x4096")

@@ -1253,6 +1253,11 @@ fs_status fs_kernel_bench(fs_model* m, const char* label, int32_t slot, int32_t 
       HIP_TRY(attn_combine(m->part, m->d_pos, 1, c.n_heads, c.head_dim, sp.chunk, sp.nchunks, m->attn, DT_F32, ls));
     } else if (std::strcmp(label, "empty") == 0) {
       HIP_TRY(empty_launch(256, ls));
+    } else if (std::strcmp(label, "mfma") == 0) {
+      // 256 workgroups x 8 waves: their 2048 sums go to the split-K partial scratch
+      const size_t part_floats = (size_t)c.max_seqs * c.n_heads * m->max_chunks * (c.head_dim + 2);
+      if (part_floats < 256 * 8) return fail(FS_ERR_UNSUPPORTED, "model scratch too small for the mfma bench");
+      HIP_TRY(mfma_peak_launch(m->part, 256, MFMA_PEAK_ITERS, ls));
     } else {
       return fail(FS_ERR_INVALID_ARG, std::string("unknown label ") + label);
     }

@@ -54,6 +54,10 @@ hipError_t convert_f32(const void* src, int dt, float* dst, size_t n, hipStream_
 hipError_t spin_wait(int us, hipStream_t s);
 // `blocks` workgroups of 256 threads that do nothing (the launch floor)
 hipError_t empty_launch(int blocks, hipStream_t s);
+// `blocks` workgroups of 8 waves, each wave 4 * iters (iters even) 32x32x16 bf16
+// matrix instructions on registers; out gets blocks * 8 floats
+constexpr int MFMA_PEAK_ITERS = 2048;
+hipError_t mfma_peak_launch(float* out, int blocks, int iters, hipStream_t s);
 // Packs gate/up [I, H] into blocks of 32 gate rows followed by the matching 32 up rows.
 hipError_t pack_gate_up(const void* gate, const void* up, int dt, int I, int H, void* dst,
                         hipStream_t s);

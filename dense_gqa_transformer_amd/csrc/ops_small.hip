@@ -640,6 +640,42 @@ hipError_t empty_launch(int blocks, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ matrix-unit throughput
+// Each wave issues 4 * iters v_mfma_f32_32x32x16_bf16 on register operands (no
+// memory traffic), in eight independent accumulator chains: 8 waves per
+// workgroup, two per SIMD, one workgroup per CU.  Lane 0 of each wave stores
+// one sum so the products are kept.  2 * 32 * 32 * 16 * 4 * iters flops per wave.
+__global__ __launch_bounds__(512) void mfma_peak_kernel(float* __restrict__ out, int iters) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (bf16)(0.001f * (float)(lane + e));
+    b[e] = (bf16)(0.002f * (float)(lane - e));
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+#pragma unroll 4
+  for (int i = 0; i < iters; i += 2) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += acc[j][r];
+  if (lane == 0) out[blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = sum;
+}
+
+hipError_t mfma_peak_launch(float* out, int blocks, int iters, hipStream_t s) {
+  mfma_peak_kernel<<<blocks, 512, 0, s>>>(out, iters);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ gate/up packing
 template <typename W>
 __global__ void pack_gate_up_kernel(const W* __restrict__ gate, const W* __restrict__ up, int H,
