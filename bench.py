@@ -575,6 +575,14 @@ def main():
     out["mfma_bf16_register_only"] = {"tflop_s": round(mflops / (mus * 1e-6) / 1e12, 1),
                                       "frac_of_peak": round(mflops / (mus * 1e-6) / MFMA_BF16_PEAK, 4),
                                       "us_per_launch": round(mus, 2)}
+    # a plain streaming read of the stored matrices (bf16): the HBM rate a
+    # read-only kernel reaches, beside the published 8 TB/s
+    hus = model.kernel_bench("hbm", reps=3, slot=4, position=P)
+    wbytes = 2 * (shape.vocab * shape.hidden +
+                  shape.n_layers * sum(int(np.prod(s)) for s in shape.layer_shapes().values() if len(s) == 2))
+    out["hbm_read_stream"] = {"gb_s": round(wbytes / (hus * 1e-6) / 1e9, 1),
+                              "frac_of_peak": round(wbytes / (hus * 1e-6) / HBM_PEAK, 4),
+                              "bytes_per_launch": int(wbytes), "us_per_launch": round(hus, 2)}
 
     if not args.no_prefill:
         pw = synth.workload("prefill_0p6b_4x4096")

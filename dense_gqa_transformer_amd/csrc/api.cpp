@@ -117,6 +117,7 @@ struct fs_model {
   int wdt = 0;          // storage of the matrices: dt, or DT_I8 / DT_F8 (codes + row scales)
   // weights
   void* wblob = nullptr;
+  size_t wblob_bytes = 0;
   float* nblob = nullptr;
   float* sblob = nullptr;         // int8 row scales
   void* wconv = nullptr;          // bf16 copy of one layer matrix's codes (MFMA operand)
@@ -716,6 +717,7 @@ fs_status fs_model_create(const fs_config* cfg, const fs_weights* w, void* strea
     return fail(st, msg);
   };
   if (dalloc(&m->wblob, wbytes) != hipSuccess) return bail(FS_ERR_OOM, "weight allocation failed");
+  m->wblob_bytes = wbytes;
   if (dalloc(&m->nblob, nfloats * 4) != hipSuccess) return bail(FS_ERR_OOM, "norm allocation failed");
   if (q8) {
     if (dalloc(&m->sblob, sfloats * 4) != hipSuccess || dalloc(&pack_tmp, 2 * I * H * es) != hipSuccess)
@@ -1258,6 +1260,12 @@ fs_status fs_kernel_bench(fs_model* m, const char* label, int32_t slot, int32_t 
       const size_t part_floats = (size_t)c.max_seqs * c.n_heads * m->max_chunks * (c.head_dim + 2);
       if (part_floats < 256 * 8) return fail(FS_ERR_UNSUPPORTED, "model scratch too small for the mfma bench");
       HIP_TRY(mfma_peak_launch(m->part, 256, MFMA_PEAK_ITERS, ls));
+    } else if (std::strcmp(label, "hbm") == 0) {
+      // the whole weight allocation, once per launch; one word per workgroup
+      // to the split-K partial scratch
+      const size_t part_floats = (size_t)c.max_seqs * c.n_heads * m->max_chunks * (c.head_dim + 2);
+      if (part_floats < 2048) return fail(FS_ERR_UNSUPPORTED, "model scratch too small for the hbm bench");
+      HIP_TRY(hbm_read_launch(m->wblob, m->wblob_bytes / 16 * 16, reinterpret_cast<unsigned*>(m->part), 2048, ls));
     } else {
       return fail(FS_ERR_INVALID_ARG, std::string("unknown label ") + label);
     }

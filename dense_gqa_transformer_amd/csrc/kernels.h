@@ -57,6 +57,8 @@ hipError_t empty_launch(int blocks, hipStream_t s);
 // `blocks` workgroups of 8 waves, each wave 4 * iters (iters even) 32x32x16 bf16
 // matrix instructions on registers; out gets blocks * 8 floats
 constexpr int MFMA_PEAK_ITERS = 2048;
+// reads `bytes` (a multiple of 16) from p with 16-byte loads; out gets one word per block
+hipError_t hbm_read_launch(const void* p, size_t bytes, unsigned* out, int blocks, hipStream_t s);
 hipError_t mfma_peak_launch(float* out, int blocks, int iters, hipStream_t s);
 // Packs gate/up [I, H] into blocks of 32 gate rows followed by the matching 32 up rows.
 hipError_t pack_gate_up(const void* gate, const void* up, int dt, int I, int H, void* dst,

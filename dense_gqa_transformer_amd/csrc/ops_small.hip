@@ -671,6 +671,41 @@ __global__ __launch_bounds__(512) void mfma_peak_kernel(float* __restrict__ out,
   if (lane == 0) out[blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = sum;
 }
 
+// ------------------------------------------------------------------ HBM read rate
+// Reads n16 16-byte chunks with 16-byte loads (each thread 8 chunks in flight)
+// and stores one word per workgroup, so the loads are kept.
+__global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4* __restrict__ p, size_t n16,
+                                                       unsigned* __restrict__ out) {
+  // workgroup b reads the contiguous span [b, b + 1) * n16 / gridDim.x, each
+  // wave 8 consecutive 1 KB rows per round
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = (size_t)blockIdx.x * per, hi = lo + per < n16 ? lo + per : n16;
+  unsigned acc = 0;
+  for (size_t i0 = lo + threadIdx.x; i0 < hi; i0 += 8 * 256) {
+    u32x4 v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const size_t i = i0 + (size_t)t * 256;
+      v[t] = __builtin_nontemporal_load(p + (i < hi ? i : i0));
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc ^= v[t][0] ^ v[t][1] ^ v[t][2] ^ v[t][3];
+  }
+  __shared__ unsigned red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned a = 0;
+    for (int t = 0; t < 256; ++t) a ^= red[t];
+    out[blockIdx.x] = a;
+  }
+}
+
+hipError_t hbm_read_launch(const void* p, size_t bytes, unsigned* out, int blocks, hipStream_t s) {
+  hbm_read_kernel<<<blocks, 256, 0, s>>>(reinterpret_cast<const u32x4*>(p), bytes / 16, out);
+  return hipGetLastError();
+}
+
 hipError_t mfma_peak_launch(float* out, int blocks, int iters, hipStream_t s) {
   mfma_peak_kernel<<<blocks, 512, 0, s>>>(out, iters);
   return hipGetLastError();

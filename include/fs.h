@@ -357,7 +357,10 @@ fs_status fs_timing_read(fs_model *m, const char *label, double *total_ms, int64
  * step's dependent kernels each pay; "mfma" launches 256 workgroups of 8
  * waves, each wave 8192 32x32x16 bf16 matrix instructions on registers in
  * eight independent chains (2 * 32 * 32 * 16 * 8192 * 2048 flops per launch),
- * the matrix unit's own throughput.  "attn" is the form of the decode attention a
+ * the matrix unit's own throughput; "hbm" reads the model's whole allocation
+ * of matrices (embedding / head and every layer's projections, as stored)
+ * once per launch with 16-byte loads, the HBM read rate a streaming kernel
+ * reaches.  "attn" is the form of the decode attention a
  * batch-1 step at this position takes (one pass over the whole context with
  * no merge launch for short contexts, split-K chunks plus the "combine"
  * merge otherwise); "attn_split" and "attn_onepass" force one form.  One launch per layer,

@@ -502,7 +502,7 @@ def test_kernel_bench_hook_leaves_decode_intact(big):
     toks = synth.tokens(57, shape.vocab, (1, 33))
     ref = model.prefill(dev_tokens(toks), [0]).cpu().numpy()[0]
     for lab in ("qkv", "attn", "attn_split", "attn_onepass", "combine", "o_proj", "gate_up", "down", "head",
-                "empty", "mfma"):
+                "empty", "mfma", "hbm"):
         us = model.kernel_bench(lab, reps=2, slot=5, position=100)
         assert 0.0 < us < 10000.0, lab
     from dense_gqa_transformer_amd import native
